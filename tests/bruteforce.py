@@ -1,0 +1,98 @@
+"""Dense brute-force decode attention in numpy/scipy float64, for tiny inputs only.
+
+Written independently of the C oracle: it gathers every sequence's logical
+K/V rows with numpy fancy indexing (the int8 tier through a little-endian byte
+view of the packed words), builds the full boolean visibility matrix over
+[0, L) with vectorised comparisons, and takes the softmax and log-sum-exp
+from scipy.special.  It is the reference the oracle is pinned against.
+"""
+from __future__ import annotations
+
+import numpy as np
+from scipy.special import logsumexp, softmax
+
+
+def scale_of(p):
+    return float(p["scale"]) if p["scale"] != 0.0 else float(np.float32(1.0 / np.sqrt(p["head_dim"])))
+
+
+def logical_rows(case, b):
+    """float64 K, V of sequence b: [L, Hkv, D]."""
+    p = case.params
+    L = int(case.seq_lens[b])
+    bs = p["block_size"]
+    t = np.arange(L)
+    if case.kind in ("paged", "sparse"):
+        blk = case.block_table[b, t // bs]
+        K = case.k_cache[blk, t % bs].astype(np.float64)
+        V = case.v_cache[blk, t % bs].astype(np.float64)
+        return K, V
+    # tiered
+    Hkv, D = p["num_kv_heads"], p["head_dim"]
+    c = int(case.cold_lens[b])
+    K = np.empty((L, Hkv, D))
+    V = np.empty((L, Hkv, D))
+    tc = t[:c]
+    blk = case.cold_block_table[b, tc // bs]
+    kb = np.ascontiguousarray(case.k_cold[blk, tc % bs]).view("<i1").reshape(c, Hkv, D).astype(np.float64)
+    vb = np.ascontiguousarray(case.v_cold[blk, tc % bs]).view("<i1").reshape(c, Hkv, D).astype(np.float64)
+    K[:c] = kb * case.k_scale[blk, tc % bs].astype(np.float64)[..., None]
+    V[:c] = vb * case.v_scale[blk, tc % bs].astype(np.float64)[..., None]
+    th = t[c:]
+    K[c:] = case.k_hot[b, th % case.hot_window].astype(np.float64)
+    V[c:] = case.v_hot[b, th % case.hot_window].astype(np.float64)
+    return K, V
+
+
+def visible_matrix(case, b):
+    """bool [H, L]: which keys each query head of sequence b attends to."""
+    p = case.params
+    H = p["num_heads"]
+    L = int(case.seq_lens[b])
+    q = int(case.q_pos[b]) if case.q_pos is not None else L - 1
+    t = np.arange(L)
+    ok = np.ones(L, bool)
+    if p["causal"]:
+        ok &= t <= q
+    W = p["sliding_window"]
+    if W > 0 and q >= W:
+        ok &= t >= q - W + 1
+    vis = np.repeat(ok[None, :], H, axis=0)
+    if case.kind == "sparse":
+        SB = case.sparse_block
+        r = q // SB
+        for h in range(H):
+            l = h % case.num_layouts
+            cols = case.col_idx[l, case.row_ptr[l, r]:case.row_ptr[l, r + 1]]
+            chosen = np.zeros(max(1, (L + SB - 1) // SB), bool)
+            cols = cols[(cols >= 0) & (cols <= r) & (cols < chosen.size)]
+            chosen[cols] = True
+            vis[h] &= chosen[t // SB]
+    return vis
+
+
+def attend(case):
+    """(out [B, H, D], lse [B, H]) in float64."""
+    p = case.params
+    B, H, Hkv, D = p["num_seqs"], p["num_heads"], p["num_kv_heads"], p["head_dim"]
+    G = H // Hkv
+    sc = scale_of(p)
+    cap = float(p["softcap"])
+    out = np.zeros((B, H, D))
+    lse = np.full((B, H), -np.inf)
+    for b in range(B):
+        K, V = logical_rows(case, b)
+        vis = visible_matrix(case, b)
+        qb = case.q[b].astype(np.float64)                     # [H, D]
+        Kh = np.repeat(K, G, axis=1).transpose(1, 0, 2)       # [H, L, D]
+        Vh = np.repeat(V, G, axis=1).transpose(1, 0, 2)
+        s = sc * np.einsum("hd,hld->hl", qb, Kh)
+        if cap > 0:
+            s = cap * np.tanh(s / cap)
+        for h in range(H):
+            if not vis[h].any():
+                continue
+            sv = s[h][vis[h]]
+            out[b, h] = softmax(sv) @ Vh[h][vis[h]]
+            lse[b, h] = logsumexp(sv)
+    return out, lse
