@@ -1,0 +1,164 @@
+/*
+ * dattn.h -- C ABI of the MI355X (gfx950) split-KV decode-attention library.
+ *
+ * One query token per sequence ("decode"), grouped-query attention (GQA):
+ * query head h reads kv head h / (num_heads / num_kv_heads)
+ * (doppler attention_decode_tiered_int8_f16kv.wgsl, get_kv_head_idx).
+ * For every sequence b and query head h the library computes
+ *
+ *     out[b,h,:] = sum_t softmax_t(s_t) * v_t          lse[b,h] = ln sum_t e^{s_t}
+ *     s_t        = softcap(scale * <q[b,h,:], k_t>)    over the visible keys t
+ *
+ * with softcap(x) = cap * tanh(x / cap) when cap > 0 (applied after scaling and
+ * before masking, the order of the doppler kernels' score loop).  Visible keys
+ * are t in [0, seq_lens[b]) that survive the masks of doppler's is_masked:
+ * with causal, keys t > q are dropped; with a window W > 0, keys t < q-W+1 are
+ * dropped once q >= W.  q is the query's absolute position: q_pos[b], or
+ * seq_lens[b]-1 when q_pos is NULL.  A query with no visible key gets out = 0
+ * and lse = -inf.  lse is the natural log-sum-exp of the capped scores
+ * (boostr paged_attention.wgsl, paged_attention_fwd_f32's lse output).
+ *
+ * Conventions shared by every entry point
+ *   - All array arguments are DEVICE pointers on the current HIP device,
+ *     C-contiguous, owned by the caller; the library keeps no reference after
+ *     the call returns and allocates no device memory.
+ *   - Work is enqueued on `stream` (a hipStream_t passed as void*, NULL = the
+ *     null stream) and is asynchronous: outputs are valid once the stream has
+ *     reached the enqueued work.  No host synchronisation happens inside.
+ *   - Scratch memory for the split partials is the caller's `workspace`
+ *     (size from dattn_workspace_size, 256-byte aligned).
+ *   - Every argument the host can see is validated before any HIP call; on
+ *     failure nothing is enqueued and a negative code is returned, with a
+ *     message available from dattn_last_error() on the calling thread.
+ *   - Device-side contents are NOT validated: block-table entries a visible
+ *     token needs must lie in [0, num_blocks), seq_lens[b] <= max_seq_len,
+ *     q_pos[b] >= 0, cold_lens[b] <= seq_lens[b], seq_lens[b]-cold_lens[b] <=
+ *     hot_window.  Breaking these is undefined behaviour.
+ *   - Concurrent calls on different streams are safe if their workspaces and
+ *     outputs do not overlap.
+ */
+#ifndef DATTN_H
+#define DATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* return codes */
+#define DATTN_OK 0
+#define DATTN_ERR_INVALID (-1)     /* an argument is out of range or inconsistent */
+#define DATTN_ERR_UNSUPPORTED (-2) /* valid but not built: head_dim, GQA group, sizes */
+#define DATTN_ERR_WORKSPACE (-3)   /* workspace NULL, misaligned or too small */
+#define DATTN_ERR_LAUNCH (-4)      /* a HIP call failed; see dattn_last_error() */
+
+/* storage type of the paged K/V pool */
+#define DATTN_F32 0
+#define DATTN_F16 1
+
+/* entry-point kinds, for dattn_workspace_size */
+#define DATTN_KIND_PAGED 0
+#define DATTN_KIND_TIERED_INT8 1
+#define DATTN_KIND_BLOCK_SPARSE 2
+
+/*
+ * Scalar parameters (doppler attention_f16kv.wgsl Uniforms and boostr
+ * PagedParams; doppler attention.js executeAttentionTieredQuant defaults).
+ */
+typedef struct dattn_params {
+  int32_t num_seqs;           /* B >= 0 (0 enqueues nothing) */
+  int32_t num_heads;          /* H >= 1 query heads */
+  int32_t num_kv_heads;       /* Hkv >= 1, H % Hkv == 0; G = H/Hkv in {1,2,4,8,16} */
+  int32_t head_dim;           /* D in {64, 128} */
+  float scale;                /* score scale; 0 => 1/sqrt(D) rounded to f32 */
+  int32_t causal;             /* 0 or 1 */
+  int32_t sliding_window;     /* W >= 0; 0 => no window */
+  float softcap;              /* cap; <= 0 => no softcap */
+  int32_t block_size;         /* tokens per physical block, >= 1 */
+  int32_t max_blocks_per_seq; /* row stride of the block table, >= 1 */
+  int32_t num_blocks;         /* physical blocks in the pool, >= 1 */
+  int32_t max_seq_len;        /* host-known upper bound of seq_lens[], >= 0; sizes the grid */
+  int32_t split_tokens;       /* keys per KV split; 0 => library choice, else a multiple of 16 */
+} dattn_params;
+
+/*
+ * Workspace bytes a call of `kind` with these parameters needs.
+ * sparse_block is read only for DATTN_KIND_BLOCK_SPARSE.
+ * Returns DATTN_OK and writes *bytes, or a negative code.
+ */
+int dattn_workspace_size(const dattn_params* p, int32_t kind, int32_t sparse_block, size_t* bytes);
+
+/*
+ * Paged cache (boostr paged_attention.wgsl: token t of sequence b lives in
+ * physical block block_table[b][t / block_size] at offset t % block_size).
+ *   q            [B, H, D] f32
+ *   k_cache,
+ *   v_cache      [num_blocks, block_size, Hkv, D], f32 or f16 per kv_dtype
+ *   block_table  [B, max_blocks_per_seq] i32
+ *   seq_lens     [B] i32
+ *   q_pos        [B] i32, or NULL for seq_lens[b]-1
+ *   out          [B, H, D] f32 (written)
+ *   lse          [B, H] f32 (written), or NULL
+ */
+int dattn_decode_paged(const dattn_params* p, const float* q, const void* k_cache, const void* v_cache,
+                       int32_t kv_dtype, const int32_t* block_table, const int32_t* seq_lens,
+                       const int32_t* q_pos, float* out, float* lse, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+/*
+ * Tiered cache (doppler attention_decode_tiered_int8_f16kv.wgsl and
+ * attention.js executeAttentionTieredQuant / executeAttentionTiered):
+ * tokens t < cold_lens[b] are int8 in a paged cold pool, tokens
+ * t >= cold_lens[b] are f16 in a per-sequence ring at slot t % hot_window.
+ *   k_hot, v_hot          [B, hot_window, Hkv, D] f16 (bit patterns)
+ *   hot_window            ring slots, >= 1
+ *   k_cold, v_cold        [num_blocks, block_size, Hkv, D/4] u32; element d of a
+ *                         row is byte d%4 of word d/4, least-significant byte
+ *                         first, two's complement (read_cold_k / read_cold_v)
+ *   k_scale, v_scale      [num_blocks, block_size, Hkv] f16 (bit patterns);
+ *                         the value of element d is int8 * f32(scale)
+ *   cold_block_table      [B, max_blocks_per_seq] i32 (block_size, num_blocks and
+ *                         max_blocks_per_seq in p describe the cold pool)
+ *   seq_lens, cold_lens   [B] i32
+ *   q_pos, out, lse       as for dattn_decode_paged
+ */
+int dattn_decode_tiered_int8(const dattn_params* p, const float* q, const uint16_t* k_hot,
+                             const uint16_t* v_hot, int32_t hot_window, const uint32_t* k_cold,
+                             const uint32_t* v_cold, const uint16_t* k_scale, const uint16_t* v_scale,
+                             const int32_t* cold_block_table, const int32_t* seq_lens, const int32_t* cold_lens,
+                             const int32_t* q_pos, float* out, float* lse, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/*
+ * Block-sparse selection over the paged f16 cache (com.microsoft.SparseAttention
+ * sparse-attention.wgsl.jinja, attention pass): head h uses CSR layout
+ * h % num_layouts; row r = q / sparse_block lists the sparse blocks (of
+ * sparse_block consecutive keys) the query may see; columns > r are ignored
+ * and a repeated column counts once.  Keys inside a chosen block still pass
+ * the causal / window masks.
+ *   sparse_block  keys per sparse block, a multiple of block_size
+ *   row_ptr       [num_layouts, row_stride] i32, row_stride = rows + 1
+ *   col_idx       [num_layouts, col_stride] i32
+ *   other arrays  as for dattn_decode_paged with kv_dtype = DATTN_F16
+ * Needs q / sparse_block < row_stride - 1 (rows beyond select nothing).
+ */
+int dattn_decode_block_sparse(const dattn_params* p, const float* q, const uint16_t* k_cache,
+                              const uint16_t* v_cache, const int32_t* block_table, const int32_t* seq_lens,
+                              const int32_t* q_pos, int32_t sparse_block, int32_t num_layouts,
+                              const int32_t* row_ptr, int32_t row_stride, const int32_t* col_idx,
+                              int32_t col_stride, float* out, float* lse, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/* Message for the last non-zero return on this thread ("" if none). */
+const char* dattn_last_error(void);
+
+/* Library version string. */
+const char* dattn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DATTN_H */

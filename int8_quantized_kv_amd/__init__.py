@@ -1,0 +1,277 @@
+"""Split-KV decode attention for MI355X (gfx950): Python binding of libdattn.so.
+
+The functions here have the names of the C entry points in include/dattn.h and
+only marshal arguments: they check tensor dtypes, devices and shapes, fill the
+``dattn_params`` struct, allocate the caller-side outputs and workspace with
+torch when the caller did not pass them, and call the library on torch's
+current HIP stream.  Every step of the attention runs in the HIP kernels; when
+the library is missing, loading fails with an error instead of falling back.
+
+Cache layouts (C-contiguous):
+  q                 [B, H, D]                  float32
+  k_cache, v_cache  [num_blocks, bs, Hkv, D]   float16 or float32
+  block_table       [B, max_blocks]            int32
+  seq_lens, q_pos   [B]                        int32
+  k_hot, v_hot      [B, hot_window, Hkv, D]    float16
+  k_cold, v_cold    [num_blocks, bs, Hkv, D/4] int32/uint32 words of 4 int8, LSB first
+  k_scale, v_scale  [num_blocks, bs, Hkv]      float16
+  row_ptr           [num_layouts, rows + 1]    int32
+  col_idx           [num_layouts, col_stride]  int32
+Outputs: out [B, H, D] float32, lse [B, H] float32.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+__all__ = [
+    "DattnError", "DattnParams", "lib", "library_path", "dattn_workspace_size", "dattn_decode_paged",
+    "dattn_decode_tiered_int8", "dattn_decode_block_sparse", "dattn_last_error", "dattn_version",
+    "KIND_PAGED", "KIND_TIERED_INT8", "KIND_BLOCK_SPARSE", "F32", "F16",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libdattn.so")
+
+OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_LAUNCH = 0, -1, -2, -3, -4
+F32, F16 = 0, 1
+KIND_PAGED, KIND_TIERED_INT8, KIND_BLOCK_SPARSE = 0, 1, 2
+
+
+class DattnParams(ctypes.Structure):
+    """Mirror of ``dattn_params`` in include/dattn.h."""
+    _fields_ = [
+        ("num_seqs", ctypes.c_int32),
+        ("num_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("causal", ctypes.c_int32),
+        ("sliding_window", ctypes.c_int32),
+        ("softcap", ctypes.c_float),
+        ("block_size", ctypes.c_int32),
+        ("max_blocks_per_seq", ctypes.c_int32),
+        ("num_blocks", ctypes.c_int32),
+        ("max_seq_len", ctypes.c_int32),
+        ("split_tokens", ctypes.c_int32),
+    ]
+
+
+class DattnError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"dattn error {code}: {message}")
+        self.code = code
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libdattn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(library_path):
+            raise ImportError(f"{library_path} is missing: build it first (int8_quantized_kv_amd.build)")
+        L = ctypes.CDLL(library_path)
+        P, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        PP = ctypes.POINTER(DattnParams)
+        L.dattn_last_error.restype = ctypes.c_char_p
+        L.dattn_version.restype = ctypes.c_char_p
+        L.dattn_workspace_size.argtypes = [PP, i32, i32, ctypes.POINTER(sz)]
+        L.dattn_decode_paged.argtypes = [PP, P, P, P, i32, P, P, P, P, P, P, sz, P]
+        L.dattn_decode_tiered_int8.argtypes = [PP, P, P, P, i32, P, P, P, P, P, P, P, P, P, P, P, sz, P]
+        L.dattn_decode_block_sparse.argtypes = [PP, P, P, P, P, P, P, i32, i32, P, i32, P, i32, P, P, P, sz, P]
+        for f in (L.dattn_workspace_size, L.dattn_decode_paged, L.dattn_decode_tiered_int8,
+                  L.dattn_decode_block_sparse):
+            f.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def dattn_last_error() -> str:
+    return lib().dattn_last_error().decode()
+
+
+def dattn_version() -> str:
+    return lib().dattn_version().decode()
+
+
+def _check(rc: int):
+    if rc != OK:
+        raise DattnError(rc, dattn_last_error())
+
+
+def dattn_workspace_size(params: DattnParams, kind: int, sparse_block: int = 0) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().dattn_workspace_size(ctypes.byref(params), kind, sparse_block, ctypes.byref(n)))
+    return int(n.value)
+
+
+# ------------------------------------------------------------ torch side
+
+def _torch():
+    import torch
+    return torch
+
+
+def _need(t, name, dtypes, ndim, device):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} must have dtype in {dtypes}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    return t
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _params(q, Hkv, D, bs, max_blocks, num_blocks, max_seq_len, scale, causal, sliding_window, softcap,
+            split_tokens):
+    B, H, _ = q.shape
+    return DattnParams(B, H, Hkv, D, float(scale), int(causal), int(sliding_window), float(softcap), bs, max_blocks,
+                       num_blocks, int(max_seq_len), int(split_tokens))
+
+
+def _outputs(q, out, lse, want_lse, workspace, ws_bytes):
+    torch = _torch()
+    B, H, D = q.shape
+    if out is None:
+        out = torch.empty((B, H, D), dtype=torch.float32, device=q.device)
+    else:
+        _need(out, "out", (torch.float32,), 3, q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    elif lse is not None:
+        _need(lse, "lse", (torch.float32,), 2, q.device)
+    if workspace is None:
+        workspace = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device=q.device)
+    return out, lse, workspace
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _max_len(seq_lens, max_seq_len):
+    if max_seq_len is None:
+        max_seq_len = int(seq_lens.max().item()) if seq_lens.numel() else 0  # synchronises
+    return max_seq_len
+
+
+def dattn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, *, q_pos=None, scale: float = 0.0,
+                       causal: bool = True, sliding_window: int = 0, softcap: float = 0.0,
+                       max_seq_len: Optional[int] = None, split_tokens: int = 0, out=None, lse=None,
+                       want_lse: bool = True, workspace=None, stream=None):
+    """Decode attention over a paged f16/f32 cache; returns (out, lse)."""
+    torch = _torch()
+    dev = q.device
+    _need(q, "q", (torch.float32,), 3, dev)
+    _need(k_cache, "k_cache", (torch.float16, torch.float32), 4, dev)
+    _need(v_cache, "v_cache", (k_cache.dtype,), 4, dev)
+    _need(block_table, "block_table", (torch.int32,), 2, dev)
+    _need(seq_lens, "seq_lens", (torch.int32,), 1, dev)
+    if q_pos is not None:
+        _need(q_pos, "q_pos", (torch.int32,), 1, dev)
+    NB, bs, Hkv, D = k_cache.shape
+    if tuple(v_cache.shape) != tuple(k_cache.shape) or q.shape[2] != D:
+        raise ValueError("k_cache, v_cache and q disagree on shape")
+    if block_table.shape[0] != q.shape[0] or seq_lens.shape[0] != q.shape[0]:
+        raise ValueError("block_table / seq_lens must have one row per sequence")
+    p = _params(q, Hkv, D, bs, block_table.shape[1], NB, _max_len(seq_lens, max_seq_len), scale, causal,
+                sliding_window, softcap, split_tokens)
+    ws = dattn_workspace_size(p, KIND_PAGED)
+    out, lse, workspace = _outputs(q, out, lse, want_lse, workspace, ws)
+    kv_dtype = F16 if k_cache.dtype == torch.float16 else F32
+    _check(lib().dattn_decode_paged(ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(v_cache), kv_dtype,
+                                    _ptr(block_table), _ptr(seq_lens), _ptr(q_pos), _ptr(out), _ptr(lse),
+                                    _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out, lse
+
+
+def dattn_decode_tiered_int8(q, k_hot, v_hot, k_cold, v_cold, k_scale, v_scale, cold_block_table, seq_lens,
+                             cold_lens, *, q_pos=None, scale: float = 0.0, causal: bool = True,
+                             sliding_window: int = 0, softcap: float = 0.0, max_seq_len: Optional[int] = None,
+                             split_tokens: int = 0, out=None, lse=None, want_lse: bool = True, workspace=None,
+                             stream=None):
+    """Decode attention over an int8 cold pool + f16 hot ring; returns (out, lse)."""
+    torch = _torch()
+    dev = q.device
+    _need(q, "q", (torch.float32,), 3, dev)
+    _need(k_hot, "k_hot", (torch.float16,), 4, dev)
+    _need(v_hot, "v_hot", (torch.float16,), 4, dev)
+    _need(k_cold, "k_cold", (torch.int32, torch.uint32), 4, dev)
+    _need(v_cold, "v_cold", (k_cold.dtype,), 4, dev)
+    _need(k_scale, "k_scale", (torch.float16,), 3, dev)
+    _need(v_scale, "v_scale", (torch.float16,), 3, dev)
+    _need(cold_block_table, "cold_block_table", (torch.int32,), 2, dev)
+    _need(seq_lens, "seq_lens", (torch.int32,), 1, dev)
+    _need(cold_lens, "cold_lens", (torch.int32,), 1, dev)
+    if q_pos is not None:
+        _need(q_pos, "q_pos", (torch.int32,), 1, dev)
+    B, H, D = q.shape
+    _, hot_window, Hkv, Dh = k_hot.shape
+    NB, bs, Hkv2, W4 = k_cold.shape
+    if Dh != D or Hkv2 != Hkv or W4 * 4 != D or tuple(v_hot.shape) != tuple(k_hot.shape) \
+            or tuple(v_cold.shape) != tuple(k_cold.shape) or tuple(k_scale.shape) != (NB, bs, Hkv) \
+            or tuple(v_scale.shape) != (NB, bs, Hkv) or k_hot.shape[0] != B:
+        raise ValueError("tiered cache tensors disagree on shape")
+    p = _params(q, Hkv, D, bs, cold_block_table.shape[1], NB, _max_len(seq_lens, max_seq_len), scale, causal,
+                sliding_window, softcap, split_tokens)
+    ws = dattn_workspace_size(p, KIND_TIERED_INT8)
+    out, lse, workspace = _outputs(q, out, lse, want_lse, workspace, ws)
+    _check(lib().dattn_decode_tiered_int8(ctypes.byref(p), _ptr(q), _ptr(k_hot), _ptr(v_hot), hot_window,
+                                          _ptr(k_cold), _ptr(v_cold), _ptr(k_scale), _ptr(v_scale),
+                                          _ptr(cold_block_table), _ptr(seq_lens), _ptr(cold_lens), _ptr(q_pos),
+                                          _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
+                                          _stream(stream)))
+    return out, lse
+
+
+def dattn_decode_block_sparse(q, k_cache, v_cache, block_table, seq_lens, sparse_block: int, row_ptr, col_idx, *,
+                              q_pos=None, scale: float = 0.0, causal: bool = True, sliding_window: int = 0,
+                              softcap: float = 0.0, max_seq_len: Optional[int] = None, split_tokens: int = 0,
+                              out=None, lse=None, want_lse: bool = True, workspace=None, stream=None):
+    """Decode attention over the paged f16 cache restricted by per-head CSR block masks."""
+    torch = _torch()
+    dev = q.device
+    _need(q, "q", (torch.float32,), 3, dev)
+    _need(k_cache, "k_cache", (torch.float16,), 4, dev)
+    _need(v_cache, "v_cache", (torch.float16,), 4, dev)
+    _need(block_table, "block_table", (torch.int32,), 2, dev)
+    _need(seq_lens, "seq_lens", (torch.int32,), 1, dev)
+    _need(row_ptr, "row_ptr", (torch.int32,), 2, dev)
+    _need(col_idx, "col_idx", (torch.int32,), 2, dev)
+    if q_pos is not None:
+        _need(q_pos, "q_pos", (torch.int32,), 1, dev)
+    NB, bs, Hkv, D = k_cache.shape
+    if row_ptr.shape[0] != col_idx.shape[0]:
+        raise ValueError("row_ptr and col_idx must have one row per layout")
+    p = _params(q, Hkv, D, bs, block_table.shape[1], NB, _max_len(seq_lens, max_seq_len), scale, causal,
+                sliding_window, softcap, split_tokens)
+    ws = dattn_workspace_size(p, KIND_BLOCK_SPARSE, sparse_block)
+    out, lse, workspace = _outputs(q, out, lse, want_lse, workspace, ws)
+    _check(lib().dattn_decode_block_sparse(ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                           _ptr(block_table), _ptr(seq_lens), _ptr(q_pos), int(sparse_block),
+                                           row_ptr.shape[0], _ptr(row_ptr), row_ptr.shape[1], _ptr(col_idx),
+                                           col_idx.shape[1], _ptr(out), _ptr(lse), _ptr(workspace),
+                                           workspace.numel(), _stream(stream)))
+    return out, lse
+
+
+def default_scale(head_dim: int) -> float:
+    """1/sqrt(head_dim) rounded to f32, the value scale=0 selects."""
+    import struct
+    return struct.unpack("f", struct.pack("f", 1.0 / math.sqrt(head_dim)))[0]

@@ -1,0 +1,333 @@
+// dattn.hip -- host side of the C ABI declared in include/dattn.h:
+// argument validation (before any HIP call), split planning, workspace
+// layout and the two launches (split kernel, combine kernel) on the caller's
+// stream.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "dattn.h"
+#include "decode_kernels.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+
+struct Plan {
+  int G = 0;
+  int split_tokens = 0;  // keys (or sparse slots) per split
+  int num_splits = 0;
+  int blocks_per_split = 0;  // sparse
+  int sparse_nblk = 0;       // sparse
+  int waves = 0;             // kv heads per workgroup
+  size_t lds = 0;
+  size_t acc_bytes = 0, ml_bytes = 0;
+  size_t workspace = 0;
+};
+
+int check_params(const dattn_params* p, int kind) {
+  if (!p) return fail(DATTN_ERR_INVALID, "params is NULL");
+  if (p->num_seqs < 0) return fail(DATTN_ERR_INVALID, "num_seqs must be >= 0 (got %d)", p->num_seqs);
+  if (p->num_seqs > 65535) return fail(DATTN_ERR_UNSUPPORTED, "num_seqs above 65535 is not supported");
+  if (p->num_heads < 1 || p->num_kv_heads < 1)
+    return fail(DATTN_ERR_INVALID, "num_heads and num_kv_heads must be >= 1 (got %d, %d)", p->num_heads,
+                p->num_kv_heads);
+  if (p->num_heads % p->num_kv_heads)
+    return fail(DATTN_ERR_INVALID, "num_heads (%d) must be a multiple of num_kv_heads (%d)", p->num_heads,
+                p->num_kv_heads);
+  const int G = p->num_heads / p->num_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8)
+    return fail(DATTN_ERR_UNSUPPORTED, "GQA group size %d not built (1, 2, 4, 8)", G);
+  if (p->head_dim != 64 && p->head_dim != 128)
+    return fail(DATTN_ERR_UNSUPPORTED, "head_dim %d not built (64, 128)", p->head_dim);
+  if (!isfinite(p->scale)) return fail(DATTN_ERR_INVALID, "scale must be finite");
+  if (!isfinite(p->softcap)) return fail(DATTN_ERR_INVALID, "softcap must be finite");
+  if (p->causal != 0 && p->causal != 1) return fail(DATTN_ERR_INVALID, "causal must be 0 or 1 (got %d)", p->causal);
+  if (p->sliding_window < 0) return fail(DATTN_ERR_INVALID, "sliding_window must be >= 0 (got %d)", p->sliding_window);
+  if (p->block_size < 1) return fail(DATTN_ERR_INVALID, "block_size must be >= 1 (got %d)", p->block_size);
+  if (p->max_blocks_per_seq < 1)
+    return fail(DATTN_ERR_INVALID, "max_blocks_per_seq must be >= 1 (got %d)", p->max_blocks_per_seq);
+  if (p->num_blocks < 1) return fail(DATTN_ERR_INVALID, "num_blocks must be >= 1 (got %d)", p->num_blocks);
+  if ((int64_t)p->num_blocks * p->block_size > INT32_MAX)
+    return fail(DATTN_ERR_UNSUPPORTED, "num_blocks * block_size must fit in int32");
+  if (p->max_seq_len < 0) return fail(DATTN_ERR_INVALID, "max_seq_len must be >= 0 (got %d)", p->max_seq_len);
+  // the tiered table maps only the cold prefix, which can be shorter than max_seq_len
+  if (kind != DATTN_KIND_TIERED_INT8 && (int64_t)p->max_seq_len > (int64_t)p->max_blocks_per_seq * p->block_size)
+    return fail(DATTN_ERR_INVALID, "max_seq_len %d exceeds max_blocks_per_seq * block_size (%lld)", p->max_seq_len,
+                (long long)p->max_blocks_per_seq * p->block_size);
+  if (p->max_seq_len > (1 << 30)) return fail(DATTN_ERR_UNSUPPORTED, "max_seq_len above 2^30 is not supported");
+  if (p->split_tokens < 0 || p->split_tokens % 16)
+    return fail(DATTN_ERR_INVALID, "split_tokens must be 0 or a positive multiple of 16 (got %d)", p->split_tokens);
+  return DATTN_OK;
+}
+
+// Keys per split: aim for 2k..8k busy wavefronts (256 CUs) with splits of
+// 64..4096 keys, unless the caller fixed it.
+int choose_split(const dattn_params* p, int64_t units_per_seq_span) {
+  if (p->split_tokens > 0) return p->split_tokens;
+  const int64_t pairs = (int64_t)p->num_seqs * p->num_kv_heads;
+  const int64_t span = units_per_seq_span > 0 ? units_per_seq_span : 1;
+  int T = 256;
+  while (T < 4096 && pairs * ((span + T - 1) / T) > 8192) T *= 2;
+  while (T > 64 && pairs * ((span + T - 1) / T) < 2048) T /= 2;
+  return T;
+}
+
+int waves_per_group(int Hkv) {
+  if (Hkv % 4 == 0) return 4;
+  if (Hkv % 2 == 0) return 2;
+  return 1;
+}
+
+int make_plan(const dattn_params* p, int kind, int32_t sparse_block, Plan& pl) {
+  int rc = check_params(p, kind);
+  if (rc) return rc;
+  pl.G = p->num_heads / p->num_kv_heads;
+  pl.waves = waves_per_group(p->num_kv_heads);
+  const int64_t L = p->max_seq_len;
+  if (kind == DATTN_KIND_PAGED || kind == DATTN_KIND_TIERED_INT8) {
+    pl.split_tokens = choose_split(p, L);
+    pl.num_splits = (int)((L + pl.split_tokens - 1) / pl.split_tokens);
+    if (pl.num_splits < 1) pl.num_splits = 1;
+    pl.lds = ((size_t)pl.split_tokens / p->block_size + 2) * sizeof(int32_t);
+  } else if (kind == DATTN_KIND_BLOCK_SPARSE) {
+    if (sparse_block < 1 || sparse_block % p->block_size)
+      return fail(DATTN_ERR_INVALID, "sparse_block (%d) must be a positive multiple of block_size (%d)", sparse_block,
+                  p->block_size);
+    if (sparse_block > 65535) return fail(DATTN_ERR_UNSUPPORTED, "sparse_block above 65535 is not supported");
+    const int64_t nb = (L + sparse_block - 1) / sparse_block;
+    if (nb > 8192) return fail(DATTN_ERR_UNSUPPORTED, "more than 8192 sparse blocks per sequence is not supported");
+    pl.sparse_nblk = (int)(nb > 0 ? nb : 1);
+    pl.split_tokens = choose_split(p, nb * sparse_block / 2);  // about half the blocks are selected
+    pl.blocks_per_split = pl.split_tokens / sparse_block > 0 ? pl.split_tokens / sparse_block : 1;
+    pl.num_splits = (int)((pl.sparse_nblk + pl.blocks_per_split - 1) / pl.blocks_per_split);
+    while (pl.waves > 1 && (size_t)pl.waves * 2 * pl.sparse_nblk * 4 > 65536) pl.waves /= 2;
+    pl.lds = (size_t)pl.waves * 2 * pl.sparse_nblk * sizeof(uint32_t);
+  } else {
+    return fail(DATTN_ERR_INVALID, "unknown kind %d", kind);
+  }
+  if (pl.lds > 65536) return fail(DATTN_ERR_UNSUPPORTED, "LDS need %zu exceeds 64 KiB", pl.lds);
+  const size_t heads = (size_t)p->num_seqs * p->num_heads;
+  pl.acc_bytes = align_up(heads * pl.num_splits * p->head_dim * sizeof(float));
+  pl.ml_bytes = align_up(heads * pl.num_splits * sizeof(float2));
+  pl.workspace = pl.acc_bytes + pl.ml_bytes;
+  return DATTN_OK;
+}
+
+dattn::DecodeArgs base_args(const dattn_params* p, const Plan& pl, const float* q, void* ws) {
+  dattn::DecodeArgs a{};
+  a.q = q;
+  a.part_acc = (float*)ws;
+  a.part_ml = (float2*)((char*)ws + pl.acc_bytes);
+  a.num_heads = p->num_heads;
+  a.num_kv_heads = p->num_kv_heads;
+  a.max_blocks = p->max_blocks_per_seq;
+  a.num_splits = pl.num_splits;
+  a.split_tokens = pl.split_tokens;
+  a.causal = p->causal;
+  a.window = p->sliding_window;
+  const double scale = p->scale != 0.0f ? (double)p->scale : (double)(float)(1.0 / sqrt((double)p->head_dim));
+  const double log2e = 1.4426950408889634;
+  if (p->softcap > 0.0f) {
+    a.qmul = (float)(scale / (double)p->softcap);
+    a.capl2 = (float)((double)p->softcap * log2e);
+  } else {
+    a.qmul = (float)(scale * log2e);
+    a.capl2 = 0.0f;
+  }
+  a.bs = dattn::make_fastdiv((uint32_t)p->block_size);
+  a.hw = dattn::make_fastdiv(1);
+  a.sb = dattn::make_fastdiv(1);
+  return a;
+}
+
+int check_workspace(const Plan& pl, void* ws, size_t bytes) {
+  if (bytes < pl.workspace)
+    return fail(DATTN_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", bytes, pl.workspace);
+  if (!ws) return fail(DATTN_ERR_WORKSPACE, "workspace is NULL");
+  if ((uintptr_t)ws % kAlign) return fail(DATTN_ERR_WORKSPACE, "workspace must be %zu-byte aligned", kAlign);
+  return DATTN_OK;
+}
+
+int check_launch(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(DATTN_ERR_LAUNCH, "%s launch failed: %s", what, hipGetErrorString(e));
+  return DATTN_OK;
+}
+
+template <template <int, int> class K, int D>
+void* pick_g(int G) {
+  switch (G) {
+    case 1: return (void*)K<D, 1>::fn();
+    case 2: return (void*)K<D, 2>::fn();
+    case 4: return (void*)K<D, 4>::fn();
+    default: return (void*)K<D, 8>::fn();
+  }
+}
+
+template <int D, int G>
+struct PagedF16 {
+  static auto fn() { return &dattn::paged_split_kernel<D, G, _Float16>; }
+};
+template <int D, int G>
+struct PagedF32 {
+  static auto fn() { return &dattn::paged_split_kernel<D, G, float>; }
+};
+template <int D, int G>
+struct Tiered {
+  static auto fn() { return &dattn::tiered_split_kernel<D, G>; }
+};
+template <int D, int G>
+struct Sparse {
+  static auto fn() { return &dattn::sparse_split_kernel<D, G>; }
+};
+
+template <template <int, int> class K>
+void* pick(int D, int G) {
+  return D == 64 ? pick_g<K, 64>(G) : pick_g<K, 128>(G);
+}
+
+int launch(void* split_fn, const dattn_params* p, const Plan& pl, dattn::DecodeArgs& a, float* out, float* lse,
+           hipStream_t st) {
+  dim3 grid(pl.num_splits, p->num_seqs, p->num_kv_heads / pl.waves);
+  dim3 block(64 * pl.waves);
+  void* args[] = {&a};
+  hipError_t e = hipLaunchKernel(split_fn, grid, block, args, pl.lds, st);
+  if (e != hipSuccess) return fail(DATTN_ERR_LAUNCH, "split kernel launch failed: %s", hipGetErrorString(e));
+  int rc = check_launch("split kernel");
+  if (rc) return rc;
+  const int nbh = p->num_seqs * p->num_heads;
+  if (p->head_dim == 64)
+    hipLaunchKernelGGL(dattn::combine_kernel<64>, dim3(nbh), dim3(256), 0, st, a.part_acc, a.part_ml, out, lse,
+                       pl.num_splits);
+  else
+    hipLaunchKernelGGL(dattn::combine_kernel<128>, dim3(nbh), dim3(256), 0, st, a.part_acc, a.part_ml, out, lse,
+                       pl.num_splits);
+  return check_launch("combine kernel");
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dattn_last_error(void) { return g_err.c_str(); }
+
+const char* dattn_version(void) { return "dattn 0.1.0 gfx950"; }
+
+int dattn_workspace_size(const dattn_params* p, int32_t kind, int32_t sparse_block, size_t* bytes) {
+  g_err.clear();
+  if (!bytes) return fail(DATTN_ERR_INVALID, "bytes is NULL");
+  Plan pl;
+  int rc = make_plan(p, kind, sparse_block, pl);
+  if (rc) return rc;
+  *bytes = pl.workspace;
+  return DATTN_OK;
+}
+
+int dattn_decode_paged(const dattn_params* p, const float* q, const void* k_cache, const void* v_cache,
+                       int32_t kv_dtype, const int32_t* block_table, const int32_t* seq_lens, const int32_t* q_pos,
+                       float* out, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  Plan pl;
+  int rc = make_plan(p, DATTN_KIND_PAGED, 0, pl);
+  if (rc) return rc;
+  if (kv_dtype != DATTN_F32 && kv_dtype != DATTN_F16)
+    return fail(DATTN_ERR_INVALID, "kv_dtype must be DATTN_F32 or DATTN_F16 (got %d)", kv_dtype);
+  if (p->num_seqs == 0) return DATTN_OK;
+  if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !out)
+    return fail(DATTN_ERR_INVALID, "q, k_cache, v_cache, block_table, seq_lens and out must be non-NULL");
+  if ((rc = check_workspace(pl, workspace, workspace_bytes))) return rc;
+  dattn::DecodeArgs a = base_args(p, pl, q, workspace);
+  a.k = k_cache;
+  a.v = v_cache;
+  a.table = block_table;
+  a.seq_lens = seq_lens;
+  a.q_pos = q_pos;
+  void* fn = kv_dtype == DATTN_F16 ? pick<PagedF16>(p->head_dim, pl.G) : pick<PagedF32>(p->head_dim, pl.G);
+  return launch(fn, p, pl, a, out, lse, (hipStream_t)stream);
+}
+
+int dattn_decode_tiered_int8(const dattn_params* p, const float* q, const uint16_t* k_hot, const uint16_t* v_hot,
+                             int32_t hot_window, const uint32_t* k_cold, const uint32_t* v_cold,
+                             const uint16_t* k_scale, const uint16_t* v_scale, const int32_t* cold_block_table,
+                             const int32_t* seq_lens, const int32_t* cold_lens, const int32_t* q_pos, float* out,
+                             float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  Plan pl;
+  int rc = make_plan(p, DATTN_KIND_TIERED_INT8, 0, pl);
+  if (rc) return rc;
+  if (hot_window < 1) return fail(DATTN_ERR_INVALID, "hot_window must be >= 1 (got %d)", hot_window);
+  if ((int64_t)p->num_seqs * hot_window > INT32_MAX)
+    return fail(DATTN_ERR_UNSUPPORTED, "num_seqs * hot_window must fit in int32");
+  if (p->num_seqs == 0) return DATTN_OK;
+  if (!q || !k_hot || !v_hot || !k_cold || !v_cold || !k_scale || !v_scale || !cold_block_table || !seq_lens ||
+      !cold_lens || !out)
+    return fail(DATTN_ERR_INVALID, "every array except q_pos and lse must be non-NULL");
+  if ((rc = check_workspace(pl, workspace, workspace_bytes))) return rc;
+  dattn::DecodeArgs a = base_args(p, pl, q, workspace);
+  a.k = k_cold;
+  a.v = v_cold;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.k_hot = k_hot;
+  a.v_hot = v_hot;
+  a.hot_window = hot_window;
+  a.hw = dattn::make_fastdiv((uint32_t)hot_window);
+  a.table = cold_block_table;
+  a.seq_lens = seq_lens;
+  a.cold_lens = cold_lens;
+  a.q_pos = q_pos;
+  return launch(pick<Tiered>(p->head_dim, pl.G), p, pl, a, out, lse, (hipStream_t)stream);
+}
+
+int dattn_decode_block_sparse(const dattn_params* p, const float* q, const uint16_t* k_cache,
+                              const uint16_t* v_cache, const int32_t* block_table, const int32_t* seq_lens,
+                              const int32_t* q_pos, int32_t sparse_block, int32_t num_layouts,
+                              const int32_t* row_ptr, int32_t row_stride, const int32_t* col_idx, int32_t col_stride,
+                              float* out, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  Plan pl;
+  int rc = make_plan(p, DATTN_KIND_BLOCK_SPARSE, sparse_block, pl);
+  if (rc) return rc;
+  if (num_layouts < 1) return fail(DATTN_ERR_INVALID, "num_layouts must be >= 1 (got %d)", num_layouts);
+  if (row_stride < 2) return fail(DATTN_ERR_INVALID, "row_stride must be >= 2 (got %d)", row_stride);
+  if (col_stride < 1) return fail(DATTN_ERR_INVALID, "col_stride must be >= 1 (got %d)", col_stride);
+  if (p->num_seqs == 0) return DATTN_OK;
+  if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !row_ptr || !col_idx || !out)
+    return fail(DATTN_ERR_INVALID, "every array except q_pos and lse must be non-NULL");
+  if ((rc = check_workspace(pl, workspace, workspace_bytes))) return rc;
+  dattn::DecodeArgs a = base_args(p, pl, q, workspace);
+  a.k = k_cache;
+  a.v = v_cache;
+  a.table = block_table;
+  a.seq_lens = seq_lens;
+  a.q_pos = q_pos;
+  a.row_ptr = row_ptr;
+  a.col_idx = col_idx;
+  a.sparse_block = sparse_block;
+  a.num_layouts = num_layouts;
+  a.row_stride = row_stride;
+  a.col_stride = col_stride;
+  a.sparse_nblk = pl.sparse_nblk;
+  a.blocks_per_split = pl.blocks_per_split;
+  a.sb = dattn::make_fastdiv((uint32_t)sparse_block);
+  return launch(pick<Sparse>(p->head_dim, pl.G), p, pl, a, out, lse, (hipStream_t)stream);
+}
+
+}  // extern "C"
