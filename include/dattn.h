@@ -70,7 +70,7 @@ extern "C" {
 typedef struct dattn_params {
   int32_t num_seqs;           /* B >= 0 (0 enqueues nothing) */
   int32_t num_heads;          /* H >= 1 query heads */
-  int32_t num_kv_heads;       /* Hkv >= 1, H % Hkv == 0; G = H/Hkv in {1,2,4,8,16} */
+  int32_t num_kv_heads;       /* Hkv >= 1, H % Hkv == 0; G = H/Hkv in {1, 2, 4, 8} */
   int32_t head_dim;           /* D in {64, 128} */
   float scale;                /* score scale; 0 => 1/sqrt(D) rounded to f32 */
   int32_t causal;             /* 0 or 1 */
@@ -81,7 +81,27 @@ typedef struct dattn_params {
   int32_t num_blocks;         /* physical blocks in the pool, >= 1 */
   int32_t max_seq_len;        /* host-known upper bound of seq_lens[], >= 0; sizes the grid */
   int32_t split_tokens;       /* keys per KV split; 0 => library choice, else a multiple of 16 */
+  int32_t phases;             /* 0 (or DATTN_PHASE_ALL) => both phases; see below */
 } dattn_params;
+
+/*
+ * Phases of one call.  A call runs two kernels on `stream`: the split kernel
+ * writes one partial (m, l, acc[D]) per (sequence, head, KV split) into the
+ * workspace, and the combine kernel merges the partials of every
+ * (sequence, head) into out / lse with the pairwise rule of
+ * SparseAttention's combine_partials (m = max(m1, m2),
+ * l = l1 e^{m1-m} + l2 e^{m2-m}, acc likewise).  DATTN_PHASE_SPLIT enqueues
+ * only the first kernel (out and lse are not touched and may be NULL);
+ * DATTN_PHASE_COMBINE enqueues only the second and reads partials left in the
+ * workspace by an earlier DATTN_PHASE_SPLIT call with identical parameters
+ * (only out, lse and workspace are read from the arguments).
+ * Workspace layout: acc f32 [B, H, S, D] at offset 0, then, at the next
+ * 256-byte boundary, (m, l) f32 pairs [B, H, S]; m is in log2 units
+ * (m_nat = m * ln 2); l == 0 marks a split with no visible key (acc unset).
+ */
+#define DATTN_PHASE_ALL 0
+#define DATTN_PHASE_SPLIT 1
+#define DATTN_PHASE_COMBINE 2
 
 /*
  * Workspace bytes a call of `kind` with these parameters needs.

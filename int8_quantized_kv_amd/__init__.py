@@ -29,7 +29,8 @@ from typing import Optional
 __all__ = [
     "DattnError", "DattnParams", "lib", "library_path", "dattn_workspace_size", "dattn_decode_paged",
     "dattn_decode_tiered_int8", "dattn_decode_block_sparse", "dattn_last_error", "dattn_version",
-    "KIND_PAGED", "KIND_TIERED_INT8", "KIND_BLOCK_SPARSE", "F32", "F16",
+    "KIND_PAGED", "KIND_TIERED_INT8", "KIND_BLOCK_SPARSE", "F32", "F16", "PHASE_ALL", "PHASE_SPLIT",
+    "PHASE_COMBINE",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -37,6 +38,7 @@ library_path = os.path.join(_HERE, "libdattn.so")
 
 OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_LAUNCH = 0, -1, -2, -3, -4
 F32, F16 = 0, 1
+PHASE_ALL, PHASE_SPLIT, PHASE_COMBINE = 0, 1, 2
 KIND_PAGED, KIND_TIERED_INT8, KIND_BLOCK_SPARSE = 0, 1, 2
 
 
@@ -56,6 +58,7 @@ class DattnParams(ctypes.Structure):
         ("num_blocks", ctypes.c_int32),
         ("max_seq_len", ctypes.c_int32),
         ("split_tokens", ctypes.c_int32),
+        ("phases", ctypes.c_int32),
     ]
 
 
@@ -136,10 +139,10 @@ def _ptr(t):
 
 
 def _params(q, Hkv, D, bs, max_blocks, num_blocks, max_seq_len, scale, causal, sliding_window, softcap,
-            split_tokens):
+            split_tokens, phases=PHASE_ALL):
     B, H, _ = q.shape
     return DattnParams(B, H, Hkv, D, float(scale), int(causal), int(sliding_window), float(softcap), bs, max_blocks,
-                       num_blocks, int(max_seq_len), int(split_tokens))
+                       num_blocks, int(max_seq_len), int(split_tokens), int(phases))
 
 
 def _outputs(q, out, lse, want_lse, workspace, ws_bytes):
@@ -174,7 +177,7 @@ def _max_len(seq_lens, max_seq_len):
 def dattn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, *, q_pos=None, scale: float = 0.0,
                        causal: bool = True, sliding_window: int = 0, softcap: float = 0.0,
                        max_seq_len: Optional[int] = None, split_tokens: int = 0, out=None, lse=None,
-                       want_lse: bool = True, workspace=None, stream=None):
+                       want_lse: bool = True, workspace=None, stream=None, phases: int = PHASE_ALL):
     """Decode attention over a paged f16/f32 cache; returns (out, lse)."""
     torch = _torch()
     dev = q.device
@@ -191,7 +194,7 @@ def dattn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, *, q_pos=None
     if block_table.shape[0] != q.shape[0] or seq_lens.shape[0] != q.shape[0]:
         raise ValueError("block_table / seq_lens must have one row per sequence")
     p = _params(q, Hkv, D, bs, block_table.shape[1], NB, _max_len(seq_lens, max_seq_len), scale, causal,
-                sliding_window, softcap, split_tokens)
+                sliding_window, softcap, split_tokens, phases)
     ws = dattn_workspace_size(p, KIND_PAGED)
     out, lse, workspace = _outputs(q, out, lse, want_lse, workspace, ws)
     kv_dtype = F16 if k_cache.dtype == torch.float16 else F32
@@ -205,7 +208,7 @@ def dattn_decode_tiered_int8(q, k_hot, v_hot, k_cold, v_cold, k_scale, v_scale, 
                              cold_lens, *, q_pos=None, scale: float = 0.0, causal: bool = True,
                              sliding_window: int = 0, softcap: float = 0.0, max_seq_len: Optional[int] = None,
                              split_tokens: int = 0, out=None, lse=None, want_lse: bool = True, workspace=None,
-                             stream=None):
+                             stream=None, phases: int = PHASE_ALL):
     """Decode attention over an int8 cold pool + f16 hot ring; returns (out, lse)."""
     torch = _torch()
     dev = q.device
@@ -229,7 +232,7 @@ def dattn_decode_tiered_int8(q, k_hot, v_hot, k_cold, v_cold, k_scale, v_scale, 
             or tuple(v_scale.shape) != (NB, bs, Hkv) or k_hot.shape[0] != B:
         raise ValueError("tiered cache tensors disagree on shape")
     p = _params(q, Hkv, D, bs, cold_block_table.shape[1], NB, _max_len(seq_lens, max_seq_len), scale, causal,
-                sliding_window, softcap, split_tokens)
+                sliding_window, softcap, split_tokens, phases)
     ws = dattn_workspace_size(p, KIND_TIERED_INT8)
     out, lse, workspace = _outputs(q, out, lse, want_lse, workspace, ws)
     _check(lib().dattn_decode_tiered_int8(ctypes.byref(p), _ptr(q), _ptr(k_hot), _ptr(v_hot), hot_window,
@@ -243,7 +246,8 @@ def dattn_decode_tiered_int8(q, k_hot, v_hot, k_cold, v_cold, k_scale, v_scale, 
 def dattn_decode_block_sparse(q, k_cache, v_cache, block_table, seq_lens, sparse_block: int, row_ptr, col_idx, *,
                               q_pos=None, scale: float = 0.0, causal: bool = True, sliding_window: int = 0,
                               softcap: float = 0.0, max_seq_len: Optional[int] = None, split_tokens: int = 0,
-                              out=None, lse=None, want_lse: bool = True, workspace=None, stream=None):
+                              out=None, lse=None, want_lse: bool = True, workspace=None, stream=None,
+                              phases: int = PHASE_ALL):
     """Decode attention over the paged f16 cache restricted by per-head CSR block masks."""
     torch = _torch()
     dev = q.device
@@ -260,7 +264,7 @@ def dattn_decode_block_sparse(q, k_cache, v_cache, block_table, seq_lens, sparse
     if row_ptr.shape[0] != col_idx.shape[0]:
         raise ValueError("row_ptr and col_idx must have one row per layout")
     p = _params(q, Hkv, D, bs, block_table.shape[1], NB, _max_len(seq_lens, max_seq_len), scale, causal,
-                sliding_window, softcap, split_tokens)
+                sliding_window, softcap, split_tokens, phases)
     ws = dattn_workspace_size(p, KIND_BLOCK_SPARSE, sparse_block)
     out, lse, workspace = _outputs(q, out, lse, want_lse, workspace, ws)
     _check(lib().dattn_decode_block_sparse(ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(v_cache),

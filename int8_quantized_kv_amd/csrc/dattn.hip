@@ -72,6 +72,8 @@ int check_params(const dattn_params* p, int kind) {
     return fail(DATTN_ERR_INVALID, "max_seq_len %d exceeds max_blocks_per_seq * block_size (%lld)", p->max_seq_len,
                 (long long)p->max_blocks_per_seq * p->block_size);
   if (p->max_seq_len > (1 << 30)) return fail(DATTN_ERR_UNSUPPORTED, "max_seq_len above 2^30 is not supported");
+  if (p->phases < 0 || p->phases > 3)
+    return fail(DATTN_ERR_INVALID, "phases must be 0..3 (got %d)", p->phases);
   if (p->split_tokens < 0 || p->split_tokens % 16)
     return fail(DATTN_ERR_INVALID, "split_tokens must be 0 or a positive multiple of 16 (got %d)", p->split_tokens);
   return DATTN_OK;
@@ -203,15 +205,28 @@ void* pick(int D, int G) {
   return D == 64 ? pick_g<K, 64>(G) : pick_g<K, 128>(G);
 }
 
+bool run_split(const dattn_params* p) { return p->phases == 0 || (p->phases & DATTN_PHASE_SPLIT); }
+bool run_combine(const dattn_params* p) { return p->phases == 0 || (p->phases & DATTN_PHASE_COMBINE); }
+
+// Pointer checks for the arrays the requested phases read or write.
+int check_io(const dattn_params* p, bool split_inputs_ok, float* out) {
+  if (run_split(p) && !split_inputs_ok) return fail(DATTN_ERR_INVALID, "an input array of the split phase is NULL");
+  if (run_combine(p) && !out) return fail(DATTN_ERR_INVALID, "out must be non-NULL");
+  return DATTN_OK;
+}
+
 int launch(void* split_fn, const dattn_params* p, const Plan& pl, dattn::DecodeArgs& a, float* out, float* lse,
            hipStream_t st) {
-  dim3 grid(pl.num_splits, p->num_seqs, p->num_kv_heads / pl.waves);
-  dim3 block(64 * pl.waves);
-  void* args[] = {&a};
-  hipError_t e = hipLaunchKernel(split_fn, grid, block, args, pl.lds, st);
-  if (e != hipSuccess) return fail(DATTN_ERR_LAUNCH, "split kernel launch failed: %s", hipGetErrorString(e));
-  int rc = check_launch("split kernel");
-  if (rc) return rc;
+  if (run_split(p)) {
+    dim3 grid(pl.num_splits, p->num_seqs, p->num_kv_heads / pl.waves);
+    dim3 block(64 * pl.waves);
+    void* args[] = {&a};
+    hipError_t e = hipLaunchKernel(split_fn, grid, block, args, pl.lds, st);
+    if (e != hipSuccess) return fail(DATTN_ERR_LAUNCH, "split kernel launch failed: %s", hipGetErrorString(e));
+    int rc = check_launch("split kernel");
+    if (rc) return rc;
+  }
+  if (!run_combine(p)) return DATTN_OK;
   const int nbh = p->num_seqs * p->num_heads;
   if (p->head_dim == 64)
     hipLaunchKernelGGL(dattn::combine_kernel<64>, dim3(nbh), dim3(256), 0, st, a.part_acc, a.part_ml, out, lse,
@@ -250,8 +265,7 @@ int dattn_decode_paged(const dattn_params* p, const float* q, const void* k_cach
   if (kv_dtype != DATTN_F32 && kv_dtype != DATTN_F16)
     return fail(DATTN_ERR_INVALID, "kv_dtype must be DATTN_F32 or DATTN_F16 (got %d)", kv_dtype);
   if (p->num_seqs == 0) return DATTN_OK;
-  if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !out)
-    return fail(DATTN_ERR_INVALID, "q, k_cache, v_cache, block_table, seq_lens and out must be non-NULL");
+  if ((rc = check_io(p, q && k_cache && v_cache && block_table && seq_lens, out))) return rc;
   if ((rc = check_workspace(pl, workspace, workspace_bytes))) return rc;
   dattn::DecodeArgs a = base_args(p, pl, q, workspace);
   a.k = k_cache;
@@ -276,9 +290,9 @@ int dattn_decode_tiered_int8(const dattn_params* p, const float* q, const uint16
   if ((int64_t)p->num_seqs * hot_window > INT32_MAX)
     return fail(DATTN_ERR_UNSUPPORTED, "num_seqs * hot_window must fit in int32");
   if (p->num_seqs == 0) return DATTN_OK;
-  if (!q || !k_hot || !v_hot || !k_cold || !v_cold || !k_scale || !v_scale || !cold_block_table || !seq_lens ||
-      !cold_lens || !out)
-    return fail(DATTN_ERR_INVALID, "every array except q_pos and lse must be non-NULL");
+  if ((rc = check_io(p, q && k_hot && v_hot && k_cold && v_cold && k_scale && v_scale && cold_block_table &&
+                            seq_lens && cold_lens, out)))
+    return rc;
   if ((rc = check_workspace(pl, workspace, workspace_bytes))) return rc;
   dattn::DecodeArgs a = base_args(p, pl, q, workspace);
   a.k = k_cold;
@@ -309,8 +323,7 @@ int dattn_decode_block_sparse(const dattn_params* p, const float* q, const uint1
   if (row_stride < 2) return fail(DATTN_ERR_INVALID, "row_stride must be >= 2 (got %d)", row_stride);
   if (col_stride < 1) return fail(DATTN_ERR_INVALID, "col_stride must be >= 1 (got %d)", col_stride);
   if (p->num_seqs == 0) return DATTN_OK;
-  if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !row_ptr || !col_idx || !out)
-    return fail(DATTN_ERR_INVALID, "every array except q_pos and lse must be non-NULL");
+  if ((rc = check_io(p, q && k_cache && v_cache && block_table && seq_lens && row_ptr && col_idx, out))) return rc;
   if ((rc = check_workspace(pl, workspace, workspace_bytes))) return rc;
   dattn::DecodeArgs a = base_args(p, pl, q, workspace);
   a.k = k_cache;
