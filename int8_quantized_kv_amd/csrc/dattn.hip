@@ -92,6 +92,9 @@ int choose_split(const dattn_params* p, int64_t units_per_seq_span) {
 }
 
 int waves_per_group(int Hkv) {
+#ifdef DATTN_WAVES
+  if (Hkv % DATTN_WAVES == 0) return DATTN_WAVES;
+#endif
   if (Hkv % 4 == 0) return 4;
   if (Hkv % 2 == 0) return 2;
   return 1;
@@ -173,36 +176,38 @@ int check_launch(const char* what) {
   return DATTN_OK;
 }
 
-template <template <int, int> class K, int D>
+template <template <int, int, bool> class K, int D, bool CAP>
 void* pick_g(int G) {
   switch (G) {
-    case 1: return (void*)K<D, 1>::fn();
-    case 2: return (void*)K<D, 2>::fn();
-    case 4: return (void*)K<D, 4>::fn();
-    default: return (void*)K<D, 8>::fn();
+    case 1: return (void*)K<D, 1, CAP>::fn();
+    case 2: return (void*)K<D, 2, CAP>::fn();
+    case 4: return (void*)K<D, 4, CAP>::fn();
+    default: return (void*)K<D, 8, CAP>::fn();
   }
 }
 
-template <int D, int G>
+template <int D, int G, bool CAP>
 struct PagedF16 {
-  static auto fn() { return &dattn::paged_split_kernel<D, G, _Float16>; }
+  static auto fn() { return &dattn::paged_split_kernel<D, G, CAP, _Float16>; }
 };
-template <int D, int G>
+template <int D, int G, bool CAP>
 struct PagedF32 {
-  static auto fn() { return &dattn::paged_split_kernel<D, G, float>; }
+  static auto fn() { return &dattn::paged_split_kernel<D, G, CAP, float>; }
 };
-template <int D, int G>
+template <int D, int G, bool CAP>
 struct Tiered {
-  static auto fn() { return &dattn::tiered_split_kernel<D, G>; }
+  static auto fn() { return &dattn::tiered_split_kernel<D, G, CAP>; }
 };
-template <int D, int G>
+template <int D, int G, bool CAP>
 struct Sparse {
-  static auto fn() { return &dattn::sparse_split_kernel<D, G>; }
+  static auto fn() { return &dattn::sparse_split_kernel<D, G, CAP>; }
 };
 
-template <template <int, int> class K>
-void* pick(int D, int G) {
-  return D == 64 ? pick_g<K, 64>(G) : pick_g<K, 128>(G);
+// Kernel instance for (head_dim, GQA group, softcap on/off).
+template <template <int, int, bool> class K>
+void* pick(int D, int G, bool cap) {
+  if (D == 64) return cap ? pick_g<K, 64, true>(G) : pick_g<K, 64, false>(G);
+  return cap ? pick_g<K, 128, true>(G) : pick_g<K, 128, false>(G);
 }
 
 bool run_split(const dattn_params* p) { return p->phases == 0 || (p->phases & DATTN_PHASE_SPLIT); }
@@ -273,7 +278,8 @@ int dattn_decode_paged(const dattn_params* p, const float* q, const void* k_cach
   a.table = block_table;
   a.seq_lens = seq_lens;
   a.q_pos = q_pos;
-  void* fn = kv_dtype == DATTN_F16 ? pick<PagedF16>(p->head_dim, pl.G) : pick<PagedF32>(p->head_dim, pl.G);
+  const bool cap = p->softcap > 0.0f;
+  void* fn = kv_dtype == DATTN_F16 ? pick<PagedF16>(p->head_dim, pl.G, cap) : pick<PagedF32>(p->head_dim, pl.G, cap);
   return launch(fn, p, pl, a, out, lse, (hipStream_t)stream);
 }
 
@@ -307,7 +313,7 @@ int dattn_decode_tiered_int8(const dattn_params* p, const float* q, const uint16
   a.seq_lens = seq_lens;
   a.cold_lens = cold_lens;
   a.q_pos = q_pos;
-  return launch(pick<Tiered>(p->head_dim, pl.G), p, pl, a, out, lse, (hipStream_t)stream);
+  return launch(pick<Tiered>(p->head_dim, pl.G, p->softcap > 0.0f), p, pl, a, out, lse, (hipStream_t)stream);
 }
 
 int dattn_decode_block_sparse(const dattn_params* p, const float* q, const uint16_t* k_cache,
@@ -340,7 +346,7 @@ int dattn_decode_block_sparse(const dattn_params* p, const float* q, const uint1
   a.sparse_nblk = pl.sparse_nblk;
   a.blocks_per_split = pl.blocks_per_split;
   a.sb = dattn::make_fastdiv((uint32_t)sparse_block);
-  return launch(pick<Sparse>(p->head_dim, pl.G), p, pl, a, out, lse, (hipStream_t)stream);
+  return launch(pick<Sparse>(p->head_dim, pl.G, p->softcap > 0.0f), p, pl, a, out, lse, (hipStream_t)stream);
 }
 
 }  // extern "C"

@@ -41,6 +41,10 @@ typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u2v __attribute__((ext_vector_type(2)));
 
 constexpr int kTile = 16;          // keys per tile
+#ifndef DATTN_PIPE
+#define DATTN_PIPE 2
+#endif
+constexpr int kPipe = DATTN_PIPE;  // tile buffers: kPipe-1 tiles of loads in flight
 constexpr float kSlack = 8.0f;     // lazy max: raise m only when a tile exceeds it by > 2^8
 constexpr float kLn2 = 0.69314718055994531f;
 
@@ -126,27 +130,52 @@ __device__ __forceinline__ h8 i8x8_to_h8(uint32_t w0, uint32_t w1) {
 __device__ __forceinline__ float h2f(uint16_t bits) { return (float)__builtin_bit_cast(_Float16, bits); }
 
 // ------------------------------------------------------------ Q fragments
+//
+// Q is read raw at kernel start (before any K/V load, so that waiting for it
+// never waits for K/V) and converted once the first K/V tiles are in flight.
 
-// f16 MFMA path: slab c (32 dims) of lane l covers dims
-// 64*(c/2) + 16*(l/16) + 8*(c%2) + [0, 8); the K fragments use the same map.
+// f16 MFMA path.  Slab c (32 dims of the contraction) of lane l covers 8
+// dims that depend on how the keys are stored, so that every K load reads 64
+// contiguous bytes of a row: f16 rows use dims 32c + 8g + [0, 8) (g = l/16);
+// int8 rows, loaded 16 dims per lane, use 64(c/2) + 16g + 8(c%2) + [0, 8).
+// The K fragments of a store and the Q fragments must use the same map.
+template <bool I8MAP>
+__device__ __forceinline__ int qdim(int c, int g) {
+  return I8MAP ? 64 * (c >> 1) + 16 * g + 8 * (c & 1) : 32 * c + 8 * g;
+}
+
+template <int D>
+struct QRaw16 {
+  f4 x[D / 16];
+};
 template <int D>
 struct QF16 {
   h8 hi[D / 32], lo[D / 32];
 };
 
-template <int D, int G>
-__device__ __forceinline__ void load_q_f16(const DecodeArgs& a, int b, int kvh, int lane, QF16<D>& qf) {
+template <int D, int G, bool I8MAP>
+__device__ __forceinline__ void load_q_raw16(const DecodeArgs& a, int b, int kvh, int lane, QRaw16<D>& r) {
   const int j = lane & 15, g = lane >> 4;
   const float* qrow = a.q + ((size_t)b * a.num_heads + (size_t)kvh * G + (j < G ? j : 0)) * D;
 #pragma unroll
   for (int c = 0; c < D / 32; ++c) {
-    const int d0 = 64 * (c >> 1) + 16 * g + 8 * (c & 1);
-    f4 x0 = *(const f4*)(qrow + d0), x1 = *(const f4*)(qrow + d0 + 4);
-    float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+    const int d0 = qdim<I8MAP>(c, g);
+    r.x[2 * c] = *(const f4*)(qrow + d0);
+    r.x[2 * c + 1] = *(const f4*)(qrow + d0 + 4);
+  }
+}
+
+template <int D, int G>
+__device__ __forceinline__ void convert_q(const DecodeArgs& a, int lane, const QRaw16<D>& r, QF16<D>& qf) {
+  const bool live = (lane & 15) < G;
+#pragma unroll
+  for (int c = 0; c < D / 32; ++c) {
+    const float x[8] = {r.x[2 * c].x, r.x[2 * c].y, r.x[2 * c].z, r.x[2 * c].w,
+                        r.x[2 * c + 1].x, r.x[2 * c + 1].y, r.x[2 * c + 1].z, r.x[2 * c + 1].w};
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      float v = j < G ? x[e] * a.qmul : 0.0f;
-      _Float16 h = (_Float16)v;
+      const float v = live ? x[e] * a.qmul : 0.0f;
+      const _Float16 h = (_Float16)v;
       qf.hi[c][e] = h;
       qf.lo[c][e] = (_Float16)(v - (float)h);
     }
@@ -155,29 +184,41 @@ __device__ __forceinline__ void load_q_f16(const DecodeArgs& a, int b, int kvh, 
 
 // f32 MFMA path (16x16x4): slab c of lane l is dim 16*(c/4) + 4*(l/16) + c%4.
 template <int D>
+struct QRaw32 {
+  f4 x[D / 16];
+};
+template <int D>
 struct QF32 {
   float v[D / 4];
 };
 
 template <int D, int G>
-__device__ __forceinline__ void load_q_f32(const DecodeArgs& a, int b, int kvh, int lane, QF32<D>& qf) {
+__device__ __forceinline__ void load_q_raw32(const DecodeArgs& a, int b, int kvh, int lane, QRaw32<D>& r) {
   const int j = lane & 15, g = lane >> 4;
   const float* qrow = a.q + ((size_t)b * a.num_heads + (size_t)kvh * G + (j < G ? j : 0)) * D;
 #pragma unroll
+  for (int m = 0; m < D / 16; ++m) r.x[m] = *(const f4*)(qrow + 16 * m + 4 * g);
+}
+
+template <int D, int G>
+__device__ __forceinline__ void convert_q(const DecodeArgs& a, int lane, const QRaw32<D>& r, QF32<D>& qf) {
+  const bool live = (lane & 15) < G;
+#pragma unroll
   for (int m = 0; m < D / 16; ++m) {
-    f4 x = *(const f4*)(qrow + 16 * m + 4 * g);
-    qf.v[4 * m + 0] = j < G ? x.x * a.qmul : 0.0f;
-    qf.v[4 * m + 1] = j < G ? x.y * a.qmul : 0.0f;
-    qf.v[4 * m + 2] = j < G ? x.z * a.qmul : 0.0f;
-    qf.v[4 * m + 3] = j < G ? x.w * a.qmul : 0.0f;
+    qf.v[4 * m + 0] = live ? r.x[m].x * a.qmul : 0.0f;
+    qf.v[4 * m + 1] = live ? r.x[m].y * a.qmul : 0.0f;
+    qf.v[4 * m + 2] = live ? r.x[m].z * a.qmul : 0.0f;
+    qf.v[4 * m + 3] = live ? r.x[m].w * a.qmul : 0.0f;
   }
 }
 
 // ------------------------------------------------------- K / V fragments
 //
-// A tile has 16 keys.  K lane l holds key l%16; V lane l holds keys
-// 4*(l/16) + vsub*NTV + e (e < NTV) and dims 8*vdim + [0, 8) where, for
-// DPR = D/8 lanes per V row, vdim = (l%16) % DPR and vsub = (l%16) / DPR.
+// A tile has 16 keys.  K lane l holds key l%16 (row l%16 of the MFMA A
+// operand); V lane l holds keys 4*(l/16) + vsub*NTV + e (e < NTV) and dims
+// 8*vdim + [0, 8), where DPR = D/8 lanes cover one V row, vdim = (l%16) % DPR
+// and vsub = (l%16) / DPR.  Every key of the tile is named by a physical row
+// index r of its pool, whose kv-head rows sit at element (r*Hkv + kvh) * RE.
 
 template <int D>
 struct Lay {
@@ -185,125 +226,329 @@ struct Lay {
   static constexpr int NTV = D / 32;
 };
 
-// f16 rows (paged pool or hot ring)
+// Per-lane constants of one wavefront.
 template <int D>
-struct KF16 {
-  u4 r[D / 32];
+struct LaneGeo {
+  int g, kkey, vdim, vsub;
+  int vkey[Lay<D>::NTV];
+  __device__ __forceinline__ void init(int lane) {
+    g = lane >> 4;
+    kkey = lane & 15;
+    vdim = (lane & 15) % Lay<D>::DPR;
+    vsub = (lane & 15) / Lay<D>::DPR;
+#pragma unroll
+    for (int e = 0; e < Lay<D>::NTV; ++e) vkey[e] = 4 * g + vsub * Lay<D>::NTV + e;
+  }
 };
-template <int D>
-__device__ __forceinline__ void load_k_f16(const _Float16* row, int g, KF16<D>& k) {
-#pragma unroll
-  for (int c2 = 0; c2 < D / 64; ++c2) {
-    const u4* p = (const u4*)(row + 64 * c2 + 16 * g);
-    k.r[2 * c2] = __builtin_nontemporal_load(p);
-    k.r[2 * c2 + 1] = __builtin_nontemporal_load(p + 1);
+
+// Rows of one tile: either 16 consecutive rows from a uniform row0 (fast) or
+// one row per key the lane touches (general).
+struct TileRows {
+  uint32_t krow;      // row of key kkey
+  uint32_t srow[4];   // rows of keys 4g + e
+  // row of the lane's V key e (keys 4g + vsub*NTV + e), without dynamic indexing
+  template <int NTV>
+  __device__ __forceinline__ uint32_t vrow(int vsub, int e) const {
+    if constexpr (NTV == 4) return srow[e];
+    else return vsub ? srow[NTV + e] : srow[e];
   }
-}
-template <int D>
-__device__ __forceinline__ f4 scores_f16(const KF16<D>& k, const QF16<D>& q) {
-  f4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int c = 0; c < D / 32; ++c) {
-    h8 a = __builtin_bit_cast(h8, k.r[c]);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, q.hi[c], acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, q.lo[c], acc, 0, 0, 0);
-  }
-  return acc;
+};
+
+template <class T>
+__device__ __forceinline__ T ntload(const void* p) {
+#if defined(DATTN_NT)
+  return __builtin_nontemporal_load((const T*)p);
+#else
+  return *(const T*)p;
+#endif
 }
 
-// int8 cold rows: D/4 words, lane loads the 16 bytes of dims 64*c2 + 16*g + [0,16)
+// ---- f16 rows of D halves (paged pool or hot ring)
 template <int D>
-struct KI8 {
-  u4 r[D / 64];
-};
-template <int D>
-__device__ __forceinline__ void load_k_i8(const uint32_t* row, int g, KI8<D>& k) {
-#pragma unroll
-  for (int c2 = 0; c2 < D / 64; ++c2) k.r[c2] = __builtin_nontemporal_load((const u4*)(row + 16 * c2 + 4 * g));
-}
-template <int D>
-__device__ __forceinline__ f4 scores_i8(const KI8<D>& k, const QF16<D>& q) {
-  f4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int c2 = 0; c2 < D / 64; ++c2) {
-    h8 a0 = i8x8_to_h8(k.r[c2].x, k.r[c2].y);
-    h8 a1 = i8x8_to_h8(k.r[c2].z, k.r[c2].w);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, q.hi[2 * c2], acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, q.lo[2 * c2], acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, q.hi[2 * c2 + 1], acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, q.lo[2 * c2 + 1], acc, 0, 0, 0);
+struct StoreF16 {
+  static constexpr int RE = D;  // elements per kv-head row
+  struct KFrag {
+    u4 r[D / 32];
+  };
+  struct VFrag {
+    u4 r[Lay<D>::NTV];
+  };
+  const _Float16* kbase;
+  const _Float16* vbase;
+  int Hkv, kvh;
+
+  __device__ __forceinline__ const _Float16* krow_ptr(const _Float16* base, uint32_t row) const {
+    return base + (size_t)(row * (uint32_t)Hkv + (uint32_t)kvh) * RE;
   }
-  return acc;
-}
-
-// f32 rows
-template <int D>
-struct KF32 {
-  f4 r[D / 16];
-};
-template <int D>
-__device__ __forceinline__ void load_k_f32(const float* row, int g, KF32<D>& k) {
+  __device__ __forceinline__ void load(const TileRows& tr, const LaneGeo<D>& lg, KFrag& k, VFrag& v) const {
+    const _Float16* kr = krow_ptr(kbase, tr.krow) + 8 * lg.g;
 #pragma unroll
-  for (int m = 0; m < D / 16; ++m) k.r[m] = __builtin_nontemporal_load((const f4*)(row + 16 * m + 4 * g));
-}
-template <int D>
-__device__ __forceinline__ f4 scores_f32(const KF32<D>& k, const QF32<D>& q) {
-  f4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < D / 32; ++c) k.r[c] = ntload<u4>(kr + 32 * c);
 #pragma unroll
-  for (int m = 0; m < D / 16; ++m) {
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(k.r[m].x, q.v[4 * m + 0], acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(k.r[m].y, q.v[4 * m + 1], acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(k.r[m].z, q.v[4 * m + 2], acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(k.r[m].w, q.v[4 * m + 3], acc, 0, 0, 0);
+    for (int e = 0; e < Lay<D>::NTV; ++e)
+      v.r[e] = ntload<u4>(krow_ptr(vbase, tr.template vrow<Lay<D>::NTV>(lg.vsub, e)) + 8 * lg.vdim);
   }
-  return acc;
-}
+  // rows row0 .. row0+15: uniform base plus per-lane constant offsets
+  __device__ __forceinline__ void load_tile(uint32_t row0, const LaneGeo<D>& lg, KFrag& k, VFrag& v) const {
+    const size_t tb = (size_t)row0 * (uint32_t)Hkv * RE;
+    const _Float16* kt = kbase + tb;
+    const _Float16* vt = vbase + tb;
+    const uint32_t ko = (uint32_t)(lg.kkey * Hkv + kvh) * RE + 8 * lg.g;
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c) k.r[c] = ntload<u4>(kt + ko + 32 * c);
+#pragma unroll
+    for (int e = 0; e < Lay<D>::NTV; ++e)
+      v.r[e] = ntload<u4>(vt + (uint32_t)(lg.vkey[e] * Hkv + kvh) * RE + 8 * lg.vdim);
+  }
+  __device__ __forceinline__ f4 scores(const KFrag& k, const QF16<D>& q) const {
+    f4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c) {
+      h8 a = __builtin_bit_cast(h8, k.r[c]);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, q.hi[c], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, q.lo[c], acc, 0, 0, 0);
+    }
+    return acc;
+  }
+  template <int G>
+  __device__ __forceinline__ void pv(const VFrag& v, int e, const float (&w)[G], float (&acc)[G][8]) const {
+    h8 x = __builtin_bit_cast(h8, v.r[e]);
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int d = 0; d < 8; ++d) acc[h][d] = __builtin_fmaf(w[h], (float)x[d], acc[h][d]);
+  }
+};
 
-// V pieces: 8 dims of one key.
-struct VF16 {
-  u4 r;
-};
-struct VI8 {
-  u2v r;
-};
-struct VF32 {
-  f4 a, b;
-};
-__device__ __forceinline__ void load_vrow(const _Float16* p, VF16& v) { v.r = __builtin_nontemporal_load((const u4*)p); }
-__device__ __forceinline__ void load_vrow(const uint32_t* p, VI8& v) { v.r = __builtin_nontemporal_load((const u2v*)p); }
-__device__ __forceinline__ void load_vrow(const float* p, VF32& v) {
-  v.a = __builtin_nontemporal_load((const f4*)p);
-  v.b = __builtin_nontemporal_load((const f4*)p + 1);
-}
+// ---- f32 rows (MFMA 16x16x4 f32: slab c of lane l is dim 16*(c/4) + 4*(l/16) + c%4)
+template <int D>
+struct StoreF32 {
+  static constexpr int RE = D;
+  struct KFrag {
+    f4 r[D / 16];
+  };
+  struct VFrag {
+    f4 a[Lay<D>::NTV], b[Lay<D>::NTV];
+  };
+  const float* kbase;
+  const float* vbase;
+  int Hkv, kvh;
 
-template <int G>
-__device__ __forceinline__ void pv_acc(const VF16& v, const float (&w)[G], float (&acc)[G][8]) {
-  h8 x = __builtin_bit_cast(h8, v.r);
+  __device__ __forceinline__ const float* row_ptr(const float* base, uint32_t row) const {
+    return base + (size_t)(row * (uint32_t)Hkv + (uint32_t)kvh) * RE;
+  }
+  __device__ __forceinline__ void load(const TileRows& tr, const LaneGeo<D>& lg, KFrag& k, VFrag& v) const {
+    const float* kr = row_ptr(kbase, tr.krow);
 #pragma unroll
-  for (int h = 0; h < G; ++h)
+    for (int m = 0; m < D / 16; ++m) k.r[m] = ntload<f4>(kr + 16 * m + 4 * lg.g);
 #pragma unroll
-    for (int d = 0; d < 8; ++d) acc[h][d] = __builtin_fmaf(w[h], (float)x[d], acc[h][d]);
-}
-template <int G>
-__device__ __forceinline__ void pv_acc(const VI8& v, const float (&w)[G], float (&acc)[G][8]) {
-  h8 x = i8x8_to_h8(v.r.x, v.r.y);
+    for (int e = 0; e < Lay<D>::NTV; ++e) {
+      const float* vr = row_ptr(vbase, tr.template vrow<Lay<D>::NTV>(lg.vsub, e)) + 8 * lg.vdim;
+      v.a[e] = ntload<f4>(vr);
+      v.b[e] = ntload<f4>(vr + 4);
+    }
+  }
+  __device__ __forceinline__ void load_tile(uint32_t row0, const LaneGeo<D>& lg, KFrag& k, VFrag& v) const {
+    TileRows tr;
+    tr.krow = row0 + lg.kkey;
 #pragma unroll
-  for (int h = 0; h < G; ++h)
+    for (int e = 0; e < 4; ++e) tr.srow[e] = row0 + 4 * lg.g + e;
+    load(tr, lg, k, v);
+  }
+  __device__ __forceinline__ f4 scores(const KFrag& k, const QF32<D>& q) const {
+    f4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int d = 0; d < 8; ++d) acc[h][d] = __builtin_fmaf(w[h], (float)x[d], acc[h][d]);
-}
-template <int G>
-__device__ __forceinline__ void pv_acc(const VF32& v, const float (&w)[G], float (&acc)[G][8]) {
-  float x[8] = {v.a.x, v.a.y, v.a.z, v.a.w, v.b.x, v.b.y, v.b.z, v.b.w};
+    for (int m = 0; m < D / 16; ++m) {
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(k.r[m].x, q.v[4 * m + 0], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(k.r[m].y, q.v[4 * m + 1], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(k.r[m].z, q.v[4 * m + 2], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(k.r[m].w, q.v[4 * m + 3], acc, 0, 0, 0);
+    }
+    return acc;
+  }
+  template <int G>
+  __device__ __forceinline__ void pv(const VFrag& v, int e, const float (&w)[G], float (&acc)[G][8]) const {
+    const float x[8] = {v.a[e].x, v.a[e].y, v.a[e].z, v.a[e].w, v.b[e].x, v.b[e].y, v.b[e].z, v.b[e].w};
 #pragma unroll
-  for (int h = 0; h < G; ++h)
+    for (int h = 0; h < G; ++h)
 #pragma unroll
-    for (int d = 0; d < 8; ++d) acc[h][d] = __builtin_fmaf(w[h], x[d], acc[h][d]);
-}
+      for (int d = 0; d < 8; ++d) acc[h][d] = __builtin_fmaf(w[h], x[d], acc[h][d]);
+  }
+};
+
+// ---- int8 rows of D/4 words + one f16 scale per (row, kv head)
+template <int D>
+struct StoreI8 {
+  static constexpr int RE = D / 4;
+  struct KFrag {
+    u4 r[D / 64];
+    uint16_t s[4];   // key scales of keys 4g + e
+  };
+  struct VFrag {
+    u2v r[Lay<D>::NTV];
+    uint16_t s[Lay<D>::NTV];
+  };
+  const uint32_t* kbase;
+  const uint32_t* vbase;
+  const uint16_t* ksc;
+  const uint16_t* vsc;
+  int Hkv, kvh;
+
+  __device__ __forceinline__ uint32_t rk(uint32_t row) const { return row * (uint32_t)Hkv + (uint32_t)kvh; }
+  __device__ __forceinline__ void load(const TileRows& tr, const LaneGeo<D>& lg, KFrag& k, VFrag& v) const {
+    const uint32_t* kr = kbase + (size_t)rk(tr.krow) * RE;
+#pragma unroll
+    for (int c2 = 0; c2 < D / 64; ++c2) k.r[c2] = ntload<u4>(kr + 16 * c2 + 4 * lg.g);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) k.s[e] = ksc[rk(tr.srow[e])];
+#pragma unroll
+    for (int e = 0; e < Lay<D>::NTV; ++e) {
+      const uint32_t r = rk(tr.template vrow<Lay<D>::NTV>(lg.vsub, e));
+      v.r[e] = ntload<u2v>(vbase + (size_t)r * RE + 2 * lg.vdim);
+      v.s[e] = vsc[r];
+    }
+  }
+  __device__ __forceinline__ void load_tile(uint32_t row0, const LaneGeo<D>& lg, KFrag& k, VFrag& v) const {
+    const uint32_t r0 = row0 * (uint32_t)Hkv;
+    const uint32_t* kt = kbase + (size_t)r0 * RE;
+    const uint32_t* vt = vbase + (size_t)r0 * RE;
+    const uint16_t* kst = ksc + r0;
+    const uint16_t* vst = vsc + r0;
+    const uint32_t ko = (uint32_t)(lg.kkey * Hkv + kvh) * RE + 4 * lg.g;
+#pragma unroll
+    for (int c2 = 0; c2 < D / 64; ++c2) k.r[c2] = ntload<u4>(kt + ko + 16 * c2);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) k.s[e] = kst[(4 * lg.g + e) * Hkv + kvh];
+#pragma unroll
+    for (int e = 0; e < Lay<D>::NTV; ++e) {
+      const uint32_t r = (uint32_t)(lg.vkey[e] * Hkv + kvh);
+      v.r[e] = ntload<u2v>(vt + r * RE + 2 * lg.vdim);
+      v.s[e] = vst[r];
+    }
+  }
+  __device__ __forceinline__ f4 scores(const KFrag& k, const QF16<D>& q) const {
+    f4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c2 = 0; c2 < D / 64; ++c2) {
+      h8 a0 = i8x8_to_h8(k.r[c2].x, k.r[c2].y);
+      h8 a1 = i8x8_to_h8(k.r[c2].z, k.r[c2].w);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, q.hi[2 * c2], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, q.lo[2 * c2], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, q.hi[2 * c2 + 1], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, q.lo[2 * c2 + 1], acc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] *= h2f(k.s[e]);
+    return acc;
+  }
+  template <int G>
+  __device__ __forceinline__ void pv(const VFrag& v, int e, const float (&w)[G], float (&acc)[G][8]) const {
+    const h8 x = i8x8_to_h8(v.r[e].x, v.r[e].y);
+    const float sc = h2f(v.s[e]);
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float ws = w[h] * sc;
+#pragma unroll
+      for (int d = 0; d < 8; ++d) acc[h][d] = __builtin_fmaf(ws, (float)x[d], acc[h][d]);
+    }
+  }
+};
+
+// ------------------------------------------------------- position -> row maps
+//
+// A map turns a position of the sweep (an absolute key, or a slot of the
+// sparse union list) into a physical row, says which (position, head) pairs
+// are visible, and, for a tile of 16 positions starting at a multiple of 16,
+// whether its keys are 16 consecutive rows (then `tile_row0` gives the first).
+
+// Paged: key t lives in block tbl[t / bs - blk0] (LDS), offset t % bs.
+struct PagedMap {
+  const int32_t* tbl;
+  int blk0, lo, hi;        // [lo, hi]: keys this sweep may touch (clamp) and see
+  FastDiv bs;
+  bool contig;             // bs % 16 == 0
+  __device__ __forceinline__ uint32_t row(int t) const {
+    t = min(max(t, lo), hi);
+    const uint32_t blk = fdiv((uint32_t)t, bs);
+    return (uint32_t)tbl[blk - blk0] * bs.d + ((uint32_t)t - blk * bs.d);
+  }
+  __device__ __forceinline__ bool full_tile(int t0) const { return contig && t0 >= lo && t0 + 15 <= hi; }
+  __device__ __forceinline__ uint32_t tile_row0(int t0) const {
+    const uint32_t blk = fdiv((uint32_t)t0, bs);
+    const uint32_t phys = (uint32_t)__builtin_amdgcn_readfirstlane(tbl[blk - blk0]);
+    return phys * bs.d + ((uint32_t)t0 - blk * bs.d);
+  }
+  __device__ __forceinline__ bool visible(int t, int) const { return t >= lo && t <= hi; }
+};
+
+// Hot ring: key t of sequence b at row b*hw + t % hw.
+struct RingMap {
+  int b, lo, hi;
+  FastDiv hw;
+  bool contig;             // hw % 16 == 0
+  __device__ __forceinline__ uint32_t row(int t) const {
+    t = min(max(t, lo), hi);
+    return (uint32_t)b * hw.d + fmod_((uint32_t)t, hw);
+  }
+  __device__ __forceinline__ bool full_tile(int t0) const { return contig && t0 >= lo && t0 + 15 <= hi; }
+  __device__ __forceinline__ uint32_t tile_row0(int t0) const { return (uint32_t)b * hw.d + fmod_((uint32_t)t0, hw); }
+  __device__ __forceinline__ bool visible(int t, int) const { return t >= lo && t <= hi; }
+};
+
+// Sparse: slot s -> union entry e = s / SB = (block << 16) | head mask (LDS),
+// key t = block*SB + s % SB, then the paged map through the global table.
+struct SparseMap {
+  const uint32_t* list;
+  const int32_t* table_row;
+  int slot_end, lo, hi;
+  FastDiv bs, sb;
+  bool contig;             // sb % 16 == 0 and bs % 16 == 0
+  __device__ __forceinline__ void resolve(int slot, int& t, uint32_t& mask) const {
+    const int s = min(slot, slot_end - 1);
+    const uint32_t e = fdiv((uint32_t)s, sb);
+    const uint32_t ent = list[e];
+    t = (int)((ent >> 16) * sb.d + ((uint32_t)s - e * sb.d));
+    mask = slot < slot_end ? (ent & 0xFFFFu) : 0u;
+  }
+  __device__ __forceinline__ uint32_t key_row(int t) const {
+    t = min(max(t, lo), hi);
+    const uint32_t blk = fdiv((uint32_t)t, bs);
+    return (uint32_t)table_row[blk] * bs.d + ((uint32_t)t - blk * bs.d);
+  }
+  __device__ __forceinline__ uint32_t row(int slot) const {
+    int t;
+    uint32_t mk;
+    resolve(slot, t, mk);
+    return key_row(t);
+  }
+  __device__ __forceinline__ bool full_tile(int s0) const {
+    if (!contig || s0 + 15 >= slot_end) return false;
+    int t;
+    uint32_t mk;
+    resolve(s0, t, mk);
+    t = __builtin_amdgcn_readfirstlane(t);
+    return t >= lo && t + 15 <= hi;
+  }
+  __device__ __forceinline__ uint32_t tile_row0(int s0) const {
+    int t;
+    uint32_t mk;
+    resolve(s0, t, mk);
+    t = __builtin_amdgcn_readfirstlane(t);
+    const uint32_t blk = fdiv((uint32_t)t, bs);
+    const uint32_t phys = (uint32_t)__builtin_amdgcn_readfirstlane(table_row[blk]);
+    return phys * bs.d + ((uint32_t)t - blk * bs.d);
+  }
+  __device__ __forceinline__ bool visible(int slot, int head) const {
+    int t;
+    uint32_t mk;
+    resolve(slot, t, mk);
+    return ((mk >> head) & 1u) && t >= lo && t <= hi;
+  }
+};
 
 // ------------------------------------------------- online softmax state
 
-template <int D, int G>
+template <int D, int G, bool CAP>
 struct Online {
   float m;            // running max (log2 units) of head lane%16 -- equal in all rows
   float l;            // denominator part of (head lane%16, keys of row lane/16)
@@ -321,13 +566,12 @@ struct Online {
   // raw: this lane's 4 scores (already multiplied by qmul and any int8 key
   // scale); valid: which of keys 4*(lane/16)+e take part.  Returns p[4] and
   // rescales the state; the caller then broadcasts p to the PV lanes.
-  __device__ __forceinline__ void softmax_tile(const DecodeArgs& a, const f4& raw, const bool (&valid)[4],
-                                               float (&p)[4]) {
+  __device__ __forceinline__ void softmax_tile(float capl2, const f4& raw, const bool (&valid)[4], float (&p)[4]) {
     float s[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       float x = raw[e];
-      if (a.capl2 > 0.f) x = a.capl2 * fast_tanh(x);
+      if constexpr (CAP) x = capl2 * fast_tanh(x);
       s[e] = valid[e] ? x : -__builtin_inff();
     }
     float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
@@ -397,217 +641,79 @@ __device__ __forceinline__ void write_empty(const DecodeArgs& a, int b, int kvh,
 
 // ------------------------------------------------------------ tile engine
 //
-// Process tiles t0 = tfirst, tfirst+16, ... < tend over "positions" (absolute
-// keys, or slots of the sparse union list).  The policy object maps a
-// position to a row pointer and says whether (position, head) is visible.
+// Sweep positions [tfirst, tend) in tiles of 16 keeping NBUF-1 tiles of loads
+// in flight while one tile is computed.  Every issue in the steady state is
+// unconditional (the wait-count pass would otherwise merge counter states at
+// the join and wait for the prefetched tiles as well); tiles past the end load
+// the last visible row again (a cache hit) and are never consumed.  The Q
+// fragments are prepared after the first loads are on their way.
 
-template <int D, int G, class Policy>
-__device__ __forceinline__ void run_tiles(const DecodeArgs& a, Policy& pol, Online<D, G>& st, int tfirst, int tend,
-                                          int lane) {
-  using KFrag = typename Policy::KFrag;
-  using VFrag = typename Policy::VFrag;
+template <int D, int G, bool CAP, int NBUF, class Store, class Map, class QF, class QPrep>
+__device__ __forceinline__ void run_tiles(const DecodeArgs& a, const Store& st, const Map& map, QF& qf,
+                                          QPrep&& prep_q, const LaneGeo<D>& lg, Online<D, G, CAP>& on, int tfirst,
+                                          int tend, int lane) {
+  using KFrag = typename Store::KFrag;
+  using VFrag = typename Store::VFrag;
   constexpr int NTV = Lay<D>::NTV;
-  constexpr int DPR = Lay<D>::DPR;
-  const int g = lane >> 4;
-  const int vdim = (lane & 15) % DPR;
-  const int vsub = (lane & 15) / DPR;
-
-  KFrag kb[2];
-  VFrag vb[2][NTV];
-  auto issue = [&](int t0, int slot) {
-    pol.load_k(t0 + (lane & 15), g, kb[slot]);
+  KFrag kb[NBUF];
+  VFrag vb[NBUF];
+  auto issue = [&](int t0, auto slotc) {
+    constexpr int slot = decltype(slotc)::value;
+    if (map.full_tile(t0)) {
+      st.load_tile(map.tile_row0(t0), lg, kb[slot], vb[slot]);
+    } else {
+      TileRows tr;
+      tr.krow = map.row(t0 + lg.kkey);
 #pragma unroll
-    for (int e = 0; e < NTV; ++e) pol.load_v(t0 + 4 * g + vsub * NTV + e, vdim, vb[slot][e]);
+      for (int e = 0; e < 4; ++e) tr.srow[e] = map.row(t0 + 4 * lg.g + e);
+      st.load(tr, lg, kb[slot], vb[slot]);
+    }
   };
-  auto consume = [&](int t0, int slot) {
-    f4 raw = pol.scores(kb[slot], t0 + 4 * g);
+  auto consume = [&](int t0, auto slotc) {
+    constexpr int slot = decltype(slotc)::value;
+    const f4 raw = st.scores(kb[slot], qf);
     bool valid[4];
-    const int head = lane & 15;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) valid[e] = pol.visible(t0 + 4 * g + e, head);
+    for (int e = 0; e < 4; ++e) valid[e] = map.visible(t0 + 4 * lg.g + e, lg.kkey);
     float p[4];
-    st.softmax_tile(a, raw, valid, p);
+    on.softmax_tile(a.capl2, raw, valid, p);
     float pb[4][G];
-    Online<D, G>::broadcast(p, pb);
+    Online<D, G, CAP>::broadcast(p, pb);
 #pragma unroll
     for (int e = 0; e < NTV; ++e) {
       float w[G];
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         float x = pb[e][h];
-        if constexpr (NTV < 4) x = vsub ? pb[NTV + e][h] : x;
+        if constexpr (NTV < 4) x = lg.vsub ? pb[NTV + e][h] : x;
         w[h] = x;
       }
-      pol.scale_v(t0 + 4 * g + vsub * NTV + e, w);
-      pv_acc<G>(vb[slot][e], w, st.acc);
+      st.template pv<G>(vb[slot], e, w, on.acc);
     }
   };
 
-  if (tfirst >= tend) return;
-  issue(tfirst, 0);
-  int t0 = tfirst;
-  for (;;) {
-    const int t1 = t0 + kTile;
-    if (t1 < tend) issue(t1, 1);
-    consume(t0, 0);
-    if (t1 >= tend) break;
-    const int t2 = t1 + kTile;
-    if (t2 < tend) issue(t2, 0);
-    consume(t1, 1);
-    if (t2 >= tend) break;
-    t0 = t2;
+  if (tfirst >= tend) {
+    prep_q(qf);
+    return;
   }
+  const int ntiles = (tend - tfirst + kTile - 1) / kTile;
+  static_for<0, NBUF - 1>([&](auto u) { issue(tfirst + decltype(u)::value * kTile, u); });
+  prep_q(qf);
+  int i = 0;
+  for (; i + NBUF <= ntiles; i += NBUF) {
+    static_for<0, NBUF>([&](auto u) {
+      constexpr int U = decltype(u)::value;
+      const int t = tfirst + (i + U) * kTile;
+      issue(t + (NBUF - 1) * kTile, std::integral_constant<int, (U + NBUF - 1) % NBUF>{});
+      consume(t, u);
+    });
+  }
+  // fewer than NBUF tiles remain; their loads are already in flight
+  static_for<0, NBUF - 1>([&](auto u) {
+    constexpr int U = decltype(u)::value;
+    if (i + U < ntiles) consume(tfirst + (i + U) * kTile, u);
+  });
 }
-
-// ------------------------------------------------------------- policies
-
-// Position = absolute key; rows of a paged pool through the block table
-// staged in LDS (entries blk0 .. blk0+n-1).
-template <int D, class T>
-struct PagedPolicy {
-  using KFrag = std::conditional_t<std::is_same_v<T, float>, KF32<D>, KF16<D>>;
-  using VFrag = std::conditional_t<std::is_same_v<T, float>, VF32, VF16>;
-  const T* kpool;
-  const T* vpool;
-  const int32_t* tbl;   // LDS
-  int blk0, kvh, Hkv, lo, hi;  // clamp / visibility range [lo, hi]
-  FastDiv bs;
-  QF16<D> qh;
-  QF32<D> qf;
-
-  __device__ __forceinline__ size_t row_off(int t) const {
-    t = min(max(t, lo), hi);
-    const uint32_t blk = fdiv((uint32_t)t, bs);
-    const uint32_t off = (uint32_t)t - blk * bs.d;
-    const int32_t phys = tbl[blk - blk0];
-    return ((size_t)((uint32_t)phys * bs.d + off) * Hkv + kvh) * D;
-  }
-  __device__ __forceinline__ void load_k(int t, int g, KFrag& k) const {
-    if constexpr (std::is_same_v<T, float>)
-      load_k_f32<D>(kpool + row_off(t), g, k);
-    else
-      load_k_f16<D>(kpool + row_off(t), g, k);
-  }
-  __device__ __forceinline__ void load_v(int t, int vdim, VFrag& v) const {
-    load_vrow(vpool + row_off(t) + 8 * vdim, v);
-  }
-  __device__ __forceinline__ f4 scores(const KFrag& k, int) const {
-    if constexpr (std::is_same_v<T, float>)
-      return scores_f32<D>(k, qf);
-    else
-      return scores_f16<D>(k, qh);
-  }
-  __device__ __forceinline__ bool visible(int t, int) const { return t >= lo && t <= hi; }
-  template <int G>
-  __device__ __forceinline__ void scale_v(int, float (&)[G]) const {}
-};
-
-// Cold tier: int8 rows through the staged cold table, f16 scales per (row, kvh).
-template <int D>
-struct ColdPolicy {
-  using KFrag = KI8<D>;
-  using VFrag = VI8;
-  const uint32_t* kw;
-  const uint32_t* vw;
-  const uint16_t* ks;
-  const uint16_t* vs;
-  const int32_t* tbl;
-  int blk0, kvh, Hkv, lo, hi;
-  FastDiv bs;
-  QF16<D> qh;
-
-  __device__ __forceinline__ size_t rowkv(int t) const {  // (phys row)*Hkv + kvh
-    t = min(max(t, lo), hi);
-    const uint32_t blk = fdiv((uint32_t)t, bs);
-    const uint32_t off = (uint32_t)t - blk * bs.d;
-    return (size_t)((uint32_t)tbl[blk - blk0] * bs.d + off) * Hkv + kvh;
-  }
-  __device__ __forceinline__ void load_k(int t, int g, KFrag& k) const { load_k_i8<D>(kw + rowkv(t) * (D / 4), g, k); }
-  __device__ __forceinline__ void load_v(int t, int vdim, VFrag& v) const {
-    load_vrow(vw + rowkv(t) * (D / 4) + 2 * vdim, v);
-  }
-  __device__ __forceinline__ f4 scores(const KFrag& k, int t4) const {
-    f4 r = scores_i8<D>(k, qh);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) r[e] *= h2f(ks[rowkv(t4 + e)]);
-    return r;
-  }
-  __device__ __forceinline__ bool visible(int t, int) const { return t >= lo && t <= hi; }
-  template <int G>
-  __device__ __forceinline__ void scale_v(int t, float (&w)[G]) const {
-    const float sc = h2f(vs[rowkv(t)]);
-#pragma unroll
-    for (int h = 0; h < G; ++h) w[h] *= sc;
-  }
-};
-
-// Hot tier: f16 ring, key t at slot t mod hot_window (doppler get_hot_pos).
-template <int D>
-struct HotPolicy {
-  using KFrag = KF16<D>;
-  using VFrag = VF16;
-  const _Float16* kh;
-  const _Float16* vh;
-  int b, kvh, Hkv, lo, hi;
-  FastDiv hw;
-  QF16<D> qh;
-
-  __device__ __forceinline__ size_t row_off(int t) const {
-    t = min(max(t, lo), hi);
-    const uint32_t slot = fmod_((uint32_t)t, hw);
-    return (((size_t)b * hw.d + slot) * Hkv + kvh) * D;
-  }
-  __device__ __forceinline__ void load_k(int t, int g, KFrag& k) const { load_k_f16<D>(kh + row_off(t), g, k); }
-  __device__ __forceinline__ void load_v(int t, int vdim, VFrag& v) const { load_vrow(vh + row_off(t) + 8 * vdim, v); }
-  __device__ __forceinline__ f4 scores(const KFrag& k, int) const { return scores_f16<D>(k, qh); }
-  __device__ __forceinline__ bool visible(int t, int) const { return t >= lo && t <= hi; }
-  template <int G>
-  __device__ __forceinline__ void scale_v(int, float (&)[G]) const {}
-};
-
-// Sparse: position = slot in the union list of selected sparse blocks of the
-// GQA group (entry = (block << 16) | head mask), then the paged f16 pool
-// through the global block table.
-template <int D>
-struct SparsePolicy {
-  using KFrag = KF16<D>;
-  using VFrag = VF16;
-  const _Float16* kpool;
-  const _Float16* vpool;
-  const int32_t* table_row;   // global, this sequence
-  const uint32_t* list;       // LDS
-  int slot_end, kvh, Hkv, lo, hi;
-  FastDiv bs, sb;
-  QF16<D> qh;
-
-  __device__ __forceinline__ void resolve(int slot, int& t, uint32_t& mask) const {
-    const int s = min(slot, slot_end - 1);
-    const uint32_t e = fdiv((uint32_t)s, sb);
-    const uint32_t ent = list[e];
-    t = (int)((ent >> 16) * sb.d + ((uint32_t)s - e * sb.d));
-    mask = slot < slot_end ? (ent & 0xFFFFu) : 0u;
-  }
-  __device__ __forceinline__ size_t row_off(int slot) const {
-    int t;
-    uint32_t mk;
-    resolve(slot, t, mk);
-    t = min(max(t, lo), hi);
-    const uint32_t blk = fdiv((uint32_t)t, bs);
-    const uint32_t off = (uint32_t)t - blk * bs.d;
-    return ((size_t)((uint32_t)table_row[blk] * bs.d + off) * Hkv + kvh) * D;
-  }
-  __device__ __forceinline__ void load_k(int s, int g, KFrag& k) const { load_k_f16<D>(kpool + row_off(s), g, k); }
-  __device__ __forceinline__ void load_v(int s, int vdim, VFrag& v) const { load_vrow(vpool + row_off(s) + 8 * vdim, v); }
-  __device__ __forceinline__ f4 scores(const KFrag& k, int) const { return scores_f16<D>(k, qh); }
-  __device__ __forceinline__ bool visible(int slot, int head) const {
-    int t;
-    uint32_t mk;
-    resolve(slot, t, mk);
-    return ((mk >> head) & 1u) && t >= lo && t <= hi;
-  }
-  template <int G>
-  __device__ __forceinline__ void scale_v(int, float (&)[G]) const {}
-};
 
 // ---------------------------------------------------------------- kernels
 
@@ -618,7 +724,7 @@ __device__ __forceinline__ void stage_table(const DecodeArgs& a, int b, int blk0
   __syncthreads();
 }
 
-template <int D, int G, class T>
+template <int D, int G, bool CAP, class T>
 __global__ __launch_bounds__(256) void paged_split_kernel(DecodeArgs a) {
   extern __shared__ int32_t lds_tbl[];
   const int split = blockIdx.x, b = blockIdx.y;
@@ -633,33 +739,39 @@ __global__ __launch_bounds__(256) void paged_split_kernel(DecodeArgs a) {
     blk0 = (int)fdiv((uint32_t)tb, a.bs);
     nblk = (int)fdiv((uint32_t)(te - 1), a.bs) - blk0 + 1;
   }
+  using QRaw = std::conditional_t<std::is_same_v<T, float>, QRaw32<D>, QRaw16<D>>;
+  QRaw qraw;
+  if (tb < te) {
+    if constexpr (std::is_same_v<T, float>)
+      load_q_raw32<D, G>(a, b, kvh, lane, qraw);
+    else
+      load_q_raw16<D, G, false>(a, b, kvh, lane, qraw);
+  }
   stage_table(a, b, blk0, nblk, lds_tbl);
   if (tb >= te) {
     write_empty<G>(a, b, kvh, split, lane);
     return;
   }
-  PagedPolicy<D, T> pol;
-  pol.kpool = (const T*)a.k;
-  pol.vpool = (const T*)a.v;
-  pol.tbl = lds_tbl;
-  pol.blk0 = blk0;
-  pol.kvh = kvh;
-  pol.Hkv = a.num_kv_heads;
-  pol.lo = tb;
-  pol.hi = te - 1;
-  pol.bs = a.bs;
-  if constexpr (std::is_same_v<T, float>)
-    load_q_f32<D, G>(a, b, kvh, lane, pol.qf);
-  else
-    load_q_f16<D, G>(a, b, kvh, lane, pol.qh);
-  Online<D, G> st;
-  st.init();
-  const int tfirst = tb & ~(kTile - 1);
-  run_tiles<D, G>(a, pol, st, tfirst, te, lane);
-  st.finish(a, b, kvh, split, lane);
+  LaneGeo<D> lg;
+  lg.init(lane);
+  PagedMap map{lds_tbl, blk0, tb, te - 1, a.bs, a.bs.d % 16 == 0};
+  Online<D, G, CAP> on;
+  on.init();
+  if constexpr (std::is_same_v<T, float>) {
+    QF32<D> qf;
+    StoreF32<D> st{(const float*)a.k, (const float*)a.v, a.num_kv_heads, kvh};
+    run_tiles<D, G, CAP, kPipe>(a, st, map, qf, [&](QF32<D>& q) { convert_q<D, G>(a, lane, qraw, q); }, lg, on,
+                                tb & ~(kTile - 1), te, lane);
+  } else {
+    QF16<D> qf;
+    StoreF16<D> st{(const _Float16*)a.k, (const _Float16*)a.v, a.num_kv_heads, kvh};
+    run_tiles<D, G, CAP, kPipe>(a, st, map, qf, [&](QF16<D>& q) { convert_q<D, G>(a, lane, qraw, q); }, lg, on,
+                                tb & ~(kTile - 1), te, lane);
+  }
+  on.finish(a, b, kvh, split, lane);
 }
 
-template <int D, int G>
+template <int D, int G, bool CAP>
 __global__ __launch_bounds__(256) void tiered_split_kernel(DecodeArgs a) {
   extern __shared__ int32_t lds_tbl[];
   const int split = blockIdx.x, b = blockIdx.y;
@@ -677,52 +789,46 @@ __global__ __launch_bounds__(256) void tiered_split_kernel(DecodeArgs a) {
     blk0 = (int)fdiv((uint32_t)tb, a.bs);
     nblk = (int)fdiv((uint32_t)(ce - 1), a.bs) - blk0 + 1;
   }
+  QRaw16<D> qraw;   // cold keys use the int8 dim map, a split of hot keys only the f16 one
+  if (tb < ce)
+    load_q_raw16<D, G, true>(a, b, kvh, lane, qraw);
+  else if (tb < te)
+    load_q_raw16<D, G, false>(a, b, kvh, lane, qraw);
   stage_table(a, b, blk0, nblk, lds_tbl);
   if (tb >= te) {
     write_empty<G>(a, b, kvh, split, lane);
     return;
   }
-  QF16<D> qh;
-  load_q_f16<D, G>(a, b, kvh, lane, qh);
-  Online<D, G> st;
-  st.init();
+  LaneGeo<D> lg;
+  lg.init(lane);
+  QF16<D> qf;
+  Online<D, G, CAP> on;
+  on.init();
   if (tb < ce) {
-    ColdPolicy<D> pol;
-    pol.kw = (const uint32_t*)a.k;
-    pol.vw = (const uint32_t*)a.v;
-    pol.ks = a.k_scale;
-    pol.vs = a.v_scale;
-    pol.tbl = lds_tbl;
-    pol.blk0 = blk0;
-    pol.kvh = kvh;
-    pol.Hkv = a.num_kv_heads;
-    pol.lo = tb;
-    pol.hi = ce - 1;
-    pol.bs = a.bs;
-    pol.qh = qh;
-    run_tiles<D, G>(a, pol, st, tb & ~(kTile - 1), ce, lane);
+    PagedMap map{lds_tbl, blk0, tb, ce - 1, a.bs, a.bs.d % 16 == 0};
+    StoreI8<D> st{(const uint32_t*)a.k, (const uint32_t*)a.v, a.k_scale, a.v_scale, a.num_kv_heads, kvh};
+    run_tiles<D, G, CAP, kPipe>(a, st, map, qf, [&](QF16<D>& q) { convert_q<D, G>(a, lane, qraw, q); }, lg, on,
+                                tb & ~(kTile - 1), ce, lane);
   }
   if (hb < te) {
-    HotPolicy<D> pol;
-    pol.kh = (const _Float16*)a.k_hot;
-    pol.vh = (const _Float16*)a.v_hot;
-    pol.b = b;
-    pol.kvh = kvh;
-    pol.Hkv = a.num_kv_heads;
-    pol.lo = hb;
-    pol.hi = te - 1;
-    pol.hw = a.hw;
-    pol.qh = qh;
-    run_tiles<D, G>(a, pol, st, hb & ~(kTile - 1), te, lane);
+    RingMap map{b, hb, te - 1, a.hw, a.hw.d % 16 == 0};
+    StoreF16<D> st{(const _Float16*)a.k_hot, (const _Float16*)a.v_hot, a.num_kv_heads, kvh};
+    const bool had_cold = tb < ce;
+    run_tiles<D, G, CAP, kPipe>(a, st, map, qf,
+                                [&](QF16<D>& q) {
+                                  if (had_cold) load_q_raw16<D, G, false>(a, b, kvh, lane, qraw);
+                                  convert_q<D, G>(a, lane, qraw, q);
+                                },
+                                lg, on, hb & ~(kTile - 1), te, lane);
   }
-  st.finish(a, b, kvh, split, lane);
+  on.finish(a, b, kvh, split, lane);
 }
 
 // Block-sparse: each wave builds the union of the CSR rows of its G heads in
 // LDS (a G-bit head mask per sparse block, then the blocks with a non-zero
 // mask compacted in increasing order), takes the slice of that list its
 // split owns and sweeps its keys.
-template <int D, int G>
+template <int D, int G, bool CAP>
 __global__ __launch_bounds__(256) void sparse_split_kernel(DecodeArgs a) {
   extern __shared__ uint32_t lds_sp[];
   const int split = blockIdx.x, b = blockIdx.y;
@@ -733,6 +839,8 @@ __global__ __launch_bounds__(256) void sparse_split_kernel(DecodeArgs a) {
   uint32_t* list = mask + nb;
   int lo, hi, qp;
   visible_range(a, b, lo, hi, qp);
+  QRaw16<D> qraw;
+  load_q_raw16<D, G, false>(a, b, kvh, lane, qraw);
   for (int i = lane; i < nb; i += 64) mask[i] = 0u;
   __syncthreads();
   const uint32_t r = fdiv((uint32_t)max(qp, 0), a.sb);
@@ -766,23 +874,17 @@ __global__ __launch_bounds__(256) void sparse_split_kernel(DecodeArgs a) {
     write_empty<G>(a, b, kvh, split, lane);
     return;
   }
-  SparsePolicy<D> pol;
-  pol.kpool = (const _Float16*)a.k;
-  pol.vpool = (const _Float16*)a.v;
-  pol.table_row = a.table + (size_t)b * a.max_blocks;
-  pol.list = list;
-  pol.slot_end = e1 * (int)a.sb.d;
-  pol.kvh = kvh;
-  pol.Hkv = a.num_kv_heads;
-  pol.lo = lo;
-  pol.hi = hi;
-  pol.bs = a.bs;
-  pol.sb = a.sb;
-  load_q_f16<D, G>(a, b, kvh, lane, pol.qh);
-  Online<D, G> st;
-  st.init();
-  run_tiles<D, G>(a, pol, st, e0 * (int)a.sb.d, pol.slot_end, lane);
-  st.finish(a, b, kvh, split, lane);
+  LaneGeo<D> lg;
+  lg.init(lane);
+  SparseMap map{list, a.table + (size_t)b * a.max_blocks, e1 * (int)a.sb.d, lo, hi, a.bs, a.sb,
+                a.sb.d % 16 == 0 && a.bs.d % 16 == 0};
+  QF16<D> qf;
+  StoreF16<D> st{(const _Float16*)a.k, (const _Float16*)a.v, a.num_kv_heads, kvh};
+  Online<D, G, CAP> on;
+  on.init();
+  run_tiles<D, G, CAP, kPipe>(a, st, map, qf, [&](QF16<D>& q) { convert_q<D, G>(a, lane, qraw, q); }, lg, on,
+                              e0 * (int)a.sb.d, map.slot_end, lane);
+  on.finish(a, b, kvh, split, lane);
 }
 
 // Merge the split partials of one (sequence, head): 4 waves stride over the
