@@ -33,6 +33,8 @@ import numpy as np  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
 MALL_BYTES = 1.0e9     # rotate cache copies until each step touches new memory
+KERNEL_SOURCE = os.path.join(ROOT, "int8_quantized_kv_amd", "csrc", "decode_kernels.h")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_paged_split_f16.json")
 
 
 def log(msg):
@@ -219,6 +221,55 @@ def measure(case, steps, warmup, copies=None):
     return r, dict(wall_s=wall, split_ms=split_ms, combine_ms=comb_ms, copies=copies)
 
 
+def kernel_source_sha():
+    import hashlib
+    return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch of the split kernel from the committed counter summary
+    (FETCH_SIZE + WRITE_SIZE, scaled by a copy kernel of known size), or None when
+    the summary is missing or was taken on a different kernel source."""
+    try:
+        t = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256") != kernel_source_sha():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def copy_calibration(mib):
+    """A plain streaming kernel of known traffic for scaling the FETCH_SIZE and
+    WRITE_SIZE counters: torch.neg over `mib` MiB of float32 reads and writes
+    exactly mib MiB each (5 launches)."""
+    import torch
+    src = torch.ones((mib << 20) // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    log(f"copy calibration: 5 x torch.neg over {mib} MiB float32")
+
+
+def copy_reference(nbytes=300 << 20, copies=4, reps=20):
+    """Read + write GB/s of torch.neg over float32 buffers rotated past the Infinity
+    Cache: what a plain streaming elementwise kernel reaches on this GPU."""
+    import torch
+    srcs = [torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0") for _ in range(copies)]
+    dsts = [torch.empty_like(x) for x in srcs]
+    for a, b in zip(srcs, dsts):
+        torch.neg(a, out=b)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(reps):
+        torch.neg(srcs[i % copies], out=dsts[i % copies])
+    e1.record()
+    torch.cuda.synchronize()
+    return round(2 * nbytes * reps / (e0.elapsed_time(e1) / 1e3) / 1e9, 1)
+
+
 def cpu_baseline(case, kvb, min_seconds=10.0):
     """The fp64 oracle (as it stands) over the whole workload, repeated until at least
     min_seconds have passed; returns KV GB/s in the same unit as the GPU line."""
@@ -271,6 +322,8 @@ def main():
     ap.add_argument("--all", action="store_true", help="also measure the other workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", type=int, default=2, help="headline workload index (default 2)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="first run 5 device copies of MIB MiB (for scaling memory counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the decode path here is the "
@@ -284,6 +337,8 @@ def main():
         sys.exit(1)
     import int8_quantized_kv_amd as dk
     dk.lib()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
 
     log("generating headline workload ...")
     case = synth.config(args.workload)
@@ -315,10 +370,11 @@ def main():
         "queries_per_s": head["queries_per_s"],
         "kernels": {"split_ms": head["split_ms"], "combine_ms": head["combine_ms"]},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                      "kernel": f"paged_split_kernel<D={D}, G={H // case.params['num_kv_heads']}, f16>",
                      "bytes_per_launch": kvb},
         "parity_sample": {k: head[k] for k in ("sample_max_abs_err", "sample_rel_err", "sample_lse_err")},
+        "copy_reference_gbs": copy_reference(),
     }
     if not args.no_cpu_baseline:
         log("timing the oracle on the host ...")

@@ -131,6 +131,8 @@ def _need(t, name, dtypes, ndim, device):
         raise ValueError(f"{name} must be contiguous")
     if t.device != device:
         raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor (got {t.device}); the library reads device memory only")
     return t
 
 

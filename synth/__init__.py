@@ -66,10 +66,31 @@ class Case:
     extra: dict = field(default_factory=dict)
 
 
+_PARALLEL_MIN = 1 << 26   # elements; larger draws are split over child generators
+
+
 def _normal(rng, shape, dtype):
-    """N(0,1) draws in float32, cast (round-to-nearest-even) to the storage dtype."""
-    x = rng.standard_normal(shape, dtype=np.float32)
-    return x if dtype == F32 else x.astype(np.float16)
+    """N(0,1) draws in float32, cast (round-to-nearest-even) to the storage dtype.
+    Draws of more than 2^26 elements are split (in C order) into 32 equal
+    chunks, each drawn from a child generator seeded by 32 integers taken from
+    `rng` (deterministic per seed, computed on 8 threads)."""
+    n = int(np.prod(shape))
+    if n < _PARALLEL_MIN:
+        x = rng.standard_normal(shape, dtype=np.float32)
+        return x if dtype == F32 else x.astype(np.float16)
+    from concurrent.futures import ThreadPoolExecutor
+    seeds = rng.integers(0, 2 ** 63 - 1, size=32)
+    out = np.empty(shape, np.float32 if dtype == F32 else np.float16)
+    flat = out.reshape(-1)
+    bounds = np.linspace(0, n, 33).astype(np.int64)
+
+    def fill(i):
+        g = np.random.default_rng(int(seeds[i]))
+        flat[bounds[i]:bounds[i + 1]] = g.standard_normal(int(bounds[i + 1] - bounds[i]), dtype=np.float32)
+
+    with ThreadPoolExecutor(8) as ex:
+        list(ex.map(fill, range(32)))
+    return out
 
 
 def pool_table(rng, lens, bs, permute=True, extra_blocks=0):
@@ -111,8 +132,27 @@ def paged_case(seed, B, H, Hkv, D, bs, lens=None, kv_dtype=F16, permute=True, q_
 def quantize_rows(x: np.ndarray):
     """Symmetric per-row int8 codes of float32 rows x[..., D]:
     s32 = max|x| / 127 (f32), s = f16(s32), i = clip(rint(x / f32(s)), -127, 127);
-    an all-zero row gives s = 0 and i = 0.  Returns (int8 codes, f16 scales)."""
+    an all-zero row gives s = 0 and i = 0.  Returns (int8 codes, f16 scales).
+    Large inputs are processed in row chunks on 8 threads (same result)."""
     x = np.asarray(x, np.float32)
+    if x.size >= _PARALLEL_MIN and x.shape[0] >= 16:
+        from concurrent.futures import ThreadPoolExecutor
+        codes = np.empty(x.shape, np.int8)
+        scales = np.empty(x.shape[:-1], np.float16)
+        bounds = np.linspace(0, x.shape[0], 17).astype(int)
+
+        def part(i):
+            c, sc = _quantize(x[bounds[i]:bounds[i + 1]])
+            codes[bounds[i]:bounds[i + 1]] = c
+            scales[bounds[i]:bounds[i + 1]] = sc
+
+        with ThreadPoolExecutor(8) as ex:
+            list(ex.map(part, range(16)))
+        return codes, scales
+    return _quantize(x)
+
+
+def _quantize(x):
     amax = np.max(np.abs(x), axis=-1)
     s16 = (amax / np.float32(127.0)).astype(np.float16)
     s32 = s16.astype(np.float32)
@@ -153,31 +193,29 @@ def tiered_case(seed, B, H, Hkv, D, bs, lens, cold_lens, hot_window, permute=Tru
     assert np.all(cold_lens <= lens) and np.all(lens - cold_lens <= hot_window)
     q = rng.standard_normal((B, H, D), dtype=np.float32)
     Lmax = max(1, int(lens.max()))
-    draw = exact_rows if exact else (lambda r, shp: r.standard_normal(shp, dtype=np.float32))
+    draw = exact_rows if exact else (lambda r, shp: _normal(r, shp, F32))
     k_log = draw(rng, (B, Lmax, Hkv, D))
     v_log = draw(rng, (B, Lmax, Hkv, D))
     table, pool = pool_table(rng, cold_lens, bs, permute, extra_blocks)
-    # cold pool; rows no live token uses hold garbage codes with scale 1
-    kc = rng.integers(-127, 128, size=(pool, bs, Hkv, D)).astype(np.int8)
-    vc = rng.integers(-127, 128, size=(pool, bs, Hkv, D)).astype(np.int8)
+    # cold pool; rows no live token uses hold the code 100 with scale 1 (value 100)
+    kc = np.full((pool, bs, Hkv, D), 100, np.int8)
+    vc = np.full((pool, bs, Hkv, D), -100, np.int8)
     ks = np.ones((pool, bs, Hkv), np.float16)
     vs = np.ones((pool, bs, Hkv), np.float16)
-    for b in range(B):
-        c = int(cold_lens[b])
-        if c == 0:
-            continue
-        t = np.arange(c)
-        blk, off = table[b, t // bs], t % bs
-        kq, ksc = quantize_rows(k_log[b, :c])
-        vq, vsc = quantize_rows(v_log[b, :c])
-        kc[blk, off], ks[blk, off] = kq, ksc
-        vc[blk, off], vs[blk, off] = vq, vsc
+    bb = np.concatenate([np.full(int(c), b) for b, c in enumerate(cold_lens)] + [np.zeros(0, int)]).astype(np.int64)
+    tt = np.concatenate([np.arange(int(c)) for c in cold_lens] + [np.zeros(0, int)]).astype(np.int64)
+    if bb.size:
+        blk, off = table[bb, tt // bs], tt % bs
+        kc[blk, off], ks[blk, off] = quantize_rows(k_log[bb, tt])
+        vc[blk, off], vs[blk, off] = quantize_rows(v_log[bb, tt])
     hk = np.full((B, hot_window, Hkv, D), 300.0, np.float16)
     hv = np.full((B, hot_window, Hkv, D), -300.0, np.float16)
-    for b in range(B):
-        t = np.arange(int(cold_lens[b]), int(lens[b]))
-        hk[b, t % hot_window] = k_log[b, t].astype(np.float16)
-        hv[b, t % hot_window] = v_log[b, t].astype(np.float16)
+    hb = np.concatenate([np.full(int(L) - int(c), b) for b, (L, c) in enumerate(zip(lens, cold_lens))]
+                        + [np.zeros(0, int)]).astype(np.int64)
+    ht = np.concatenate([np.arange(int(c), int(L)) for L, c in zip(lens, cold_lens)] + [np.zeros(0, int)]).astype(np.int64)
+    if hb.size:
+        hk[hb, ht % hot_window] = k_log[hb, ht].astype(np.float16)
+        hv[hb, ht % hot_window] = v_log[hb, ht].astype(np.float16)
     del k_log, v_log
     qp = None if q_pos is None else np.asarray(q_pos, np.int32)
     return Case("tiered", _params(B, H, Hkv, D, bs, table.shape[1], pool, scale, causal, window, softcap), q, lens,

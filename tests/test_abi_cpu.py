@@ -1,0 +1,203 @@
+"""CPU checks of the C-ABI library: it loads, exports what include/dattn.h
+declares, lays out dattn_params as the binding does, and rejects every bad
+argument the host can see with the documented code before touching HIP."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dattn.h")
+
+dk = pytest.importorskip("int8_quantized_kv_amd")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(dk.library_path):
+        pytest.skip("libdattn.so not built")
+    return dk.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dattn_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("dattn_decode_paged", "dattn_decode_tiered_int8", "dattn_decode_block_sparse", "dattn_workspace_size",
+              "dattn_last_error", "dattn_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", dk.library_path], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (dattn_[a-z0-9_]+)", out))
+    missing = [n for n in declared_functions() if n not in exported]
+    assert not missing, missing
+
+
+def test_params_layout_matches_the_header(tmp_path):
+    fields = [f[0] for f in dk.DattnParams._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "dattn.h"\nint main(void){\n'
+                   + "".join(f'printf("%zu\\n", offsetof(dattn_params, {f}));\n' for f in fields)
+                   + 'printf("%zu\\n", sizeof(dattn_params));\nreturn 0;}\n')
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c11", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
+    want = [getattr(dk.DattnParams, f).offset for f in fields] + [ctypes.sizeof(dk.DattnParams)]
+    assert got == want
+
+
+def test_fastdiv_is_exact(tmp_path):
+    src = tmp_path / "fd.cpp"
+    src.write_text(r'''
+#include "fastdiv.h"
+#include <cstdio>
+#include <random>
+int main() {
+  std::mt19937_64 r(7); long bad = 0;
+  for (uint32_t d = 1; d < 3000; ++d) {
+    auto f = dattn::make_fastdiv(d);
+    for (int k = 0; k < 500; ++k) { uint32_t x = (uint32_t)(r() & 0x7fffffff); bad += dattn::fdiv(x, f) != x / d; }
+    for (uint32_t x = 0; x < 4 * d + 5; ++x) bad += dattn::fdiv(x, f) != x / d || dattn::fmod_(x, f) != x % d;
+    for (uint32_t x = 0x7fffffff - 2 * d; x < 0x7fffffff; ++x) bad += dattn::fdiv(x, f) != x / d;
+  }
+  for (int k = 0; k < 100000; ++k) {
+    uint32_t d = (uint32_t)(r() % 0x7fffffff) + 1, x = (uint32_t)(r() & 0x7fffffff);
+    auto f = dattn::make_fastdiv(d); bad += dattn::fdiv(x, f) != x / d;
+  }
+  printf("%ld\n", bad); return bad != 0;
+}''')
+    exe = tmp_path / "fd"
+    subprocess.run(["g++", "-O2", "-std=c++17", "-I", os.path.join(ROOT, "int8_quantized_kv_amd", "csrc"), str(src),
+                    "-o", str(exe)], check=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert r.returncode == 0 and r.stdout.strip() == "0"
+
+
+def good_params(**kw):
+    p = dict(num_seqs=2, num_heads=8, num_kv_heads=2, head_dim=128, scale=0.0, causal=1, sliding_window=0,
+             softcap=0.0, block_size=16, max_blocks_per_seq=8, num_blocks=16, max_seq_len=100, split_tokens=0,
+             phases=0)
+    p.update(kw)
+    return dk.DattnParams(**p)
+
+
+def ws_size(lib, p, kind=0, sb=0):
+    n = ctypes.c_size_t(0)
+    rc = lib.dattn_workspace_size(ctypes.byref(p) if p is not None else None, kind, sb, ctypes.byref(n))
+    return rc, n.value, lib.dattn_last_error().decode()
+
+
+BAD = [
+    (dict(num_seqs=-1), dk.ERR_INVALID, "num_seqs"),
+    (dict(num_heads=0), dk.ERR_INVALID, "num_heads"),
+    (dict(num_heads=6, num_kv_heads=4), dk.ERR_INVALID, "multiple"),
+    (dict(num_heads=32, num_kv_heads=2), dk.ERR_UNSUPPORTED, "GQA"),
+    (dict(num_heads=6, num_kv_heads=2), dk.ERR_UNSUPPORTED, "GQA"),
+    (dict(head_dim=96), dk.ERR_UNSUPPORTED, "head_dim"),
+    (dict(scale=float("nan")), dk.ERR_INVALID, "scale"),
+    (dict(softcap=float("inf")), dk.ERR_INVALID, "softcap"),
+    (dict(causal=2), dk.ERR_INVALID, "causal"),
+    (dict(sliding_window=-3), dk.ERR_INVALID, "sliding_window"),
+    (dict(block_size=0), dk.ERR_INVALID, "block_size"),
+    (dict(max_blocks_per_seq=0), dk.ERR_INVALID, "max_blocks_per_seq"),
+    (dict(num_blocks=0), dk.ERR_INVALID, "num_blocks"),
+    (dict(max_seq_len=-1), dk.ERR_INVALID, "max_seq_len"),
+    (dict(max_seq_len=129), dk.ERR_INVALID, "exceeds"),
+    (dict(split_tokens=24), dk.ERR_INVALID, "split_tokens"),
+    (dict(split_tokens=-16), dk.ERR_INVALID, "split_tokens"),
+    (dict(phases=7), dk.ERR_INVALID, "phases"),
+    (dict(num_seqs=70000), dk.ERR_UNSUPPORTED, "num_seqs"),
+]
+
+
+@pytest.mark.parametrize("kw,code,word", BAD)
+def test_workspace_size_rejects(lib, kw, code, word):
+    rc, _, msg = ws_size(lib, good_params(**kw))
+    assert rc == code and word in msg, (rc, msg)
+
+
+def test_workspace_size_null_arguments(lib):
+    rc, _, msg = ws_size(lib, None)
+    assert rc == dk.ERR_INVALID and "NULL" in msg
+    assert lib.dattn_workspace_size(ctypes.byref(good_params()), 0, 0, None) == dk.ERR_INVALID
+    rc, _, msg = ws_size(lib, good_params(), kind=9)
+    assert rc == dk.ERR_INVALID and "kind" in msg
+
+
+def test_workspace_size_values(lib):
+    rc, n, _ = ws_size(lib, good_params(split_tokens=32))
+    assert rc == 0
+    S, B, H, D = 4, 2, 8, 128          # ceil(100 / 32) splits
+    acc = B * H * S * D * 4
+    ml = B * H * S * 8
+    up = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    assert n == up(acc) + up(ml)
+    # the tiered table only maps the cold prefix: max_seq_len may exceed it
+    assert ws_size(lib, good_params(max_seq_len=500), kind=dk.KIND_TIERED_INT8)[0] == 0
+    # sparse: sparse_block must be a positive multiple of block_size
+    assert ws_size(lib, good_params(), kind=dk.KIND_BLOCK_SPARSE, sb=24)[0] == dk.ERR_INVALID
+    assert ws_size(lib, good_params(), kind=dk.KIND_BLOCK_SPARSE, sb=32)[0] == 0
+
+
+def test_decode_calls_validate_before_any_hip_call(lib):
+    p = good_params()
+    P = ctypes.c_void_p
+    fake = P(0x1000)   # never dereferenced: every call below fails validation
+    # bad dtype
+    rc = lib.dattn_decode_paged(ctypes.byref(p), fake, fake, fake, 5, fake, fake, None, fake, None, fake, 1 << 20, None)
+    assert rc == dk.ERR_INVALID and "kv_dtype" in dk.dattn_last_error()
+    # NULL input
+    rc = lib.dattn_decode_paged(ctypes.byref(p), None, fake, fake, dk.F16, fake, fake, None, fake, None, fake, 1 << 20,
+                                None)
+    assert rc == dk.ERR_INVALID and "NULL" in dk.dattn_last_error()
+    # workspace too small / NULL / misaligned
+    rc = lib.dattn_decode_paged(ctypes.byref(p), fake, fake, fake, dk.F16, fake, fake, None, fake, None, fake, 16, None)
+    assert rc == dk.ERR_WORKSPACE and "smaller" in dk.dattn_last_error()
+    rc = lib.dattn_decode_paged(ctypes.byref(p), fake, fake, fake, dk.F16, fake, fake, None, fake, None, None, 1 << 20,
+                                None)
+    assert rc == dk.ERR_WORKSPACE
+    rc = lib.dattn_decode_paged(ctypes.byref(p), fake, fake, fake, dk.F16, fake, fake, None, fake, None, P(0x1004),
+                                1 << 20, None)
+    assert rc == dk.ERR_WORKSPACE and "aligned" in dk.dattn_last_error()
+    # tiered: hot_window
+    rc = lib.dattn_decode_tiered_int8(ctypes.byref(p), fake, fake, fake, 0, fake, fake, fake, fake, fake, fake, fake,
+                                      None, fake, None, fake, 1 << 20, None)
+    assert rc == dk.ERR_INVALID and "hot_window" in dk.dattn_last_error()
+    # sparse: layouts / strides
+    for args, word in (((64, 0, fake, 5, fake, 5), "num_layouts"), ((64, 2, fake, 1, fake, 5), "row_stride"),
+                       ((64, 2, fake, 5, fake, 0), "col_stride"), ((20, 2, fake, 5, fake, 5), "sparse_block")):
+        rc = lib.dattn_decode_block_sparse(ctypes.byref(p), fake, fake, fake, fake, fake, None, *args, fake, None,
+                                           fake, 1 << 20, None)
+        assert rc == dk.ERR_INVALID and word in dk.dattn_last_error()
+    # combine-only phase does not need the inputs, but needs out
+    pc = good_params(phases=dk.PHASE_COMBINE)
+    rc = lib.dattn_decode_paged(ctypes.byref(pc), None, None, None, dk.F16, None, None, None, None, None, fake,
+                                1 << 20, None)
+    assert rc == dk.ERR_INVALID and "out" in dk.dattn_last_error()
+
+
+def test_empty_batch_is_a_no_op(lib):
+    p = good_params(num_seqs=0)
+    rc = lib.dattn_decode_paged(ctypes.byref(p), None, None, None, dk.F16, None, None, None, None, None, None, 0, None)
+    assert rc == 0 and dk.dattn_last_error() == ""
+
+
+def test_binding_refuses_host_tensors(lib):
+    torch = pytest.importorskip("torch")
+    q = torch.zeros((1, 4, 64), dtype=torch.float32)
+    k = torch.zeros((1, 16, 2, 64), dtype=torch.float16)
+    bt = torch.zeros((1, 1), dtype=torch.int32)
+    sl = torch.ones((1,), dtype=torch.int32)
+    with pytest.raises(ValueError, match="GPU"):
+        dk.dattn_decode_paged(q, k, k, bt, sl, max_seq_len=1)
+    with pytest.raises(TypeError):
+        dk.dattn_decode_paged(q.double(), k, k, bt, sl, max_seq_len=1)
