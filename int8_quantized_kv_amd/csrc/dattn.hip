@@ -7,7 +7,10 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <map>
+#include <mutex>
 #include <string>
+#include <tuple>
 
 #include "dattn.h"
 #include "decode_kernels.h"
@@ -37,9 +40,18 @@ struct Plan {
   int sparse_nblk = 0;       // sparse
   int waves = 0;             // kv heads per workgroup
   size_t lds = 0;
-  size_t acc_bytes = 0, ml_bytes = 0;
+  size_t acc_bytes = 0, ml_bytes = 0;  // static-split layout
+  bool balanced_ok = false;            // the balanced schedule may be used (decided at launch)
+  size_t bal_acc_bytes = 0, bal_ml_bytes = 0, bal_sched_bytes = 0;
   size_t workspace = 0;
 };
+
+// Balanced schedule bounds: at most kMaxWorkers workgroups, so at most
+// kMaxWorkers + B partial slots; sequences up to kMaxBalancedSeqs (their tile
+// prefix lives in LDS).
+constexpr int kMaxWorkers = 1024;
+constexpr int kMaxBalancedSeqs = 4096;
+constexpr size_t kMaxBalancedLds = 16384;
 
 int check_params(const dattn_params* p, int kind) {
   if (!p) return fail(DATTN_ERR_INVALID, "params is NULL");
@@ -132,7 +144,74 @@ int make_plan(const dattn_params* p, int kind, int32_t sparse_block, Plan& pl) {
   pl.acc_bytes = align_up(heads * pl.num_splits * p->head_dim * sizeof(float));
   pl.ml_bytes = align_up(heads * pl.num_splits * sizeof(float2));
   pl.workspace = pl.acc_bytes + pl.ml_bytes;
+  pl.balanced_ok = p->split_tokens == 0 && kind != DATTN_KIND_BLOCK_SPARSE && p->num_seqs >= 1 &&
+                   p->num_seqs <= kMaxBalancedSeqs;
+  if (pl.balanced_ok) {
+    const size_t slots = (size_t)kMaxWorkers + p->num_seqs;
+    pl.bal_acc_bytes = align_up(slots * p->num_heads * p->head_dim * sizeof(float));
+    pl.bal_ml_bytes = align_up(slots * p->num_heads * sizeof(float2));
+    pl.bal_sched_bytes = align_up((size_t)(p->num_seqs + 3) * sizeof(int32_t));
+    const size_t bal = pl.bal_acc_bytes + pl.bal_ml_bytes + pl.bal_sched_bytes;
+    if (bal > pl.workspace) pl.workspace = bal;
+  }
   return DATTN_OK;
+}
+
+// ---- device properties (cached per device) for sizing the balanced grid
+
+std::mutex g_mu;
+std::map<int, int> g_cus;
+std::map<std::tuple<int, const void*, int>, int> g_occ;
+
+// Workgroups of `fn` (block threads, 16 KiB LDS) resident per CU; 0 on error.
+int resident_groups(const void* fn, int block, int& cus) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  std::lock_guard<std::mutex> lk(g_mu);
+  auto it = g_cus.find(dev);
+  if (it == g_cus.end()) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    it = g_cus.emplace(dev, n).first;
+  }
+  cus = it->second;
+  const auto key = std::make_tuple(dev, fn, block);
+  auto jt = g_occ.find(key);
+  if (jt == g_occ.end()) {
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, block, kMaxBalancedLds) != hipSuccess) return 0;
+    jt = g_occ.emplace(key, nb).first;
+  }
+  return jt->second;
+}
+
+struct Balanced {
+  bool on = false;
+  int workers = 0;  // workgroups per kv-head group (grid.x)
+  size_t lds = 0;
+};
+
+// Use the balanced schedule when allowed and it fits: one round of resident
+// workgroups, and the per-worker block-table staging within kMaxBalancedLds.
+Balanced plan_balanced(const dattn_params* p, const Plan& pl, const void* fn) {
+  Balanced bl;
+  if (!pl.balanced_ok) return bl;
+  int cus = 0;
+  const int per_cu = resident_groups(fn, 64 * pl.waves, cus);
+  if (per_cu <= 0 || cus <= 0) {
+    (void)hipGetLastError();
+    return bl;
+  }
+  const int groups = p->num_kv_heads / pl.waves;
+  int total = cus * per_cu;
+  if (total > kMaxWorkers) total = kMaxWorkers;
+  bl.workers = total / groups > 0 ? total / groups : 1;
+  const int64_t nmax = (int64_t)p->num_seqs * (((int64_t)p->max_seq_len + 15) / 16 + 1);
+  const int64_t cmax = (nmax + bl.workers - 1) / bl.workers;
+  const int64_t entries = cmax * 16 / p->block_size + 2;
+  bl.lds = (size_t)(((p->num_seqs + 4) & ~3) + entries) * sizeof(int32_t);
+  bl.on = bl.lds <= kMaxBalancedLds;
+  return bl;
 }
 
 dattn::DecodeArgs base_args(const dattn_params* p, const Plan& pl, const float* q, void* ws) {
@@ -140,6 +219,7 @@ dattn::DecodeArgs base_args(const dattn_params* p, const Plan& pl, const float* 
   a.q = q;
   a.part_acc = (float*)ws;
   a.part_ml = (float2*)((char*)ws + pl.acc_bytes);
+  a.num_seqs = p->num_seqs;
   a.num_heads = p->num_heads;
   a.num_kv_heads = p->num_kv_heads;
   a.max_blocks = p->max_blocks_per_seq;
@@ -202,6 +282,18 @@ template <int D, int G, bool CAP>
 struct Sparse {
   static auto fn() { return &dattn::sparse_split_kernel<D, G, CAP>; }
 };
+template <int D, int G, bool CAP>
+struct BalF16 {
+  static auto fn() { return &dattn::balanced_kernel<D, G, CAP, 0>; }
+};
+template <int D, int G, bool CAP>
+struct BalF32 {
+  static auto fn() { return &dattn::balanced_kernel<D, G, CAP, 1>; }
+};
+template <int D, int G, bool CAP>
+struct BalTiered {
+  static auto fn() { return &dattn::balanced_kernel<D, G, CAP, 2>; }
+};
 
 // Kernel instance for (head_dim, GQA group, softcap on/off).
 template <template <int, int, bool> class K>
@@ -220,25 +312,41 @@ int check_io(const dattn_params* p, bool split_inputs_ok, float* out) {
   return DATTN_OK;
 }
 
-int launch(void* split_fn, const dattn_params* p, const Plan& pl, dattn::DecodeArgs& a, float* out, float* lse,
-           hipStream_t st) {
+int launch(void* split_fn, void* bal_fn, const dattn_params* p, const Plan& pl, dattn::DecodeArgs& a, float* out,
+           float* lse, hipStream_t st) {
+  const Balanced bl = bal_fn ? plan_balanced(p, pl, bal_fn) : Balanced{};
+  if (bl.on) {
+    a.part_ml = (float2*)((char*)a.part_acc + pl.bal_acc_bytes);
+    a.sched = (int32_t*)((char*)a.part_acc + pl.bal_acc_bytes + pl.bal_ml_bytes);
+  }
   if (run_split(p)) {
-    dim3 grid(pl.num_splits, p->num_seqs, p->num_kv_heads / pl.waves);
-    dim3 block(64 * pl.waves);
+    const dim3 grid = bl.on ? dim3(bl.workers, 1, p->num_kv_heads / pl.waves)
+                            : dim3(pl.num_splits, p->num_seqs, p->num_kv_heads / pl.waves);
+    const dim3 block(64 * pl.waves);
     void* args[] = {&a};
-    hipError_t e = hipLaunchKernel(split_fn, grid, block, args, pl.lds, st);
+    hipError_t e = hipLaunchKernel(bl.on ? bal_fn : split_fn, grid, block, args, bl.on ? bl.lds : pl.lds, st);
     if (e != hipSuccess) return fail(DATTN_ERR_LAUNCH, "split kernel launch failed: %s", hipGetErrorString(e));
     int rc = check_launch("split kernel");
     if (rc) return rc;
   }
   if (!run_combine(p)) return DATTN_OK;
   const int nbh = p->num_seqs * p->num_heads;
-  if (p->head_dim == 64)
-    hipLaunchKernelGGL(dattn::combine_kernel<64>, dim3(nbh), dim3(256), 0, st, a.part_acc, a.part_ml, out, lse,
-                       pl.num_splits);
-  else
-    hipLaunchKernelGGL(dattn::combine_kernel<128>, dim3(nbh), dim3(256), 0, st, a.part_acc, a.part_ml, out, lse,
-                       pl.num_splits);
+  const dim3 cgrid(nbh);   // one workgroup per (sequence, head)
+  if (bl.on) {
+    if (p->head_dim == 64)
+      hipLaunchKernelGGL(dattn::combine_balanced_kernel<64>, cgrid, dim3(256), 0, st, a.part_acc, a.part_ml,
+                         a.sched, out, lse, p->num_heads, nbh);
+    else
+      hipLaunchKernelGGL(dattn::combine_balanced_kernel<128>, cgrid, dim3(256), 0, st, a.part_acc, a.part_ml,
+                         a.sched, out, lse, p->num_heads, nbh);
+  } else {
+    if (p->head_dim == 64)
+      hipLaunchKernelGGL(dattn::combine_kernel<64>, cgrid, dim3(256), 0, st, a.part_acc, a.part_ml, out, lse,
+                         pl.num_splits, nbh);
+    else
+      hipLaunchKernelGGL(dattn::combine_kernel<128>, cgrid, dim3(256), 0, st, a.part_acc, a.part_ml, out, lse,
+                         pl.num_splits, nbh);
+  }
   return check_launch("combine kernel");
 }
 
@@ -279,8 +387,10 @@ int dattn_decode_paged(const dattn_params* p, const float* q, const void* k_cach
   a.seq_lens = seq_lens;
   a.q_pos = q_pos;
   const bool cap = p->softcap > 0.0f;
-  void* fn = kv_dtype == DATTN_F16 ? pick<PagedF16>(p->head_dim, pl.G, cap) : pick<PagedF32>(p->head_dim, pl.G, cap);
-  return launch(fn, p, pl, a, out, lse, (hipStream_t)stream);
+  const bool f16 = kv_dtype == DATTN_F16;
+  void* fn = f16 ? pick<PagedF16>(p->head_dim, pl.G, cap) : pick<PagedF32>(p->head_dim, pl.G, cap);
+  void* bal = f16 ? pick<BalF16>(p->head_dim, pl.G, cap) : pick<BalF32>(p->head_dim, pl.G, cap);
+  return launch(fn, bal, p, pl, a, out, lse, (hipStream_t)stream);
 }
 
 int dattn_decode_tiered_int8(const dattn_params* p, const float* q, const uint16_t* k_hot, const uint16_t* v_hot,
@@ -313,7 +423,9 @@ int dattn_decode_tiered_int8(const dattn_params* p, const float* q, const uint16
   a.seq_lens = seq_lens;
   a.cold_lens = cold_lens;
   a.q_pos = q_pos;
-  return launch(pick<Tiered>(p->head_dim, pl.G, p->softcap > 0.0f), p, pl, a, out, lse, (hipStream_t)stream);
+  const bool cap = p->softcap > 0.0f;
+  return launch(pick<Tiered>(p->head_dim, pl.G, cap), pick<BalTiered>(p->head_dim, pl.G, cap), p, pl, a, out, lse,
+                (hipStream_t)stream);
 }
 
 int dattn_decode_block_sparse(const dattn_params* p, const float* q, const uint16_t* k_cache,
@@ -346,7 +458,8 @@ int dattn_decode_block_sparse(const dattn_params* p, const float* q, const uint1
   a.sparse_nblk = pl.sparse_nblk;
   a.blocks_per_split = pl.blocks_per_split;
   a.sb = dattn::make_fastdiv((uint32_t)sparse_block);
-  return launch(pick<Sparse>(p->head_dim, pl.G, p->softcap > 0.0f), p, pl, a, out, lse, (hipStream_t)stream);
+  return launch(pick<Sparse>(p->head_dim, pl.G, p->softcap > 0.0f), nullptr, p, pl, a, out, lse,
+                (hipStream_t)stream);
 }
 
 }  // extern "C"

@@ -63,9 +63,10 @@ struct DecodeArgs {
   const int32_t* q_pos;      // may be null
   const int32_t* row_ptr;    // sparse CSR
   const int32_t* col_idx;
-  float* part_acc;           // [B, H, S, D]
-  float2* part_ml;           // [B, H, S]  (m in log2 units, l)
-  int32_t num_heads, num_kv_heads, max_blocks, num_splits, split_tokens;
+  float* part_acc;           // [B, H, S, D] (static splits) or [slots, H, D] (balanced)
+  float2* part_ml;           // [B, H, S] or [slots, H]  (m in log2 units, l)
+  int32_t* sched;            // balanced: N, C, P[0..B]
+  int32_t num_seqs, num_heads, num_kv_heads, max_blocks, num_splits, split_tokens;
   int32_t causal, window, hot_window;
   int32_t sparse_block, num_layouts, row_stride, col_stride, sparse_nblk, blocks_per_split;
   float qmul;    // scale * log2(e) without softcap, scale / cap with softcap
@@ -548,6 +549,27 @@ struct SparseMap {
 
 // ------------------------------------------------- online softmax state
 
+// Where the partial (acc[D], (m, l)) of heads kvh*G + h, h < G, goes.
+struct PartialDst {
+  float* acc;            // head 0's acc row
+  size_t acc_hstride;    // floats between consecutive heads
+  float2* ml;            // head 0's (m, l)
+  size_t ml_hstride;
+};
+
+// Static splits: partials [B, H, S, D] and [B, H, S].
+__device__ __forceinline__ PartialDst split_dst(const DecodeArgs& a, int b, int kvh, int G, int split, int D) {
+  const size_t S = (size_t)a.num_splits;
+  const size_t head0 = (size_t)b * a.num_heads + (size_t)kvh * G;
+  return PartialDst{a.part_acc + (head0 * S + split) * D, S * D, a.part_ml + head0 * S + split, S};
+}
+
+// Balanced schedule: partials [slots, H, D] and [slots, H].
+__device__ __forceinline__ PartialDst slot_dst(const DecodeArgs& a, int slot, int kvh, int G, int D) {
+  const size_t head0 = (size_t)slot * a.num_heads + (size_t)kvh * G;
+  return PartialDst{a.part_acc + head0 * D, (size_t)D, a.part_ml + head0, 1};
+}
+
 template <int D, int G, bool CAP>
 struct Online {
   float m;            // running max (log2 units) of head lane%16 -- equal in all rows
@@ -603,8 +625,8 @@ struct Online {
     });
   }
 
-  // Reduce across lanes and write the split partial of heads kvh*G + [0, G).
-  __device__ __forceinline__ void finish(const DecodeArgs& a, int b, int kvh, int split, int lane) {
+  // Reduce across lanes and write the partial of heads kvh*G + [0, G).
+  __device__ __forceinline__ void finish(const PartialDst& dst, int lane) {
     float lt = l + shfl_xor_f(l, 16);
     lt += shfl_xor_f(lt, 32);
 #pragma unroll
@@ -617,26 +639,21 @@ struct Online {
         x += shfl_xor_f(x, 32);
         acc[h][d] = x;
       }
-    const size_t S = (size_t)a.num_splits;
-    const size_t head0 = (size_t)b * a.num_heads + (size_t)kvh * G;
     if (lane < Lay<D>::DPR) {
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        float* dst = a.part_acc + ((head0 + h) * S + split) * D + 8 * lane;
-        *(f4*)dst = f4{acc[h][0], acc[h][1], acc[h][2], acc[h][3]};
-        *(f4*)(dst + 4) = f4{acc[h][4], acc[h][5], acc[h][6], acc[h][7]};
+        float* o = dst.acc + h * dst.acc_hstride + 8 * lane;
+        *(f4*)o = f4{acc[h][0], acc[h][1], acc[h][2], acc[h][3]};
+        *(f4*)(o + 4) = f4{acc[h][4], acc[h][5], acc[h][6], acc[h][7]};
       }
     }
-    if (lane < G) a.part_ml[(head0 + lane) * S + split] = make_float2(m, lt);
+    if (lane < G) dst.ml[lane * dst.ml_hstride] = make_float2(m, lt);
   }
 };
 
 template <int G>
-__device__ __forceinline__ void write_empty(const DecodeArgs& a, int b, int kvh, int split, int lane) {
-  if (lane < G) {
-    const size_t head0 = (size_t)b * a.num_heads + (size_t)kvh * G;
-    a.part_ml[(head0 + lane) * (size_t)a.num_splits + split] = make_float2(-__builtin_inff(), 0.f);
-  }
+__device__ __forceinline__ void write_empty(const PartialDst& dst, int lane) {
+  if (lane < G) dst.ml[lane * dst.ml_hstride] = make_float2(-__builtin_inff(), 0.f);
 }
 
 // ------------------------------------------------------------ tile engine
@@ -717,28 +734,31 @@ __device__ __forceinline__ void run_tiles(const DecodeArgs& a, const Store& st, 
 
 // ---------------------------------------------------------------- kernels
 
-// Stage block-table entries [blk0, blk0 + n) of sequence b into LDS.
+// Stage block-table entries [blk0, blk0 + n) of sequence b into LDS, once
+// every wave of the workgroup is done with the previous contents.
 __device__ __forceinline__ void stage_table(const DecodeArgs& a, int b, int blk0, int n, int32_t* lds) {
+  __syncthreads();
   const int32_t* src = a.table + (size_t)b * a.max_blocks + blk0;
   for (int i = threadIdx.x; i < n; i += blockDim.x) lds[i] = src[i];
   __syncthreads();
 }
 
-template <int D, int G, bool CAP, class T>
-__global__ __launch_bounds__(256) void paged_split_kernel(DecodeArgs a) {
-  extern __shared__ int32_t lds_tbl[];
-  const int split = blockIdx.x, b = blockIdx.y;
-  const int lane = threadIdx.x & 63;
-  const int kvh = blockIdx.z * (blockDim.x >> 6) + (threadIdx.x >> 6);
-  int lo, hi, qp;
-  visible_range(a, b, lo, hi, qp);
-  const int tb = max(split * a.split_tokens, lo);
-  const int te = min((split + 1) * a.split_tokens, hi + 1);   // [tb, te)
-  int blk0 = 0, nblk = 0;
-  if (tb < te) {
-    blk0 = (int)fdiv((uint32_t)tb, a.bs);
-    nblk = (int)fdiv((uint32_t)(te - 1), a.bs) - blk0 + 1;
+// Blocks holding keys [t0, t1).
+__device__ __forceinline__ void table_span(const DecodeArgs& a, int t0, int t1, int& blk0, int& n) {
+  blk0 = 0;
+  n = 0;
+  if (t0 < t1) {
+    blk0 = (int)fdiv((uint32_t)t0, a.bs);
+    n = (int)fdiv((uint32_t)(t1 - 1), a.bs) - blk0 + 1;
   }
+}
+
+// Sweep keys [tb, te) of sequence b for one kv head of a paged cache and write
+// the partial to dst.  Every wave of the workgroup calls it with the same
+// (b, tb, te): the block-table staging is shared.
+template <int D, int G, bool CAP, class T>
+__device__ __forceinline__ void paged_segment(const DecodeArgs& a, int b, int kvh, int lane, int tb, int te,
+                                              int32_t* lds_tbl, const PartialDst& dst) {
   using QRaw = std::conditional_t<std::is_same_v<T, float>, QRaw32<D>, QRaw16<D>>;
   QRaw qraw;
   if (tb < te) {
@@ -747,9 +767,11 @@ __global__ __launch_bounds__(256) void paged_split_kernel(DecodeArgs a) {
     else
       load_q_raw16<D, G, false>(a, b, kvh, lane, qraw);
   }
+  int blk0, nblk;
+  table_span(a, tb, te, blk0, nblk);
   stage_table(a, b, blk0, nblk, lds_tbl);
   if (tb >= te) {
-    write_empty<G>(a, b, kvh, split, lane);
+    write_empty<G>(dst, lane);
     return;
   }
   LaneGeo<D> lg;
@@ -768,35 +790,27 @@ __global__ __launch_bounds__(256) void paged_split_kernel(DecodeArgs a) {
     run_tiles<D, G, CAP, kPipe>(a, st, map, qf, [&](QF16<D>& q) { convert_q<D, G>(a, lane, qraw, q); }, lg, on,
                                 tb & ~(kTile - 1), te, lane);
   }
-  on.finish(a, b, kvh, split, lane);
+  on.finish(dst, lane);
 }
 
+// The same for the tiered cache: keys below cold_lens[b] from the paged int8
+// pool, the rest from the f16 ring.
 template <int D, int G, bool CAP>
-__global__ __launch_bounds__(256) void tiered_split_kernel(DecodeArgs a) {
-  extern __shared__ int32_t lds_tbl[];
-  const int split = blockIdx.x, b = blockIdx.y;
-  const int lane = threadIdx.x & 63;
-  const int kvh = blockIdx.z * (blockDim.x >> 6) + (threadIdx.x >> 6);
-  int lo, hi, qp;
-  visible_range(a, b, lo, hi, qp);
+__device__ __forceinline__ void tiered_segment(const DecodeArgs& a, int b, int kvh, int lane, int tb, int te,
+                                               int32_t* lds_tbl, const PartialDst& dst) {
   const int C = a.cold_lens[b];
-  const int tb = max(split * a.split_tokens, lo);
-  const int te = min((split + 1) * a.split_tokens, hi + 1);
-  const int ce = min(te, C);          // cold part [tb, ce)
-  const int hb = max(tb, C);          // hot part  [hb, te)
-  int blk0 = 0, nblk = 0;
-  if (tb < ce) {
-    blk0 = (int)fdiv((uint32_t)tb, a.bs);
-    nblk = (int)fdiv((uint32_t)(ce - 1), a.bs) - blk0 + 1;
-  }
-  QRaw16<D> qraw;   // cold keys use the int8 dim map, a split of hot keys only the f16 one
+  const int ce = min(te, C);   // cold part [tb, ce)
+  const int hb = max(tb, C);   // hot part  [hb, te)
+  QRaw16<D> qraw;              // cold keys use the int8 dim map, a sweep of hot keys only the f16 one
   if (tb < ce)
     load_q_raw16<D, G, true>(a, b, kvh, lane, qraw);
   else if (tb < te)
     load_q_raw16<D, G, false>(a, b, kvh, lane, qraw);
+  int blk0, nblk;
+  table_span(a, tb, ce, blk0, nblk);
   stage_table(a, b, blk0, nblk, lds_tbl);
   if (tb >= te) {
-    write_empty<G>(a, b, kvh, split, lane);
+    write_empty<G>(dst, lane);
     return;
   }
   LaneGeo<D> lg;
@@ -821,7 +835,131 @@ __global__ __launch_bounds__(256) void tiered_split_kernel(DecodeArgs a) {
                                 },
                                 lg, on, hb & ~(kTile - 1), te, lane);
   }
-  on.finish(a, b, kvh, split, lane);
+  on.finish(dst, lane);
+}
+
+// Static splits: workgroup (split, b, z) sweeps keys [split*T, (split+1)*T)
+// of sequence b for kv heads z*waves + [0, waves).
+template <int D, int G, bool CAP, class T>
+__global__ __launch_bounds__(256) void paged_split_kernel(DecodeArgs a) {
+  extern __shared__ int32_t lds_tbl[];
+  const int split = blockIdx.x, b = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int kvh = blockIdx.z * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  int lo, hi, qp;
+  visible_range(a, b, lo, hi, qp);
+  const int tb = max(split * a.split_tokens, lo);
+  const int te = min((split + 1) * a.split_tokens, hi + 1);
+  paged_segment<D, G, CAP, T>(a, b, kvh, lane, tb, te, lds_tbl, split_dst(a, b, kvh, G, split, D));
+}
+
+template <int D, int G, bool CAP>
+__global__ __launch_bounds__(256) void tiered_split_kernel(DecodeArgs a) {
+  extern __shared__ int32_t lds_tbl[];
+  const int split = blockIdx.x, b = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int kvh = blockIdx.z * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  int lo, hi, qp;
+  visible_range(a, b, lo, hi, qp);
+  const int tb = max(split * a.split_tokens, lo);
+  const int te = min((split + 1) * a.split_tokens, hi + 1);
+  tiered_segment<D, G, CAP>(a, b, kvh, lane, tb, te, lds_tbl, split_dst(a, b, kvh, G, split, D));
+}
+
+// ------------------------------------------------------- balanced schedule
+//
+// The visible keys of sequence b are cut into 16-key tiles aligned to
+// absolute positions; b owns tiles [P[b], P[b+1]) of the concatenation over
+// all sequences (N tiles in all).  Worker w of a kv-head group (blockIdx.x)
+// owns tiles [w*C, min((w+1)*C, N)) with C = ceil(N / gridDim.x), so every
+// worker streams the same number of tiles whatever the length mix, and the
+// grid is one round of resident workgroups.  A worker's range can cross
+// sequence boundaries; its piece of sequence b is partial slot w + b, which
+// no other (worker, sequence) pair shares because each boundary along the
+// concatenation advances w, b or both.  Worker 0 of group 0 leaves N, C and
+// P in the schedule area of the workspace for the combine kernel.
+
+__device__ __forceinline__ int seq_tiles(const DecodeArgs& a, int b) {
+  int lo, hi, q;
+  visible_range(a, b, lo, hi, q);
+  return hi < lo ? 0 : (hi >> 4) - (lo >> 4) + 1;
+}
+
+// P[0..B] (exclusive prefix of tile counts) into LDS; returns N = P[B].
+__device__ __forceinline__ int tile_prefix(const DecodeArgs& a, int32_t* P) {
+  const int B = a.num_seqs;
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    int run = 0;
+    for (int base = 0; base < B; base += 64) {
+      const int b = base + lane;
+      const int c = b < B ? seq_tiles(a, b) : 0;
+      int x = c;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o, 64);
+        if (lane >= o) x += y;
+      }
+      if (b < B) P[b] = run + x - c;
+      run += __shfl(x, 63, 64);
+    }
+    if (lane == 0) P[B] = run;
+  }
+  __syncthreads();
+  return P[B];
+}
+
+// KIND: 0 paged f16, 1 paged f32, 2 tiered.  Registers are capped for two
+// waves per SIMD when the GQA group is at most 4 (more waves keep more loads
+// in flight than the register savings cost).
+template <int D, int G, bool CAP, int KIND>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 2 : 1)))
+void balanced_kernel(DecodeArgs a) {
+  extern __shared__ int32_t lds[];
+  const int B = a.num_seqs;
+  int32_t* P = lds;
+  int32_t* tbl = lds + ((B + 4) & ~3);
+  const int w = blockIdx.x, nw = gridDim.x;
+  const int lane = threadIdx.x & 63;
+  const int kvh = blockIdx.z * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  const int N = tile_prefix(a, P);
+  const int C = (N + nw - 1) / nw;
+  if (w == 0 && blockIdx.z == 0) {
+    for (int i = threadIdx.x; i <= B; i += blockDim.x) a.sched[2 + i] = P[i];
+    if (threadIdx.x == 0) {
+      a.sched[0] = N;
+      a.sched[1] = C;
+    }
+  }
+  int x0 = w * C;
+  const int x1 = min(x0 + C, N);
+  if (x0 >= x1) return;
+  int b = 0, top = B - 1;   // last b with P[b] <= x0
+  while (b < top) {
+    const int mid = (b + top + 1) >> 1;
+    if (P[mid] <= x0)
+      b = mid;
+    else
+      top = mid - 1;
+  }
+  while (x0 < x1) {
+    while (P[b + 1] <= x0) ++b;
+    const int seg_end = min(x1, P[b + 1]);
+    int lo, hi, qp;
+    visible_range(a, b, lo, hi, qp);
+    const int base = lo & ~(kTile - 1);
+    const int tb = max(lo, base + kTile * (x0 - P[b]));
+    const int te = min(hi + 1, base + kTile * (seg_end - P[b]));
+    const PartialDst dst = slot_dst(a, w + b, kvh, G, D);
+    if constexpr (KIND == 2)
+      tiered_segment<D, G, CAP>(a, b, kvh, lane, tb, te, tbl, dst);
+    else if constexpr (KIND == 1)
+      paged_segment<D, G, CAP, float>(a, b, kvh, lane, tb, te, tbl, dst);
+    else
+      paged_segment<D, G, CAP, _Float16>(a, b, kvh, lane, tb, te, tbl, dst);
+    x0 = seg_end;
+    ++b;
+  }
 }
 
 // Block-sparse: each wave builds the union of the CSR rows of its G heads in
@@ -868,10 +1006,11 @@ __global__ __launch_bounds__(256) void sparse_split_kernel(DecodeArgs a) {
     count += __builtin_popcountll(bal);
   }
   __syncthreads();
+  const PartialDst dst = split_dst(a, b, kvh, G, split, D);
   const int e0 = split * a.blocks_per_split;
   const int e1 = min(e0 + a.blocks_per_split, count);
   if (e0 >= e1 || lo > hi) {
-    write_empty<G>(a, b, kvh, split, lane);
+    write_empty<G>(dst, lane);
     return;
   }
   LaneGeo<D> lg;
@@ -884,58 +1023,118 @@ __global__ __launch_bounds__(256) void sparse_split_kernel(DecodeArgs a) {
   on.init();
   run_tiles<D, G, CAP, kPipe>(a, st, map, qf, [&](QF16<D>& q) { convert_q<D, G>(a, lane, qraw, q); }, lg, on,
                               e0 * (int)a.sb.d, map.slot_end, lane);
-  on.finish(a, b, kvh, split, lane);
+  on.finish(dst, lane);
 }
 
-// Merge the split partials of one (sequence, head): 4 waves stride over the
-// splits, lane owns dims lane + 64*j.
-template <int D>
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ part_acc,
-                                                      const float2* __restrict__ part_ml, float* __restrict__ out,
-                                                      float* __restrict__ lse, int S) {
-  constexpr int NJ = D / 64;
-  __shared__ float red[4][D];
-  __shared__ float redl[4], redm[4];
-  const size_t bh = blockIdx.x;
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const float2* ml = part_ml + bh * S;
+// ------------------------------------------------------------------ combine
+//
+// Merge the partials of one (sequence, head): M = max m_s,
+// l = sum l_s 2^{m_s - M}, out = sum acc_s 2^{m_s - M} / l, lse = (M + log2 l) ln 2.
+// One workgroup per (sequence, head).  Partials with l = 0 (no visible key)
+// are skipped.
+
+template <int D, class Loc>
+__device__ __forceinline__ void merge_partials(const Loc& loc, int n, float* __restrict__ out,
+                                               float* __restrict__ lse_out) {
+  // 256 threads: slot group sg = tid / 32 takes partials sg, sg + 8, ...;
+  // within a group, thread c owns dims 4c + 128j.  (m, l) pairs are staged
+  // in LDS (first 256 partials), the rest read again from memory.
+  constexpr int NJ = D / 128 > 0 ? D / 128 : 1;
+  constexpr int DC = D >= 128 ? 32 : D / 4;   // threads per group carrying dims
+  __shared__ float2 mls[256];
+  __shared__ float red[8][D];
+  __shared__ float redm[8], redl[8];
+  const int tid = threadIdx.x, sg = tid >> 5, c = tid & 31;
   float M = -__builtin_inff();
-  for (int s = threadIdx.x; s < S; s += 256) {
-    float2 v = ml[s];
+  for (int s = tid; s < n; s += 256) {
+    const float2 v = loc.ml(s);
+    if (s < 256) mls[s] = v;
     if (v.y > 0.f) M = fmaxf(M, v.x);
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, shfl_xor_f(M, o));
-  if (lane == 0) redm[w] = M;
+  if ((tid & 63) == 0) redm[tid >> 6] = M;
   __syncthreads();
   M = fmaxf(fmaxf(redm[0], redm[1]), fmaxf(redm[2], redm[3]));
-  float L = 0.f, o[NJ];
+  float L = 0.f;
+  f4 o[NJ];
 #pragma unroll
-  for (int j = 0; j < NJ; ++j) o[j] = 0.f;
-  for (int s = w; s < S; s += 4) {
-    const float2 v = ml[s];
+  for (int j = 0; j < NJ; ++j) o[j] = f4{0.f, 0.f, 0.f, 0.f};
+  for (int s = sg; s < n; s += 8) {
+    const float2 v = s < 256 ? mls[s] : loc.ml(s);
     if (v.y > 0.f) {
       const float wt = fast_exp2(v.x - M);
       L += wt * v.y;
-      const float* row = part_acc + (bh * S + s) * D;
+      if (c < DC) {
+        const float* row = loc.acc(s);
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) o[j] += wt * row[lane + 64 * j];
+        for (int j = 0; j < NJ; ++j) o[j] += wt * *(const f4*)(row + 128 * j + 4 * c);
+      }
     }
   }
+  if (c < DC) {
 #pragma unroll
-  for (int j = 0; j < NJ; ++j) red[w][lane + 64 * j] = o[j];
-  if (lane == 0) redl[w] = L;
+    for (int j = 0; j < NJ; ++j) *(f4*)&red[sg][128 * j + 4 * c] = o[j];
+  }
+  if (c == 0) redl[sg] = L;
   __syncthreads();
-  if (w == 0) {
-    const float Lt = (redl[0] + redl[1]) + (redl[2] + redl[3]);
+  const float Lt = ((redl[0] + redl[1]) + (redl[2] + redl[3])) + ((redl[4] + redl[5]) + (redl[6] + redl[7]));
+  for (int d = tid; d < D; d += 256) {
+    float ot = 0.f;
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int d = lane + 64 * j;
-      const float ot = (red[0][d] + red[1][d]) + (red[2][d] + red[3][d]);
-      out[bh * D + d] = Lt > 0.f ? ot / Lt : 0.f;
-    }
-    if (lane == 0 && lse) lse[bh] = Lt > 0.f ? (M + __builtin_log2f(Lt)) * kLn2 : -__builtin_inff();
+    for (int g = 0; g < 8; ++g) ot += red[g][d];
+    out[d] = Lt > 0.f ? ot / Lt : 0.f;
   }
+  if (tid == 0 && lse_out) *lse_out = Lt > 0.f ? (M + __builtin_log2f(Lt)) * kLn2 : -__builtin_inff();
+}
+
+// Static splits: partials of (b, h) at [bh, s] for s < S.
+struct SplitLoc {
+  const float* acc0;
+  const float2* ml0;
+  int D;
+  __device__ __forceinline__ float2 ml(int s) const { return ml0[s]; }
+  __device__ __forceinline__ const float* acc(int s) const { return acc0 + (size_t)s * D; }
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ part_acc,
+                                                      const float2* __restrict__ part_ml, float* __restrict__ out,
+                                                      float* __restrict__ lse, int S, int nbh) {
+  const int bh = blockIdx.x;
+  const SplitLoc loc{part_acc + (size_t)bh * S * D, part_ml + (size_t)bh * S, D};
+  merge_partials<D>(loc, S, out + (size_t)bh * D, lse ? lse + bh : nullptr);
+}
+
+// Balanced schedule: the partials of (b, h) sit in slots w + b for the
+// workers w that own tiles of b, at [slot, h].
+struct SlotLoc {
+  const float* acc0;   // slot (w0 + b), head h
+  const float2* ml0;
+  int H, D;
+  __device__ __forceinline__ float2 ml(int s) const { return ml0[(size_t)s * H]; }
+  __device__ __forceinline__ const float* acc(int s) const { return acc0 + (size_t)s * H * D; }
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void combine_balanced_kernel(const float* __restrict__ part_acc,
+                                                               const float2* __restrict__ part_ml,
+                                                               const int32_t* __restrict__ sched,
+                                                               float* __restrict__ out, float* __restrict__ lse,
+                                                               int H, int nbh) {
+  const int bh = blockIdx.x;
+  const int b = bh / H, h = bh - b * H;
+  const int C = sched[1];
+  const int p0 = sched[2 + b], p1 = sched[3 + b];
+  int n = 0;
+  size_t slot0 = 0;
+  if (p1 > p0 && C > 0) {
+    const int w0 = p0 / C, w1 = (p1 - 1) / C;
+    n = w1 - w0 + 1;
+    slot0 = (size_t)(w0 + b);
+  }
+  const SlotLoc loc{part_acc + (slot0 * H + h) * D, part_ml + slot0 * H + h, H, D};
+  merge_partials<D>(loc, n, out + (size_t)bh * D, lse ? lse + bh : nullptr);
 }
 
 }  // namespace dattn
