@@ -134,6 +134,11 @@ def test_workspace_size_null_arguments(lib):
 
 
 def test_workspace_size_values(lib):
+    # the library-chosen split (split_tokens = 0) also sizes the balanced schedule's slots
+    rc, n0, _ = ws_size(lib, good_params())
+    up = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    slots = 1024 + 2
+    assert rc == 0 and n0 >= up(slots * 8 * 128 * 4) + up(slots * 8 * 8) + up(5 * 4)
     rc, n, _ = ws_size(lib, good_params(split_tokens=32))
     assert rc == 0
     S, B, H, D = 4, 2, 8, 128          # ceil(100 / 32) splits
@@ -166,7 +171,7 @@ def test_decode_calls_validate_before_any_hip_call(lib):
                                 None)
     assert rc == dk.ERR_WORKSPACE
     rc = lib.dattn_decode_paged(ctypes.byref(p), fake, fake, fake, dk.F16, fake, fake, None, fake, None, P(0x1004),
-                                1 << 20, None)
+                                1 << 40, None)
     assert rc == dk.ERR_WORKSPACE and "aligned" in dk.dattn_last_error()
     # tiered: hot_window
     rc = lib.dattn_decode_tiered_int8(ctypes.byref(p), fake, fake, fake, 0, fake, fake, fake, fake, fake, fake, fake,
