@@ -34,7 +34,7 @@ import numpy as np  # noqa: E402
 HBM_PEAK_GBS = 8000.0
 MALL_BYTES = 1.0e9     # rotate cache copies until each step touches new memory
 KERNEL_SOURCE = os.path.join(ROOT, "int8_quantized_kv_amd", "csrc", "decode_kernels.h")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_paged_split_f16.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_balanced_paged_f16_B32_H32x8_D128.txt")
 
 
 def log(msg):
@@ -371,7 +371,7 @@ def main():
         "kernels": {"split_ms": head["split_ms"], "combine_ms": head["combine_ms"]},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
-                     "kernel": f"paged_split_kernel<D={D}, G={H // case.params['num_kv_heads']}, f16>",
+                     "kernel": f"balanced_kernel<D={D}, G={H // case.params['num_kv_heads']}, paged f16>",
                      "bytes_per_launch": kvb},
         "parity_sample": {k: head[k] for k in ("sample_max_abs_err", "sample_rel_err", "sample_lse_err")},
         "copy_reference_gbs": copy_reference(),
