@@ -41,6 +41,9 @@ typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u2v __attribute__((ext_vector_type(2)));
 
 constexpr int kTile = 16;          // keys per tile
+#ifndef DATTN_MAX_THREADS
+#define DATTN_MAX_THREADS 256
+#endif
 #ifndef DATTN_PIPE
 #define DATTN_PIPE 2
 #endif
@@ -113,18 +116,20 @@ __device__ __forceinline__ void visible_range(const DecodeArgs& a, int b, int& l
 }
 
 // int8 x 8 (two LSB-first words, two's complement) -> exact f16 x 8.
-// Bias each byte by 128, drop it into the mantissa of 1024.0h (0x6400) and
-// subtract 1152: (1024 + i + 128) - 1152 = i exactly.
-__device__ __forceinline__ h2 i8pair_to_h2(uint32_t lo_byte_word) {
-  h2 v = __builtin_bit_cast(h2, lo_byte_word | 0x64006400u);
+// Bias each byte by 128 (xor 0x80), place it in the low mantissa byte of
+// 1024.0h (0x64xx) with one byte permute per pair, and subtract 1152:
+// (1024 + i + 128) - 1152 = i exactly.  v_perm_b32 picks bytes of {S0, S1}
+// (S1 = bytes 0-3, S0 = bytes 4-7); S0 = 0x64646464 supplies the 0x64 bytes.
+__device__ __forceinline__ h2 i8pair_to_h2(uint32_t biased, uint32_t sel) {
+  const h2 v = __builtin_bit_cast(h2, __builtin_amdgcn_perm(0x64646464u, biased, sel));
   return v - h2{(_Float16)1152.0f, (_Float16)1152.0f};
 }
 __device__ __forceinline__ h8 i8x8_to_h8(uint32_t w0, uint32_t w1) {
-  uint32_t x0 = w0 ^ 0x80808080u, x1 = w1 ^ 0x80808080u;
-  h2 a = i8pair_to_h2((x0 & 0xFFu) | ((x0 & 0xFF00u) << 8));
-  h2 b = i8pair_to_h2(((x0 >> 16) & 0xFFu) | ((x0 >> 8) & 0xFF0000u));
-  h2 c = i8pair_to_h2((x1 & 0xFFu) | ((x1 & 0xFF00u) << 8));
-  h2 d = i8pair_to_h2(((x1 >> 16) & 0xFFu) | ((x1 >> 8) & 0xFF0000u));
+  const uint32_t x0 = w0 ^ 0x80808080u, x1 = w1 ^ 0x80808080u;
+  const h2 a = i8pair_to_h2(x0, 0x04010400u);   // bytes 0, 1
+  const h2 b = i8pair_to_h2(x0, 0x04030402u);   // bytes 2, 3
+  const h2 c = i8pair_to_h2(x1, 0x04010400u);
+  const h2 d = i8pair_to_h2(x1, 0x04030402u);
   return h8{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
 }
 
@@ -311,6 +316,7 @@ struct StoreF16 {
     }
     return acc;
   }
+  __device__ __forceinline__ void scale_p(const KFrag&, float (&)[4]) const {}
   template <int G>
   __device__ __forceinline__ void pv(const VFrag& v, int e, const float (&w)[G], float (&acc)[G][8]) const {
     h8 x = __builtin_bit_cast(h8, v.r[e]);
@@ -367,6 +373,7 @@ struct StoreF32 {
     }
     return acc;
   }
+  __device__ __forceinline__ void scale_p(const KFrag&, float (&)[4]) const {}
   template <int G>
   __device__ __forceinline__ void pv(const VFrag& v, int e, const float (&w)[G], float (&acc)[G][8]) const {
     const float x[8] = {v.a[e].x, v.a[e].y, v.a[e].z, v.a[e].w, v.b[e].x, v.b[e].y, v.b[e].z, v.b[e].w};
@@ -384,10 +391,10 @@ struct StoreI8 {
   struct KFrag {
     u4 r[D / 64];
     uint16_t s[4];   // key scales of keys 4g + e
+    uint16_t vs[4];  // value scales of keys 4g + e
   };
   struct VFrag {
     u2v r[Lay<D>::NTV];
-    uint16_t s[Lay<D>::NTV];
   };
   const uint32_t* kbase;
   const uint32_t* vbase;
@@ -401,12 +408,14 @@ struct StoreI8 {
 #pragma unroll
     for (int c2 = 0; c2 < D / 64; ++c2) k.r[c2] = ntload<u4>(kr + 16 * c2 + 4 * lg.g);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) k.s[e] = ksc[rk(tr.srow[e])];
+    for (int e = 0; e < 4; ++e) {
+      k.s[e] = ksc[rk(tr.srow[e])];
+      k.vs[e] = vsc[rk(tr.srow[e])];
+    }
 #pragma unroll
     for (int e = 0; e < Lay<D>::NTV; ++e) {
       const uint32_t r = rk(tr.template vrow<Lay<D>::NTV>(lg.vsub, e));
       v.r[e] = ntload<u2v>(vbase + (size_t)r * RE + 2 * lg.vdim);
-      v.s[e] = vsc[r];
     }
   }
   __device__ __forceinline__ void load_tile(uint32_t row0, const LaneGeo<D>& lg, KFrag& k, VFrag& v) const {
@@ -419,12 +428,14 @@ struct StoreI8 {
 #pragma unroll
     for (int c2 = 0; c2 < D / 64; ++c2) k.r[c2] = ntload<u4>(kt + ko + 16 * c2);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) k.s[e] = kst[(4 * lg.g + e) * Hkv + kvh];
+    for (int e = 0; e < 4; ++e) {
+      k.s[e] = kst[(4 * lg.g + e) * Hkv + kvh];
+      k.vs[e] = vst[(4 * lg.g + e) * Hkv + kvh];
+    }
 #pragma unroll
     for (int e = 0; e < Lay<D>::NTV; ++e) {
       const uint32_t r = (uint32_t)(lg.vkey[e] * Hkv + kvh);
       v.r[e] = ntload<u2v>(vt + r * RE + 2 * lg.vdim);
-      v.s[e] = vst[r];
     }
   }
   __device__ __forceinline__ f4 scores(const KFrag& k, const QF16<D>& q) const {
@@ -442,16 +453,18 @@ struct StoreI8 {
     for (int e = 0; e < 4; ++e) acc[e] *= h2f(k.s[e]);
     return acc;
   }
+  // value scales of keys 4g + e, applied to p before it is broadcast
+  __device__ __forceinline__ void scale_p(const KFrag& k, float (&p)[4]) const {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) p[e] *= h2f(k.vs[e]);
+  }
   template <int G>
   __device__ __forceinline__ void pv(const VFrag& v, int e, const float (&w)[G], float (&acc)[G][8]) const {
     const h8 x = i8x8_to_h8(v.r[e].x, v.r[e].y);
-    const float sc = h2f(v.s[e]);
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float ws = w[h] * sc;
+    for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int d = 0; d < 8; ++d) acc[h][d] = __builtin_fmaf(ws, (float)x[d], acc[h][d]);
-    }
+      for (int d = 0; d < 8; ++d) acc[h][d] = __builtin_fmaf(w[h], (float)x[d], acc[h][d]);
   }
 };
 
@@ -694,6 +707,7 @@ __device__ __forceinline__ void run_tiles(const DecodeArgs& a, const Store& st, 
     for (int e = 0; e < 4; ++e) valid[e] = map.visible(t0 + 4 * lg.g + e, lg.kkey);
     float p[4];
     on.softmax_tile(a.capl2, raw, valid, p);
+    st.scale_p(kb[slot], p);
     float pb[4][G];
     Online<D, G, CAP>::broadcast(p, pb);
 #pragma unroll
@@ -841,7 +855,7 @@ __device__ __forceinline__ void tiered_segment(const DecodeArgs& a, int b, int k
 // Static splits: workgroup (split, b, z) sweeps keys [split*T, (split+1)*T)
 // of sequence b for kv heads z*waves + [0, waves).
 template <int D, int G, bool CAP, class T>
-__global__ __launch_bounds__(256) void paged_split_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(DATTN_MAX_THREADS) void paged_split_kernel(DecodeArgs a) {
   extern __shared__ int32_t lds_tbl[];
   const int split = blockIdx.x, b = blockIdx.y;
   const int lane = threadIdx.x & 63;
@@ -854,7 +868,7 @@ __global__ __launch_bounds__(256) void paged_split_kernel(DecodeArgs a) {
 }
 
 template <int D, int G, bool CAP>
-__global__ __launch_bounds__(256) void tiered_split_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(DATTN_MAX_THREADS) void tiered_split_kernel(DecodeArgs a) {
   extern __shared__ int32_t lds_tbl[];
   const int split = blockIdx.x, b = blockIdx.y;
   const int lane = threadIdx.x & 63;
@@ -913,7 +927,7 @@ __device__ __forceinline__ int tile_prefix(const DecodeArgs& a, int32_t* P) {
 // waves per SIMD when the GQA group is at most 4 (more waves keep more loads
 // in flight than the register savings cost).
 template <int D, int G, bool CAP, int KIND>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 2 : 1)))
+__global__ __launch_bounds__(DATTN_MAX_THREADS) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 2 : 1)))
 void balanced_kernel(DecodeArgs a) {
   extern __shared__ int32_t lds[];
   const int B = a.num_seqs;
@@ -967,7 +981,7 @@ void balanced_kernel(DecodeArgs a) {
 // mask compacted in increasing order), takes the slice of that list its
 // split owns and sweeps its keys.
 template <int D, int G, bool CAP>
-__global__ __launch_bounds__(256) void sparse_split_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(DATTN_MAX_THREADS) void sparse_split_kernel(DecodeArgs a) {
   extern __shared__ uint32_t lds_sp[];
   const int split = blockIdx.x, b = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
