@@ -10,20 +10,29 @@
 // rule of SparseAttention's combine_partials
 // (m = max(m1, m2), d = d1 e^{m1-m} + d2 e^{m2-m}), extended to acc.
 //
-// Inside a wavefront, keys are processed in tiles of 16:
-//   QK^T  on the matrix cores as S^T = K . Q^T with v_mfma_f32_16x16x32_f16
-//         (A = 16 keys x 32 dims of K, B = 32 dims x 16 heads of Q^T).  Q is
-//         f32, so it enters as an f16 hi/lo pair (q = hi + lo) and the two
-//         products are accumulated in f32; f16 and int8 keys are exact in f16.
-//         f32 caches use v_mfma_f32_16x16x4_f32 instead.
-//         The output lands as lane l <-> head l%16, keys 4*(l/16)+e (e<4).
+// Inside a wavefront, keys are processed in tiles of 16; both products of a
+// tile run on the matrix cores and the VALU only unpacks, masks and exponentiates:
+//   QK^T  as S^T = K . Q^T with v_mfma_f32_16x16x32_f16 (A = 16 keys x 32 dims
+//         of K, B = 32 dims x 16 heads of Q^T).  Q is f32, so it enters as an
+//         f16 hi/lo pair (q = hi + lo) and the two products are accumulated in
+//         f32; f16 and int8 keys are exact in f16.  f32 caches use
+//         v_mfma_f32_16x16x4_f32 instead.  The scores land as
+//         lane l <-> head l%16, keys 4*(l/16)+e (e<4).
 //   softmax online, in the log2 domain, per head (one head per lane column).
-//   PV    on the VALU: lane l owns 8 output dims and a group of keys of the
-//         tile; the probabilities of those keys sit in lane (16*(l/16) + head)
-//         of the same row, so one DPP row broadcast per (head, key) delivers
-//         them without touching LDS.
-// Loads are 128-bit and each instruction reads whole 64-byte pieces of K
-// rows (16 keys per instruction) or whole V rows (4 keys per instruction).
+//   PV    as O = P . V with 16x16x16 products, one per 16 output dims.  The
+//         score layout above is exactly the A operand (rows = heads, k = keys
+//         4*(l/16)+e), so the probabilities never move between lanes.  Lane l
+//         reads keys 4*(l/16)+e, dims (D/16)*(l%16) + [0, D/16) of V and
+//         regroups them in registers into B operands (n-tile t = dims
+//         (D/16)*c + t of column c).  f16 V uses f16 products with p as an f16
+//         hi/lo pair; int8 V becomes exact bf16 integers, and the value scale
+//         goes with p (p * scale as a bf16 hi/lo pair, which keeps f32 range);
+//         f32 V uses v_mfma_f32_16x16x4_f32 with p as is.  The accumulator
+//         holds heads 4*(l/16)+e, dims (D/16)*(l%16)+t, so a partial needs no
+//         cross-lane reduction.
+// Loads are 128-bit where the row allows; each K instruction reads whole
+// 64-byte pieces of 16 K rows, each V instruction (D/2) contiguous bytes of
+// 4 V rows per 16 lanes.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -39,6 +48,10 @@ typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u2v __attribute__((ext_vector_type(2)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef short s4 __attribute__((ext_vector_type(4)));
+typedef float f2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
 
 constexpr int kTile = 16;          // keys per tile
 #ifndef DATTN_MAX_THREADS
@@ -96,6 +109,38 @@ __device__ __forceinline__ float row_bcast(float x) {
 
 __device__ __forceinline__ float shfl_xor_f(float x, int m) { return __shfl_xor(x, m, 64); }
 
+// Reductions over the four 16-lane rows (lanes l, l^16, l^32, l^48) with the
+// gfx950 row swaps: v_permlane32_swap exchanges the upper half of its first
+// operand with the lower half of its second, v_permlane16_swap the odd rows of
+// the first with the even rows of the second, so with both operands equal to x
+// the two results hold x of lane l and of its partner at distance 32 (16).
+__device__ __forceinline__ void swap32(float x, float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x),
+                                                  false, false);
+  a = __builtin_bit_cast(float, (uint32_t)r[0]);
+  b = __builtin_bit_cast(float, (uint32_t)r[1]);
+}
+__device__ __forceinline__ void swap16(float x, float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x),
+                                                  false, false);
+  a = __builtin_bit_cast(float, (uint32_t)r[0]);
+  b = __builtin_bit_cast(float, (uint32_t)r[1]);
+}
+__device__ __forceinline__ float rows_max(float x) {
+  float a, b;
+  swap32(x, a, b);
+  x = a > b ? a : b;
+  swap16(x, a, b);
+  return a > b ? a : b;
+}
+__device__ __forceinline__ float rows_sum(float x) {
+  float a, b;
+  swap32(x, a, b);
+  x = a + b;
+  swap16(x, a, b);
+  return a + b;
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // tanh(x) = 1 - 2 / (e^{2x} + 1); saturates correctly at +-inf.
@@ -134,6 +179,40 @@ __device__ __forceinline__ h8 i8x8_to_h8(uint32_t w0, uint32_t w1) {
 }
 
 __device__ __forceinline__ float h2f(uint16_t bits) { return (float)__builtin_bit_cast(_Float16, bits); }
+
+// p = hi + lo with hi, lo in f16 (about 22 significant bits while p stays in
+// f16 range; p <= 2^8 here).
+__device__ __forceinline__ void split_f16(const float (&p)[4], h4& hi, h4& lo) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const _Float16 h = (_Float16)p[e];
+    hi[e] = h;
+    lo[e] = (_Float16)(p[e] - (float)h);
+  }
+}
+
+// Four floats rounded to bf16 (round to nearest even), as an MFMA operand.
+// Whole vectors are bit-cast: this clang reads element 0 when
+// __builtin_bit_cast is applied to an element of an ext_vector lvalue.
+__device__ __forceinline__ s4 pack_bf16(float a, float b, float c, float d) {
+  const uint32_t x = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{a, b}, bf2));
+  const uint32_t y = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{c, d}, bf2));
+  return __builtin_bit_cast(s4, u2v{x, y});
+}
+__device__ __forceinline__ float bf16_bits_to_f32(short h) {
+  return __builtin_bit_cast(float, (uint32_t)(uint16_t)h << 16);
+}
+// q = hi + lo with hi, lo in bf16: about 16 significant bits over the whole
+// f32 exponent range (q - hi is exact in f32).
+__device__ __forceinline__ void split_bf16(const float (&q)[4], s4& hi, s4& lo) {
+  hi = pack_bf16(q[0], q[1], q[2], q[3]);
+  lo = pack_bf16(q[0] - bf16_bits_to_f32(hi[0]), q[1] - bf16_bits_to_f32(hi[1]), q[2] - bf16_bits_to_f32(hi[2]),
+                 q[3] - bf16_bits_to_f32(hi[3]));
+}
+
+// Byte `byte` of w as a signed integer, converted exactly to f32 (the
+// compiler selects v_cvt_f32_i32 with a sign-extended byte operand).
+__device__ __forceinline__ float i8_at(uint32_t w, int byte) { return (float)(int8_t)(w >> (8 * byte)); }
 
 // ------------------------------------------------------------ Q fragments
 //
@@ -221,63 +300,73 @@ __device__ __forceinline__ void convert_q(const DecodeArgs& a, int lane, const Q
 // ------------------------------------------------------- K / V fragments
 //
 // A tile has 16 keys.  K lane l holds key l%16 (row l%16 of the MFMA A
-// operand); V lane l holds keys 4*(l/16) + vsub*NTV + e (e < NTV) and dims
-// 8*vdim + [0, 8), where DPR = D/8 lanes cover one V row, vdim = (l%16) % DPR
-// and vsub = (l%16) / DPR.  Every key of the tile is named by a physical row
-// index r of its pool, whose kv-head rows sit at element (r*Hkv + kvh) * RE.
+// operand).  V lane l holds keys 4*(l/16) + e (e < 4), dims (D/16)*(l%16) +
+// [0, D/16): the k range of the lane in the B operand of the PV products, for
+// the output column l%16 of every n-tile.  Every key of the tile is named by a
+// physical row index r of its pool, whose kv-head rows sit at element
+// (r*Hkv + kvh) * RE.
 
 template <int D>
 struct Lay {
-  static constexpr int DPR = D / 8;
-  static constexpr int NTV = D / 32;
+  static constexpr int NT = D / 16;   // PV n-tiles = V dims per lane and key
 };
 
 // Per-lane constants of one wavefront.
-template <int D>
 struct LaneGeo {
-  int g, kkey, vdim, vsub;
-  int vkey[Lay<D>::NTV];
+  int g;      // lane / 16: keys 4g + e of the score and V layouts
+  int kkey;   // lane % 16: K row of the lane, PV output column
   __device__ __forceinline__ void init(int lane) {
     g = lane >> 4;
     kkey = lane & 15;
-    vdim = (lane & 15) % Lay<D>::DPR;
-    vsub = (lane & 15) / Lay<D>::DPR;
-#pragma unroll
-    for (int e = 0; e < Lay<D>::NTV; ++e) vkey[e] = 4 * g + vsub * Lay<D>::NTV + e;
   }
 };
 
-// Rows of one tile: either 16 consecutive rows from a uniform row0 (fast) or
-// one row per key the lane touches (general).
+// Rows of one tile, for the general path (one row per key the lane touches).
 struct TileRows {
   uint32_t krow;      // row of key kkey
   uint32_t srow[4];   // rows of keys 4g + e
-  // row of the lane's V key e (keys 4g + vsub*NTV + e), without dynamic indexing
-  template <int NTV>
-  __device__ __forceinline__ uint32_t vrow(int vsub, int e) const {
-    if constexpr (NTV == 4) return srow[e];
-    else return vsub ? srow[NTV + e] : srow[e];
-  }
+  uint32_t xrow;      // row of key 4g + kkey%4 (whose per-token scales the lane loads)
 };
+
+template <int N>
+struct WordVec {
+  typedef uint32_t T __attribute__((ext_vector_type(N)));
+};
+template <>
+struct WordVec<1> {
+  typedef uint32_t T;
+};
+template <class T>
+__device__ __forceinline__ uint32_t word_at(const T& x, int i) {
+  if constexpr (std::is_same_v<T, uint32_t>)
+    return x;
+  else
+    return x[i];
+}
 
 template <class T>
 __device__ __forceinline__ T ntload(const void* p) {
-#if defined(DATTN_NT)
-  return __builtin_nontemporal_load((const T*)p);
-#else
   return *(const T*)p;
-#endif
+}
+// Load from a wave-uniform base plus a 32-bit per-lane byte offset, so that
+// the address is one SGPR pair plus one VGPR (global_load ... saddr).
+template <class T>
+__device__ __forceinline__ T load_at(const void* base, uint32_t off) {
+  return *(const T*)((const char*)base + off);
 }
 
 // ---- f16 rows of D halves (paged pool or hot ring)
 template <int D>
 struct StoreF16 {
   static constexpr int RE = D;  // elements per kv-head row
+  static constexpr int NT = Lay<D>::NT;
+  static constexpr bool kScaled = false;
+  using VW = typename WordVec<D / 32>::T;   // D/16 halves of one V row
   struct KFrag {
     u4 r[D / 32];
   };
   struct VFrag {
-    u4 r[Lay<D>::NTV];
+    VW r[4];
   };
   const _Float16* kbase;
   const _Float16* vbase;
@@ -286,25 +375,24 @@ struct StoreF16 {
   __device__ __forceinline__ const _Float16* krow_ptr(const _Float16* base, uint32_t row) const {
     return base + (size_t)(row * (uint32_t)Hkv + (uint32_t)kvh) * RE;
   }
-  __device__ __forceinline__ void load(const TileRows& tr, const LaneGeo<D>& lg, KFrag& k, VFrag& v) const {
+  __device__ __forceinline__ void load(const TileRows& tr, const LaneGeo& lg, KFrag& k, VFrag& v) const {
     const _Float16* kr = krow_ptr(kbase, tr.krow) + 8 * lg.g;
 #pragma unroll
     for (int c = 0; c < D / 32; ++c) k.r[c] = ntload<u4>(kr + 32 * c);
 #pragma unroll
-    for (int e = 0; e < Lay<D>::NTV; ++e)
-      v.r[e] = ntload<u4>(krow_ptr(vbase, tr.template vrow<Lay<D>::NTV>(lg.vsub, e)) + 8 * lg.vdim);
+    for (int e = 0; e < 4; ++e) v.r[e] = ntload<VW>(krow_ptr(vbase, tr.srow[e]) + NT * lg.kkey);
   }
-  // rows row0 .. row0+15: uniform base plus per-lane constant offsets
-  __device__ __forceinline__ void load_tile(uint32_t row0, const LaneGeo<D>& lg, KFrag& k, VFrag& v) const {
-    const size_t tb = (size_t)row0 * (uint32_t)Hkv * RE;
-    const _Float16* kt = kbase + tb;
-    const _Float16* vt = vbase + tb;
-    const uint32_t ko = (uint32_t)(lg.kkey * Hkv + kvh) * RE + 8 * lg.g;
+  // rows row0 .. row0+15: uniform base plus per-lane constant byte offsets
+  __device__ __forceinline__ void load_tile(uint32_t row0, const LaneGeo& lg, KFrag& k, VFrag& v) const {
+    const size_t tb = (size_t)row0 * (uint32_t)Hkv * (RE * 2);
+    const char* kt = (const char*)kbase + tb;
+    const char* vt = (const char*)vbase + tb;
+    const uint32_t ko = ((uint32_t)(lg.kkey * Hkv + kvh) * RE + 8 * lg.g) * 2;
 #pragma unroll
-    for (int c = 0; c < D / 32; ++c) k.r[c] = ntload<u4>(kt + ko + 32 * c);
+    for (int c = 0; c < D / 32; ++c) k.r[c] = load_at<u4>(kt, ko + 64 * c);
 #pragma unroll
-    for (int e = 0; e < Lay<D>::NTV; ++e)
-      v.r[e] = ntload<u4>(vt + (uint32_t)(lg.vkey[e] * Hkv + kvh) * RE + 8 * lg.vdim);
+    for (int e = 0; e < 4; ++e)
+      v.r[e] = load_at<VW>(vt, ((uint32_t)((4 * lg.g + e) * Hkv + kvh) * RE + NT * lg.kkey) * 2);
   }
   __device__ __forceinline__ f4 scores(const KFrag& k, const QF16<D>& q) const {
     f4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -316,26 +404,35 @@ struct StoreF16 {
     }
     return acc;
   }
-  __device__ __forceinline__ void scale_p(const KFrag&, float (&)[4]) const {}
-  template <int G>
-  __device__ __forceinline__ void pv(const VFrag& v, int e, const float (&w)[G], float (&acc)[G][8]) const {
-    h8 x = __builtin_bit_cast(h8, v.r[e]);
+  // o[t] += P . V for n-tile t: the B operand of lane l is the halves of
+  // dim (D/16)*(l%16) + t of its four keys, two keys per dword (one byte
+  // permute each: low halves for even t, high halves for odd t).
+  __device__ __forceinline__ void pv(const KFrag&, const VFrag& v, const float (&p)[4], f4 (&o)[NT]) const {
+    h4 hi, lo;
+    split_f16(p, hi, lo);
 #pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int d = 0; d < 8; ++d) acc[h][d] = __builtin_fmaf(w[h], (float)x[d], acc[h][d]);
+    for (int t = 0; t < NT; ++t) {
+      const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;
+      const uint32_t b01 = __builtin_amdgcn_perm(word_at(v.r[1], t >> 1), word_at(v.r[0], t >> 1), sel);
+      const uint32_t b23 = __builtin_amdgcn_perm(word_at(v.r[3], t >> 1), word_at(v.r[2], t >> 1), sel);
+      const h4 b = __builtin_bit_cast(h4, u2v{b01, b23});
+      o[t] = __builtin_amdgcn_mfma_f32_16x16x16f16(hi, b, o[t], 0, 0, 0);
+      o[t] = __builtin_amdgcn_mfma_f32_16x16x16f16(lo, b, o[t], 0, 0, 0);
+    }
   }
 };
 
-// ---- f32 rows (MFMA 16x16x4 f32: slab c of lane l is dim 16*(c/4) + 4*(l/16) + c%4)
+// ---- f32 rows (QK^T on MFMA 16x16x4 f32: slab c of lane l is dim 16*(c/4) + 4*(l/16) + c%4)
 template <int D>
 struct StoreF32 {
   static constexpr int RE = D;
+  static constexpr int NT = Lay<D>::NT;
+  static constexpr bool kScaled = false;
   struct KFrag {
     f4 r[D / 16];
   };
   struct VFrag {
-    f4 a[Lay<D>::NTV], b[Lay<D>::NTV];
+    f4 r[4][D / 64];   // D/16 floats of each of the lane's four keys
   };
   const float* kbase;
   const float* vbase;
@@ -344,18 +441,18 @@ struct StoreF32 {
   __device__ __forceinline__ const float* row_ptr(const float* base, uint32_t row) const {
     return base + (size_t)(row * (uint32_t)Hkv + (uint32_t)kvh) * RE;
   }
-  __device__ __forceinline__ void load(const TileRows& tr, const LaneGeo<D>& lg, KFrag& k, VFrag& v) const {
+  __device__ __forceinline__ void load(const TileRows& tr, const LaneGeo& lg, KFrag& k, VFrag& v) const {
     const float* kr = row_ptr(kbase, tr.krow);
 #pragma unroll
     for (int m = 0; m < D / 16; ++m) k.r[m] = ntload<f4>(kr + 16 * m + 4 * lg.g);
 #pragma unroll
-    for (int e = 0; e < Lay<D>::NTV; ++e) {
-      const float* vr = row_ptr(vbase, tr.template vrow<Lay<D>::NTV>(lg.vsub, e)) + 8 * lg.vdim;
-      v.a[e] = ntload<f4>(vr);
-      v.b[e] = ntload<f4>(vr + 4);
+    for (int e = 0; e < 4; ++e) {
+      const float* vr = row_ptr(vbase, tr.srow[e]) + NT * lg.kkey;
+#pragma unroll
+      for (int h = 0; h < D / 64; ++h) v.r[e][h] = ntload<f4>(vr + 4 * h);
     }
   }
-  __device__ __forceinline__ void load_tile(uint32_t row0, const LaneGeo<D>& lg, KFrag& k, VFrag& v) const {
+  __device__ __forceinline__ void load_tile(uint32_t row0, const LaneGeo& lg, KFrag& k, VFrag& v) const {
     TileRows tr;
     tr.krow = row0 + lg.kkey;
 #pragma unroll
@@ -373,14 +470,14 @@ struct StoreF32 {
     }
     return acc;
   }
-  __device__ __forceinline__ void scale_p(const KFrag&, float (&)[4]) const {}
-  template <int G>
-  __device__ __forceinline__ void pv(const VFrag& v, int e, const float (&w)[G], float (&acc)[G][8]) const {
-    const float x[8] = {v.a[e].x, v.a[e].y, v.a[e].z, v.a[e].w, v.b[e].x, v.b[e].y, v.b[e].z, v.b[e].w};
+  // One 16x16x4 product per (key e, n-tile t): A = p of key 4*(l/16)+e for
+  // head l%16 (k = l/16), B = that key's dim (D/16)*(l%16) + t.
+  __device__ __forceinline__ void pv(const KFrag&, const VFrag& v, const float (&p)[4], f4 (&o)[NT]) const {
 #pragma unroll
-    for (int h = 0; h < G; ++h)
+    for (int e = 0; e < 4; ++e)
 #pragma unroll
-      for (int d = 0; d < 8; ++d) acc[h][d] = __builtin_fmaf(w[h], x[d], acc[h][d]);
+      for (int t = 0; t < NT; ++t)
+        o[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(p[e], v.r[e][t >> 2][t & 3], o[t], 0, 0, 0);
   }
 };
 
@@ -388,13 +485,15 @@ struct StoreF32 {
 template <int D>
 struct StoreI8 {
   static constexpr int RE = D / 4;
+  static constexpr int NT = Lay<D>::NT;
+  static constexpr bool kScaled = true;
+  using VW = typename WordVec<D / 64>::T;   // D/16 codes of one V row
   struct KFrag {
     u4 r[D / 64];
-    uint16_t s[4];   // key scales of keys 4g + e
-    uint16_t vs[4];  // value scales of keys 4g + e
+    uint16_t ks, vs;   // scales of key 4g + kkey%4 (row-broadcast to the score layout)
   };
   struct VFrag {
-    u2v r[Lay<D>::NTV];
+    VW r[4];
   };
   const uint32_t* kbase;
   const uint32_t* vbase;
@@ -403,40 +502,30 @@ struct StoreI8 {
   int Hkv, kvh;
 
   __device__ __forceinline__ uint32_t rk(uint32_t row) const { return row * (uint32_t)Hkv + (uint32_t)kvh; }
-  __device__ __forceinline__ void load(const TileRows& tr, const LaneGeo<D>& lg, KFrag& k, VFrag& v) const {
+  __device__ __forceinline__ void load(const TileRows& tr, const LaneGeo& lg, KFrag& k, VFrag& v) const {
     const uint32_t* kr = kbase + (size_t)rk(tr.krow) * RE;
 #pragma unroll
     for (int c2 = 0; c2 < D / 64; ++c2) k.r[c2] = ntload<u4>(kr + 16 * c2 + 4 * lg.g);
+    k.ks = ksc[rk(tr.xrow)];
+    k.vs = vsc[rk(tr.xrow)];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      k.s[e] = ksc[rk(tr.srow[e])];
-      k.vs[e] = vsc[rk(tr.srow[e])];
-    }
-#pragma unroll
-    for (int e = 0; e < Lay<D>::NTV; ++e) {
-      const uint32_t r = rk(tr.template vrow<Lay<D>::NTV>(lg.vsub, e));
-      v.r[e] = ntload<u2v>(vbase + (size_t)r * RE + 2 * lg.vdim);
-    }
+    for (int e = 0; e < 4; ++e) v.r[e] = ntload<VW>(vbase + (size_t)rk(tr.srow[e]) * RE + (NT / 4) * lg.kkey);
   }
-  __device__ __forceinline__ void load_tile(uint32_t row0, const LaneGeo<D>& lg, KFrag& k, VFrag& v) const {
-    const uint32_t r0 = row0 * (uint32_t)Hkv;
-    const uint32_t* kt = kbase + (size_t)r0 * RE;
-    const uint32_t* vt = vbase + (size_t)r0 * RE;
-    const uint16_t* kst = ksc + r0;
-    const uint16_t* vst = vsc + r0;
-    const uint32_t ko = (uint32_t)(lg.kkey * Hkv + kvh) * RE + 4 * lg.g;
+  __device__ __forceinline__ void load_tile(uint32_t row0, const LaneGeo& lg, KFrag& k, VFrag& v) const {
+    const size_t r0 = (size_t)row0 * (uint32_t)Hkv;
+    const char* kt = (const char*)(kbase + r0 * RE);
+    const char* vt = (const char*)(vbase + r0 * RE);
+    const char* kst = (const char*)(ksc + r0);
+    const char* vst = (const char*)(vsc + r0);
+    const uint32_t ko = ((uint32_t)(lg.kkey * Hkv + kvh) * RE + 4 * lg.g) * 4;
 #pragma unroll
-    for (int c2 = 0; c2 < D / 64; ++c2) k.r[c2] = ntload<u4>(kt + ko + 16 * c2);
+    for (int c2 = 0; c2 < D / 64; ++c2) k.r[c2] = load_at<u4>(kt, ko + 64 * c2);
+    const uint32_t so = (uint32_t)((4 * lg.g + (lg.kkey & 3)) * Hkv + kvh) * 2;
+    k.ks = load_at<uint16_t>(kst, so);
+    k.vs = load_at<uint16_t>(vst, so);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      k.s[e] = kst[(4 * lg.g + e) * Hkv + kvh];
-      k.vs[e] = vst[(4 * lg.g + e) * Hkv + kvh];
-    }
-#pragma unroll
-    for (int e = 0; e < Lay<D>::NTV; ++e) {
-      const uint32_t r = (uint32_t)(lg.vkey[e] * Hkv + kvh);
-      v.r[e] = ntload<u2v>(vt + r * RE + 2 * lg.vdim);
-    }
+    for (int e = 0; e < 4; ++e)
+      v.r[e] = load_at<VW>(vt, ((uint32_t)((4 * lg.g + e) * Hkv + kvh) * RE + (NT / 4) * lg.kkey) * 4);
   }
   __device__ __forceinline__ f4 scores(const KFrag& k, const QF16<D>& q) const {
     f4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -449,22 +538,30 @@ struct StoreI8 {
       acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, q.hi[2 * c2 + 1], acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, q.lo[2 * c2 + 1], acc, 0, 0, 0);
     }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) acc[e] *= h2f(k.s[e]);
+    // key scale of key 4g + e sits in lane e of the row
+    const float s = h2f(k.ks);
+    acc[0] *= row_bcast<0>(s);
+    acc[1] *= row_bcast<1>(s);
+    acc[2] *= row_bcast<2>(s);
+    acc[3] *= row_bcast<3>(s);
     return acc;
   }
-  // value scales of keys 4g + e, applied to p before it is broadcast
-  __device__ __forceinline__ void scale_p(const KFrag& k, float (&p)[4]) const {
+  // The value scale of each key goes with p (A = p * scale as a bf16 hi/lo
+  // pair); B = the lane's four codes of dim (D/16)*(l%16) + t, exact in bf16.
+  __device__ __forceinline__ void pv(const KFrag& k, const VFrag& v, const float (&p)[4], f4 (&o)[NT]) const {
+    const float s = h2f(k.vs);
+    const float q[4] = {p[0] * row_bcast<0>(s), p[1] * row_bcast<1>(s), p[2] * row_bcast<2>(s),
+                        p[3] * row_bcast<3>(s)};
+    s4 hi, lo;
+    split_bf16(q, hi, lo);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) p[e] *= h2f(k.vs[e]);
-  }
-  template <int G>
-  __device__ __forceinline__ void pv(const VFrag& v, int e, const float (&w)[G], float (&acc)[G][8]) const {
-    const h8 x = i8x8_to_h8(v.r[e].x, v.r[e].y);
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int d = 0; d < 8; ++d) acc[h][d] = __builtin_fmaf(w[h], (float)x[d], acc[h][d]);
+    for (int t = 0; t < NT; ++t) {
+      const int w = t >> 2, byte = t & 3;
+      const s4 b = pack_bf16(i8_at(word_at(v.r[0], w), byte), i8_at(word_at(v.r[1], w), byte),
+                             i8_at(word_at(v.r[2], w), byte), i8_at(word_at(v.r[3], w), byte));
+      o[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(hi, b, o[t], 0, 0, 0);
+      o[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(lo, b, o[t], 0, 0, 0);
+    }
   }
 };
 
@@ -585,23 +682,24 @@ __device__ __forceinline__ PartialDst slot_dst(const DecodeArgs& a, int slot, in
 
 template <int D, int G, bool CAP>
 struct Online {
-  float m;            // running max (log2 units) of head lane%16 -- equal in all rows
-  float l;            // denominator part of (head lane%16, keys of row lane/16)
-  float acc[G][8];    // PV part of (dims 8*vdim.., keys of this lane)
+  static constexpr int NT = Lay<D>::NT;
+  float m;       // running max (log2 units) of head lane%16 -- equal in all rows
+  float l;       // denominator part of (head lane%16, keys of row lane/16)
+  f4 o[NT];      // o[t][e]: PV sum of head 4*(lane/16)+e, dim NT*(lane%16)+t
 
   __device__ __forceinline__ void init() {
     m = -__builtin_inff();
     l = 0.f;
 #pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int d = 0; d < 8; ++d) acc[h][d] = 0.f;
+    for (int t = 0; t < NT; ++t) o[t] = f4{0.f, 0.f, 0.f, 0.f};
   }
 
   // raw: this lane's 4 scores (already multiplied by qmul and any int8 key
-  // scale); valid: which of keys 4*(lane/16)+e take part.  Returns p[4] and
-  // rescales the state; the caller then broadcasts p to the PV lanes.
-  __device__ __forceinline__ void softmax_tile(float capl2, const f4& raw, const bool (&valid)[4], float (&p)[4]) {
+  // scale); valid: which of keys 4*(lane/16)+e take part.  Returns p[4] in
+  // the score layout, which is the A operand of the PV products, and rescales
+  // the state.
+  __device__ __forceinline__ void softmax_tile(float capl2, const f4& raw, const bool (&valid)[4], float (&p)[4],
+                                               int lane) {
     float s[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -609,9 +707,7 @@ struct Online {
       if constexpr (CAP) x = capl2 * fast_tanh(x);
       s[e] = valid[e] ? x : -__builtin_inff();
     }
-    float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-    mx = fmaxf(mx, shfl_xor_f(mx, 16));
-    mx = fmaxf(mx, shfl_xor_f(mx, 32));
+    const float mx = rows_max(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])));
     const float m_new = (mx > m + kSlack) ? mx : m;
     const float c = (m_new == m) ? 1.0f : fast_exp2(m - m_new);
     m = m_new;
@@ -620,44 +716,31 @@ struct Online {
     for (int e = 0; e < 4; ++e) p[e] = fast_exp2(s[e] - m_use);
     l = l * c + ((p[0] + p[1]) + (p[2] + p[3]));
     if (__builtin_amdgcn_ballot_w64(c != 1.0f)) {
-      static_for<0, G>([&](auto hc) {
-        constexpr int h = decltype(hc)::value;
-        const float ch = row_bcast<h>(c);
+      // row 4g+e of the accumulator is head 4g+e, whose factor lane 4g+e holds
+      const int g = lane >> 4;
+      float ce[4];
 #pragma unroll
-        for (int d = 0; d < 8; ++d) acc[h][d] *= ch;
-      });
+      for (int e = 0; e < 4; ++e) ce[e] = __shfl(c, 4 * g + e, 64);
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[t][e] *= ce[e];
     }
   }
 
-  // p of keys 4*(lane/16) + e for every head h < G, as seen by this lane.
-  __device__ __forceinline__ static void broadcast(const float (&p)[4], float (&pb)[4][G]) {
-    static_for<0, G>([&](auto hc) {
-      constexpr int h = decltype(hc)::value;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) pb[e][h] = row_bcast<h>(p[e]);
-    });
-  }
-
-  // Reduce across lanes and write the partial of heads kvh*G + [0, G).
+  // Write the partial of heads kvh*G + [0, G): head 4g+e's dims
+  // NT*(lane%16) + [0, NT) from the lanes of row g, (m, l) from lanes h < G.
   __device__ __forceinline__ void finish(const PartialDst& dst, int lane) {
-    float lt = l + shfl_xor_f(l, 16);
-    lt += shfl_xor_f(lt, 32);
+    const float lt = rows_sum(l);
+    const int g = lane >> 4, c = lane & 15;
 #pragma unroll
-    for (int h = 0; h < G; ++h)
+    for (int e = 0; e < 4; ++e) {
+      const int h = 4 * g + e;
+      if (h < G) {
+        float* out = dst.acc + h * dst.acc_hstride + NT * c;
 #pragma unroll
-      for (int d = 0; d < 8; ++d) {
-        float x = acc[h][d];
-        if constexpr (Lay<D>::DPR < 16) x += shfl_xor_f(x, 8);
-        x += shfl_xor_f(x, 16);
-        x += shfl_xor_f(x, 32);
-        acc[h][d] = x;
-      }
-    if (lane < Lay<D>::DPR) {
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        float* o = dst.acc + h * dst.acc_hstride + 8 * lane;
-        *(f4*)o = f4{acc[h][0], acc[h][1], acc[h][2], acc[h][3]};
-        *(f4*)(o + 4) = f4{acc[h][4], acc[h][5], acc[h][6], acc[h][7]};
+        for (int t4 = 0; t4 < NT / 4; ++t4)
+          *(f4*)(out + 4 * t4) = f4{o[4 * t4][e], o[4 * t4 + 1][e], o[4 * t4 + 2][e], o[4 * t4 + 3][e]};
       }
     }
     if (lane < G) dst.ml[lane * dst.ml_hstride] = make_float2(m, lt);
@@ -680,11 +763,10 @@ __device__ __forceinline__ void write_empty(const PartialDst& dst, int lane) {
 
 template <int D, int G, bool CAP, int NBUF, class Store, class Map, class QF, class QPrep>
 __device__ __forceinline__ void run_tiles(const DecodeArgs& a, const Store& st, const Map& map, QF& qf,
-                                          QPrep&& prep_q, const LaneGeo<D>& lg, Online<D, G, CAP>& on, int tfirst,
+                                          QPrep&& prep_q, const LaneGeo& lg, Online<D, G, CAP>& on, int tfirst,
                                           int tend, int lane) {
   using KFrag = typename Store::KFrag;
   using VFrag = typename Store::VFrag;
-  constexpr int NTV = Lay<D>::NTV;
   KFrag kb[NBUF];
   VFrag vb[NBUF];
   auto issue = [&](int t0, auto slotc) {
@@ -696,6 +778,10 @@ __device__ __forceinline__ void run_tiles(const DecodeArgs& a, const Store& st, 
       tr.krow = map.row(t0 + lg.kkey);
 #pragma unroll
       for (int e = 0; e < 4; ++e) tr.srow[e] = map.row(t0 + 4 * lg.g + e);
+      if constexpr (Store::kScaled) {
+        const int x = lg.kkey & 3;
+        tr.xrow = (x & 2) ? ((x & 1) ? tr.srow[3] : tr.srow[2]) : ((x & 1) ? tr.srow[1] : tr.srow[0]);
+      }
       st.load(tr, lg, kb[slot], vb[slot]);
     }
   };
@@ -706,21 +792,8 @@ __device__ __forceinline__ void run_tiles(const DecodeArgs& a, const Store& st, 
 #pragma unroll
     for (int e = 0; e < 4; ++e) valid[e] = map.visible(t0 + 4 * lg.g + e, lg.kkey);
     float p[4];
-    on.softmax_tile(a.capl2, raw, valid, p);
-    st.scale_p(kb[slot], p);
-    float pb[4][G];
-    Online<D, G, CAP>::broadcast(p, pb);
-#pragma unroll
-    for (int e = 0; e < NTV; ++e) {
-      float w[G];
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        float x = pb[e][h];
-        if constexpr (NTV < 4) x = lg.vsub ? pb[NTV + e][h] : x;
-        w[h] = x;
-      }
-      st.template pv<G>(vb[slot], e, w, on.acc);
-    }
+    on.softmax_tile(a.capl2, raw, valid, p, lane);
+    st.pv(kb[slot], vb[slot], p, on.o);
   };
 
   if (tfirst >= tend) {
@@ -788,7 +861,7 @@ __device__ __forceinline__ void paged_segment(const DecodeArgs& a, int b, int kv
     write_empty<G>(dst, lane);
     return;
   }
-  LaneGeo<D> lg;
+  LaneGeo lg;
   lg.init(lane);
   PagedMap map{lds_tbl, blk0, tb, te - 1, a.bs, a.bs.d % 16 == 0};
   Online<D, G, CAP> on;
@@ -827,7 +900,7 @@ __device__ __forceinline__ void tiered_segment(const DecodeArgs& a, int b, int k
     write_empty<G>(dst, lane);
     return;
   }
-  LaneGeo<D> lg;
+  LaneGeo lg;
   lg.init(lane);
   QF16<D> qf;
   Online<D, G, CAP> on;
@@ -1027,7 +1100,7 @@ __global__ __launch_bounds__(DATTN_MAX_THREADS) void sparse_split_kernel(DecodeA
     write_empty<G>(dst, lane);
     return;
   }
-  LaneGeo<D> lg;
+  LaneGeo lg;
   lg.init(lane);
   SparseMap map{list, a.table + (size_t)b * a.max_blocks, e1 * (int)a.sb.d, lo, hi, a.bs, a.sb,
                 a.sb.d % 16 == 0 && a.bs.d % 16 == 0};
