@@ -14,6 +14,7 @@
 
 #include "dattn.h"
 #include "decode_kernels.h"
+#include "kernel_table.h"
 
 namespace {
 
@@ -256,52 +257,6 @@ int check_launch(const char* what) {
   return DATTN_OK;
 }
 
-template <template <int, int, bool> class K, int D, bool CAP>
-void* pick_g(int G) {
-  switch (G) {
-    case 1: return (void*)K<D, 1, CAP>::fn();
-    case 2: return (void*)K<D, 2, CAP>::fn();
-    case 4: return (void*)K<D, 4, CAP>::fn();
-    default: return (void*)K<D, 8, CAP>::fn();
-  }
-}
-
-template <int D, int G, bool CAP>
-struct PagedF16 {
-  static auto fn() { return &dattn::paged_split_kernel<D, G, CAP, _Float16>; }
-};
-template <int D, int G, bool CAP>
-struct PagedF32 {
-  static auto fn() { return &dattn::paged_split_kernel<D, G, CAP, float>; }
-};
-template <int D, int G, bool CAP>
-struct Tiered {
-  static auto fn() { return &dattn::tiered_split_kernel<D, G, CAP>; }
-};
-template <int D, int G, bool CAP>
-struct Sparse {
-  static auto fn() { return &dattn::sparse_split_kernel<D, G, CAP>; }
-};
-template <int D, int G, bool CAP>
-struct BalF16 {
-  static auto fn() { return &dattn::balanced_kernel<D, G, CAP, 0>; }
-};
-template <int D, int G, bool CAP>
-struct BalF32 {
-  static auto fn() { return &dattn::balanced_kernel<D, G, CAP, 1>; }
-};
-template <int D, int G, bool CAP>
-struct BalTiered {
-  static auto fn() { return &dattn::balanced_kernel<D, G, CAP, 2>; }
-};
-
-// Kernel instance for (head_dim, GQA group, softcap on/off).
-template <template <int, int, bool> class K>
-void* pick(int D, int G, bool cap) {
-  if (D == 64) return cap ? pick_g<K, 64, true>(G) : pick_g<K, 64, false>(G);
-  return cap ? pick_g<K, 128, true>(G) : pick_g<K, 128, false>(G);
-}
-
 bool run_split(const dattn_params* p) { return p->phases == 0 || (p->phases & DATTN_PHASE_SPLIT); }
 bool run_combine(const dattn_params* p) { return p->phases == 0 || (p->phases & DATTN_PHASE_COMBINE); }
 
@@ -388,8 +343,9 @@ int dattn_decode_paged(const dattn_params* p, const float* q, const void* k_cach
   a.q_pos = q_pos;
   const bool cap = p->softcap > 0.0f;
   const bool f16 = kv_dtype == DATTN_F16;
-  void* fn = f16 ? pick<PagedF16>(p->head_dim, pl.G, cap) : pick<PagedF32>(p->head_dim, pl.G, cap);
-  void* bal = f16 ? pick<BalF16>(p->head_dim, pl.G, cap) : pick<BalF32>(p->head_dim, pl.G, cap);
+  const bool contig = p->block_size % 16 == 0;
+  void* fn = dattn::split_kernel(f16 ? dattn::kPagedF16 : dattn::kPagedF32, p->head_dim, cap, pl.G, contig);
+  void* bal = dattn::split_kernel(f16 ? dattn::kBalF16 : dattn::kBalF32, p->head_dim, cap, pl.G, contig);
   return launch(fn, bal, p, pl, a, out, lse, (hipStream_t)stream);
 }
 
@@ -424,7 +380,9 @@ int dattn_decode_tiered_int8(const dattn_params* p, const float* q, const uint16
   a.cold_lens = cold_lens;
   a.q_pos = q_pos;
   const bool cap = p->softcap > 0.0f;
-  return launch(pick<Tiered>(p->head_dim, pl.G, cap), pick<BalTiered>(p->head_dim, pl.G, cap), p, pl, a, out, lse,
+  const bool contig = p->block_size % 16 == 0 && hot_window % 16 == 0;
+  return launch(dattn::split_kernel(dattn::kTiered, p->head_dim, cap, pl.G, contig),
+                dattn::split_kernel(dattn::kBalTiered, p->head_dim, cap, pl.G, contig), p, pl, a, out, lse,
                 (hipStream_t)stream);
 }
 
@@ -458,8 +416,9 @@ int dattn_decode_block_sparse(const dattn_params* p, const float* q, const uint1
   a.sparse_nblk = pl.sparse_nblk;
   a.blocks_per_split = pl.blocks_per_split;
   a.sb = dattn::make_fastdiv((uint32_t)sparse_block);
-  return launch(pick<Sparse>(p->head_dim, pl.G, p->softcap > 0.0f), nullptr, p, pl, a, out, lse,
-                (hipStream_t)stream);
+  const bool contig = p->block_size % 16 == 0 && sparse_block % 16 == 0;
+  return launch(dattn::split_kernel(dattn::kSparse, p->head_dim, p->softcap > 0.0f, pl.G, contig), nullptr, p, pl,
+                a, out, lse, (hipStream_t)stream);
 }
 
 }  // extern "C"

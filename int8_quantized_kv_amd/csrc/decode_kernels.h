@@ -348,11 +348,19 @@ template <class T>
 __device__ __forceinline__ T ntload(const void* p) {
   return *(const T*)p;
 }
-// Load from a wave-uniform base plus a 32-bit per-lane byte offset, so that
-// the address is one SGPR pair plus one VGPR (global_load ... saddr).
+// Loads of a contiguous tile: a wave-uniform base (SGPRs, recomputed per
+// tile) plus a loop-invariant 32-bit per-lane byte offset plus an immediate,
+// which is global_load's saddr form.  `tie` makes the offset a value of the
+// tile (an empty asm that only names the base): otherwise the 64-bit sum of
+// the pointer and the zero-extended offset is hoisted out of the loop and
+// every load pays a 64-bit VALU add of the tile offset.
+__device__ __forceinline__ uint32_t tie(uint32_t off, const void* base) {
+  asm("" : "+v"(off) : "s"(base));
+  return off;
+}
 template <class T>
-__device__ __forceinline__ T load_at(const void* base, uint32_t off) {
-  return *(const T*)((const char*)base + off);
+__device__ __forceinline__ T load_at(const char* base, uint32_t off, uint32_t imm = 0) {
+  return *(const T*)(base + off + imm);
 }
 
 // ---- f16 rows of D halves (paged pool or hot ring)
@@ -384,15 +392,15 @@ struct StoreF16 {
   }
   // rows row0 .. row0+15: uniform base plus per-lane constant byte offsets
   __device__ __forceinline__ void load_tile(uint32_t row0, const LaneGeo& lg, KFrag& k, VFrag& v) const {
-    const size_t tb = (size_t)row0 * (uint32_t)Hkv * (RE * 2);
-    const char* kt = (const char*)kbase + tb;
-    const char* vt = (const char*)vbase + tb;
-    const uint32_t ko = ((uint32_t)(lg.kkey * Hkv + kvh) * RE + 8 * lg.g) * 2;
+    const size_t rs = (size_t)(uint32_t)Hkv * (RE * 2);   // bytes per row of the pool
+    const char* kt = (const char*)kbase + row0 * rs;
+    const char* vt = (const char*)vbase + row0 * rs;
+    const uint32_t ko = tie(((uint32_t)(lg.kkey * Hkv + kvh) * RE + 8 * lg.g) * 2, kt);
+    const uint32_t vo = tie(((uint32_t)(4 * lg.g * Hkv + kvh) * RE + NT * lg.kkey) * 2, vt);
 #pragma unroll
-    for (int c = 0; c < D / 32; ++c) k.r[c] = load_at<u4>(kt, ko + 64 * c);
+    for (int c = 0; c < D / 32; ++c) k.r[c] = load_at<u4>(kt, ko, 64 * c);
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      v.r[e] = load_at<VW>(vt, ((uint32_t)((4 * lg.g + e) * Hkv + kvh) * RE + NT * lg.kkey) * 2);
+    for (int e = 0; e < 4; ++e) v.r[e] = load_at<VW>(vt + e * rs, vo);
   }
   __device__ __forceinline__ f4 scores(const KFrag& k, const QF16<D>& q) const {
     f4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -407,7 +415,17 @@ struct StoreF16 {
   // o[t] += P . V for n-tile t: the B operand of lane l is the halves of
   // dim (D/16)*(l%16) + t of its four keys, two keys per dword (one byte
   // permute each: low halves for even t, high halves for odd t).
-  __device__ __forceinline__ void pv(const KFrag&, const VFrag& v, const float (&p)[4], f4 (&o)[NT]) const {
+  // With SAN the rows of keys outside the key range (kvalid false: p = 0,
+  // contents unknown) are zeroed first, so that no Inf or NaN they may hold
+  // reaches the sum.
+  template <bool SAN>
+  __device__ __forceinline__ void pv(const KFrag&, const VFrag& v_in, const float (&p)[4], const bool (&valid)[4],
+                                     f4 (&o)[NT]) const {
+    VFrag v = v_in;
+    if constexpr (SAN) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v.r[e] = valid[e] ? v.r[e] : VW{};
+    }
     h4 hi, lo;
     split_f16(p, hi, lo);
 #pragma unroll
@@ -453,11 +471,17 @@ struct StoreF32 {
     }
   }
   __device__ __forceinline__ void load_tile(uint32_t row0, const LaneGeo& lg, KFrag& k, VFrag& v) const {
-    TileRows tr;
-    tr.krow = row0 + lg.kkey;
+    const size_t rs = (size_t)(uint32_t)Hkv * (RE * 4);
+    const char* kt = (const char*)kbase + row0 * rs;
+    const char* vt = (const char*)vbase + row0 * rs;
+    const uint32_t ko = tie(((uint32_t)(lg.kkey * Hkv + kvh) * RE + 4 * lg.g) * 4, kt);
+    const uint32_t vo = tie(((uint32_t)(4 * lg.g * Hkv + kvh) * RE + NT * lg.kkey) * 4, vt);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) tr.srow[e] = row0 + 4 * lg.g + e;
-    load(tr, lg, k, v);
+    for (int m = 0; m < D / 16; ++m) k.r[m] = load_at<f4>(kt, ko, 64 * m);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+      for (int h = 0; h < D / 64; ++h) v.r[e][h] = load_at<f4>(vt + e * rs, vo, 16 * h);
   }
   __device__ __forceinline__ f4 scores(const KFrag& k, const QF32<D>& q) const {
     f4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -472,7 +496,16 @@ struct StoreF32 {
   }
   // One 16x16x4 product per (key e, n-tile t): A = p of key 4*(l/16)+e for
   // head l%16 (k = l/16), B = that key's dim (D/16)*(l%16) + t.
-  __device__ __forceinline__ void pv(const KFrag&, const VFrag& v, const float (&p)[4], f4 (&o)[NT]) const {
+  template <bool SAN>
+  __device__ __forceinline__ void pv(const KFrag&, const VFrag& v_in, const float (&p)[4], const bool (&valid)[4],
+                                     f4 (&o)[NT]) const {
+    VFrag v = v_in;
+    if constexpr (SAN) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int h = 0; h < D / 64; ++h) v.r[e][h] = valid[e] ? v.r[e][h] : f4{0.f, 0.f, 0.f, 0.f};
+    }
 #pragma unroll
     for (int e = 0; e < 4; ++e)
 #pragma unroll
@@ -513,19 +546,20 @@ struct StoreI8 {
   }
   __device__ __forceinline__ void load_tile(uint32_t row0, const LaneGeo& lg, KFrag& k, VFrag& v) const {
     const size_t r0 = (size_t)row0 * (uint32_t)Hkv;
+    const size_t rs = (size_t)(uint32_t)Hkv * (RE * 4);   // bytes per row of the pool
     const char* kt = (const char*)(kbase + r0 * RE);
     const char* vt = (const char*)(vbase + r0 * RE);
     const char* kst = (const char*)(ksc + r0);
     const char* vst = (const char*)(vsc + r0);
-    const uint32_t ko = ((uint32_t)(lg.kkey * Hkv + kvh) * RE + 4 * lg.g) * 4;
+    const uint32_t ko = tie(((uint32_t)(lg.kkey * Hkv + kvh) * RE + 4 * lg.g) * 4, kt);
+    const uint32_t vo = tie(((uint32_t)(4 * lg.g * Hkv + kvh) * RE + (NT / 4) * lg.kkey) * 4, vt);
+    const uint32_t so = tie((uint32_t)((4 * lg.g + (lg.kkey & 3)) * Hkv + kvh) * 2, kst);
 #pragma unroll
-    for (int c2 = 0; c2 < D / 64; ++c2) k.r[c2] = load_at<u4>(kt, ko + 64 * c2);
-    const uint32_t so = (uint32_t)((4 * lg.g + (lg.kkey & 3)) * Hkv + kvh) * 2;
+    for (int c2 = 0; c2 < D / 64; ++c2) k.r[c2] = load_at<u4>(kt, ko, 64 * c2);
     k.ks = load_at<uint16_t>(kst, so);
     k.vs = load_at<uint16_t>(vst, so);
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      v.r[e] = load_at<VW>(vt, ((uint32_t)((4 * lg.g + e) * Hkv + kvh) * RE + (NT / 4) * lg.kkey) * 4);
+    for (int e = 0; e < 4; ++e) v.r[e] = load_at<VW>(vt + e * rs, vo);
   }
   __device__ __forceinline__ f4 scores(const KFrag& k, const QF16<D>& q) const {
     f4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -548,10 +582,17 @@ struct StoreI8 {
   }
   // The value scale of each key goes with p (A = p * scale as a bf16 hi/lo
   // pair); B = the lane's four codes of dim (D/16)*(l%16) + t, exact in bf16.
-  __device__ __forceinline__ void pv(const KFrag& k, const VFrag& v, const float (&p)[4], f4 (&o)[NT]) const {
+  // With SAN, q of keys outside the key range is set to 0 (their scale may be
+  // anything); codes are finite whatever the bytes.
+  template <bool SAN>
+  __device__ __forceinline__ void pv(const KFrag& k, const VFrag& v, const float (&p)[4], const bool (&valid)[4],
+                                     f4 (&o)[NT]) const {
     const float s = h2f(k.vs);
-    const float q[4] = {p[0] * row_bcast<0>(s), p[1] * row_bcast<1>(s), p[2] * row_bcast<2>(s),
-                        p[3] * row_bcast<3>(s)};
+    float q[4] = {p[0] * row_bcast<0>(s), p[1] * row_bcast<1>(s), p[2] * row_bcast<2>(s), p[3] * row_bcast<3>(s)};
+    if constexpr (SAN) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) q[e] = valid[e] ? q[e] : 0.0f;
+    }
     s4 hi, lo;
     split_bf16(q, hi, lo);
 #pragma unroll
@@ -568,14 +609,18 @@ struct StoreI8 {
 // ------------------------------------------------------- position -> row maps
 //
 // A map turns a position of the sweep (an absolute key, or a slot of the
-// sparse union list) into a physical row, says which (position, head) pairs
-// are visible, and, for a tile of 16 positions starting at a multiple of 16,
-// whether its keys are 16 consecutive rows (then `tile_row0` gives the first).
+// sparse union list) into a physical row and says which (position, head)
+// pairs are visible.  When the map is contiguous (`contig`), every tile of 16
+// positions starting at a multiple of 16 is 16 consecutive rows of one
+// physical block, and `tile_row0` gives the first row of the tile, clamped
+// into the tiles the sweep may touch so that it always names an allocated
+// block; rows of invisible keys are then read but masked.  Otherwise `row`
+// gives each key's row, clamped to a visible key.
 
 // Paged: key t lives in block tbl[t / bs - blk0] (LDS), offset t % bs.
 struct PagedMap {
   const int32_t* tbl;
-  int blk0, lo, hi;        // [lo, hi]: keys this sweep may touch (clamp) and see
+  int blk0, lo, hi;        // [lo, hi]: keys this sweep may touch and see
   FastDiv bs;
   bool contig;             // bs % 16 == 0
   __device__ __forceinline__ uint32_t row(int t) const {
@@ -583,13 +628,20 @@ struct PagedMap {
     const uint32_t blk = fdiv((uint32_t)t, bs);
     return (uint32_t)tbl[blk - blk0] * bs.d + ((uint32_t)t - blk * bs.d);
   }
-  __device__ __forceinline__ bool full_tile(int t0) const { return contig && t0 >= lo && t0 + 15 <= hi; }
   __device__ __forceinline__ uint32_t tile_row0(int t0) const {
+    t0 = min(max(t0, lo & ~15), hi & ~15);
     const uint32_t blk = fdiv((uint32_t)t0, bs);
     const uint32_t phys = (uint32_t)__builtin_amdgcn_readfirstlane(tbl[blk - blk0]);
     return phys * bs.d + ((uint32_t)t0 - blk * bs.d);
   }
   __device__ __forceinline__ bool visible(int t, int) const { return t >= lo && t <= hi; }
+  // valid: (key t0 + 4g + e, head lane%16) takes part; kvalid: that key is
+  // inside [lo, hi], so its row holds cache data (one unsigned compare each)
+  __device__ __forceinline__ void tile_valid(int t0, const LaneGeo& lg, bool (&valid)[4], bool (&kvalid)[4]) const {
+    const uint32_t rel = (uint32_t)(t0 + 4 * lg.g - lo), span = (uint32_t)(hi - lo);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) kvalid[e] = valid[e] = rel + e <= span;
+  }
 };
 
 // Hot ring: key t of sequence b at row b*hw + t % hw.
@@ -601,9 +653,16 @@ struct RingMap {
     t = min(max(t, lo), hi);
     return (uint32_t)b * hw.d + fmod_((uint32_t)t, hw);
   }
-  __device__ __forceinline__ bool full_tile(int t0) const { return contig && t0 >= lo && t0 + 15 <= hi; }
-  __device__ __forceinline__ uint32_t tile_row0(int t0) const { return (uint32_t)b * hw.d + fmod_((uint32_t)t0, hw); }
+  __device__ __forceinline__ uint32_t tile_row0(int t0) const {
+    t0 = min(max(t0, lo & ~15), hi & ~15);
+    return (uint32_t)b * hw.d + fmod_((uint32_t)t0, hw);
+  }
   __device__ __forceinline__ bool visible(int t, int) const { return t >= lo && t <= hi; }
+  __device__ __forceinline__ void tile_valid(int t0, const LaneGeo& lg, bool (&valid)[4], bool (&kvalid)[4]) const {
+    const uint32_t rel = (uint32_t)(t0 + 4 * lg.g - lo), span = (uint32_t)(hi - lo);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) kvalid[e] = valid[e] = rel + e <= span;
+  }
 };
 
 // Sparse: slot s -> union entry e = s / SB = (block << 16) | head mask (LDS),
@@ -614,6 +673,7 @@ struct SparseMap {
   int slot_end, lo, hi;
   FastDiv bs, sb;
   bool contig;             // sb % 16 == 0 and bs % 16 == 0
+  uint32_t gmask;          // bits of the G heads of the group
   __device__ __forceinline__ void resolve(int slot, int& t, uint32_t& mask) const {
     const int s = min(slot, slot_end - 1);
     const uint32_t e = fdiv((uint32_t)s, sb);
@@ -632,19 +692,14 @@ struct SparseMap {
     resolve(slot, t, mk);
     return key_row(t);
   }
-  __device__ __forceinline__ bool full_tile(int s0) const {
-    if (!contig || s0 + 15 >= slot_end) return false;
-    int t;
-    uint32_t mk;
-    resolve(s0, t, mk);
-    t = __builtin_amdgcn_readfirstlane(t);
-    return t >= lo && t + 15 <= hi;
-  }
+  // slots past the end fall back to the last tile; keys of a block outside
+  // [lo, hi] to the tile of lo or hi, whose paged block is allocated
   __device__ __forceinline__ uint32_t tile_row0(int s0) const {
     int t;
     uint32_t mk;
-    resolve(s0, t, mk);
+    resolve(min(s0, slot_end - 16), t, mk);
     t = __builtin_amdgcn_readfirstlane(t);
+    t = min(max(t, lo & ~15), hi & ~15);
     const uint32_t blk = fdiv((uint32_t)t, bs);
     const uint32_t phys = (uint32_t)__builtin_amdgcn_readfirstlane(table_row[blk]);
     return phys * bs.d + ((uint32_t)t - blk * bs.d);
@@ -654,6 +709,32 @@ struct SparseMap {
     uint32_t mk;
     resolve(slot, t, mk);
     return ((mk >> head) & 1u) && t >= lo && t <= hi;
+  }
+  // A contiguous tile lies in one union entry: resolve it once.  valid adds
+  // the head mask (lane%16 is the head in the score layout); kvalid is the
+  // key range alone (slots past the end have no key: never valid).
+  __device__ __forceinline__ void tile_valid(int s0, const LaneGeo& lg, bool (&valid)[4], bool (&kvalid)[4]) const {
+    if (contig) {
+      int t;
+      uint32_t mk;
+      resolve(s0, t, mk);
+      t = __builtin_amdgcn_readfirstlane(t);
+      mk = (uint32_t)__builtin_amdgcn_readfirstlane((int)mk);
+      const bool head_on = (mk >> lg.kkey) & 1u;
+      const bool live = s0 < slot_end;
+      const uint32_t rel = (uint32_t)(t + 4 * lg.g - lo), span = (uint32_t)(hi - lo);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        kvalid[e] = live && rel + e <= span;
+        valid[e] = head_on && kvalid[e];
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        valid[e] = visible(s0 + 4 * lg.g + e, lg.kkey);
+        kvalid[e] = valid[e];   // rows are clamped to visible keys: only p is masked
+      }
+    }
   }
 };
 
@@ -758,10 +839,15 @@ __device__ __forceinline__ void write_empty(const PartialDst& dst, int lane) {
 // in flight while one tile is computed.  Every issue in the steady state is
 // unconditional (the wait-count pass would otherwise merge counter states at
 // the join and wait for the prefetched tiles as well); tiles past the end load
-// the last visible row again (a cache hit) and are never consumed.  The Q
-// fragments are prepared after the first loads are on their way.
+// the last tile again (a cache hit) and are never consumed.  With FAST (a
+// contiguous map) every tile is read as 16 consecutive rows from a
+// wave-uniform address, rows of invisible keys included, so their V is
+// zeroed before the product; otherwise each lane gathers its rows, clamped to
+// visible keys.  Masking is branch-free (a branch around the accumulating
+// products costs accumulator copies at the join).  The Q fragments are
+// prepared after the first loads are on their way.
 
-template <int D, int G, bool CAP, int NBUF, class Store, class Map, class QF, class QPrep>
+template <int D, int G, bool CAP, int NBUF, bool FAST, class Store, class Map, class QF, class QPrep>
 __device__ __forceinline__ void run_tiles(const DecodeArgs& a, const Store& st, const Map& map, QF& qf,
                                           QPrep&& prep_q, const LaneGeo& lg, Online<D, G, CAP>& on, int tfirst,
                                           int tend, int lane) {
@@ -771,7 +857,7 @@ __device__ __forceinline__ void run_tiles(const DecodeArgs& a, const Store& st, 
   VFrag vb[NBUF];
   auto issue = [&](int t0, auto slotc) {
     constexpr int slot = decltype(slotc)::value;
-    if (map.full_tile(t0)) {
+    if constexpr (FAST) {
       st.load_tile(map.tile_row0(t0), lg, kb[slot], vb[slot]);
     } else {
       TileRows tr;
@@ -788,12 +874,11 @@ __device__ __forceinline__ void run_tiles(const DecodeArgs& a, const Store& st, 
   auto consume = [&](int t0, auto slotc) {
     constexpr int slot = decltype(slotc)::value;
     const f4 raw = st.scores(kb[slot], qf);
-    bool valid[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) valid[e] = map.visible(t0 + 4 * lg.g + e, lg.kkey);
+    bool valid[4], kvalid[4];
+    map.tile_valid(t0, lg, valid, kvalid);
     float p[4];
     on.softmax_tile(a.capl2, raw, valid, p, lane);
-    st.pv(kb[slot], vb[slot], p, on.o);
+    st.template pv<FAST>(kb[slot], vb[slot], p, kvalid, on.o);
   };
 
   if (tfirst >= tend) {
@@ -820,6 +905,13 @@ __device__ __forceinline__ void run_tiles(const DecodeArgs& a, const Store& st, 
 }
 
 // ---------------------------------------------------------------- kernels
+//
+// FM (chosen by the host): every cache the kernel sweeps is contiguous in
+// 16-row tiles -- paged block size, hot-ring size and sparse block all
+// multiples of 16 -- so tiles are read with uniform-base loads.  Kernels are
+// instantiated once per FM value instead of branching at run time: holding
+// both sweep loops in one function costs the register allocator dozens of
+// VGPRs.
 
 // Stage block-table entries [blk0, blk0 + n) of sequence b into LDS, once
 // every wave of the workgroup is done with the previous contents.
@@ -843,7 +935,7 @@ __device__ __forceinline__ void table_span(const DecodeArgs& a, int t0, int t1, 
 // Sweep keys [tb, te) of sequence b for one kv head of a paged cache and write
 // the partial to dst.  Every wave of the workgroup calls it with the same
 // (b, tb, te): the block-table staging is shared.
-template <int D, int G, bool CAP, class T>
+template <int D, int G, bool CAP, class T, bool FM>
 __device__ __forceinline__ void paged_segment(const DecodeArgs& a, int b, int kvh, int lane, int tb, int te,
                                               int32_t* lds_tbl, const PartialDst& dst) {
   using QRaw = std::conditional_t<std::is_same_v<T, float>, QRaw32<D>, QRaw16<D>>;
@@ -863,18 +955,18 @@ __device__ __forceinline__ void paged_segment(const DecodeArgs& a, int b, int kv
   }
   LaneGeo lg;
   lg.init(lane);
-  PagedMap map{lds_tbl, blk0, tb, te - 1, a.bs, a.bs.d % 16 == 0};
+  PagedMap map{lds_tbl, blk0, tb, te - 1, a.bs, FM};
   Online<D, G, CAP> on;
   on.init();
   if constexpr (std::is_same_v<T, float>) {
     QF32<D> qf;
     StoreF32<D> st{(const float*)a.k, (const float*)a.v, a.num_kv_heads, kvh};
-    run_tiles<D, G, CAP, kPipe>(a, st, map, qf, [&](QF32<D>& q) { convert_q<D, G>(a, lane, qraw, q); }, lg, on,
+    run_tiles<D, G, CAP, kPipe, FM>(a, st, map, qf, [&](QF32<D>& q) { convert_q<D, G>(a, lane, qraw, q); }, lg, on,
                                 tb & ~(kTile - 1), te, lane);
   } else {
     QF16<D> qf;
     StoreF16<D> st{(const _Float16*)a.k, (const _Float16*)a.v, a.num_kv_heads, kvh};
-    run_tiles<D, G, CAP, kPipe>(a, st, map, qf, [&](QF16<D>& q) { convert_q<D, G>(a, lane, qraw, q); }, lg, on,
+    run_tiles<D, G, CAP, kPipe, FM>(a, st, map, qf, [&](QF16<D>& q) { convert_q<D, G>(a, lane, qraw, q); }, lg, on,
                                 tb & ~(kTile - 1), te, lane);
   }
   on.finish(dst, lane);
@@ -882,7 +974,7 @@ __device__ __forceinline__ void paged_segment(const DecodeArgs& a, int b, int kv
 
 // The same for the tiered cache: keys below cold_lens[b] from the paged int8
 // pool, the rest from the f16 ring.
-template <int D, int G, bool CAP>
+template <int D, int G, bool CAP, bool FM>
 __device__ __forceinline__ void tiered_segment(const DecodeArgs& a, int b, int kvh, int lane, int tb, int te,
                                                int32_t* lds_tbl, const PartialDst& dst) {
   const int C = a.cold_lens[b];
@@ -906,16 +998,16 @@ __device__ __forceinline__ void tiered_segment(const DecodeArgs& a, int b, int k
   Online<D, G, CAP> on;
   on.init();
   if (tb < ce) {
-    PagedMap map{lds_tbl, blk0, tb, ce - 1, a.bs, a.bs.d % 16 == 0};
+    PagedMap map{lds_tbl, blk0, tb, ce - 1, a.bs, FM};
     StoreI8<D> st{(const uint32_t*)a.k, (const uint32_t*)a.v, a.k_scale, a.v_scale, a.num_kv_heads, kvh};
-    run_tiles<D, G, CAP, kPipe>(a, st, map, qf, [&](QF16<D>& q) { convert_q<D, G>(a, lane, qraw, q); }, lg, on,
+    run_tiles<D, G, CAP, kPipe, FM>(a, st, map, qf, [&](QF16<D>& q) { convert_q<D, G>(a, lane, qraw, q); }, lg, on,
                                 tb & ~(kTile - 1), ce, lane);
   }
   if (hb < te) {
-    RingMap map{b, hb, te - 1, a.hw, a.hw.d % 16 == 0};
+    RingMap map{b, hb, te - 1, a.hw, FM};
     StoreF16<D> st{(const _Float16*)a.k_hot, (const _Float16*)a.v_hot, a.num_kv_heads, kvh};
     const bool had_cold = tb < ce;
-    run_tiles<D, G, CAP, kPipe>(a, st, map, qf,
+    run_tiles<D, G, CAP, kPipe, FM>(a, st, map, qf,
                                 [&](QF16<D>& q) {
                                   if (had_cold) load_q_raw16<D, G, false>(a, b, kvh, lane, qraw);
                                   convert_q<D, G>(a, lane, qraw, q);
@@ -927,7 +1019,7 @@ __device__ __forceinline__ void tiered_segment(const DecodeArgs& a, int b, int k
 
 // Static splits: workgroup (split, b, z) sweeps keys [split*T, (split+1)*T)
 // of sequence b for kv heads z*waves + [0, waves).
-template <int D, int G, bool CAP, class T>
+template <int D, int G, bool CAP, class T, bool FM>
 __global__ __launch_bounds__(DATTN_MAX_THREADS) void paged_split_kernel(DecodeArgs a) {
   extern __shared__ int32_t lds_tbl[];
   const int split = blockIdx.x, b = blockIdx.y;
@@ -937,10 +1029,10 @@ __global__ __launch_bounds__(DATTN_MAX_THREADS) void paged_split_kernel(DecodeAr
   visible_range(a, b, lo, hi, qp);
   const int tb = max(split * a.split_tokens, lo);
   const int te = min((split + 1) * a.split_tokens, hi + 1);
-  paged_segment<D, G, CAP, T>(a, b, kvh, lane, tb, te, lds_tbl, split_dst(a, b, kvh, G, split, D));
+  paged_segment<D, G, CAP, T, FM>(a, b, kvh, lane, tb, te, lds_tbl, split_dst(a, b, kvh, G, split, D));
 }
 
-template <int D, int G, bool CAP>
+template <int D, int G, bool CAP, bool FM>
 __global__ __launch_bounds__(DATTN_MAX_THREADS) void tiered_split_kernel(DecodeArgs a) {
   extern __shared__ int32_t lds_tbl[];
   const int split = blockIdx.x, b = blockIdx.y;
@@ -950,37 +1042,60 @@ __global__ __launch_bounds__(DATTN_MAX_THREADS) void tiered_split_kernel(DecodeA
   visible_range(a, b, lo, hi, qp);
   const int tb = max(split * a.split_tokens, lo);
   const int te = min((split + 1) * a.split_tokens, hi + 1);
-  tiered_segment<D, G, CAP>(a, b, kvh, lane, tb, te, lds_tbl, split_dst(a, b, kvh, G, split, D));
+  tiered_segment<D, G, CAP, FM>(a, b, kvh, lane, tb, te, lds_tbl, split_dst(a, b, kvh, G, split, D));
 }
 
 // ------------------------------------------------------- balanced schedule
 //
 // The visible keys of sequence b are cut into 16-key tiles aligned to
-// absolute positions; b owns tiles [P[b], P[b+1]) of the concatenation over
-// all sequences (N tiles in all).  Worker w of a kv-head group (blockIdx.x)
-// owns tiles [w*C, min((w+1)*C, N)) with C = ceil(N / gridDim.x), so every
-// worker streams the same number of tiles whatever the length mix, and the
-// grid is one round of resident workgroups.  A worker's range can cross
-// sequence boundaries; its piece of sequence b is partial slot w + b, which
-// no other (worker, sequence) pair shares because each boundary along the
-// concatenation advances w, b or both.  Worker 0 of group 0 leaves N, C and
-// P in the schedule area of the workspace for the combine kernel.
+// absolute positions.  Each tile costs units in proportion to the bytes it
+// reads: 1 for a paged tile or an int8 cold tile, 2 for an f16 hot-ring tile
+// of the tiered cache (16 rows of 2*D halves against 16 rows of 2*D bytes).
+// b owns units [P[b], P[b+1]) of the concatenation over all sequences (N
+// units in all).  Worker w of a kv-head group (blockIdx.x) owns units
+// [w*C, min((w+1)*C, N)) with C = ceil(N / gridDim.x) and sweeps the tiles
+// whose first unit lies there, so every worker streams about the same number
+// of bytes whatever the length mix, and the grid is one round of resident
+// workgroups.  A worker's range can cross sequence boundaries; its piece of
+// sequence b (possibly empty, when its range lies inside one hot tile) is
+// partial slot w + b, which no other (worker, sequence) pair shares because
+// each boundary along the concatenation advances w, b or both.  Worker 0 of
+// group 0 leaves N, C and P in the schedule area of the workspace for the
+// combine kernel.
 
-__device__ __forceinline__ int seq_tiles(const DecodeArgs& a, int b) {
-  int lo, hi, q;
-  visible_range(a, b, lo, hi, q);
-  return hi < lo ? 0 : (hi >> 4) - (lo >> 4) + 1;
-}
+// Tiles of sequence b and the unit cost of each.
+template <int KIND>
+struct SeqCost {
+  int lo, hi, base;   // visible keys [lo, hi]; tile i starts at key base + 16i
+  int ntiles, ncold;  // tiles < ncold cost 1 unit, the others 2 (tiered only)
+  __device__ __forceinline__ void init(const DecodeArgs& a, int b) {
+    int q;
+    visible_range(a, b, lo, hi, q);
+    base = lo & ~(kTile - 1);
+    ntiles = hi < lo ? 0 : (hi >> 4) - (lo >> 4) + 1;
+    ncold = ntiles;
+    if constexpr (KIND == 2) ncold = min(ntiles, max(0, (a.cold_lens[b] - base + kTile - 1) / kTile));
+  }
+  __device__ __forceinline__ int units() const { return ncold + 2 * (ntiles - ncold); }
+  // first tile whose first unit is >= u (0 <= u <= units())
+  __device__ __forceinline__ int tile_at(int u) const { return u <= ncold ? u : ncold + (u - ncold + 1) / 2; }
+};
 
-// P[0..B] (exclusive prefix of tile counts) into LDS; returns N = P[B].
-__device__ __forceinline__ int tile_prefix(const DecodeArgs& a, int32_t* P) {
+// P[0..B] (exclusive prefix of unit counts) into LDS; returns N = P[B].
+template <int KIND>
+__device__ __forceinline__ int unit_prefix(const DecodeArgs& a, int32_t* P) {
   const int B = a.num_seqs;
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
     int run = 0;
     for (int base = 0; base < B; base += 64) {
       const int b = base + lane;
-      const int c = b < B ? seq_tiles(a, b) : 0;
+      int c = 0;
+      if (b < B) {
+        SeqCost<KIND> sc;
+        sc.init(a, b);
+        c = sc.units();
+      }
       int x = c;
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) {
@@ -997,10 +1112,10 @@ __device__ __forceinline__ int tile_prefix(const DecodeArgs& a, int32_t* P) {
 }
 
 // KIND: 0 paged f16, 1 paged f32, 2 tiered.  Registers are capped for two
-// waves per SIMD when the GQA group is at most 4 (more waves keep more loads
-// in flight than the register savings cost).
-template <int D, int G, bool CAP, int KIND>
-__global__ __launch_bounds__(DATTN_MAX_THREADS) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 2 : 1)))
+// waves per SIMD (more waves keep more loads in flight than the register
+// savings cost).
+template <int D, int G, bool CAP, int KIND, bool FM>
+__global__ __launch_bounds__(DATTN_MAX_THREADS) __attribute__((amdgpu_waves_per_eu(2)))
 void balanced_kernel(DecodeArgs a) {
   extern __shared__ int32_t lds[];
   const int B = a.num_seqs;
@@ -1009,7 +1124,7 @@ void balanced_kernel(DecodeArgs a) {
   const int w = blockIdx.x, nw = gridDim.x;
   const int lane = threadIdx.x & 63;
   const int kvh = blockIdx.z * (blockDim.x >> 6) + (threadIdx.x >> 6);
-  const int N = tile_prefix(a, P);
+  const int N = unit_prefix<KIND>(a, P);
   const int C = (N + nw - 1) / nw;
   if (w == 0 && blockIdx.z == 0) {
     for (int i = threadIdx.x; i <= B; i += blockDim.x) a.sched[2 + i] = P[i];
@@ -1032,18 +1147,17 @@ void balanced_kernel(DecodeArgs a) {
   while (x0 < x1) {
     while (P[b + 1] <= x0) ++b;
     const int seg_end = min(x1, P[b + 1]);
-    int lo, hi, qp;
-    visible_range(a, b, lo, hi, qp);
-    const int base = lo & ~(kTile - 1);
-    const int tb = max(lo, base + kTile * (x0 - P[b]));
-    const int te = min(hi + 1, base + kTile * (seg_end - P[b]));
+    SeqCost<KIND> sc;
+    sc.init(a, b);
+    const int tb = max(sc.lo, sc.base + kTile * sc.tile_at(x0 - P[b]));
+    const int te = min(sc.hi + 1, sc.base + kTile * sc.tile_at(seg_end - P[b]));
     const PartialDst dst = slot_dst(a, w + b, kvh, G, D);
     if constexpr (KIND == 2)
-      tiered_segment<D, G, CAP>(a, b, kvh, lane, tb, te, tbl, dst);
+      tiered_segment<D, G, CAP, FM>(a, b, kvh, lane, tb, te, tbl, dst);
     else if constexpr (KIND == 1)
-      paged_segment<D, G, CAP, float>(a, b, kvh, lane, tb, te, tbl, dst);
+      paged_segment<D, G, CAP, float, FM>(a, b, kvh, lane, tb, te, tbl, dst);
     else
-      paged_segment<D, G, CAP, _Float16>(a, b, kvh, lane, tb, te, tbl, dst);
+      paged_segment<D, G, CAP, _Float16, FM>(a, b, kvh, lane, tb, te, tbl, dst);
     x0 = seg_end;
     ++b;
   }
@@ -1053,7 +1167,7 @@ void balanced_kernel(DecodeArgs a) {
 // LDS (a G-bit head mask per sparse block, then the blocks with a non-zero
 // mask compacted in increasing order), takes the slice of that list its
 // split owns and sweeps its keys.
-template <int D, int G, bool CAP>
+template <int D, int G, bool CAP, bool FM>
 __global__ __launch_bounds__(DATTN_MAX_THREADS) void sparse_split_kernel(DecodeArgs a) {
   extern __shared__ uint32_t lds_sp[];
   const int split = blockIdx.x, b = blockIdx.y;
@@ -1103,12 +1217,12 @@ __global__ __launch_bounds__(DATTN_MAX_THREADS) void sparse_split_kernel(DecodeA
   LaneGeo lg;
   lg.init(lane);
   SparseMap map{list, a.table + (size_t)b * a.max_blocks, e1 * (int)a.sb.d, lo, hi, a.bs, a.sb,
-                a.sb.d % 16 == 0 && a.bs.d % 16 == 0};
+                FM, (1u << G) - 1u};
   QF16<D> qf;
   StoreF16<D> st{(const _Float16*)a.k, (const _Float16*)a.v, a.num_kv_heads, kvh};
   Online<D, G, CAP> on;
   on.init();
-  run_tiles<D, G, CAP, kPipe>(a, st, map, qf, [&](QF16<D>& q) { convert_q<D, G>(a, lane, qraw, q); }, lg, on,
+  run_tiles<D, G, CAP, kPipe, FM>(a, st, map, qf, [&](QF16<D>& q) { convert_q<D, G>(a, lane, qraw, q); }, lg, on,
                               e0 * (int)a.sb.d, map.slot_end, lane);
   on.finish(dst, lane);
 }
@@ -1194,7 +1308,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 }
 
 // Balanced schedule: the partials of (b, h) sit in slots w + b for the
-// workers w that own tiles of b, at [slot, h].
+// workers w whose unit range meets b's, at [slot, h] (an empty piece has l = 0).
 struct SlotLoc {
   const float* acc0;   // slot (w0 + b), head h
   const float2* ml0;

@@ -1,0 +1,31 @@
+// kernel_table.h -- host handles of the split kernels.  The instances of
+// one (head_dim, softcap) pair live in their own translation unit
+// (kernels.hip built with -DDATTN_D and -DDATTN_CAP) so that the four units
+// compile in parallel.
+#pragma once
+
+namespace dattn {
+
+enum SplitKind : int {
+  kPagedF16 = 0,   // static splits, paged f16 cache
+  kPagedF32,       // static splits, paged f32 cache
+  kTiered,         // static splits, int8 cold pool + f16 hot ring
+  kSparse,         // static splits over the CSR union, paged f16 cache
+  kBalF16,         // balanced schedule, paged f16
+  kBalF32,         // balanced schedule, paged f32
+  kBalTiered,      // balanced schedule, tiered
+};
+
+// Split kernel for (kind, GQA group G in {1, 2, 4, 8}, contiguous 16-row
+// tiles); nullptr for an unknown kind.
+void* split_kernel_d64_cap0(int kind, int G, bool contig);
+void* split_kernel_d64_cap1(int kind, int G, bool contig);
+void* split_kernel_d128_cap0(int kind, int G, bool contig);
+void* split_kernel_d128_cap1(int kind, int G, bool contig);
+
+inline void* split_kernel(int kind, int D, bool cap, int G, bool contig) {
+  if (D == 64) return cap ? split_kernel_d64_cap1(kind, G, contig) : split_kernel_d64_cap0(kind, G, contig);
+  return cap ? split_kernel_d128_cap1(kind, G, contig) : split_kernel_d128_cap0(kind, G, contig);
+}
+
+}  // namespace dattn

@@ -1,0 +1,48 @@
+// kernels.hip -- the split-kernel instances of one (head_dim, softcap) pair,
+// chosen with -DDATTN_D=<64|128> -DDATTN_CAP=<0|1>.
+#include "decode_kernels.h"
+#include "kernel_table.h"
+
+#if !defined(DATTN_D) || !defined(DATTN_CAP)
+#error "kernels.hip is built with -DDATTN_D=<64|128> -DDATTN_CAP=<0|1>"
+#endif
+
+namespace dattn {
+namespace {
+
+template <int G, bool FM>
+void* instance(int kind) {
+  constexpr int D = DATTN_D;
+  constexpr bool CAP = DATTN_CAP != 0;
+  switch (kind) {
+    case kPagedF16: return (void*)&paged_split_kernel<D, G, CAP, _Float16, FM>;
+    case kPagedF32: return (void*)&paged_split_kernel<D, G, CAP, float, FM>;
+    case kTiered: return (void*)&tiered_split_kernel<D, G, CAP, FM>;
+    case kSparse: return (void*)&sparse_split_kernel<D, G, CAP, FM>;
+    case kBalF16: return (void*)&balanced_kernel<D, G, CAP, 0, FM>;
+    case kBalF32: return (void*)&balanced_kernel<D, G, CAP, 1, FM>;
+    case kBalTiered: return (void*)&balanced_kernel<D, G, CAP, 2, FM>;
+    default: return nullptr;
+  }
+}
+
+template <bool FM>
+void* by_group(int kind, int G) {
+  switch (G) {
+    case 1: return instance<1, FM>(kind);
+    case 2: return instance<2, FM>(kind);
+    case 4: return instance<4, FM>(kind);
+    default: return instance<8, FM>(kind);
+  }
+}
+
+}  // namespace
+
+#define DATTN_NAME2(d, c) split_kernel_d##d##_cap##c
+#define DATTN_NAME(d, c) DATTN_NAME2(d, c)
+
+void* DATTN_NAME(DATTN_D, DATTN_CAP)(int kind, int G, bool contig) {
+  return contig ? by_group<true>(kind, G) : by_group<false>(kind, G);
+}
+
+}  // namespace dattn
