@@ -37,7 +37,6 @@ struct Plan {
   int G = 0;
   int split_tokens = 0;  // keys (or sparse slots) per split
   int num_splits = 0;
-  int blocks_per_split = 0;  // sparse
   int sparse_nblk = 0;       // sparse
   int waves = 0;             // kv heads per workgroup
   size_t lds = 0;
@@ -53,6 +52,32 @@ struct Plan {
 constexpr int kMaxWorkers = 1024;
 constexpr int kMaxBalancedSeqs = 4096;
 constexpr size_t kMaxBalancedLds = 16384;
+
+// Per-device cache of the CU count and of kernel occupancies.
+std::mutex g_mu;
+std::map<int, int> g_cus;
+std::map<std::tuple<int, const void*, int>, int> g_occ;
+
+// CU count of the current device; 256 (MI355X) when no device can be queried,
+// so that host-only callers of dattn_workspace_size get the same answer.
+int device_cus() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  std::lock_guard<std::mutex> lk(g_mu);
+  auto it = g_cus.find(dev);
+  if (it == g_cus.end()) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+      (void)hipGetLastError();
+      return 256;
+    }
+    it = g_cus.emplace(dev, n).first;
+  }
+  return it->second;
+}
 
 int check_params(const dattn_params* p, int kind) {
   if (!p) return fail(DATTN_ERR_INVALID, "params is NULL");
@@ -132,9 +157,21 @@ int make_plan(const dattn_params* p, int kind, int32_t sparse_block, Plan& pl) {
     const int64_t nb = (L + sparse_block - 1) / sparse_block;
     if (nb > 8192) return fail(DATTN_ERR_UNSUPPORTED, "more than 8192 sparse blocks per sequence is not supported");
     pl.sparse_nblk = (int)(nb > 0 ? nb : 1);
-    pl.split_tokens = choose_split(p, nb * sparse_block / 2);  // about half the blocks are selected
-    pl.blocks_per_split = pl.split_tokens / sparse_block > 0 ? pl.split_tokens / sparse_block : 1;
-    pl.num_splits = (int)((pl.sparse_nblk + pl.blocks_per_split - 1) / pl.blocks_per_split);
+    // Each split takes an equal share of the union list the kernel builds
+    // (its length is only known on the device).  By default the splits fill
+    // one round of resident waves (8 per CU); split_tokens > 0 asks for
+    // split_tokens / sparse_block union blocks per split at most.
+    if (p->split_tokens > 0) {
+      const int64_t per = p->split_tokens / sparse_block > 0 ? p->split_tokens / sparse_block : 1;
+      pl.num_splits = (int)((pl.sparse_nblk + per - 1) / per);
+    } else {
+      const int64_t pairs = (int64_t)p->num_seqs * p->num_kv_heads;
+      const int64_t target = (int64_t)device_cus() * 8;
+      int64_t S = pairs > 0 ? (target + pairs - 1) / pairs : 1;
+      if (S > pl.sparse_nblk) S = pl.sparse_nblk;
+      pl.num_splits = (int)(S > 0 ? S : 1);
+    }
+    pl.split_tokens = 0;
     while (pl.waves > 1 && (size_t)pl.waves * 2 * pl.sparse_nblk * 4 > 65536) pl.waves /= 2;
     pl.lds = (size_t)pl.waves * 2 * pl.sparse_nblk * sizeof(uint32_t);
   } else {
@@ -160,22 +197,12 @@ int make_plan(const dattn_params* p, int kind, int32_t sparse_block, Plan& pl) {
 
 // ---- device properties (cached per device) for sizing the balanced grid
 
-std::mutex g_mu;
-std::map<int, int> g_cus;
-std::map<std::tuple<int, const void*, int>, int> g_occ;
-
 // Workgroups of `fn` (block threads, 16 KiB LDS) resident per CU; 0 on error.
 int resident_groups(const void* fn, int block, int& cus) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
+  cus = device_cus();
   std::lock_guard<std::mutex> lk(g_mu);
-  auto it = g_cus.find(dev);
-  if (it == g_cus.end()) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    it = g_cus.emplace(dev, n).first;
-  }
-  cus = it->second;
   const auto key = std::make_tuple(dev, fn, block);
   auto jt = g_occ.find(key);
   if (jt == g_occ.end()) {
@@ -207,7 +234,11 @@ Balanced plan_balanced(const dattn_params* p, const Plan& pl, const void* fn) {
   int total = cus * per_cu;
   if (total > kMaxWorkers) total = kMaxWorkers;
   bl.workers = total / groups > 0 ? total / groups : 1;
-  const int64_t nmax = (int64_t)p->num_seqs * (((int64_t)p->max_seq_len + 15) / 16 + 1);
+  // A worker's piece of one sequence has at most C tiles (every tile costs at
+  // least one unit); C <= ceil(N / workers) with N bounded by two units per
+  // tile plus the start-up units of every sequence.
+  const int64_t tmax = ((int64_t)p->max_seq_len + 15) / 16 + 1;
+  const int64_t nmax = (int64_t)p->num_seqs * (2 * tmax + dattn::kSeqUnits);
   const int64_t cmax = (nmax + bl.workers - 1) / bl.workers;
   const int64_t entries = cmax * 16 / p->block_size + 2;
   bl.lds = (size_t)(((p->num_seqs + 4) & ~3) + entries) * sizeof(int32_t);
@@ -414,7 +445,6 @@ int dattn_decode_block_sparse(const dattn_params* p, const float* q, const uint1
   a.row_stride = row_stride;
   a.col_stride = col_stride;
   a.sparse_nblk = pl.sparse_nblk;
-  a.blocks_per_split = pl.blocks_per_split;
   a.sb = dattn::make_fastdiv((uint32_t)sparse_block);
   const bool contig = p->block_size % 16 == 0 && sparse_block % 16 == 0;
   return launch(dattn::split_kernel(dattn::kSparse, p->head_dim, p->softcap > 0.0f, pl.G, contig), nullptr, p, pl,

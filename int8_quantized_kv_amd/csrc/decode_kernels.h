@@ -60,6 +60,12 @@ constexpr int kTile = 16;          // keys per tile
 #ifndef DATTN_PIPE
 #define DATTN_PIPE 2
 #endif
+#ifndef DATTN_QK2
+#define DATTN_QK2 0
+#endif
+#ifndef DATTN_WPE
+#define DATTN_WPE 2
+#endif
 constexpr int kPipe = DATTN_PIPE;  // tile buffers: kPipe-1 tiles of loads in flight
 constexpr float kSlack = 8.0f;     // lazy max: raise m only when a tile exceeds it by > 2^8
 constexpr float kLn2 = 0.69314718055994531f;
@@ -84,7 +90,7 @@ struct DecodeArgs {
   int32_t* sched;            // balanced: N, C, P[0..B]
   int32_t num_seqs, num_heads, num_kv_heads, max_blocks, num_splits, split_tokens;
   int32_t causal, window, hot_window;
-  int32_t sparse_block, num_layouts, row_stride, col_stride, sparse_nblk, blocks_per_split;
+  int32_t sparse_block, num_layouts, row_stride, col_stride, sparse_nblk;
   float qmul;    // scale * log2(e) without softcap, scale / cap with softcap
   float capl2;   // cap * log2(e), 0 without softcap
   FastDiv bs, hw, sb;
@@ -403,6 +409,16 @@ struct StoreF16 {
     for (int e = 0; e < 4; ++e) v.r[e] = load_at<VW>(vt + e * rs, vo);
   }
   __device__ __forceinline__ f4 scores(const KFrag& k, const QF16<D>& q) const {
+#if DATTN_QK2
+    f4 ah = {0.f, 0.f, 0.f, 0.f}, al = ah;
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c) {
+      h8 a = __builtin_bit_cast(h8, k.r[c]);
+      ah = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, q.hi[c], ah, 0, 0, 0);
+      al = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, q.lo[c], al, 0, 0, 0);
+    }
+    return ah + al;
+#else
     f4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < D / 32; ++c) {
@@ -411,6 +427,7 @@ struct StoreF16 {
       acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, q.lo[c], acc, 0, 0, 0);
     }
     return acc;
+#endif
   }
   // o[t] += P . V for n-tile t: the B operand of lane l is the halves of
   // dim (D/16)*(l%16) + t of its four keys, two keys per dword (one byte
@@ -562,6 +579,19 @@ struct StoreI8 {
     for (int e = 0; e < 4; ++e) v.r[e] = load_at<VW>(vt + e * rs, vo);
   }
   __device__ __forceinline__ f4 scores(const KFrag& k, const QF16<D>& q) const {
+#if DATTN_QK2
+    f4 ah = {0.f, 0.f, 0.f, 0.f}, al = ah;
+#pragma unroll
+    for (int c2 = 0; c2 < D / 64; ++c2) {
+      h8 a0 = i8x8_to_h8(k.r[c2].x, k.r[c2].y);
+      h8 a1 = i8x8_to_h8(k.r[c2].z, k.r[c2].w);
+      ah = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, q.hi[2 * c2], ah, 0, 0, 0);
+      al = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, q.lo[2 * c2], al, 0, 0, 0);
+      ah = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, q.hi[2 * c2 + 1], ah, 0, 0, 0);
+      al = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, q.lo[2 * c2 + 1], al, 0, 0, 0);
+    }
+    f4 acc = ah + al;
+#else
     f4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c2 = 0; c2 < D / 64; ++c2) {
@@ -572,6 +602,7 @@ struct StoreI8 {
       acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, q.hi[2 * c2 + 1], acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, q.lo[2 * c2 + 1], acc, 0, 0, 0);
     }
+#endif
     // key scale of key 4g + e sits in lane e of the row
     const float s = h2f(k.ks);
     acc[0] *= row_bcast<0>(s);
@@ -1020,7 +1051,7 @@ __device__ __forceinline__ void tiered_segment(const DecodeArgs& a, int b, int k
 // Static splits: workgroup (split, b, z) sweeps keys [split*T, (split+1)*T)
 // of sequence b for kv heads z*waves + [0, waves).
 template <int D, int G, bool CAP, class T, bool FM>
-__global__ __launch_bounds__(DATTN_MAX_THREADS) void paged_split_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(DATTN_MAX_THREADS) __attribute__((amdgpu_waves_per_eu(2))) void paged_split_kernel(DecodeArgs a) {
   extern __shared__ int32_t lds_tbl[];
   const int split = blockIdx.x, b = blockIdx.y;
   const int lane = threadIdx.x & 63;
@@ -1033,7 +1064,7 @@ __global__ __launch_bounds__(DATTN_MAX_THREADS) void paged_split_kernel(DecodeAr
 }
 
 template <int D, int G, bool CAP, bool FM>
-__global__ __launch_bounds__(DATTN_MAX_THREADS) void tiered_split_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(DATTN_MAX_THREADS) __attribute__((amdgpu_waves_per_eu(2))) void tiered_split_kernel(DecodeArgs a) {
   extern __shared__ int32_t lds_tbl[];
   const int split = blockIdx.x, b = blockIdx.y;
   const int lane = threadIdx.x & 63;
@@ -1050,7 +1081,8 @@ __global__ __launch_bounds__(DATTN_MAX_THREADS) void tiered_split_kernel(DecodeA
 // The visible keys of sequence b are cut into 16-key tiles aligned to
 // absolute positions.  Each tile costs units in proportion to the bytes it
 // reads: 1 for a paged tile or an int8 cold tile, 2 for an f16 hot-ring tile
-// of the tiered cache (16 rows of 2*D halves against 16 rows of 2*D bytes).
+// of the tiered cache (16 rows of 2*D halves against 16 rows of 2*D bytes);
+// each sequence adds a fixed start-up cost.
 // b owns units [P[b], P[b+1]) of the concatenation over all sequences (N
 // units in all).  Worker w of a kv-head group (blockIdx.x) owns units
 // [w*C, min((w+1)*C, N)) with C = ceil(N / gridDim.x) and sweeps the tiles
@@ -1063,11 +1095,20 @@ __global__ __launch_bounds__(DATTN_MAX_THREADS) void tiered_split_kernel(DecodeA
 // group 0 leaves N, C and P in the schedule area of the workspace for the
 // combine kernel.
 
-// Tiles of sequence b and the unit cost of each.
+// Tiles of sequence b and the unit cost of each.  A sequence with visible
+// keys also costs kSeqUnits up front, the start-up of a segment (table
+// staging, Q, the first dependent loads), so that a worker which starts a
+// second sequence is given fewer tiles.
+#ifndef DATTN_SEQ_UNITS
+#define DATTN_SEQ_UNITS 4
+#endif
+constexpr int kSeqUnits = DATTN_SEQ_UNITS;
+
 template <int KIND>
 struct SeqCost {
   int lo, hi, base;   // visible keys [lo, hi]; tile i starts at key base + 16i
   int ntiles, ncold;  // tiles < ncold cost 1 unit, the others 2 (tiered only)
+  int head;           // start-up units (0 for a sequence with no visible key)
   __device__ __forceinline__ void init(const DecodeArgs& a, int b) {
     int q;
     visible_range(a, b, lo, hi, q);
@@ -1075,10 +1116,14 @@ struct SeqCost {
     ntiles = hi < lo ? 0 : (hi >> 4) - (lo >> 4) + 1;
     ncold = ntiles;
     if constexpr (KIND == 2) ncold = min(ntiles, max(0, (a.cold_lens[b] - base + kTile - 1) / kTile));
+    head = ntiles > 0 ? kSeqUnits : 0;
   }
-  __device__ __forceinline__ int units() const { return ncold + 2 * (ntiles - ncold); }
+  __device__ __forceinline__ int units() const { return head + ncold + 2 * (ntiles - ncold); }
   // first tile whose first unit is >= u (0 <= u <= units())
-  __device__ __forceinline__ int tile_at(int u) const { return u <= ncold ? u : ncold + (u - ncold + 1) / 2; }
+  __device__ __forceinline__ int tile_at(int u) const {
+    u = max(u - head, 0);
+    return u <= ncold ? u : ncold + (u - ncold + 1) / 2;
+  }
 };
 
 // P[0..B] (exclusive prefix of unit counts) into LDS; returns N = P[B].
@@ -1115,7 +1160,7 @@ __device__ __forceinline__ int unit_prefix(const DecodeArgs& a, int32_t* P) {
 // waves per SIMD (more waves keep more loads in flight than the register
 // savings cost).
 template <int D, int G, bool CAP, int KIND, bool FM>
-__global__ __launch_bounds__(DATTN_MAX_THREADS) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(DATTN_MAX_THREADS) __attribute__((amdgpu_waves_per_eu(DATTN_WPE)))
 void balanced_kernel(DecodeArgs a) {
   extern __shared__ int32_t lds[];
   const int B = a.num_seqs;
@@ -1168,7 +1213,7 @@ void balanced_kernel(DecodeArgs a) {
 // mask compacted in increasing order), takes the slice of that list its
 // split owns and sweeps its keys.
 template <int D, int G, bool CAP, bool FM>
-__global__ __launch_bounds__(DATTN_MAX_THREADS) void sparse_split_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(DATTN_MAX_THREADS) __attribute__((amdgpu_waves_per_eu(2))) void sparse_split_kernel(DecodeArgs a) {
   extern __shared__ uint32_t lds_sp[];
   const int split = blockIdx.x, b = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -1208,8 +1253,8 @@ __global__ __launch_bounds__(DATTN_MAX_THREADS) void sparse_split_kernel(DecodeA
   }
   __syncthreads();
   const PartialDst dst = split_dst(a, b, kvh, G, split, D);
-  const int e0 = split * a.blocks_per_split;
-  const int e1 = min(e0 + a.blocks_per_split, count);
+  const int e0 = (int)((int64_t)split * count / a.num_splits);
+  const int e1 = (int)((int64_t)(split + 1) * count / a.num_splits);
   if (e0 >= e1 || lo > hi) {
     write_empty<G>(dst, lane);
     return;
@@ -1237,39 +1282,45 @@ __global__ __launch_bounds__(DATTN_MAX_THREADS) void sparse_split_kernel(DecodeA
 template <int D, class Loc>
 __device__ __forceinline__ void merge_partials(const Loc& loc, int n, float* __restrict__ out,
                                                float* __restrict__ lse_out) {
-  // 256 threads: slot group sg = tid / 32 takes partials sg, sg + 8, ...;
-  // within a group, thread c owns dims 4c + 128j.  (m, l) pairs are staged
-  // in LDS (first 256 partials), the rest read again from memory.
+  // 256 threads: slot group sg = tid / 32 takes partials sg, sg + 8, ... and
+  // folds them in with a running max (the rule above, one partial at a
+  // time), loading four partials at once; thread c of a group owns dims
+  // 4c + 128j.  The eight groups are then merged through LDS.  (m, l) and acc
+  // are loaded together, so the merge waits on one round of loads.
   constexpr int NJ = D / 128 > 0 ? D / 128 : 1;
   constexpr int DC = D >= 128 ? 32 : D / 4;   // threads per group carrying dims
-  __shared__ float2 mls[256];
+  constexpr int U = 4;                        // partials per group per round
   __shared__ float red[8][D];
   __shared__ float redm[8], redl[8];
   const int tid = threadIdx.x, sg = tid >> 5, c = tid & 31;
-  float M = -__builtin_inff();
-  for (int s = tid; s < n; s += 256) {
-    const float2 v = loc.ml(s);
-    if (s < 256) mls[s] = v;
-    if (v.y > 0.f) M = fmaxf(M, v.x);
-  }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, shfl_xor_f(M, o));
-  if ((tid & 63) == 0) redm[tid >> 6] = M;
-  __syncthreads();
-  M = fmaxf(fmaxf(redm[0], redm[1]), fmaxf(redm[2], redm[3]));
-  float L = 0.f;
+  float m = -__builtin_inff(), L = 0.f;
   f4 o[NJ];
 #pragma unroll
   for (int j = 0; j < NJ; ++j) o[j] = f4{0.f, 0.f, 0.f, 0.f};
-  for (int s = sg; s < n; s += 8) {
-    const float2 v = s < 256 ? mls[s] : loc.ml(s);
-    if (v.y > 0.f) {
-      const float wt = fast_exp2(v.x - M);
-      L += wt * v.y;
-      if (c < DC) {
+  for (int s0 = sg; s0 < n; s0 += 8 * U) {
+    float2 v[U];
+    f4 x[U][NJ];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int s = s0 + 8 * u;
+      v[u] = s < n ? loc.ml(s) : make_float2(-__builtin_inff(), 0.f);
+      if (s < n && c < DC) {
         const float* row = loc.acc(s);
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) o[j] += wt * *(const f4*)(row + 128 * j + 4 * c);
+        for (int j = 0; j < NJ; ++j) x[u][j] = *(const f4*)(row + 128 * j + 4 * c);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (v[u].y > 0.f) {   // skipped: empty pieces (their acc is never read into the sum)
+        const float m_new = fmaxf(m, v[u].x);
+        const float ca = fast_exp2(m - m_new), cb = fast_exp2(v[u].x - m_new);
+        L = L * ca + v[u].y * cb;
+        if (c < DC) {
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) o[j] = o[j] * ca + x[u][j] * cb;
+        }
+        m = m_new;
       }
     }
   }
@@ -1277,13 +1328,24 @@ __device__ __forceinline__ void merge_partials(const Loc& loc, int n, float* __r
 #pragma unroll
     for (int j = 0; j < NJ; ++j) *(f4*)&red[sg][128 * j + 4 * c] = o[j];
   }
-  if (c == 0) redl[sg] = L;
+  if (c == 0) {
+    redm[sg] = m;
+    redl[sg] = L;
+  }
   __syncthreads();
-  const float Lt = ((redl[0] + redl[1]) + (redl[2] + redl[3])) + ((redl[4] + redl[5]) + (redl[6] + redl[7]));
+  float M = -__builtin_inff();
+#pragma unroll
+  for (int g = 0; g < 8; ++g) M = redl[g] > 0.f ? fmaxf(M, redm[g]) : M;
+  float wg[8], Lt = 0.f;
+#pragma unroll
+  for (int g = 0; g < 8; ++g) {
+    wg[g] = redl[g] > 0.f ? fast_exp2(redm[g] - M) : 0.f;
+    Lt += redl[g] * wg[g];
+  }
   for (int d = tid; d < D; d += 256) {
     float ot = 0.f;
 #pragma unroll
-    for (int g = 0; g < 8; ++g) ot += red[g][d];
+    for (int g = 0; g < 8; ++g) ot += red[g][d] * wg[g];
     out[d] = Lt > 0.f ? ot / Lt : 0.f;
   }
   if (tid == 0 && lse_out) *lse_out = Lt > 0.f ? (M + __builtin_log2f(Lt)) * kLn2 : -__builtin_inff();
