@@ -207,17 +207,20 @@ def measure(case, steps, warmup, copies=None):
         r.call(i, "all")
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / steps
-    # per-kernel durations from events recorded on the launch stream around each phase
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    # Per-kernel durations: `steps` back-to-back launches of one phase between two
+    # events recorded on the launch stream (events around a single launch would add
+    # the dispatch overhead of that launch to every sample).
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    ev[0].record()
     for i in range(steps):
-        ev[i][0].record()
         r.call(i, "split")
-        ev[i][1].record()
+    ev[1].record()
+    for i in range(steps):
         r.call(i, "combine")
-        ev[i][2].record()
+    ev[2].record()
     torch.cuda.synchronize()
-    split_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
-    comb_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    split_ms = ev[0].elapsed_time(ev[1]) / steps
+    comb_ms = ev[1].elapsed_time(ev[2]) / steps
     return r, dict(wall_s=wall, split_ms=split_ms, combine_ms=comb_ms, copies=copies)
 
 
@@ -226,7 +229,7 @@ def kernel_source_sha():
     return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
 
 
-def measured_traffic():
+def measured_traffic(workload=None):
     """HBM bytes per launch of the split kernel from the committed counter summary
     (FETCH_SIZE + WRITE_SIZE, scaled by a copy kernel of known size), or None when
     the summary is missing or was taken on a different kernel source."""
@@ -234,7 +237,7 @@ def measured_traffic():
         t = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
-    if t.get("kernel_source_sha256") != kernel_source_sha():
+    if t.get("kernel_source_sha256") != kernel_source_sha() or (workload and t.get("workload") != workload):
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -349,6 +352,10 @@ def main():
     split_s = m["split_ms"] / 1e3
     achieved = kvb / split_s / 1e9
     B, H, D = case.q.shape
+    G = H // case.params["num_kv_heads"]
+    kind = {"paged": "paged f16" if case.k_cache is not None and case.k_cache.dtype == np.float16 else "paged f32",
+            "tiered": "tiered int8 + f16 ring", "sparse": "block-sparse f16"}[case.kind]
+    lens = case.seq_lens
     out = {
         "metric": "KV-read HBM GB/s (% of peak) and decode queries/sec, 1 MI355X",
         "value": head["kv_gbs"],
@@ -364,14 +371,15 @@ def main():
         "data": "synthetic (seeded numpy N(0,1) Q/K/V, uniform lengths, permuted block pool)",
         "config": {"workload": case.name, "global_batch": int(B), "num_heads": int(H),
                    "num_kv_heads": int(case.params["num_kv_heads"]), "head_dim": int(D),
-                   "block_size": int(case.params["block_size"]), "seq_len_range": [512, 4096],
-                   "total_tokens": int(case.seq_lens.sum()), "parallelism": "single GPU"},
+                   "block_size": int(case.params["block_size"]),
+                   "seq_len_range": [int(lens.min()), int(lens.max())],
+                   "total_tokens": int(lens.sum()), "parallelism": "single GPU"},
         "pct_of_hbm_peak": head["pct_peak"],
         "queries_per_s": head["queries_per_s"],
         "kernels": {"split_ms": head["split_ms"], "combine_ms": head["combine_ms"]},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
-                     "kernel": f"balanced_kernel<D={D}, G={H // case.params['num_kv_heads']}, paged f16>",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(case.name),
+                     "kernel": f"split kernel <D={D}, G={G}, {kind}>",
                      "bytes_per_launch": kvb},
         "parity_sample": {k: head[k] for k in ("sample_max_abs_err", "sample_rel_err", "sample_lse_err")},
         "copy_reference_gbs": copy_reference(),
