@@ -80,7 +80,8 @@ typedef struct dattn_params {
   int32_t max_blocks_per_seq; /* row stride of the block table, >= 1 */
   int32_t num_blocks;         /* physical blocks in the pool, >= 1 */
   int32_t max_seq_len;        /* host-known upper bound of seq_lens[], >= 0; sizes the grid */
-  int32_t split_tokens;       /* keys per KV split; 0 => library choice, else a multiple of 16 */
+  int32_t split_tokens;       /* keys per KV split (block-sparse: at most split_tokens / sparse_block
+                                 union blocks per split); 0 => library choice, else a multiple of 16 */
   int32_t phases;             /* 0 (or DATTN_PHASE_ALL) => both phases; see below */
 } dattn_params;
 
@@ -105,7 +106,10 @@ typedef struct dattn_params {
 
 /*
  * Workspace bytes a call of `kind` with these parameters needs.
- * sparse_block is read only for DATTN_KIND_BLOCK_SPARSE.
+ * sparse_block is read only for DATTN_KIND_BLOCK_SPARSE.  For that kind with
+ * split_tokens == 0 the split count follows the current device's CU count
+ * (256 assumed when no device can be queried), so query the size with the
+ * device current that the calls will run on.
  * Returns DATTN_OK and writes *bytes, or a negative code.
  */
 int dattn_workspace_size(const dattn_params* p, int32_t kind, int32_t sparse_block, size_t* bytes);
