@@ -239,3 +239,48 @@ def test_hot_cold_split_point_on_gpu():
         if ref is None:
             ref = oracle_run(c)
         compare(o, l, *ref, what=f"exact tiered cold={cold}")
+
+
+# ------------------------------------------- rows that hold no live token
+
+def _poison_paged(k, v, table, lens, bs):
+    """NaN / Inf in every pool row that holds no token of any sequence."""
+    live = np.zeros(k.shape[:2], bool)
+    for b, L in enumerate(lens):
+        t = np.arange(int(L))
+        live[table[b, t // bs], t % bs] = True
+    k[~live] = np.float16(np.nan)
+    v[~live] = np.float16(np.inf)
+
+
+@pytest.mark.parametrize("bs", [16, 5])
+def test_paged_nonlive_rows_hold_nan(bs):
+    """Tiles that straddle the end of a sequence read whole rows when the block
+    size is a multiple of 16: whatever the rows past the end hold must not reach
+    the output (the oracle never reads them)."""
+    c = synth.paged_case(120 + bs, 3, 16, 4, 128, bs, lens=[77, 300, 1], kv_dtype=synth.F16, window=0,
+                         q_pos=[70, 299, 0])
+    _poison_paged(c.k_cache, c.v_cache, c.block_table, c.seq_lens, bs)
+    _check(c, what=f"paged f16 bs{bs} NaN/Inf outside the live rows")
+
+
+def test_tiered_nonlive_rows_hold_nan():
+    c = synth.tiered_case(122, 3, 16, 4, 128, 16, [700, 300, 40], [450, 260, 0], 256, softcap=30.0, window=200)
+    live = np.zeros(c.k_scale.shape[:2], bool)
+    for b, C in enumerate(c.cold_lens):
+        t = np.arange(int(C))
+        live[c.cold_block_table[b, t // 16], t % 16] = True
+    c.k_scale[~live] = np.float16(np.nan)
+    c.v_scale[~live] = np.float16(np.inf)
+    ring_live = np.zeros(c.k_hot.shape[:2], bool)
+    for b, (L, C) in enumerate(zip(c.seq_lens, c.cold_lens)):
+        ring_live[b, np.arange(int(C), int(L)) % c.hot_window] = True
+    c.k_hot[~ring_live] = np.float16(np.nan)
+    c.v_hot[~ring_live] = np.float16(np.inf)
+    _check(c, what="tiered NaN/Inf outside the live rows and ring slots")
+
+
+def test_sparse_nonlive_rows_hold_nan():
+    c = synth.sparse_case(123, 2, 16, 4, 128, 16, 64, 3, [1000, 333])
+    _poison_paged(c.k_cache, c.v_cache, c.block_table, c.seq_lens, 16)
+    _check(c, what="sparse NaN/Inf outside the live rows")
