@@ -262,7 +262,9 @@ dattn::DecodeArgs base_args(const dattn_params* p, const Plan& pl, const float* 
   const double scale = p->scale != 0.0f ? (double)p->scale : (double)(float)(1.0 / sqrt((double)p->head_dim));
   const double log2e = 1.4426950408889634;
   if (p->softcap > 0.0f) {
-    a.qmul = (float)(scale / (double)p->softcap);
+    // the kernel's raw score is then 2 log2(e) * scale * <q, k> / cap, the
+    // exponent of e^{2x} in tanh(x) = 1 - 2 / (e^{2x} + 1)
+    a.qmul = (float)(2.0 * log2e * scale / (double)p->softcap);
     a.capl2 = (float)((double)p->softcap * log2e);
   } else {
     a.qmul = (float)(scale * log2e);

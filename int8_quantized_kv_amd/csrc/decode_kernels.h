@@ -85,7 +85,7 @@ struct DecodeArgs {
   int32_t num_seqs, num_heads, num_kv_heads, max_blocks, num_splits, split_tokens;
   int32_t causal, window, hot_window;
   int32_t sparse_block, num_layouts, row_stride, col_stride, sparse_nblk;
-  float qmul;    // scale * log2(e) without softcap, scale / cap with softcap
+  float qmul;    // scale * log2(e) without softcap, 2 log2(e) * scale / cap with softcap
   float capl2;   // cap * log2(e), 0 without softcap
   FastDiv bs, hw, sb;
 };
@@ -143,10 +143,11 @@ __device__ __forceinline__ float rows_sum(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// tanh(x) = 1 - 2 / (e^{2x} + 1); saturates correctly at +-inf.
-__device__ __forceinline__ float fast_tanh(float x) {
-  float e = fast_exp2(x * 2.8853900817779268f);
-  return 1.0f - 2.0f * __builtin_amdgcn_rcpf(e + 1.0f);
+// Softcapped score in log2 units from y = 2 log2(e) x (x = scaled score / cap):
+// cap log2(e) tanh(x) = capl2 - 2 capl2 / (2^y + 1), which saturates correctly
+// at y = +-inf.
+__device__ __forceinline__ float softcap_l2(float y, float capl2) {
+  return __builtin_fmaf(-2.0f * capl2, __builtin_amdgcn_rcpf(fast_exp2(y) + 1.0f), capl2);
 }
 
 // Visible absolute key range [lo, hi] of sequence b (hi < lo when empty):
@@ -783,6 +784,7 @@ struct Online {
   static constexpr int NT = Lay<D>::NT;
   float m;       // running max (log2 units) of head lane%16 -- equal in all rows
   float l;       // denominator part of (head lane%16, keys of row lane/16)
+  float c_last;  // correction factor of the last tile (1 when m did not move)
   f4 o[NT];      // o[t][e]: PV sum of head 4*(lane/16)+e, dim NT*(lane%16)+t
 
   __device__ __forceinline__ void init() {
@@ -794,15 +796,14 @@ struct Online {
 
   // raw: this lane's 4 scores (already multiplied by qmul and any int8 key
   // scale); valid: which of keys 4*(lane/16)+e take part.  Returns p[4] in
-  // the score layout, which is the A operand of the PV products, and rescales
-  // the state.
-  __device__ __forceinline__ void softmax_tile(float capl2, const f4& raw, const bool (&valid)[4], float (&p)[4],
-                                               int lane) {
+  // the score layout, which is the A operand of the PV products, updates m
+  // and l, and says whether the accumulator must be rescaled (rescale()).
+  __device__ __forceinline__ bool softmax_tile(float capl2, const f4& raw, const bool (&valid)[4], float (&p)[4]) {
     float s[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       float x = raw[e];
-      if constexpr (CAP) x = capl2 * fast_tanh(x);
+      if constexpr (CAP) x = softcap_l2(x, capl2);
       s[e] = valid[e] ? x : -__builtin_inff();
     }
     const float mx = rows_max(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])));
@@ -813,17 +814,21 @@ struct Online {
 #pragma unroll
     for (int e = 0; e < 4; ++e) p[e] = fast_exp2(s[e] - m_use);
     l = l * c + ((p[0] + p[1]) + (p[2] + p[3]));
-    if (__builtin_amdgcn_ballot_w64(c != 1.0f)) {
-      // row 4g+e of the accumulator is head 4g+e, whose factor lane 4g+e holds
-      const int g = lane >> 4;
-      float ce[4];
+    c_last = c;
+    return __builtin_amdgcn_ballot_w64(c != 1.0f) != 0;
+  }
+
+  // Rescale the accumulator after softmax_tile returned true: row 4g+e of it
+  // is head 4g+e, whose factor lane 4g+e holds.
+  __device__ __forceinline__ void rescale(int lane) {
+    const int g = lane >> 4;
+    float ce[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) ce[e] = __shfl(c, 4 * g + e, 64);
+    for (int e = 0; e < 4; ++e) ce[e] = __shfl(c_last, 4 * g + e, 64);
 #pragma unroll
-      for (int t = 0; t < NT; ++t)
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o[t][e] *= ce[e];
-    }
+      for (int e = 0; e < 4; ++e) o[t][e] *= ce[e];
   }
 
   // Write the partial of heads kvh*G + [0, G): head 4g+e's dims
@@ -894,7 +899,7 @@ __device__ __forceinline__ void run_tiles(const DecodeArgs& a, const Store& st, 
     bool valid[4], kvalid[4];
     map.tile_valid(t0, lg, valid, kvalid);
     float p[4];
-    on.softmax_tile(a.capl2, raw, valid, p, lane);
+    if (on.softmax_tile(a.capl2, raw, valid, p)) on.rescale(lane);
     st.template pv<FAST>(kb[slot], vb[slot], p, kvalid, on.o);
   };
 
