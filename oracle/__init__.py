@@ -1,4 +1,5 @@
-"""fp64 CPU oracle for decode attention (paged, tiered int8/f16, block-sparse).
+"""fp64 CPU oracle for decode attention (paged, tiered int8/f16, block-sparse)
+and for the tiered cache's quantise-on-evict write path.
 
 TEST INFRASTRUCTURE ONLY: the product library never imports this package.
 Only the tests, the smoke check and the benchmark's CPU-baseline leg use it.
@@ -103,6 +104,12 @@ def load(path: str = _LIB):
                                             i32, P, i32, i32, P, P]
     for f in (lib.orc_decode_paged, lib.orc_decode_tiered_int8, lib.orc_decode_block_sparse):
         f.restype = ctypes.c_int
+    lib.orc_f32_to_f16.argtypes = [ctypes.c_float]
+    lib.orc_f32_to_f16.restype = ctypes.c_uint16
+    lib.orc_quantize_row.argtypes = [P, i32, P, P]
+    lib.orc_quantize_row.restype = None
+    lib.orc_append_tiered_int8.argtypes = [ctypes.POINTER(_Params), P, P, P, P, i32, P, P, P, P, P, P, P]
+    lib.orc_append_tiered_int8.restype = ctypes.c_int
     _libs[path] = lib
     return lib
 
@@ -252,3 +259,42 @@ def run(case, pairs=None, nthreads=0, lib=None):
                                    case.sparse_block, case.num_layouts, case.row_ptr, case.col_idx, case.q_pos,
                                    pairs, nthreads, lib)
     raise ValueError(case.kind)
+
+
+def f32_to_f16(x: float, lib=None) -> int:
+    """IEEE binary16 bits of the f32 value x, rounded to nearest even."""
+    return int(_load(lib).orc_f32_to_f16(float(np.float32(x))))
+
+
+def quantize_row(x_f16, lib=None):
+    """One row of D f16 values -> (D/4 packed u32 words, f16 scale bits)."""
+    lib = _load(lib)
+    x = _arr(np.asarray(x_f16).view(np.float16).reshape(-1), np.float16)
+    D = int(x.size)
+    words = np.zeros(D // 4, np.uint32)
+    sc = np.zeros(1, np.uint16)
+    lib.orc_quantize_row(_ptr(x), D, _ptr(words), _ptr(sc))
+    return words, int(sc[0])
+
+
+def append_tiered_int8(p: Params, k_new, v_new, k_hot, v_hot, hot_window, k_cold, v_cold, k_scale, v_scale,
+                       cold_block_table, seq_lens, cold_lens, lib=None):
+    """Append one token per sequence (k_new, v_new [B, Hkv, D] f16) to a tiered cache.
+    Works on copies and returns (k_hot, v_hot, k_cold, v_cold, k_scale, v_scale, seq_lens, cold_lens)."""
+    lib = _load(lib)
+    kn = _arr(k_new, np.float16)
+    vn = _arr(v_new, np.float16)
+    kh = np.array(_arr(k_hot, np.float16), copy=True)
+    vh = np.array(_arr(v_hot, np.float16), copy=True)
+    kc = np.array(_arr(k_cold, np.uint32), copy=True)
+    vc = np.array(_arr(v_cold, np.uint32), copy=True)
+    ks = np.array(_arr(k_scale, np.float16), copy=True)
+    vs = np.array(_arr(v_scale, np.float16), copy=True)
+    bt = _arr(cold_block_table, np.int32)
+    sl = np.array(_arr(seq_lens, np.int32), copy=True)
+    cl = np.array(_arr(cold_lens, np.int32), copy=True)
+    cp = p.c()
+    rc = lib.orc_append_tiered_int8(ctypes.byref(cp), _ptr(kn), _ptr(vn), _ptr(kh), _ptr(vh), int(hot_window),
+                                    _ptr(kc), _ptr(vc), _ptr(ks), _ptr(vs), _ptr(bt), _ptr(sl), _ptr(cl))
+    _check(rc, "orc_append_tiered_int8")
+    return kh, vh, kc, vc, ks, vs, sl, cl

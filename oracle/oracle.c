@@ -48,9 +48,22 @@
  *           (com.microsoft.SparseAttention sparse-attention.wgsl.jinja, the
  *           slot-resolution loop of the attention pass).
  *
+ * The write path (orc_append_tiered_int8) appends one token per sequence to
+ * the tiered cache: when the hot ring already holds hot_window tokens, the
+ * oldest hot token (absolute position cold_len[b], ring slot
+ * cold_len[b] mod hot_window) is first quantised into the paged cold tier at
+ * position cold_len[b] and cold_len[b] grows by one; the new token then goes
+ * to ring slot seq_len[b] mod hot_window and seq_len[b] grows by one.  The
+ * quantiser is not on the pages; it is the one the tiered workload's data is
+ * described with (a per-(token, kv head) f16 scale max|x|/127), read as:
+ * s32 = max|x| / 127 in f32, s = s32 rounded to f16 (nearest even),
+ * i = clamp(rint(x / f32(s)), -127, 127) in f32, an all-zero row giving
+ * s = 0 and i = 0.
+ *
  * Every function validates its inputs enough never to read out of bounds and
  * returns a negative code otherwise.
  */
+#include <float.h>
 #include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -389,4 +402,107 @@ int orc_max_threads(void) {
 #else
   return 1;
 #endif
+}
+
+/* ------------------------------------------------------- the write path */
+
+/* f32 -> IEEE binary16 bits, rounded to nearest, ties to even, from the
+ * format's definition: the value is scaled so that one unit is the f16 step
+ * at its exponent (2^-24 below 2^-14, 2^(e-10) in [2^e, 2^(e+1))) and rounded
+ * with rint; a carry into the next binade or past 65504 is handled
+ * explicitly.  Every f32 is exact in double, so the scaling is exact. */
+uint16_t orc_f32_to_f16(float f) {
+  double v = (double)f;
+  if (isnan(v)) return 0x7e00;
+  const uint16_t sign = signbit(v) ? 0x8000 : 0;
+  v = fabs(v);
+  if (isinf(v)) return sign | 0x7c00;
+  if (v < ldexp(1.0, -14)) {                 /* subnormal result (or zero) */
+    const double r = rint(ldexp(v, 24));     /* r == 1024 is the smallest normal */
+    return sign | (uint16_t)r;
+  }
+  int e;
+  frexp(v, &e);
+  e -= 1;                                    /* v in [2^e, 2^(e+1)) */
+  double r = rint(ldexp(v, 10 - e));         /* in [1024, 2048] */
+  if (r == 2048.0) {
+    r = 1024.0;
+    e += 1;
+  }
+  if (e > 15) return sign | 0x7c00;
+  return sign | (uint16_t)((e + 15) << 10) | (uint16_t)(r - 1024.0);
+}
+
+/* One row of D f16 values -> D/4 packed words (element d is byte d % 4 of
+ * word d / 4, least-significant byte first, two's complement) and its f16
+ * scale, with the quantiser reading above; every step on floats is an f32
+ * operation. */
+void orc_quantize_row(const uint16_t* x, int32_t D, uint32_t* words, uint16_t* scale) {
+  float amax = 0.0f;
+  for (int32_t d = 0; d < D; ++d) {
+    const float v = (float)orc_f16_to_f64(x[d]);
+    if (fabsf(v) > amax) amax = fabsf(v);
+  }
+  const float s32 = amax / 127.0f;
+  const uint16_t s16 = orc_f32_to_f16(s32);
+  const float s = (float)orc_f16_to_f64(s16);
+  for (int32_t w = 0; w < D / 4; ++w) words[w] = 0u;
+  for (int32_t d = 0; d < D; ++d) {
+    int32_t i = 0;
+    if (s > 0.0f) {
+      const float r = rintf((float)orc_f16_to_f64(x[d]) / s);
+      i = r > 127.0f ? 127 : (r < -127.0f ? -127 : (int32_t)r);
+    }
+    words[d / 4] |= ((uint32_t)(uint8_t)(int8_t)i) << (8 * (d % 4));
+  }
+  *scale = s16;
+}
+
+/* Append one token per sequence (k_new, v_new [B][Hkv][D] f16) to the tiered
+ * cache, updating seq_lens and cold_lens in place.  Returns ORC_EINVAL, with
+ * nothing written, if a sequence breaks 0 <= cold_len <= seq_len,
+ * seq_len - cold_len <= hot_window, or needs a cold block-table entry that is
+ * out of range. */
+int orc_append_tiered_int8(const orc_params* p, const uint16_t* k_new, const uint16_t* v_new, uint16_t* k_hot,
+                           uint16_t* v_hot, int32_t hot_window, uint32_t* k_cold, uint32_t* v_cold,
+                           uint16_t* k_scale, uint16_t* v_scale, const int32_t* cold_block_table,
+                           int32_t* seq_lens, int32_t* cold_lens) {
+  const int32_t B = p->num_seqs, Hkv = p->num_kv_heads, D = p->head_dim, bs = p->block_size;
+  if (B < 0 || Hkv < 1 || D < 4 || D % 4 || bs < 1 || hot_window < 1 || p->max_blocks_per_seq < 1 ||
+      p->num_blocks < 1)
+    return ORC_EINVAL;
+  for (int32_t b = 0; b < B; ++b) {
+    const int64_t L = seq_lens[b], C = cold_lens[b];
+    if (C < 0 || C > L || L - C > hot_window || L >= INT32_MAX) return ORC_EINVAL;
+    if (L - C == hot_window) {
+      if (C / bs >= p->max_blocks_per_seq) return ORC_EINVAL;
+      const int32_t blk = cold_block_table[(size_t)b * p->max_blocks_per_seq + C / bs];
+      if (blk < 0 || blk >= p->num_blocks) return ORC_EINVAL;
+    }
+  }
+  for (int32_t b = 0; b < B; ++b) {
+    int64_t L = seq_lens[b], C = cold_lens[b];
+    if (L - C == hot_window) {               /* ring full: evict position C */
+      const int64_t slot = orc_ring_slot(C, hot_window);
+      const int64_t blk = cold_block_table[(size_t)b * p->max_blocks_per_seq + C / bs];
+      const int64_t row = blk * bs + C % bs;
+      for (int32_t g = 0; g < Hkv; ++g) {
+        const size_t hot = (((size_t)b * hot_window + slot) * Hkv + g) * D;
+        const size_t cold = ((size_t)row * Hkv + g);
+        orc_quantize_row(k_hot + hot, D, k_cold + cold * (D / 4), k_scale + cold);
+        orc_quantize_row(v_hot + hot, D, v_cold + cold * (D / 4), v_scale + cold);
+      }
+      C += 1;
+    }
+    const int64_t slot = orc_ring_slot(L, hot_window);
+    for (int32_t g = 0; g < Hkv; ++g) {
+      const size_t hot = (((size_t)b * hot_window + slot) * Hkv + g) * D;
+      const size_t src = ((size_t)b * Hkv + g) * D;
+      memcpy(k_hot + hot, k_new + src, (size_t)D * sizeof(uint16_t));
+      memcpy(v_hot + hot, v_new + src, (size_t)D * sizeof(uint16_t));
+    }
+    seq_lens[b] = (int32_t)(L + 1);
+    cold_lens[b] = (int32_t)C;
+  }
+  return ORC_OK;
 }

@@ -96,3 +96,59 @@ def attend(case):
             out[b, h] = softmax(sv) @ Vh[h][vis[h]]
             lse[b, h] = logsumexp(sv)
     return out, lse
+
+
+# ----------------------------------------------- the tiered write path
+
+def quantize_f16_rows(x16):
+    """The quantiser reading restated with numpy on f16 rows [..., D]: in f32,
+    s32 = max|x| / 127, s = numpy's f16 rounding of s32, i = clip(rint(x / s),
+    -127, 127); s == 0 gives i == 0.  Returns (int8 codes, f16 scales)."""
+    x = np.asarray(x16, np.float16).astype(np.float32)
+    s32 = (np.max(np.abs(x), axis=-1) / np.float32(127.0)).astype(np.float32)
+    s16 = s32.astype(np.float16)
+    s = s16.astype(np.float32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        i = np.rint((x / s[..., None]).astype(np.float32))
+    i = np.where(s[..., None] > 0, i, 0.0)
+    return np.clip(i, -127, 127).astype(np.int8), s16
+
+
+def pack_bytes(codes):
+    """int8 [..., D] -> u32 [..., D/4]: element d is byte d % 4 of word d / 4, LSB first."""
+    u = np.asarray(codes, np.int8).view(np.uint8).astype(np.uint32).reshape(codes.shape[:-1] + (-1, 4))
+    return u[..., 0] | (u[..., 1] << 8) | (u[..., 2] << 16) | (u[..., 3] << 24)
+
+
+def tiered_after_appends(tokens_k, tokens_v, hot_window, table, bs, num_blocks):
+    """The tiered cache that holds the token histories tokens_k/v[b] ([T_b, Hkv, D] f16)
+    when every token was appended one at a time: the last min(T, hot_window)
+    tokens sit in ring slot t mod hot_window, the older ones are int8 in the
+    cold pool at row table[b][t // bs] * bs + t % bs."""
+    B = len(tokens_k)
+    Hkv, D = tokens_k[0].shape[1:]
+    k_hot = np.zeros((B, hot_window, Hkv, D), np.float16)
+    v_hot = np.zeros_like(k_hot)
+    k_cold = np.zeros((num_blocks, bs, Hkv, D // 4), np.uint32)
+    v_cold = np.zeros_like(k_cold)
+    k_sc = np.zeros((num_blocks, bs, Hkv), np.float16)
+    v_sc = np.zeros_like(k_sc)
+    seq = np.zeros(B, np.int32)
+    cold = np.zeros(B, np.int32)
+    for b in range(B):
+        T = len(tokens_k[b])
+        C = max(0, T - hot_window)
+        seq[b], cold[b] = T, C
+        for t in range(C, T):
+            k_hot[b, t % hot_window] = tokens_k[b][t]
+            v_hot[b, t % hot_window] = tokens_v[b][t]
+        if C:
+            ck, sk = quantize_f16_rows(tokens_k[b][:C])
+            cv, sv = quantize_f16_rows(tokens_v[b][:C])
+            t = np.arange(C)
+            blk, off = table[b, t // bs], t % bs
+            k_cold[blk, off] = pack_bytes(ck)
+            v_cold[blk, off] = pack_bytes(cv)
+            k_sc[blk, off] = sk
+            v_sc[blk, off] = sv
+    return k_hot, v_hot, k_cold, v_cold, k_sc, v_sc, seq, cold

@@ -34,7 +34,17 @@ MUTANTS = {
                            "for (int32_t d = 0; d < D - 1; ++d) dot += qv[d] * row[d];"),
     "value_scale_uses_key_scale": ("(is_v ? s->v_scale : s->k_scale)[row]", "s->k_scale[row]"),
     "empty_set_lse_zero": ("*lse = -INFINITY;", "*lse = 0.0;"),
+    # the write path
+    "evict_next_slot": ("const int64_t slot = orc_ring_slot(C, hot_window);",
+                        "const int64_t slot = orc_ring_slot(C + 1, hot_window);"),
+    "new_token_next_slot": ("const int64_t slot = orc_ring_slot(L, hot_window);",
+                            "const int64_t slot = orc_ring_slot(L + 1, hot_window);"),
+    "scale_not_rounded_to_f16": ("const float s = (float)orc_f16_to_f64(s16);", "const float s = s32;"),
+    "codes_round_half_away": ("const float r = rintf(", "const float r = roundf("),
+    "f16_ties_round_up": ("double r = rint(ldexp(v, 10 - e));", "double r = floor(ldexp(v, 10 - e) + 0.5);"),
+    "cold_len_not_advanced": ("      C += 1;\n", "      C += 0;\n"),
 }
+PIN_FILES = ["test_oracle_pins.py", "test_oracle_append_pins.py"]
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
@@ -49,6 +59,6 @@ def test_pins_catch_planted_mistake(name, tmp_path):
                    check=True)
     env = dict(os.environ, ORACLE_LIB_OVERRIDE=str(lib), OMP_NUM_THREADS="2")
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                        *[os.path.join(ROOT, "tests", f) for f in PIN_FILES]],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, f"mutant {name} survived the pins:\n{r.stdout[-2000:]}"
