@@ -224,6 +224,46 @@ def measure(case, steps, warmup, copies=None):
     return r, dict(wall_s=wall, split_ms=split_ms, combine_ms=comb_ms, copies=copies)
 
 
+def measure_append(B=16, Hkv=8, D=128, hot_window=512, bs=16, calls=200, warmup=20):
+    """The tiered write path in its steady state: every sequence's ring is full, so
+    each call quantises one token per (sequence, kv head) into the cold tier and
+    writes the new token to the ring.  Times `calls` back-to-back calls between two
+    HIP events on the current stream."""
+    import torch
+    import int8_quantized_kv_amd as dk
+    g = torch.Generator(device="cpu").manual_seed(9)
+    dev = "cuda:0"
+    total = calls + warmup
+    max_blocks = total // bs + 2
+    nb = B * max_blocks
+    k_hot = torch.randn(B, hot_window, Hkv, D, generator=g).half().to(dev)
+    v_hot = torch.randn(B, hot_window, Hkv, D, generator=g).half().to(dev)
+    k_new = torch.randn(total, B, Hkv, D, generator=g).half().to(dev)
+    v_new = torch.randn(total, B, Hkv, D, generator=g).half().to(dev)
+    k_cold = torch.zeros(nb, bs, Hkv, D // 4, dtype=torch.int32, device=dev)
+    v_cold = torch.zeros_like(k_cold)
+    k_sc = torch.zeros(nb, bs, Hkv, dtype=torch.float16, device=dev)
+    v_sc = torch.zeros_like(k_sc)
+    table = torch.randperm(nb, generator=g).to(torch.int32).reshape(B, max_blocks).to(dev)
+    seq = torch.full((B,), hot_window, dtype=torch.int32, device=dev)
+    cold = torch.zeros(B, dtype=torch.int32, device=dev)
+    args = (k_hot, v_hot, k_cold, v_cold, k_sc, v_sc, table, seq, cold)
+    for i in range(warmup):
+        dk.dattn_append_tiered_int8(k_new[i], v_new[i], *args)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(warmup, total):
+        dk.dattn_append_tiered_int8(k_new[i], v_new[i], *args)
+    e1.record()
+    torch.cuda.synchronize()
+    assert int(cold[0]) == total and int(seq[0]) == hot_window + total
+    us = e0.elapsed_time(e1) * 1e3 / calls
+    # per (sequence, kv head): new K, V read; evicted K, V read; codes + scales written; ring written
+    nbytes = B * Hkv * (2 * D * 2 + 2 * D * 2 + 2 * (D + 2) + 2 * D * 2)
+    return dict(workload=f"append_evict_tiered_int8_B{B}_Hkv{Hkv}_D{D}_hw{hot_window}", us_per_call=round(us, 3),
+                bytes_per_call=nbytes, gbs=round(nbytes / us / 1e3, 2))
+
+
 def kernel_source_sha():
     import hashlib
     return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
@@ -384,6 +424,8 @@ def main():
         "parity_sample": {k: head[k] for k in ("sample_max_abs_err", "sample_rel_err", "sample_lse_err")},
         "copy_reference_gbs": copy_reference(),
     }
+    log("timing the tiered write path ...")
+    out["write_path"] = measure_append()
     if not args.no_cpu_baseline:
         log("timing the oracle on the host ...")
         out["cpu_baseline"] = cpu_baseline(case, kvb)

@@ -175,6 +175,41 @@ int dattn_decode_block_sparse(const dattn_params* p, const float* q, const uint1
                               int32_t col_stride, float* out, float* lse, void* workspace, size_t workspace_bytes,
                               void* stream);
 
+/*
+ * Write path of the tiered cache: append one token per sequence (the step
+ * that produces the data dattn_decode_tiered_int8 reads).  For every
+ * sequence b with L = seq_lens[b], C = cold_lens[b]:
+ *   - if the ring is full (L - C == hot_window), the oldest hot token
+ *     (absolute position C, ring slot C % hot_window) is quantised into the
+ *     cold tier at position C (block cold_block_table[b][C / block_size],
+ *     offset C % block_size) and cold_lens[b] becomes C + 1;
+ *   - the new token k_new[b], v_new[b] goes to ring slot L % hot_window and
+ *     seq_lens[b] becomes L + 1.
+ * The ring slot and cold-row conventions are those of the tiered decode
+ * (doppler attention_decode_tiered_int8_f16kv.wgsl get_hot_pos and
+ * read_cold_k; attention.js pages the cold tier).  The quantiser is not on
+ * the pages; it follows the tiered workload's description (f16 scale =
+ * max|x| / 127 per (token, kv head)), every decision in f32:
+ * s = f16(max|x| / 127) rounded to nearest even,
+ * code = clamp(rint(x / s), -127, 127), an all-zero row giving s = 0.
+ *   k_new, v_new          [B, Hkv, D] f16 (bit patterns), read
+ *   k_hot, v_hot          [B, hot_window, Hkv, D] f16, updated
+ *   k_cold, v_cold        [num_blocks, block_size, Hkv, D/4] u32, updated
+ *   k_scale, v_scale      [num_blocks, block_size, Hkv] f16, updated
+ *   cold_block_table      [B, max_blocks_per_seq] i32; the entry for the block
+ *                         of position C must be allocated before an eviction
+ *   seq_lens, cold_lens   [B] i32 on the device, advanced in place
+ * Reads num_seqs, num_kv_heads, head_dim (64 or 128), block_size,
+ * max_blocks_per_seq and num_blocks from p.  Needs no workspace.  A sequence
+ * whose device state breaks 0 <= C <= L, L - C <= hot_window, or whose
+ * needed table entry is outside [0, num_blocks), is left unchanged.
+ * Overlapping calls on the same cache race.
+ */
+int dattn_append_tiered_int8(const dattn_params* p, const uint16_t* k_new, const uint16_t* v_new, uint16_t* k_hot,
+                             uint16_t* v_hot, int32_t hot_window, uint32_t* k_cold, uint32_t* v_cold,
+                             uint16_t* k_scale, uint16_t* v_scale, const int32_t* cold_block_table,
+                             int32_t* seq_lens, int32_t* cold_lens, void* stream);
+
 /* Message for the last non-zero return on this thread ("" if none). */
 const char* dattn_last_error(void);
 

@@ -28,7 +28,8 @@ from typing import Optional
 
 __all__ = [
     "DattnError", "DattnParams", "lib", "library_path", "dattn_workspace_size", "dattn_decode_paged",
-    "dattn_decode_tiered_int8", "dattn_decode_block_sparse", "dattn_last_error", "dattn_version",
+    "dattn_decode_tiered_int8", "dattn_decode_block_sparse", "dattn_append_tiered_int8", "dattn_last_error",
+    "dattn_version",
     "KIND_PAGED", "KIND_TIERED_INT8", "KIND_BLOCK_SPARSE", "F32", "F16", "PHASE_ALL", "PHASE_SPLIT",
     "PHASE_COMBINE",
 ]
@@ -86,8 +87,9 @@ def lib():
         L.dattn_decode_paged.argtypes = [PP, P, P, P, i32, P, P, P, P, P, P, sz, P]
         L.dattn_decode_tiered_int8.argtypes = [PP, P, P, P, i32, P, P, P, P, P, P, P, P, P, P, P, sz, P]
         L.dattn_decode_block_sparse.argtypes = [PP, P, P, P, P, P, P, i32, i32, P, i32, P, i32, P, P, P, sz, P]
+        L.dattn_append_tiered_int8.argtypes = [PP, P, P, P, P, i32, P, P, P, P, P, P, P, P]
         for f in (L.dattn_workspace_size, L.dattn_decode_paged, L.dattn_decode_tiered_int8,
-                  L.dattn_decode_block_sparse):
+                  L.dattn_decode_block_sparse, L.dattn_append_tiered_int8):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -243,6 +245,39 @@ def dattn_decode_tiered_int8(q, k_hot, v_hot, k_cold, v_cold, k_scale, v_scale, 
                                           _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
                                           _stream(stream)))
     return out, lse
+
+
+def dattn_append_tiered_int8(k_new, v_new, k_hot, v_hot, k_cold, v_cold, k_scale, v_scale, cold_block_table,
+                             seq_lens, cold_lens, *, stream=None):
+    """Append one token per sequence (k_new, v_new [B, Hkv, D] f16) to a tiered cache in place,
+    quantising the oldest hot token into the cold tier when the ring is full; seq_lens and
+    cold_lens (device int32) advance in place."""
+    torch = _torch()
+    dev = k_new.device
+    _need(k_new, "k_new", (torch.float16,), 3, dev)
+    _need(v_new, "v_new", (torch.float16,), 3, dev)
+    _need(k_hot, "k_hot", (torch.float16,), 4, dev)
+    _need(v_hot, "v_hot", (torch.float16,), 4, dev)
+    _need(k_cold, "k_cold", (torch.int32, torch.uint32), 4, dev)
+    _need(v_cold, "v_cold", (k_cold.dtype,), 4, dev)
+    _need(k_scale, "k_scale", (torch.float16,), 3, dev)
+    _need(v_scale, "v_scale", (torch.float16,), 3, dev)
+    _need(cold_block_table, "cold_block_table", (torch.int32,), 2, dev)
+    _need(seq_lens, "seq_lens", (torch.int32,), 1, dev)
+    _need(cold_lens, "cold_lens", (torch.int32,), 1, dev)
+    B, Hkv, D = k_new.shape
+    _, hot_window, Hkv2, Dh = k_hot.shape
+    NB, bs, Hkv3, W4 = k_cold.shape
+    if tuple(v_new.shape) != (B, Hkv, D) or k_hot.shape[0] != B or Hkv2 != Hkv or Dh != D or Hkv3 != Hkv \
+            or W4 * 4 != D or tuple(v_hot.shape) != tuple(k_hot.shape) or tuple(v_cold.shape) != tuple(k_cold.shape) \
+            or tuple(k_scale.shape) != (NB, bs, Hkv) or tuple(v_scale.shape) != (NB, bs, Hkv) \
+            or cold_block_table.shape[0] != B or seq_lens.shape[0] != B or cold_lens.shape[0] != B:
+        raise ValueError("tiered cache tensors disagree on shape")
+    p = DattnParams(B, Hkv, Hkv, D, 0.0, 0, 0, 0.0, bs, cold_block_table.shape[1], NB, 0, 0, 0)
+    _check(lib().dattn_append_tiered_int8(ctypes.byref(p), _ptr(k_new), _ptr(v_new), _ptr(k_hot), _ptr(v_hot),
+                                          hot_window, _ptr(k_cold), _ptr(v_cold), _ptr(k_scale), _ptr(v_scale),
+                                          _ptr(cold_block_table), _ptr(seq_lens), _ptr(cold_lens),
+                                          _stream(stream)))
 
 
 def dattn_decode_block_sparse(q, k_cache, v_cache, block_table, seq_lens, sparse_block: int, row_ptr, col_idx, *,

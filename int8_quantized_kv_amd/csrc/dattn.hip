@@ -13,6 +13,7 @@
 #include <tuple>
 
 #include "dattn.h"
+#include "append_kernel.h"
 #include "decode_kernels.h"
 #include "kernel_table.h"
 
@@ -451,6 +452,38 @@ int dattn_decode_block_sparse(const dattn_params* p, const float* q, const uint1
   const bool contig = p->block_size % 16 == 0 && sparse_block % 16 == 0;
   return launch(dattn::split_kernel(dattn::kSparse, p->head_dim, p->softcap > 0.0f, pl.G, contig), nullptr, p, pl,
                 a, out, lse, (hipStream_t)stream);
+}
+
+int dattn_append_tiered_int8(const dattn_params* p, const uint16_t* k_new, const uint16_t* v_new, uint16_t* k_hot,
+                             uint16_t* v_hot, int32_t hot_window, uint32_t* k_cold, uint32_t* v_cold,
+                             uint16_t* k_scale, uint16_t* v_scale, const int32_t* cold_block_table,
+                             int32_t* seq_lens, int32_t* cold_lens, void* stream) {
+  g_err.clear();
+  if (!p) return fail(DATTN_ERR_INVALID, "params is NULL");
+  if (p->num_seqs < 0) return fail(DATTN_ERR_INVALID, "num_seqs must be >= 0 (got %d)", p->num_seqs);
+  if (p->num_kv_heads < 1) return fail(DATTN_ERR_INVALID, "num_kv_heads must be >= 1 (got %d)", p->num_kv_heads);
+  if (p->head_dim != 64 && p->head_dim != 128)
+    return fail(DATTN_ERR_UNSUPPORTED, "head_dim %d not built (64, 128)", p->head_dim);
+  if (p->block_size < 1) return fail(DATTN_ERR_INVALID, "block_size must be >= 1 (got %d)", p->block_size);
+  if (p->max_blocks_per_seq < 1)
+    return fail(DATTN_ERR_INVALID, "max_blocks_per_seq must be >= 1 (got %d)", p->max_blocks_per_seq);
+  if (p->num_blocks < 1) return fail(DATTN_ERR_INVALID, "num_blocks must be >= 1 (got %d)", p->num_blocks);
+  if (hot_window < 1) return fail(DATTN_ERR_INVALID, "hot_window must be >= 1 (got %d)", hot_window);
+  if (p->num_seqs == 0) return DATTN_OK;
+  if (!k_new || !v_new || !k_hot || !v_hot || !k_cold || !v_cold || !k_scale || !v_scale || !cold_block_table ||
+      !seq_lens || !cold_lens)
+    return fail(DATTN_ERR_INVALID, "an array argument is NULL");
+  dattn::AppendArgs a{k_new,    v_new,      k_hot,           v_hot,         k_cold,
+                      v_cold,   k_scale,    v_scale,         cold_block_table, seq_lens,
+                      cold_lens, p->num_kv_heads, p->block_size, p->max_blocks_per_seq, p->num_blocks,
+                      hot_window};
+  const int waves = p->num_kv_heads < 16 ? p->num_kv_heads : 16;
+  const dim3 grid(p->num_seqs), block(64 * waves);
+  if (p->head_dim == 64)
+    hipLaunchKernelGGL(dattn::append_tiered_int8_kernel<64>, grid, block, 0, (hipStream_t)stream, a);
+  else
+    hipLaunchKernelGGL(dattn::append_tiered_int8_kernel<128>, grid, block, 0, (hipStream_t)stream, a);
+  return check_launch("append kernel");
 }
 
 }  // extern "C"

@@ -206,3 +206,29 @@ def test_binding_refuses_host_tensors(lib):
         dk.dattn_decode_paged(q, k, k, bt, sl, max_seq_len=1)
     with pytest.raises(TypeError):
         dk.dattn_decode_paged(q.double(), k, k, bt, sl, max_seq_len=1)
+
+
+def test_append_validates_before_any_hip_call(lib):
+    P = ctypes.c_void_p
+    fake = P(0x1000)   # never dereferenced: every call below fails validation or is empty
+    args = [fake] * 4 + [8] + [fake] * 7 + [None]
+    for kw, code, word in ((dict(head_dim=96), dk.ERR_UNSUPPORTED, "head_dim"),
+                           (dict(num_kv_heads=0), dk.ERR_INVALID, "num_kv_heads"),
+                           (dict(block_size=0), dk.ERR_INVALID, "block_size"),
+                           (dict(num_blocks=0), dk.ERR_INVALID, "num_blocks"),
+                           (dict(num_seqs=-1), dk.ERR_INVALID, "num_seqs")):
+        p = good_params(**kw)
+        rc = lib.dattn_append_tiered_int8(ctypes.byref(p), *args)
+        assert rc == code and word in dk.dattn_last_error(), kw
+    p = good_params()
+    bad_hw = list(args)
+    bad_hw[4] = 0
+    rc = lib.dattn_append_tiered_int8(ctypes.byref(p), *bad_hw)
+    assert rc == dk.ERR_INVALID and "hot_window" in dk.dattn_last_error()
+    null = list(args)
+    null[7] = None
+    rc = lib.dattn_append_tiered_int8(ctypes.byref(p), *null)
+    assert rc == dk.ERR_INVALID and "NULL" in dk.dattn_last_error()
+    p0 = good_params(num_seqs=0)
+    rc = lib.dattn_append_tiered_int8(ctypes.byref(p0), *([None] * 4 + [8] + [None] * 8))
+    assert rc == 0 and dk.dattn_last_error() == ""
