@@ -57,8 +57,7 @@ __device__ __forceinline__ void quantize_row_wave(const float (&x)[4], int lane,
   scale = __builtin_bit_cast(uint16_t, s16);
 }
 
-__device__ __forceinline__ void load4_f16(const uint16_t* p, float (&x)[4]) {
-  const uint2 w = *(const uint2*)p;
+__device__ __forceinline__ void unpack4_f16(uint2 w, float (&x)[4]) {
   x[0] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w.x & 0xFFFFu));
   x[1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w.x >> 16));
   x[2] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w.y & 0xFFFFu));
@@ -68,41 +67,55 @@ __device__ __forceinline__ void load4_f16(const uint16_t* p, float (&x)[4]) {
 // One workgroup per sequence, one wave per kv head (strided when Hkv exceeds
 // the waves); lane l < D/4 owns elements 4l .. 4l+3 of every row it touches.
 // A sequence whose lengths or cold block-table entry break the preconditions
-// is left unchanged.
+// is left unchanged.  The rows of the first kv head a wave handles are loaded
+// while the block-table entry is still in flight (their addresses depend only
+// on the lengths), so a call costs two dependent memory round trips, not three.
 template <int D>
 __global__ __launch_bounds__(1024) void append_tiered_int8_kernel(AppendArgs a) {
   const int b = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, waves = blockDim.x >> 6;
   const int64_t L = a.seq_lens[b], C = a.cold_lens[b];
   const int hw = a.hot_window, bs = a.block_size, Hkv = a.num_kv_heads;
-  bool ok = C >= 0 && C <= L && L - C <= hw && L < 0x7FFFFFFF;
-  const bool evict = ok && L - C == hw;
-  int64_t row = 0;
-  if (evict) {
-    const int64_t bi = C / bs;
-    const int32_t blk = bi < a.max_blocks ? a.table[(int64_t)b * a.max_blocks + bi] : -1;
-    if (blk < 0 || blk >= a.num_blocks)
-      ok = false;
-    else
-      row = (int64_t)blk * bs + C % bs;
-  }
-  if (!ok) return;   // uniform over the workgroup
+  if (!(C >= 0 && C <= L && L - C <= hw && L < 0x7FFFFFFF)) return;   // uniform over the workgroup
+  const bool evict = L - C == hw;
+  const int64_t bi = C / bs;
+  int32_t blk = 0;
+  if (evict) blk = bi < a.max_blocks ? a.table[(int64_t)b * a.max_blocks + bi] : -1;
   const int64_t slot_old = C % hw, slot_new = L % hw;
   const int c0 = 4 * lane;
+  const bool row_lane = lane < D / 4;
+  auto hot_at = [&](int64_t slot, int g) { return (((int64_t)b * hw + slot) * Hkv + g) * D + c0; };
+  auto new_at = [&](int g) { return ((int64_t)b * Hkv + g) * D + c0; };
+  uint2 hk = {0u, 0u}, hv = {0u, 0u}, nk = {0u, 0u}, nv = {0u, 0u};
+  if (wave < Hkv && row_lane) {
+    if (evict) {
+      hk = *(const uint2*)(a.k_hot + hot_at(slot_old, wave));
+      hv = *(const uint2*)(a.v_hot + hot_at(slot_old, wave));
+    }
+    nk = *(const uint2*)(a.k_new + new_at(wave));
+    nv = *(const uint2*)(a.v_new + new_at(wave));
+  }
+  if (evict && (blk < 0 || blk >= a.num_blocks)) return;   // uniform over the workgroup
+  const int64_t row = (int64_t)blk * bs + C % bs;
   for (int g = wave; g < Hkv; g += waves) {
-    const int64_t hot_old = (((int64_t)b * hw + slot_old) * Hkv + g) * D;
+    if (g != wave && row_lane) {
+      if (evict) {
+        hk = *(const uint2*)(a.k_hot + hot_at(slot_old, g));
+        hv = *(const uint2*)(a.v_hot + hot_at(slot_old, g));
+      }
+      nk = *(const uint2*)(a.k_new + new_at(g));
+      nv = *(const uint2*)(a.v_new + new_at(g));
+    }
     if (evict) {
       const int64_t cold = row * Hkv + g;
-      float xk[4] = {0.f, 0.f, 0.f, 0.f}, xv[4] = {0.f, 0.f, 0.f, 0.f};
-      if (lane < D / 4) {
-        load4_f16(a.k_hot + hot_old + c0, xk);
-        load4_f16(a.v_hot + hot_old + c0, xv);
-      }
+      float xk[4], xv[4];
+      unpack4_f16(hk, xk);
+      unpack4_f16(hv, xv);
       uint32_t wk, wv;
       uint16_t sk, sv;
       quantize_row_wave<D>(xk, lane, wk, sk);
       quantize_row_wave<D>(xv, lane, wv, sv);
-      if (lane < D / 4) {
+      if (row_lane) {
         a.k_cold[cold * (D / 4) + lane] = wk;
         a.v_cold[cold * (D / 4) + lane] = wv;
       }
@@ -112,12 +125,10 @@ __global__ __launch_bounds__(1024) void append_tiered_int8_kernel(AppendArgs a) 
       }
     }
     // the new token goes to slot L mod hw (the evicted slot when the ring was
-    // full: its old contents were read above, before this store)
-    if (lane < D / 4) {
-      const int64_t src = ((int64_t)b * Hkv + g) * D + c0;
-      const int64_t dst = (((int64_t)b * hw + slot_new) * Hkv + g) * D + c0;
-      *(uint2*)(a.k_hot + dst) = *(const uint2*)(a.k_new + src);
-      *(uint2*)(a.v_hot + dst) = *(const uint2*)(a.v_new + src);
+    // full: its old contents are already in registers)
+    if (row_lane) {
+      *(uint2*)(a.k_hot + hot_at(slot_new, g)) = nk;
+      *(uint2*)(a.v_hot + hot_at(slot_new, g)) = nv;
     }
   }
   __syncthreads();   // every thread has read seq_lens[b] and cold_lens[b]
