@@ -102,7 +102,10 @@ def load(path: str = _LIB):
                                            P, i32, i32, P, P]
     lib.orc_decode_block_sparse.argtypes = [ctypes.POINTER(_Params), P, P, P, P, P, P, i32, i32, P, i32, P,
                                             i32, P, i32, i32, P, P]
-    for f in (lib.orc_decode_paged, lib.orc_decode_tiered_int8, lib.orc_decode_block_sparse):
+    lib.orc_decode_tiered_f16.argtypes = [ctypes.POINTER(_Params), P, P, P, i32, P, P, P, P, P, P, P, i32, i32,
+                                          P, P]
+    for f in (lib.orc_decode_paged, lib.orc_decode_tiered_int8, lib.orc_decode_tiered_f16,
+              lib.orc_decode_block_sparse):
         f.restype = ctypes.c_int
     lib.orc_f32_to_f16.argtypes = [ctypes.c_float]
     lib.orc_f32_to_f16.restype = ctypes.c_uint16
@@ -221,6 +224,30 @@ def decode_tiered_int8(p: Params, q, k_hot, v_hot, hot_window, k_cold, v_cold, k
     return out, lse
 
 
+def decode_tiered_f16(p: Params, q, k_hot, v_hot, hot_window, k_cold, v_cold, cold_block_table, seq_lens,
+                      cold_lens, q_pos=None, pairs=None, nthreads=0, lib=None):
+    """Hot ring [B, hot_window, Hkv, D] f16; cold pool [Nc, bs, Hkv, D] f16 read through cold_block_table."""
+    lib = _load(lib)
+    q = _arr(q, np.float32)
+    kh = _arr(k_hot, np.float16)
+    vh = _arr(v_hot, np.float16)
+    kc = _arr(k_cold, np.float16)
+    vc = _arr(v_cold, np.float16)
+    bt = _arr(cold_block_table, np.int32)
+    sl = _arr(seq_lens, np.int32)
+    cl = _arr(cold_lens, np.int32)
+    qp = _arr(q_pos, np.int32)
+    pa, n = _pairs(p, pairs)
+    out = np.zeros((n, p.head_dim), np.float64)
+    lse = np.zeros((n,), np.float64)
+    cp = p.c()
+    rc = lib.orc_decode_tiered_f16(ctypes.byref(cp), _ptr(q), _ptr(kh), _ptr(vh), int(hot_window), _ptr(kc),
+                                   _ptr(vc), _ptr(bt), _ptr(sl), _ptr(cl), _ptr(qp), _ptr(pa), n, nthreads,
+                                   _ptr(out), _ptr(lse))
+    _check(rc, "orc_decode_tiered_f16")
+    return out, lse
+
+
 def decode_block_sparse(p: Params, q, k_cache, v_cache, block_table, seq_lens, sparse_block, num_layouts,
                         row_ptr, col_idx, q_pos=None, pairs=None, nthreads=0, lib=None):
     """CSR row_ptr [NL, R+1], col_idx [NL, col_stride]; paged f16 cache."""
@@ -254,6 +281,10 @@ def run(case, pairs=None, nthreads=0, lib=None):
         return decode_tiered_int8(p, case.q, case.k_hot, case.v_hot, case.hot_window, case.k_cold, case.v_cold,
                                   case.k_scale, case.v_scale, case.cold_block_table, case.seq_lens, case.cold_lens,
                                   case.q_pos, pairs, nthreads, lib)
+    if case.kind == "tiered_f16":
+        return decode_tiered_f16(p, case.q, case.k_hot, case.v_hot, case.hot_window, case.k_cold, case.v_cold,
+                                 case.cold_block_table, case.seq_lens, case.cold_lens, case.q_pos, pairs, nthreads,
+                                 lib)
     if case.kind == "sparse":
         return decode_block_sparse(p, case.q, case.k_cache, case.v_cache, case.block_table, case.seq_lens,
                                    case.sparse_block, case.num_layouts, case.row_ptr, case.col_idx, case.q_pos,

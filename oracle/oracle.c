@@ -1,7 +1,8 @@
 /*
  * oracle.c -- plain, slow fp64 CPU oracle for single-query (decode) GQA
  * attention over a paged f16/f32 KV cache, a tiered int8-cold / f16-hot
- * cache, and a block-sparse (CSR) selection over the paged cache.
+ * cache, a tiered f16-cold / f16-hot cache, and a block-sparse (CSR)
+ * selection over the paged cache.
  *
  * TEST INFRASTRUCTURE ONLY.  Nothing in the product library calls, links or
  * includes this file; it exists so that the HIP path can be compared against
@@ -42,6 +43,10 @@
  *           t >= cold_len[b]: hot ring slot t mod hot_window of
  *           hot[b][slot][g][0..D) in f16 (get_hot_pos, with the hot tier's
  *           first absolute position equal to cold_len[b]).
+ *   tiered f16: as tiered, but the cold row is D f16 values, the paged
+ *           layout of the paged cache read through cold_block_table
+ *           (attention.js executeAttentionTiered: f16 hot and cold buffers,
+ *           the cold tier paged by default).
  *   sparse: the paged cache, and t is visible to head h only if its sparse
  *           block j = t / SB is a column of row r = q / SB of CSR layout
  *           (h mod NL) and j <= r; repeated columns count once
@@ -196,6 +201,24 @@ static void tiered_fetch(const void* vsrc, int32_t b, int32_t g, int64_t t, int3
     int64_t base = (((int64_t)b * s->hot_window + slot) * p->num_kv_heads + g) * D;
     for (int32_t d = 0; d < D; ++d) dst[d] = orc_f16_to_f64(hot[base + d]);
   }
+}
+
+/* Tiered f16: paged f16 cold rows through cold_block_table, then the ring. */
+static void tiered_f16_fetch(const void* vsrc, int32_t b, int32_t g, int64_t t, int32_t is_v, double* dst) {
+  const tiered_src* s = (const tiered_src*)vsrc;
+  const orc_params* p = s->p;
+  int32_t D = p->head_dim;
+  const uint16_t* rows;
+  int64_t base;
+  const int32_t in_cold = t < s->cold_lens[b];
+  if (in_cold) {
+    rows = (const uint16_t*)(is_v ? (const void*)s->v_cold : (const void*)s->k_cold);
+    base = (paged_row(p, s->cold_block_table, b, t) * p->num_kv_heads + g) * D;
+  } else {
+    rows = is_v ? s->v_hot : s->k_hot;
+    base = (((int64_t)b * s->hot_window + orc_ring_slot(t, s->hot_window)) * p->num_kv_heads + g) * D;
+  }
+  for (int32_t d = 0; d < D; ++d) dst[d] = orc_f16_to_f64(rows[base + d]);
 }
 
 /* -------------------------------------------------------------- attention */
@@ -375,6 +398,27 @@ int orc_decode_tiered_int8(const orc_params* p, const float* q, const uint16_t* 
   }
   tiered_src src = {p, k_hot, v_hot, hot_window, k_cold, v_cold, k_scale, v_scale, cold_block_table, cold_lens};
   return run_pairs(p, q, seq_lens, q_pos, NULL, tiered_fetch, &src, pairs, npairs, nthreads, out, lse);
+}
+
+/* Tiered cache with an f16 cold tier: paged f16 cold history + f16 hot ring.
+ * k_cold / v_cold are [num_blocks, block_size, Hkv, D] f16 bit patterns. */
+int orc_decode_tiered_f16(const orc_params* p, const float* q, const uint16_t* k_hot, const uint16_t* v_hot,
+                          int32_t hot_window, const uint16_t* k_cold, const uint16_t* v_cold,
+                          const int32_t* cold_block_table, const int32_t* seq_lens, const int32_t* cold_lens,
+                          const int32_t* q_pos, const int32_t* pairs, int32_t npairs, int32_t nthreads, double* out,
+                          double* lse) {
+  int rc = check_common(p);
+  if (rc) return rc;
+  if (hot_window <= 0) return ORC_EINVAL;
+  for (int32_t b = 0; b < p->num_seqs; ++b) {
+    if (seq_lens[b] < 0 || cold_lens[b] < 0 || cold_lens[b] > seq_lens[b]) return ORC_EINVAL;
+    if (seq_lens[b] - cold_lens[b] > hot_window) return ORC_EINVAL;
+    if ((rc = check_table(p, cold_block_table, b, cold_lens[b]))) return rc;
+  }
+  /* the cold words/scales fields carry the f16 rows; the scales are unused */
+  tiered_src src = {p, k_hot, v_hot, hot_window, (const uint32_t*)(const void*)k_cold,
+                    (const uint32_t*)(const void*)v_cold, NULL, NULL, cold_block_table, cold_lens};
+  return run_pairs(p, q, seq_lens, q_pos, NULL, tiered_f16_fetch, &src, pairs, npairs, nthreads, out, lse);
 }
 
 /* Block-sparse CSR selection over the paged f16 cache. */

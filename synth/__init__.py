@@ -16,6 +16,7 @@ Cache layouts (all C-contiguous numpy arrays):
   hot ring        k_hot, v_hot      [B, hot_window, Hkv, D]          f16
   cold pool       k_cold, v_cold    [num_cold_blocks, bs, Hkv, D/4]  u32, 4 x int8 LSB-first
   cold scales     k_scale, v_scale  [num_cold_blocks, bs, Hkv]       f16
+  f16 cold pool   k_cold, v_cold    [num_cold_blocks, bs, Hkv, D]    f16 (the tiered f16 kind)
   CSR             row_ptr [NL, R+1], col_idx [NL, col_stride]        i32
 """
 from __future__ import annotations
@@ -38,7 +39,7 @@ def _params(B, H, Hkv, D, bs, max_blocks, num_blocks, scale=0.0, causal=1, windo
 @dataclass
 class Case:
     """Every array a decode call needs, plus the scalar parameters."""
-    kind: str                      # "paged", "tiered" or "sparse"
+    kind: str                      # "paged", "tiered", "tiered_f16" or "sparse"
     params: dict
     q: np.ndarray
     seq_lens: np.ndarray
@@ -224,6 +225,43 @@ def tiered_case(seed, B, H, Hkv, D, bs, lens, cold_lens, hot_window, permute=Tru
                 extra=dict(k_codes=kc, v_codes=vc))
 
 
+def tiered_f16_case(seed, B, H, Hkv, D, bs, lens, cold_lens, hot_window, permute=True, q_pos=None, causal=1,
+                    window=0, softcap=0.0, scale=0.0, extra_blocks=0, name="") -> Case:
+    """As ``tiered_case`` with an f16 cold tier: token t < cold_lens[b] is stored as f16 in the
+    paged cold pool [pool, bs, Hkv, D], token t >= cold_lens[b] as f16 in the ring at slot
+    t mod hot_window.  Pool rows and ring slots that hold no live token carry +-300."""
+    rng = np.random.default_rng(seed)
+    lens = np.asarray(lens, np.int32)
+    cold_lens = np.asarray(cold_lens, np.int32)
+    assert np.all(cold_lens <= lens) and np.all(lens - cold_lens <= hot_window)
+    q = rng.standard_normal((B, H, D), dtype=np.float32)
+    Lmax = max(1, int(lens.max()))
+    k_log = _normal(rng, (B, Lmax, Hkv, D), F16)
+    v_log = _normal(rng, (B, Lmax, Hkv, D), F16)
+    table, pool = pool_table(rng, cold_lens, bs, permute, extra_blocks)
+    kc = np.full((pool, bs, Hkv, D), 300.0, np.float16)
+    vc = np.full((pool, bs, Hkv, D), -300.0, np.float16)
+    bb = np.concatenate([np.full(int(c), b) for b, c in enumerate(cold_lens)] + [np.zeros(0, int)]).astype(np.int64)
+    tt = np.concatenate([np.arange(int(c)) for c in cold_lens] + [np.zeros(0, int)]).astype(np.int64)
+    if bb.size:
+        blk, off = table[bb, tt // bs], tt % bs
+        kc[blk, off] = k_log[bb, tt]
+        vc[blk, off] = v_log[bb, tt]
+    hk = np.full((B, hot_window, Hkv, D), 300.0, np.float16)
+    hv = np.full((B, hot_window, Hkv, D), -300.0, np.float16)
+    hb = np.concatenate([np.full(int(L) - int(c), b) for b, (L, c) in enumerate(zip(lens, cold_lens))]
+                        + [np.zeros(0, int)]).astype(np.int64)
+    ht = np.concatenate([np.arange(int(c), int(L)) for L, c in zip(lens, cold_lens)] + [np.zeros(0, int)]).astype(np.int64)
+    if hb.size:
+        hk[hb, ht % hot_window] = k_log[hb, ht]
+        hv[hb, ht % hot_window] = v_log[hb, ht]
+    del k_log, v_log
+    qp = None if q_pos is None else np.asarray(q_pos, np.int32)
+    return Case("tiered_f16", _params(B, H, Hkv, D, bs, table.shape[1], pool, scale, causal, window, softcap), q,
+                lens, qp, k_hot=hk, v_hot=hv, hot_window=int(hot_window), k_cold=kc, v_cold=vc,
+                cold_block_table=table, cold_lens=cold_lens, name=name)
+
+
 # ------------------------------------------------------------------- sparse
 
 def csr_from_rows(rows_per_layout):
@@ -333,3 +371,12 @@ def config(i: int, window: int = 0) -> Case:
         return sparse_case(5, 8, 32, 8, 128, 64, 64, 4, lens=[16384] * 8,
                            scale=float(np.float32(1.0 / math.sqrt(128))), name="sparse_f16_B8_H32x8_D128_L16384")
     raise ValueError(i)
+
+
+def tiered_f16_workload(window: int = 0) -> Case:
+    """The tiered workload's shape with an f16 cold tier: B=16, 32/8 heads, D=128,
+    L=8192 = 7680 f16 cold (bs=16, permuted pool) + 512 f16 hot (ring of 512), softcap 50."""
+    B = 16
+    return tiered_f16_case(6, B, 32, 8, 128, 16, lens=[8192] * B, cold_lens=[7680] * B, hot_window=512,
+                           softcap=50.0, window=window, scale=float(np.float32(1.0 / math.sqrt(128))),
+                           name=f"tiered_f16_B16_H32x8_D128_L8192_W{window}_cap50")

@@ -27,9 +27,15 @@ def logical_rows(case, b):
         K = case.k_cache[blk, t % bs].astype(np.float64)
         V = case.v_cache[blk, t % bs].astype(np.float64)
         return K, V
-    # tiered
     Hkv, D = p["num_kv_heads"], p["head_dim"]
     c = int(case.cold_lens[b])
+    if case.kind == "tiered_f16":
+        tc, th = t[:c], t[c:]
+        blk = case.cold_block_table[b, tc // bs]
+        K = np.concatenate([case.k_cold[blk, tc % bs], case.k_hot[b, th % case.hot_window]]).astype(np.float64)
+        V = np.concatenate([case.v_cold[blk, tc % bs], case.v_hot[b, th % case.hot_window]]).astype(np.float64)
+        return K.reshape(L, Hkv, D), V.reshape(L, Hkv, D)
+    # tiered int8
     K = np.empty((L, Hkv, D))
     V = np.empty((L, Hkv, D))
     tc = t[:c]

@@ -43,8 +43,14 @@ MUTANTS = {
     "codes_round_half_away": ("const float r = rintf(", "const float r = roundf("),
     "f16_ties_round_up": ("double r = rint(ldexp(v, 10 - e));", "double r = floor(ldexp(v, 10 - e) + 0.5);"),
     "cold_len_not_advanced": ("      C += 1;\n", "      C += 0;\n"),
+    "f16_cold_boundary": ("const int32_t in_cold = t < s->cold_lens[b];", "const int32_t in_cold = t <= s->cold_lens[b];"),
+    "f16_cold_drops_kv_head": ("base = (paged_row(p, s->cold_block_table, b, t) * p->num_kv_heads + g) * D;",
+                               "base = (paged_row(p, s->cold_block_table, b, t) * p->num_kv_heads) * D;"),
+    "f16_hot_slot_from_hot_start": (
+        "base = (((int64_t)b * s->hot_window + orc_ring_slot(t, s->hot_window)) * p->num_kv_heads + g) * D;",
+        "base = (((int64_t)b * s->hot_window + (t - s->cold_lens[b])) * p->num_kv_heads + g) * D;"),
 }
-PIN_FILES = ["test_oracle_pins.py", "test_oracle_append_pins.py"]
+PIN_FILES = ["test_oracle_pins.py", "test_oracle_append_pins.py", "test_oracle_tiered_f16_pins.py"]
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
