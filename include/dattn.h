@@ -54,7 +54,7 @@ extern "C" {
 #define DATTN_ERR_WORKSPACE (-3)   /* workspace NULL, misaligned or too small */
 #define DATTN_ERR_LAUNCH (-4)      /* a HIP call failed; see dattn_last_error() */
 
-/* storage type of the paged K/V pool */
+/* storage type of the paged K/V pool and of out */
 #define DATTN_F32 0
 #define DATTN_F16 1
 
@@ -62,6 +62,7 @@ extern "C" {
 #define DATTN_KIND_PAGED 0
 #define DATTN_KIND_TIERED_INT8 1
 #define DATTN_KIND_BLOCK_SPARSE 2
+#define DATTN_KIND_TIERED_F16 3
 
 /*
  * Scalar parameters (doppler attention_f16kv.wgsl Uniforms and boostr
@@ -83,6 +84,9 @@ typedef struct dattn_params {
   int32_t split_tokens;       /* keys per KV split (block-sparse: at most split_tokens / sparse_block
                                  union blocks per split); 0 => library choice, else a multiple of 16 */
   int32_t phases;             /* 0 (or DATTN_PHASE_ALL) => both phases; see below */
+  int32_t out_dtype;          /* storage type of out: DATTN_F32 (0) or DATTN_F16, the f32
+                                 result rounded to nearest even (attention.js sizes its output
+                                 by the kernel variant's outputDtype, f16 or f32) */
 } dattn_params;
 
 /*
@@ -123,12 +127,13 @@ int dattn_workspace_size(const dattn_params* p, int32_t kind, int32_t sparse_blo
  *   block_table  [B, max_blocks_per_seq] i32
  *   seq_lens     [B] i32
  *   q_pos        [B] i32, or NULL for seq_lens[b]-1
- *   out          [B, H, D] f32 (written)
- *   lse          [B, H] f32 (written), or NULL
+ *   out          [B, H, D] f32 or f16 per p->out_dtype (written), or NULL to
+ *                write lse only (the split kernel still reads K and V)
+ *   lse          [B, H] f32 (written), or NULL; out and lse are not both NULL
  */
 int dattn_decode_paged(const dattn_params* p, const float* q, const void* k_cache, const void* v_cache,
                        int32_t kv_dtype, const int32_t* block_table, const int32_t* seq_lens,
-                       const int32_t* q_pos, float* out, float* lse, void* workspace, size_t workspace_bytes,
+                       const int32_t* q_pos, void* out, float* lse, void* workspace, size_t workspace_bytes,
                        void* stream);
 
 /*
@@ -152,8 +157,29 @@ int dattn_decode_tiered_int8(const dattn_params* p, const float* q, const uint16
                              const uint16_t* v_hot, int32_t hot_window, const uint32_t* k_cold,
                              const uint32_t* v_cold, const uint16_t* k_scale, const uint16_t* v_scale,
                              const int32_t* cold_block_table, const int32_t* seq_lens, const int32_t* cold_lens,
-                             const int32_t* q_pos, float* out, float* lse, void* workspace,
+                             const int32_t* q_pos, void* out, float* lse, void* workspace,
                              size_t workspace_bytes, void* stream);
+
+/*
+ * Tiered cache with an f16 cold tier (attention.js executeAttentionTiered:
+ * f16 hot and cold buffers, the cold tier paged through a page table by
+ * default, the hot tier a ring): tokens t < cold_lens[b] are f16 rows of a
+ * paged cold pool, tokens t >= cold_lens[b] f16 rows of the ring at slot
+ * t % hot_window, exactly as for dattn_decode_tiered_int8.
+ *   k_hot, v_hot          [B, hot_window, Hkv, D] f16 (bit patterns)
+ *   hot_window            ring slots, >= 1
+ *   k_cold, v_cold        [num_blocks, block_size, Hkv, D] f16 (bit patterns)
+ *   cold_block_table      [B, max_blocks_per_seq] i32 (block_size, num_blocks and
+ *                         max_blocks_per_seq in p describe the cold pool)
+ *   seq_lens, cold_lens   [B] i32
+ *   q_pos, out, lse       as for dattn_decode_paged
+ * Workspace size: kind DATTN_KIND_TIERED_F16.
+ */
+int dattn_decode_tiered_f16(const dattn_params* p, const float* q, const uint16_t* k_hot, const uint16_t* v_hot,
+                            int32_t hot_window, const uint16_t* k_cold, const uint16_t* v_cold,
+                            const int32_t* cold_block_table, const int32_t* seq_lens, const int32_t* cold_lens,
+                            const int32_t* q_pos, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                            void* stream);
 
 /*
  * Block-sparse selection over the paged f16 cache (com.microsoft.SparseAttention
@@ -172,7 +198,7 @@ int dattn_decode_block_sparse(const dattn_params* p, const float* q, const uint1
                               const uint16_t* v_cache, const int32_t* block_table, const int32_t* seq_lens,
                               const int32_t* q_pos, int32_t sparse_block, int32_t num_layouts,
                               const int32_t* row_ptr, int32_t row_stride, const int32_t* col_idx,
-                              int32_t col_stride, float* out, float* lse, void* workspace, size_t workspace_bytes,
+                              int32_t col_stride, void* out, float* lse, void* workspace, size_t workspace_bytes,
                               void* stream);
 
 /*

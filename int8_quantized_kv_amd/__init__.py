@@ -15,9 +15,11 @@ Cache layouts (C-contiguous):
   k_hot, v_hot      [B, hot_window, Hkv, D]    float16
   k_cold, v_cold    [num_blocks, bs, Hkv, D/4] int32/uint32 words of 4 int8, LSB first
   k_scale, v_scale  [num_blocks, bs, Hkv]      float16
+  k_cold, v_cold    [num_blocks, bs, Hkv, D]   float16 (the tiered f16 cache)
   row_ptr           [num_layouts, rows + 1]    int32
   col_idx           [num_layouts, col_stride]  int32
-Outputs: out [B, H, D] float32, lse [B, H] float32.
+Outputs: out [B, H, D] float32 or float16 (out_dtype), lse [B, H] float32;
+want_out=False writes lse only.
 """
 from __future__ import annotations
 
@@ -28,9 +30,9 @@ from typing import Optional
 
 __all__ = [
     "DattnError", "DattnParams", "lib", "library_path", "dattn_workspace_size", "dattn_decode_paged",
-    "dattn_decode_tiered_int8", "dattn_decode_block_sparse", "dattn_append_tiered_int8", "dattn_last_error",
+    "dattn_decode_tiered_int8", "dattn_decode_tiered_f16", "dattn_decode_block_sparse", "dattn_append_tiered_int8", "dattn_last_error",
     "dattn_version",
-    "KIND_PAGED", "KIND_TIERED_INT8", "KIND_BLOCK_SPARSE", "F32", "F16", "PHASE_ALL", "PHASE_SPLIT",
+    "KIND_PAGED", "KIND_TIERED_INT8", "KIND_BLOCK_SPARSE", "KIND_TIERED_F16", "F32", "F16", "PHASE_ALL", "PHASE_SPLIT",
     "PHASE_COMBINE",
 ]
 
@@ -40,7 +42,7 @@ library_path = os.path.join(_HERE, "libdattn.so")
 OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_LAUNCH = 0, -1, -2, -3, -4
 F32, F16 = 0, 1
 PHASE_ALL, PHASE_SPLIT, PHASE_COMBINE = 0, 1, 2
-KIND_PAGED, KIND_TIERED_INT8, KIND_BLOCK_SPARSE = 0, 1, 2
+KIND_PAGED, KIND_TIERED_INT8, KIND_BLOCK_SPARSE, KIND_TIERED_F16 = 0, 1, 2, 3
 
 
 class DattnParams(ctypes.Structure):
@@ -60,6 +62,7 @@ class DattnParams(ctypes.Structure):
         ("max_seq_len", ctypes.c_int32),
         ("split_tokens", ctypes.c_int32),
         ("phases", ctypes.c_int32),
+        ("out_dtype", ctypes.c_int32),
     ]
 
 
@@ -86,10 +89,11 @@ def lib():
         L.dattn_workspace_size.argtypes = [PP, i32, i32, ctypes.POINTER(sz)]
         L.dattn_decode_paged.argtypes = [PP, P, P, P, i32, P, P, P, P, P, P, sz, P]
         L.dattn_decode_tiered_int8.argtypes = [PP, P, P, P, i32, P, P, P, P, P, P, P, P, P, P, P, sz, P]
+        L.dattn_decode_tiered_f16.argtypes = [PP, P, P, P, i32, P, P, P, P, P, P, P, P, P, sz, P]
         L.dattn_decode_block_sparse.argtypes = [PP, P, P, P, P, P, P, i32, i32, P, i32, P, i32, P, P, P, sz, P]
         L.dattn_append_tiered_int8.argtypes = [PP, P, P, P, P, i32, P, P, P, P, P, P, P, P]
         for f in (L.dattn_workspace_size, L.dattn_decode_paged, L.dattn_decode_tiered_int8,
-                  L.dattn_decode_block_sparse, L.dattn_append_tiered_int8):
+                  L.dattn_decode_tiered_f16, L.dattn_decode_block_sparse, L.dattn_append_tiered_int8):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -142,20 +146,34 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _out_code(out_dtype):
+    torch = _torch()
+    if out_dtype not in (torch.float32, torch.float16):
+        raise TypeError(f"out_dtype must be torch.float32 or torch.float16, got {out_dtype}")
+    return F16 if out_dtype == torch.float16 else F32
+
+
 def _params(q, Hkv, D, bs, max_blocks, num_blocks, max_seq_len, scale, causal, sliding_window, softcap,
-            split_tokens, phases=PHASE_ALL):
+            split_tokens, phases=PHASE_ALL, out_dtype=None):
     B, H, _ = q.shape
+    code = F32 if out_dtype is None else _out_code(out_dtype)
     return DattnParams(B, H, Hkv, D, float(scale), int(causal), int(sliding_window), float(softcap), bs, max_blocks,
-                       num_blocks, int(max_seq_len), int(split_tokens), int(phases))
+                       num_blocks, int(max_seq_len), int(split_tokens), int(phases), code)
 
 
-def _outputs(q, out, lse, want_lse, workspace, ws_bytes):
+def _outputs(q, out, lse, want_lse, workspace, ws_bytes, out_dtype=None, want_out=True):
     torch = _torch()
     B, H, D = q.shape
-    if out is None:
-        out = torch.empty((B, H, D), dtype=torch.float32, device=q.device)
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    if not want_out:
+        if out is not None:
+            raise ValueError("out given with want_out=False")
+        if lse is None and not want_lse:
+            raise ValueError("want_out=False needs lse")
+    elif out is None:
+        out = torch.empty((B, H, D), dtype=out_dtype, device=q.device)
     else:
-        _need(out, "out", (torch.float32,), 3, q.device)
+        _need(out, "out", (out_dtype,), 3, q.device)
     if lse is None and want_lse:
         lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
     elif lse is not None:
@@ -181,7 +199,8 @@ def _max_len(seq_lens, max_seq_len):
 def dattn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, *, q_pos=None, scale: float = 0.0,
                        causal: bool = True, sliding_window: int = 0, softcap: float = 0.0,
                        max_seq_len: Optional[int] = None, split_tokens: int = 0, out=None, lse=None,
-                       want_lse: bool = True, workspace=None, stream=None, phases: int = PHASE_ALL):
+                       want_lse: bool = True, workspace=None, stream=None, phases: int = PHASE_ALL,
+                       out_dtype=None, want_out: bool = True):
     """Decode attention over a paged f16/f32 cache; returns (out, lse)."""
     torch = _torch()
     dev = q.device
@@ -198,9 +217,9 @@ def dattn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, *, q_pos=None
     if block_table.shape[0] != q.shape[0] or seq_lens.shape[0] != q.shape[0]:
         raise ValueError("block_table / seq_lens must have one row per sequence")
     p = _params(q, Hkv, D, bs, block_table.shape[1], NB, _max_len(seq_lens, max_seq_len), scale, causal,
-                sliding_window, softcap, split_tokens, phases)
+                sliding_window, softcap, split_tokens, phases, out_dtype)
     ws = dattn_workspace_size(p, KIND_PAGED)
-    out, lse, workspace = _outputs(q, out, lse, want_lse, workspace, ws)
+    out, lse, workspace = _outputs(q, out, lse, want_lse, workspace, ws, out_dtype, want_out)
     kv_dtype = F16 if k_cache.dtype == torch.float16 else F32
     _check(lib().dattn_decode_paged(ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(v_cache), kv_dtype,
                                     _ptr(block_table), _ptr(seq_lens), _ptr(q_pos), _ptr(out), _ptr(lse),
@@ -212,7 +231,7 @@ def dattn_decode_tiered_int8(q, k_hot, v_hot, k_cold, v_cold, k_scale, v_scale, 
                              cold_lens, *, q_pos=None, scale: float = 0.0, causal: bool = True,
                              sliding_window: int = 0, softcap: float = 0.0, max_seq_len: Optional[int] = None,
                              split_tokens: int = 0, out=None, lse=None, want_lse: bool = True, workspace=None,
-                             stream=None, phases: int = PHASE_ALL):
+                             stream=None, phases: int = PHASE_ALL, out_dtype=None, want_out: bool = True):
     """Decode attention over an int8 cold pool + f16 hot ring; returns (out, lse)."""
     torch = _torch()
     dev = q.device
@@ -236,14 +255,49 @@ def dattn_decode_tiered_int8(q, k_hot, v_hot, k_cold, v_cold, k_scale, v_scale, 
             or tuple(v_scale.shape) != (NB, bs, Hkv) or k_hot.shape[0] != B:
         raise ValueError("tiered cache tensors disagree on shape")
     p = _params(q, Hkv, D, bs, cold_block_table.shape[1], NB, _max_len(seq_lens, max_seq_len), scale, causal,
-                sliding_window, softcap, split_tokens, phases)
+                sliding_window, softcap, split_tokens, phases, out_dtype)
     ws = dattn_workspace_size(p, KIND_TIERED_INT8)
-    out, lse, workspace = _outputs(q, out, lse, want_lse, workspace, ws)
+    out, lse, workspace = _outputs(q, out, lse, want_lse, workspace, ws, out_dtype, want_out)
     _check(lib().dattn_decode_tiered_int8(ctypes.byref(p), _ptr(q), _ptr(k_hot), _ptr(v_hot), hot_window,
                                           _ptr(k_cold), _ptr(v_cold), _ptr(k_scale), _ptr(v_scale),
                                           _ptr(cold_block_table), _ptr(seq_lens), _ptr(cold_lens), _ptr(q_pos),
                                           _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
                                           _stream(stream)))
+    return out, lse
+
+
+def dattn_decode_tiered_f16(q, k_hot, v_hot, k_cold, v_cold, cold_block_table, seq_lens, cold_lens, *, q_pos=None,
+                            scale: float = 0.0, causal: bool = True, sliding_window: int = 0, softcap: float = 0.0,
+                            max_seq_len: Optional[int] = None, split_tokens: int = 0, out=None, lse=None,
+                            want_lse: bool = True, workspace=None, stream=None, phases: int = PHASE_ALL,
+                            out_dtype=None, want_out: bool = True):
+    """Decode attention over an f16 paged cold pool + f16 hot ring; returns (out, lse)."""
+    torch = _torch()
+    dev = q.device
+    _need(q, "q", (torch.float32,), 3, dev)
+    _need(k_hot, "k_hot", (torch.float16,), 4, dev)
+    _need(v_hot, "v_hot", (torch.float16,), 4, dev)
+    _need(k_cold, "k_cold", (torch.float16,), 4, dev)
+    _need(v_cold, "v_cold", (torch.float16,), 4, dev)
+    _need(cold_block_table, "cold_block_table", (torch.int32,), 2, dev)
+    _need(seq_lens, "seq_lens", (torch.int32,), 1, dev)
+    _need(cold_lens, "cold_lens", (torch.int32,), 1, dev)
+    if q_pos is not None:
+        _need(q_pos, "q_pos", (torch.int32,), 1, dev)
+    B, H, D = q.shape
+    _, hot_window, Hkv, Dh = k_hot.shape
+    NB, bs, Hkv2, Dc = k_cold.shape
+    if Dh != D or Dc != D or Hkv2 != Hkv or tuple(v_hot.shape) != tuple(k_hot.shape) \
+            or tuple(v_cold.shape) != tuple(k_cold.shape) or k_hot.shape[0] != B:
+        raise ValueError("tiered cache tensors disagree on shape")
+    p = _params(q, Hkv, D, bs, cold_block_table.shape[1], NB, _max_len(seq_lens, max_seq_len), scale, causal,
+                sliding_window, softcap, split_tokens, phases, out_dtype)
+    ws = dattn_workspace_size(p, KIND_TIERED_F16)
+    out, lse, workspace = _outputs(q, out, lse, want_lse, workspace, ws, out_dtype, want_out)
+    _check(lib().dattn_decode_tiered_f16(ctypes.byref(p), _ptr(q), _ptr(k_hot), _ptr(v_hot), hot_window,
+                                         _ptr(k_cold), _ptr(v_cold), _ptr(cold_block_table), _ptr(seq_lens),
+                                         _ptr(cold_lens), _ptr(q_pos), _ptr(out), _ptr(lse), _ptr(workspace),
+                                         workspace.numel(), _stream(stream)))
     return out, lse
 
 
@@ -284,7 +338,7 @@ def dattn_decode_block_sparse(q, k_cache, v_cache, block_table, seq_lens, sparse
                               q_pos=None, scale: float = 0.0, causal: bool = True, sliding_window: int = 0,
                               softcap: float = 0.0, max_seq_len: Optional[int] = None, split_tokens: int = 0,
                               out=None, lse=None, want_lse: bool = True, workspace=None, stream=None,
-                              phases: int = PHASE_ALL):
+                              phases: int = PHASE_ALL, out_dtype=None, want_out: bool = True):
     """Decode attention over the paged f16 cache restricted by per-head CSR block masks."""
     torch = _torch()
     dev = q.device
@@ -301,9 +355,9 @@ def dattn_decode_block_sparse(q, k_cache, v_cache, block_table, seq_lens, sparse
     if row_ptr.shape[0] != col_idx.shape[0]:
         raise ValueError("row_ptr and col_idx must have one row per layout")
     p = _params(q, Hkv, D, bs, block_table.shape[1], NB, _max_len(seq_lens, max_seq_len), scale, causal,
-                sliding_window, softcap, split_tokens, phases)
+                sliding_window, softcap, split_tokens, phases, out_dtype)
     ws = dattn_workspace_size(p, KIND_BLOCK_SPARSE, sparse_block)
-    out, lse, workspace = _outputs(q, out, lse, want_lse, workspace, ws)
+    out, lse, workspace = _outputs(q, out, lse, want_lse, workspace, ws, out_dtype, want_out)
     _check(lib().dattn_decode_block_sparse(ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(v_cache),
                                            _ptr(block_table), _ptr(seq_lens), _ptr(q_pos), int(sparse_block),
                                            row_ptr.shape[0], _ptr(row_ptr), row_ptr.shape[1], _ptr(col_idx),

@@ -80,6 +80,8 @@ int device_cus() {
   return it->second;
 }
 
+bool is_tiered(int kind) { return kind == DATTN_KIND_TIERED_INT8 || kind == DATTN_KIND_TIERED_F16; }
+
 int check_params(const dattn_params* p, int kind) {
   if (!p) return fail(DATTN_ERR_INVALID, "params is NULL");
   if (p->num_seqs < 0) return fail(DATTN_ERR_INVALID, "num_seqs must be >= 0 (got %d)", p->num_seqs);
@@ -107,12 +109,14 @@ int check_params(const dattn_params* p, int kind) {
     return fail(DATTN_ERR_UNSUPPORTED, "num_blocks * block_size must fit in int32");
   if (p->max_seq_len < 0) return fail(DATTN_ERR_INVALID, "max_seq_len must be >= 0 (got %d)", p->max_seq_len);
   // the tiered table maps only the cold prefix, which can be shorter than max_seq_len
-  if (kind != DATTN_KIND_TIERED_INT8 && (int64_t)p->max_seq_len > (int64_t)p->max_blocks_per_seq * p->block_size)
+  if (!is_tiered(kind) && (int64_t)p->max_seq_len > (int64_t)p->max_blocks_per_seq * p->block_size)
     return fail(DATTN_ERR_INVALID, "max_seq_len %d exceeds max_blocks_per_seq * block_size (%lld)", p->max_seq_len,
                 (long long)p->max_blocks_per_seq * p->block_size);
   if (p->max_seq_len > (1 << 30)) return fail(DATTN_ERR_UNSUPPORTED, "max_seq_len above 2^30 is not supported");
   if (p->phases < 0 || p->phases > 3)
     return fail(DATTN_ERR_INVALID, "phases must be 0..3 (got %d)", p->phases);
+  if (p->out_dtype != DATTN_F32 && p->out_dtype != DATTN_F16)
+    return fail(DATTN_ERR_INVALID, "out_dtype must be DATTN_F32 or DATTN_F16 (got %d)", p->out_dtype);
   if (p->split_tokens < 0 || p->split_tokens % 16)
     return fail(DATTN_ERR_INVALID, "split_tokens must be 0 or a positive multiple of 16 (got %d)", p->split_tokens);
   return DATTN_OK;
@@ -145,7 +149,7 @@ int make_plan(const dattn_params* p, int kind, int32_t sparse_block, Plan& pl) {
   pl.G = p->num_heads / p->num_kv_heads;
   pl.waves = waves_per_group(p->num_kv_heads);
   const int64_t L = p->max_seq_len;
-  if (kind == DATTN_KIND_PAGED || kind == DATTN_KIND_TIERED_INT8) {
+  if (kind == DATTN_KIND_PAGED || is_tiered(kind)) {
     pl.split_tokens = choose_split(p, L);
     pl.num_splits = (int)((L + pl.split_tokens - 1) / pl.split_tokens);
     if (pl.num_splits < 1) pl.num_splits = 1;
@@ -295,13 +299,13 @@ bool run_split(const dattn_params* p) { return p->phases == 0 || (p->phases & DA
 bool run_combine(const dattn_params* p) { return p->phases == 0 || (p->phases & DATTN_PHASE_COMBINE); }
 
 // Pointer checks for the arrays the requested phases read or write.
-int check_io(const dattn_params* p, bool split_inputs_ok, float* out) {
+int check_io(const dattn_params* p, bool split_inputs_ok, void* out, float* lse) {
   if (run_split(p) && !split_inputs_ok) return fail(DATTN_ERR_INVALID, "an input array of the split phase is NULL");
-  if (run_combine(p) && !out) return fail(DATTN_ERR_INVALID, "out must be non-NULL");
+  if (run_combine(p) && !out && !lse) return fail(DATTN_ERR_INVALID, "out and lse are both NULL");
   return DATTN_OK;
 }
 
-int launch(void* split_fn, void* bal_fn, const dattn_params* p, const Plan& pl, dattn::DecodeArgs& a, float* out,
+int launch(void* split_fn, void* bal_fn, const dattn_params* p, const Plan& pl, dattn::DecodeArgs& a, void* out,
            float* lse, hipStream_t st) {
   const Balanced bl = bal_fn ? plan_balanced(p, pl, bal_fn) : Balanced{};
   if (bl.on) {
@@ -321,20 +325,21 @@ int launch(void* split_fn, void* bal_fn, const dattn_params* p, const Plan& pl, 
   if (!run_combine(p)) return DATTN_OK;
   const int nbh = p->num_seqs * p->num_heads;
   const dim3 cgrid(nbh);   // one workgroup per (sequence, head)
+  const int f16 = p->out_dtype == DATTN_F16;
   if (bl.on) {
     if (p->head_dim == 64)
       hipLaunchKernelGGL(dattn::combine_balanced_kernel<64>, cgrid, dim3(256), 0, st, a.part_acc, a.part_ml,
-                         a.sched, out, lse, p->num_heads, nbh);
+                         a.sched, out, f16, lse, p->num_heads, nbh);
     else
       hipLaunchKernelGGL(dattn::combine_balanced_kernel<128>, cgrid, dim3(256), 0, st, a.part_acc, a.part_ml,
-                         a.sched, out, lse, p->num_heads, nbh);
+                         a.sched, out, f16, lse, p->num_heads, nbh);
   } else {
     if (p->head_dim == 64)
-      hipLaunchKernelGGL(dattn::combine_kernel<64>, cgrid, dim3(256), 0, st, a.part_acc, a.part_ml, out, lse,
+      hipLaunchKernelGGL(dattn::combine_kernel<64>, cgrid, dim3(256), 0, st, a.part_acc, a.part_ml, out, f16, lse,
                          pl.num_splits, nbh);
     else
-      hipLaunchKernelGGL(dattn::combine_kernel<128>, cgrid, dim3(256), 0, st, a.part_acc, a.part_ml, out, lse,
-                         pl.num_splits, nbh);
+      hipLaunchKernelGGL(dattn::combine_kernel<128>, cgrid, dim3(256), 0, st, a.part_acc, a.part_ml, out, f16,
+                         lse, pl.num_splits, nbh);
   }
   return check_launch("combine kernel");
 }
@@ -359,7 +364,7 @@ int dattn_workspace_size(const dattn_params* p, int32_t kind, int32_t sparse_blo
 
 int dattn_decode_paged(const dattn_params* p, const float* q, const void* k_cache, const void* v_cache,
                        int32_t kv_dtype, const int32_t* block_table, const int32_t* seq_lens, const int32_t* q_pos,
-                       float* out, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+                       void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
   g_err.clear();
   Plan pl;
   int rc = make_plan(p, DATTN_KIND_PAGED, 0, pl);
@@ -367,7 +372,7 @@ int dattn_decode_paged(const dattn_params* p, const float* q, const void* k_cach
   if (kv_dtype != DATTN_F32 && kv_dtype != DATTN_F16)
     return fail(DATTN_ERR_INVALID, "kv_dtype must be DATTN_F32 or DATTN_F16 (got %d)", kv_dtype);
   if (p->num_seqs == 0) return DATTN_OK;
-  if ((rc = check_io(p, q && k_cache && v_cache && block_table && seq_lens, out))) return rc;
+  if ((rc = check_io(p, q && k_cache && v_cache && block_table && seq_lens, out, lse))) return rc;
   if ((rc = check_workspace(pl, workspace, workspace_bytes))) return rc;
   dattn::DecodeArgs a = base_args(p, pl, q, workspace);
   a.k = k_cache;
@@ -386,7 +391,7 @@ int dattn_decode_paged(const dattn_params* p, const float* q, const void* k_cach
 int dattn_decode_tiered_int8(const dattn_params* p, const float* q, const uint16_t* k_hot, const uint16_t* v_hot,
                              int32_t hot_window, const uint32_t* k_cold, const uint32_t* v_cold,
                              const uint16_t* k_scale, const uint16_t* v_scale, const int32_t* cold_block_table,
-                             const int32_t* seq_lens, const int32_t* cold_lens, const int32_t* q_pos, float* out,
+                             const int32_t* seq_lens, const int32_t* cold_lens, const int32_t* q_pos, void* out,
                              float* lse, void* workspace, size_t workspace_bytes, void* stream) {
   g_err.clear();
   Plan pl;
@@ -397,7 +402,7 @@ int dattn_decode_tiered_int8(const dattn_params* p, const float* q, const uint16
     return fail(DATTN_ERR_UNSUPPORTED, "num_seqs * hot_window must fit in int32");
   if (p->num_seqs == 0) return DATTN_OK;
   if ((rc = check_io(p, q && k_hot && v_hot && k_cold && v_cold && k_scale && v_scale && cold_block_table &&
-                            seq_lens && cold_lens, out)))
+                            seq_lens && cold_lens, out, lse)))
     return rc;
   if ((rc = check_workspace(pl, workspace, workspace_bytes))) return rc;
   dattn::DecodeArgs a = base_args(p, pl, q, workspace);
@@ -420,11 +425,46 @@ int dattn_decode_tiered_int8(const dattn_params* p, const float* q, const uint16
                 (hipStream_t)stream);
 }
 
+int dattn_decode_tiered_f16(const dattn_params* p, const float* q, const uint16_t* k_hot, const uint16_t* v_hot,
+                            int32_t hot_window, const uint16_t* k_cold, const uint16_t* v_cold,
+                            const int32_t* cold_block_table, const int32_t* seq_lens, const int32_t* cold_lens,
+                            const int32_t* q_pos, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  g_err.clear();
+  Plan pl;
+  int rc = make_plan(p, DATTN_KIND_TIERED_F16, 0, pl);
+  if (rc) return rc;
+  if (hot_window < 1) return fail(DATTN_ERR_INVALID, "hot_window must be >= 1 (got %d)", hot_window);
+  if ((int64_t)p->num_seqs * hot_window > INT32_MAX)
+    return fail(DATTN_ERR_UNSUPPORTED, "num_seqs * hot_window must fit in int32");
+  if (p->num_seqs == 0) return DATTN_OK;
+  if ((rc = check_io(p, q && k_hot && v_hot && k_cold && v_cold && cold_block_table && seq_lens && cold_lens, out,
+                     lse)))
+    return rc;
+  if ((rc = check_workspace(pl, workspace, workspace_bytes))) return rc;
+  dattn::DecodeArgs a = base_args(p, pl, q, workspace);
+  a.k = k_cold;
+  a.v = v_cold;
+  a.k_hot = k_hot;
+  a.v_hot = v_hot;
+  a.hot_window = hot_window;
+  a.hw = dattn::make_fastdiv((uint32_t)hot_window);
+  a.table = cold_block_table;
+  a.seq_lens = seq_lens;
+  a.cold_lens = cold_lens;
+  a.q_pos = q_pos;
+  const bool cap = p->softcap > 0.0f;
+  const bool contig = p->block_size % 16 == 0 && hot_window % 16 == 0;
+  return launch(dattn::split_kernel(dattn::kTieredF16, p->head_dim, cap, pl.G, contig),
+                dattn::split_kernel(dattn::kBalTieredF16, p->head_dim, cap, pl.G, contig), p, pl, a, out, lse,
+                (hipStream_t)stream);
+}
+
 int dattn_decode_block_sparse(const dattn_params* p, const float* q, const uint16_t* k_cache,
                               const uint16_t* v_cache, const int32_t* block_table, const int32_t* seq_lens,
                               const int32_t* q_pos, int32_t sparse_block, int32_t num_layouts,
                               const int32_t* row_ptr, int32_t row_stride, const int32_t* col_idx, int32_t col_stride,
-                              float* out, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+                              void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
   g_err.clear();
   Plan pl;
   int rc = make_plan(p, DATTN_KIND_BLOCK_SPARSE, sparse_block, pl);
@@ -433,7 +473,8 @@ int dattn_decode_block_sparse(const dattn_params* p, const float* q, const uint1
   if (row_stride < 2) return fail(DATTN_ERR_INVALID, "row_stride must be >= 2 (got %d)", row_stride);
   if (col_stride < 1) return fail(DATTN_ERR_INVALID, "col_stride must be >= 1 (got %d)", col_stride);
   if (p->num_seqs == 0) return DATTN_OK;
-  if ((rc = check_io(p, q && k_cache && v_cache && block_table && seq_lens && row_ptr && col_idx, out))) return rc;
+  if ((rc = check_io(p, q && k_cache && v_cache && block_table && seq_lens && row_ptr && col_idx, out, lse)))
+    return rc;
   if ((rc = check_workspace(pl, workspace, workspace_bytes))) return rc;
   dattn::DecodeArgs a = base_args(p, pl, q, workspace);
   a.k = k_cache;

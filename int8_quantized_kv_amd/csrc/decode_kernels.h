@@ -994,17 +994,18 @@ __device__ __forceinline__ void paged_segment(const DecodeArgs& a, int b, int kv
   on.finish(dst, lane);
 }
 
-// The same for the tiered cache: keys below cold_lens[b] from the paged int8
-// pool, the rest from the f16 ring.
-template <int D, int G, bool CAP, bool FM>
+// The same for the tiered cache: keys below cold_lens[b] from the paged cold
+// pool (int8 words with f16 scales, or f16 rows when CF16), the rest from the
+// f16 ring.
+template <int D, int G, bool CAP, bool FM, bool CF16>
 __device__ __forceinline__ void tiered_segment(const DecodeArgs& a, int b, int kvh, int lane, int tb, int te,
                                                int32_t* lds_tbl, const PartialDst& dst) {
   const int C = a.cold_lens[b];
   const int ce = min(te, C);   // cold part [tb, ce)
   const int hb = max(tb, C);   // hot part  [hb, te)
-  QRaw16<D> qraw;              // cold keys use the int8 dim map, a sweep of hot keys only the f16 one
+  QRaw16<D> qraw;              // int8 cold keys use the int8 dim map, f16 keys the f16 one
   if (tb < ce)
-    load_q_raw16<D, G, true>(a, b, kvh, lane, qraw);
+    load_q_raw16<D, G, !CF16>(a, b, kvh, lane, qraw);
   else if (tb < te)
     load_q_raw16<D, G, false>(a, b, kvh, lane, qraw);
   int blk0, nblk;
@@ -1021,14 +1022,20 @@ __device__ __forceinline__ void tiered_segment(const DecodeArgs& a, int b, int k
   on.init();
   if (tb < ce) {
     PagedMap map{lds_tbl, blk0, tb, ce - 1, a.bs, FM};
-    StoreI8<D> st{(const uint32_t*)a.k, (const uint32_t*)a.v, a.k_scale, a.v_scale, a.num_kv_heads, kvh};
-    run_tiles<D, G, CAP, kPipe, FM>(a, st, map, qf, [&](QF16<D>& q) { convert_q<D, G>(a, lane, qraw, q); }, lg, on,
-                                tb & ~(kTile - 1), ce, lane);
+    if constexpr (CF16) {
+      StoreF16<D> st{(const _Float16*)a.k, (const _Float16*)a.v, a.num_kv_heads, kvh};
+      run_tiles<D, G, CAP, kPipe, FM>(a, st, map, qf, [&](QF16<D>& q) { convert_q<D, G>(a, lane, qraw, q); }, lg,
+                                      on, tb & ~(kTile - 1), ce, lane);
+    } else {
+      StoreI8<D> st{(const uint32_t*)a.k, (const uint32_t*)a.v, a.k_scale, a.v_scale, a.num_kv_heads, kvh};
+      run_tiles<D, G, CAP, kPipe, FM>(a, st, map, qf, [&](QF16<D>& q) { convert_q<D, G>(a, lane, qraw, q); }, lg,
+                                      on, tb & ~(kTile - 1), ce, lane);
+    }
   }
   if (hb < te) {
     RingMap map{b, hb, te - 1, a.hw, FM};
     StoreF16<D> st{(const _Float16*)a.k_hot, (const _Float16*)a.v_hot, a.num_kv_heads, kvh};
-    const bool had_cold = tb < ce;
+    const bool had_cold = !CF16 && tb < ce;   // Q was laid out for int8 keys
     run_tiles<D, G, CAP, kPipe, FM>(a, st, map, qf,
                                 [&](QF16<D>& q) {
                                   if (had_cold) load_q_raw16<D, G, false>(a, b, kvh, lane, qraw);
@@ -1054,7 +1061,7 @@ __global__ __launch_bounds__(DATTN_MAX_THREADS) __attribute__((amdgpu_waves_per_
   paged_segment<D, G, CAP, T, FM>(a, b, kvh, lane, tb, te, lds_tbl, split_dst(a, b, kvh, G, split, D));
 }
 
-template <int D, int G, bool CAP, bool FM>
+template <int D, int G, bool CAP, bool FM, bool CF16>
 __global__ __launch_bounds__(DATTN_MAX_THREADS) __attribute__((amdgpu_waves_per_eu(2))) void tiered_split_kernel(DecodeArgs a) {
   extern __shared__ int32_t lds_tbl[];
   const int split = blockIdx.x, b = blockIdx.y;
@@ -1064,7 +1071,7 @@ __global__ __launch_bounds__(DATTN_MAX_THREADS) __attribute__((amdgpu_waves_per_
   visible_range(a, b, lo, hi, qp);
   const int tb = max(split * a.split_tokens, lo);
   const int te = min((split + 1) * a.split_tokens, hi + 1);
-  tiered_segment<D, G, CAP, FM>(a, b, kvh, lane, tb, te, lds_tbl, split_dst(a, b, kvh, G, split, D));
+  tiered_segment<D, G, CAP, FM, CF16>(a, b, kvh, lane, tb, te, lds_tbl, split_dst(a, b, kvh, G, split, D));
 }
 
 // ------------------------------------------------------- balanced schedule
@@ -1072,7 +1079,8 @@ __global__ __launch_bounds__(DATTN_MAX_THREADS) __attribute__((amdgpu_waves_per_
 // The visible keys of sequence b are cut into 16-key tiles aligned to
 // absolute positions.  Each tile costs units in proportion to the bytes it
 // reads: 1 for a paged tile or an int8 cold tile, 2 for an f16 hot-ring tile
-// of the tiered cache (16 rows of 2*D halves against 16 rows of 2*D bytes);
+// of the int8 tiered cache (16 rows of 2*D halves against 16 rows of 2*D
+// bytes); every tile of the f16 tiered cache costs 1, as in the paged cache;
 // each sequence adds a fixed start-up cost.
 // b owns units [P[b], P[b+1]) of the concatenation over all sequences (N
 // units in all).  Worker w of a kv-head group (blockIdx.x) owns units
@@ -1098,7 +1106,7 @@ constexpr int kSeqUnits = DATTN_SEQ_UNITS;
 template <int KIND>
 struct SeqCost {
   int lo, hi, base;   // visible keys [lo, hi]; tile i starts at key base + 16i
-  int ntiles, ncold;  // tiles < ncold cost 1 unit, the others 2 (tiered only)
+  int ntiles, ncold;  // tiles < ncold cost 1 unit, the others 2 (int8 tiered only)
   int head;           // start-up units (0 for a sequence with no visible key)
   __device__ __forceinline__ void init(const DecodeArgs& a, int b) {
     int q;
@@ -1147,7 +1155,7 @@ __device__ __forceinline__ int unit_prefix(const DecodeArgs& a, int32_t* P) {
   return P[B];
 }
 
-// KIND: 0 paged f16, 1 paged f32, 2 tiered.  Registers are capped for two
+// KIND: 0 paged f16, 1 paged f32, 2 tiered int8, 3 tiered f16.  Registers are capped for two
 // waves per SIMD: measured, a third wave (with Q moved to LDS to make room)
 // and a third tile of loads in flight per wave are both slower -- about
 // 32 KiB of loads in flight per SIMD is what HBM rewards here.
@@ -1190,7 +1198,9 @@ void balanced_kernel(DecodeArgs a) {
     const int te = min(sc.hi + 1, sc.base + kTile * sc.tile_at(seg_end - P[b]));
     const PartialDst dst = slot_dst(a, w + b, kvh, G, D);
     if constexpr (KIND == 2)
-      tiered_segment<D, G, CAP, FM>(a, b, kvh, lane, tb, te, tbl, dst);
+      tiered_segment<D, G, CAP, FM, false>(a, b, kvh, lane, tb, te, tbl, dst);
+    else if constexpr (KIND == 3)
+      tiered_segment<D, G, CAP, FM, true>(a, b, kvh, lane, tb, te, tbl, dst);
     else if constexpr (KIND == 1)
       paged_segment<D, G, CAP, float, FM>(a, b, kvh, lane, tb, te, tbl, dst);
     else
@@ -1269,11 +1279,27 @@ __global__ __launch_bounds__(DATTN_MAX_THREADS) __attribute__((amdgpu_waves_per_
 // Merge the partials of one (sequence, head): M = max m_s,
 // l = sum l_s 2^{m_s - M}, out = sum acc_s 2^{m_s - M} / l, lse = (M + log2 l) ln 2.
 // One workgroup per (sequence, head).  Partials with l = 0 (no visible key)
-// are skipped.
+// are skipped.  out is f32, or f16 rounded to nearest even from the f32
+// result; with out == nullptr only lse is written (acc is then not read).
+
+struct OutRow {
+  void* p;     // first element of the (sequence, head) row, or nullptr
+  bool f16;
+  __device__ __forceinline__ void store(int d, float x) const {
+    if (f16)
+      ((_Float16*)p)[d] = (_Float16)x;
+    else
+      ((float*)p)[d] = x;
+  }
+};
+
+__device__ __forceinline__ OutRow out_row(void* out, bool f16, int bh, int D) {
+  if (!out) return OutRow{nullptr, f16};
+  return OutRow{f16 ? (void*)((_Float16*)out + (size_t)bh * D) : (void*)((float*)out + (size_t)bh * D), f16};
+}
 
 template <int D, class Loc>
-__device__ __forceinline__ void merge_partials(const Loc& loc, int n, float* __restrict__ out,
-                                               float* __restrict__ lse_out) {
+__device__ __forceinline__ void merge_partials(const Loc& loc, int n, const OutRow out, float* __restrict__ lse_out) {
   // 256 threads: slot group sg = tid / 32 takes partials sg, sg + 8, ... and
   // folds them in with a running max (the rule above, one partial at a
   // time), loading four partials at once; thread c of a group owns dims
@@ -1296,7 +1322,7 @@ __device__ __forceinline__ void merge_partials(const Loc& loc, int n, float* __r
     for (int u = 0; u < U; ++u) {
       const int s = s0 + 8 * u;
       v[u] = s < n ? loc.ml(s) : make_float2(-__builtin_inff(), 0.f);
-      if (s < n && c < DC) {
+      if (s < n && c < DC && out.p) {
         const float* row = loc.acc(s);
 #pragma unroll
         for (int j = 0; j < NJ; ++j) x[u][j] = *(const f4*)(row + 128 * j + 4 * c);
@@ -1334,11 +1360,13 @@ __device__ __forceinline__ void merge_partials(const Loc& loc, int n, float* __r
     wg[g] = redl[g] > 0.f ? fast_exp2(redm[g] - M) : 0.f;
     Lt += redl[g] * wg[g];
   }
-  for (int d = tid; d < D; d += 256) {
-    float ot = 0.f;
+  if (out.p) {
+    for (int d = tid; d < D; d += 256) {
+      float ot = 0.f;
 #pragma unroll
-    for (int g = 0; g < 8; ++g) ot += red[g][d] * wg[g];
-    out[d] = Lt > 0.f ? ot / Lt : 0.f;
+      for (int g = 0; g < 8; ++g) ot += red[g][d] * wg[g];
+      out.store(d, Lt > 0.f ? ot / Lt : 0.f);
+    }
   }
   if (tid == 0 && lse_out) *lse_out = Lt > 0.f ? (M + __builtin_log2f(Lt)) * kLn2 : -__builtin_inff();
 }
@@ -1354,11 +1382,11 @@ struct SplitLoc {
 
 template <int D>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ part_acc,
-                                                      const float2* __restrict__ part_ml, float* __restrict__ out,
-                                                      float* __restrict__ lse, int S, int nbh) {
+                                                      const float2* __restrict__ part_ml, void* __restrict__ out,
+                                                      int out_f16, float* __restrict__ lse, int S, int nbh) {
   const int bh = blockIdx.x;
   const SplitLoc loc{part_acc + (size_t)bh * S * D, part_ml + (size_t)bh * S, D};
-  merge_partials<D>(loc, S, out + (size_t)bh * D, lse ? lse + bh : nullptr);
+  merge_partials<D>(loc, S, out_row(out, out_f16 != 0, bh, D), lse ? lse + bh : nullptr);
 }
 
 // Balanced schedule: the partials of (b, h) sit in slots w + b for the
@@ -1375,8 +1403,8 @@ template <int D>
 __global__ __launch_bounds__(256) void combine_balanced_kernel(const float* __restrict__ part_acc,
                                                                const float2* __restrict__ part_ml,
                                                                const int32_t* __restrict__ sched,
-                                                               float* __restrict__ out, float* __restrict__ lse,
-                                                               int H, int nbh) {
+                                                               void* __restrict__ out, int out_f16,
+                                                               float* __restrict__ lse, int H, int nbh) {
   const int bh = blockIdx.x;
   const int b = bh / H, h = bh - b * H;
   const int C = sched[1];
@@ -1389,7 +1417,7 @@ __global__ __launch_bounds__(256) void combine_balanced_kernel(const float* __re
     slot0 = (size_t)(w0 + b);
   }
   const SlotLoc loc{part_acc + (slot0 * H + h) * D, part_ml + slot0 * H + h, H, D};
-  merge_partials<D>(loc, n, out + (size_t)bh * D, lse ? lse + bh : nullptr);
+  merge_partials<D>(loc, n, out_row(out, out_f16 != 0, bh, D), lse ? lse + bh : nullptr);
 }
 
 }  // namespace dattn

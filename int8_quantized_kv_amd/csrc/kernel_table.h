@@ -14,6 +14,8 @@ enum SplitKind : int {
   kBalF16,         // balanced schedule, paged f16
   kBalF32,         // balanced schedule, paged f32
   kBalTiered,      // balanced schedule, tiered
+  kTieredF16,      // static splits, f16 cold pool + f16 hot ring
+  kBalTieredF16,   // balanced schedule, tiered f16
 };
 
 // Split kernel for (kind, GQA group G in {1, 2, 4, 8}, contiguous 16-row

@@ -17,11 +17,13 @@ void* instance(int kind) {
   switch (kind) {
     case kPagedF16: return (void*)&paged_split_kernel<D, G, CAP, _Float16, FM>;
     case kPagedF32: return (void*)&paged_split_kernel<D, G, CAP, float, FM>;
-    case kTiered: return (void*)&tiered_split_kernel<D, G, CAP, FM>;
+    case kTiered: return (void*)&tiered_split_kernel<D, G, CAP, FM, false>;
+    case kTieredF16: return (void*)&tiered_split_kernel<D, G, CAP, FM, true>;
     case kSparse: return (void*)&sparse_split_kernel<D, G, CAP, FM>;
     case kBalF16: return (void*)&balanced_kernel<D, G, CAP, 0, FM>;
     case kBalF32: return (void*)&balanced_kernel<D, G, CAP, 1, FM>;
     case kBalTiered: return (void*)&balanced_kernel<D, G, CAP, 2, FM>;
+    case kBalTieredF16: return (void*)&balanced_kernel<D, G, CAP, 3, FM>;
     default: return nullptr;
   }
 }

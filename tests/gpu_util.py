@@ -40,15 +40,16 @@ class DeviceCase:
             self.k_cache = dev(c.k_cache, device)
             self.v_cache = dev(c.v_cache, device)
             self.block_table = dev(c.block_table, device)
-        if c.kind == "tiered":
+        if c.kind in ("tiered", "tiered_f16"):
             self.k_hot = dev(c.k_hot, device)
             self.v_hot = dev(c.v_hot, device)
             self.k_cold = dev(c.k_cold, device)
             self.v_cold = dev(c.v_cold, device)
-            self.k_scale = dev(c.k_scale, device)
-            self.v_scale = dev(c.v_scale, device)
             self.cold_block_table = dev(c.cold_block_table, device)
             self.cold_lens = dev(c.cold_lens, device)
+        if c.kind == "tiered":
+            self.k_scale = dev(c.k_scale, device)
+            self.v_scale = dev(c.v_scale, device)
         if c.kind == "sparse":
             self.row_ptr = dev(c.row_ptr, device)
             self.col_idx = dev(c.col_idx, device)
@@ -70,6 +71,9 @@ class DeviceCase:
             return dk.dattn_decode_tiered_int8(self.q, self.k_hot, self.v_hot, self.k_cold, self.v_cold,
                                                self.k_scale, self.v_scale, self.cold_block_table, self.seq_lens,
                                                self.cold_lens, **kw)
+        if c.kind == "tiered_f16":
+            return dk.dattn_decode_tiered_f16(self.q, self.k_hot, self.v_hot, self.k_cold, self.v_cold,
+                                              self.cold_block_table, self.seq_lens, self.cold_lens, **kw)
         return dk.dattn_decode_block_sparse(self.q, self.k_cache, self.v_cache, self.block_table, self.seq_lens,
                                             c.sparse_block, self.row_ptr, self.col_idx, **kw)
 
@@ -77,7 +81,7 @@ class DeviceCase:
         import torch
         out, lse = self.run(split_tokens, **over)
         torch.cuda.synchronize()
-        return out.cpu().numpy(), lse.cpu().numpy()
+        return (None if out is None else out.cpu().numpy()), (None if lse is None else lse.cpu().numpy())
 
 
 def oracle_run(case, pairs=None):

@@ -30,8 +30,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("dattn_decode_paged", "dattn_decode_tiered_int8", "dattn_decode_block_sparse", "dattn_workspace_size",
-              "dattn_last_error", "dattn_version"):
+    for n in ("dattn_decode_paged", "dattn_decode_tiered_int8", "dattn_decode_tiered_f16", "dattn_decode_block_sparse",
+              "dattn_append_tiered_int8", "dattn_workspace_size", "dattn_last_error", "dattn_version"):
         assert n in names
 
 
@@ -85,7 +85,7 @@ int main() {
 def good_params(**kw):
     p = dict(num_seqs=2, num_heads=8, num_kv_heads=2, head_dim=128, scale=0.0, causal=1, sliding_window=0,
              softcap=0.0, block_size=16, max_blocks_per_seq=8, num_blocks=16, max_seq_len=100, split_tokens=0,
-             phases=0)
+             phases=0, out_dtype=0)
     p.update(kw)
     return dk.DattnParams(**p)
 
@@ -115,6 +115,7 @@ BAD = [
     (dict(split_tokens=24), dk.ERR_INVALID, "split_tokens"),
     (dict(split_tokens=-16), dk.ERR_INVALID, "split_tokens"),
     (dict(phases=7), dk.ERR_INVALID, "phases"),
+    (dict(out_dtype=2), dk.ERR_INVALID, "out_dtype"),
     (dict(num_seqs=70000), dk.ERR_UNSUPPORTED, "num_seqs"),
 ]
 
@@ -148,6 +149,9 @@ def test_workspace_size_values(lib):
     assert n == up(acc) + up(ml)
     # the tiered table only maps the cold prefix: max_seq_len may exceed it
     assert ws_size(lib, good_params(max_seq_len=500), kind=dk.KIND_TIERED_INT8)[0] == 0
+    assert ws_size(lib, good_params(max_seq_len=500), kind=dk.KIND_TIERED_F16)[0] == 0
+    assert ws_size(lib, good_params(), kind=dk.KIND_TIERED_F16)[1] == ws_size(lib, good_params(),
+                                                                              kind=dk.KIND_TIERED_INT8)[1]
     # sparse: sparse_block must be a positive multiple of block_size
     assert ws_size(lib, good_params(), kind=dk.KIND_BLOCK_SPARSE, sb=24)[0] == dk.ERR_INVALID
     assert ws_size(lib, good_params(), kind=dk.KIND_BLOCK_SPARSE, sb=32)[0] == 0
@@ -183,11 +187,23 @@ def test_decode_calls_validate_before_any_hip_call(lib):
         rc = lib.dattn_decode_block_sparse(ctypes.byref(p), fake, fake, fake, fake, fake, None, *args, fake, None,
                                            fake, 1 << 20, None)
         assert rc == dk.ERR_INVALID and word in dk.dattn_last_error()
-    # combine-only phase does not need the inputs, but needs out
+    # tiered f16: hot_window, NULL cold pool
+    rc = lib.dattn_decode_tiered_f16(ctypes.byref(p), fake, fake, fake, 0, fake, fake, fake, fake, fake, None, fake,
+                                     None, fake, 1 << 20, None)
+    assert rc == dk.ERR_INVALID and "hot_window" in dk.dattn_last_error()
+    rc = lib.dattn_decode_tiered_f16(ctypes.byref(p), fake, fake, fake, 16, None, fake, fake, fake, fake, None, fake,
+                                     None, fake, 1 << 20, None)
+    assert rc == dk.ERR_INVALID and "NULL" in dk.dattn_last_error()
+    # combine-only phase does not need the inputs, but needs out or lse
     pc = good_params(phases=dk.PHASE_COMBINE)
     rc = lib.dattn_decode_paged(ctypes.byref(pc), None, None, None, dk.F16, None, None, None, None, None, fake,
                                 1 << 20, None)
-    assert rc == dk.ERR_INVALID and "out" in dk.dattn_last_error()
+    assert rc == dk.ERR_INVALID and "out and lse" in dk.dattn_last_error()
+    # out_dtype is checked on every entry point
+    po = good_params(out_dtype=3)
+    rc = lib.dattn_decode_paged(ctypes.byref(po), fake, fake, fake, dk.F16, fake, fake, None, fake, None, fake,
+                                1 << 20, None)
+    assert rc == dk.ERR_INVALID and "out_dtype" in dk.dattn_last_error()
 
 
 def test_empty_batch_is_a_no_op(lib):
