@@ -68,6 +68,8 @@ def kv_bytes(case) -> int:
         if case.kind == "paged":
             esz = case.k_cache.dtype.itemsize
             total += (hi - lo + 1) * Hkv * 2 * D * esz
+        elif case.kind == "tiered_f16":
+            total += (hi - lo + 1) * Hkv * 2 * D * 2
         elif case.kind == "tiered":
             c = int(case.cold_lens[b])
             ncold = max(0, min(hi, c - 1) - lo + 1)
@@ -117,10 +119,10 @@ class Runner:
         self.out = torch.empty((B, H, D), dtype=torch.float32, device=dev)
         self.lse = torch.empty((B, H), dtype=torch.float32, device=dev)
         max_len = int(c.seq_lens.max())
-        if c.kind == "tiered":
+        if c.kind in ("tiered", "tiered_f16"):
             NB, bs = c.k_cold.shape[0], c.k_cold.shape[1]
             mb = c.cold_block_table.shape[1]
-            kind = dk.KIND_TIERED_INT8
+            kind = dk.KIND_TIERED_INT8 if c.kind == "tiered" else dk.KIND_TIERED_F16
         else:
             NB, bs = c.k_cache.shape[0], c.k_cache.shape[1]
             mb = c.block_table.shape[1]
@@ -158,6 +160,16 @@ class Runner:
                             P(self.lse), P(self.ws), self.ws.numel(), self.stream)
                     self.calls.append(rest)
                 self.fn = L.dattn_decode_block_sparse
+        elif c.kind == "tiered_f16":
+            kh, vh, kc0, vc0 = T(c.k_hot), T(c.v_hot), T(c.k_cold), T(c.v_cold)
+            tbl, cl = T(c.cold_block_table), T(c.cold_lens)
+            reps = [(kh, vh, kc0, vc0)] + [tuple(x.clone() for x in (kh, vh, kc0, vc0)) for _ in range(copies - 1)]
+            self.keep = (reps, tbl, cl)
+            for (a, b_, kc, vc) in reps:
+                rest = (P(self.q), P(a), P(b_), c.hot_window, P(kc), P(vc), P(tbl), P(self.seq_lens), P(cl),
+                        P(self.q_pos), P(self.out), P(self.lse), P(self.ws), self.ws.numel(), self.stream)
+                self.calls.append(rest)
+            self.fn = L.dattn_decode_tiered_f16
         else:
             kh, vh, kc0, vc0 = T(c.k_hot), T(c.v_hot), T(c.k_cold), T(c.v_cold)
             ks0, vs0, tbl, cl = T(c.k_scale), T(c.v_scale), T(c.cold_block_table), T(c.cold_lens)
@@ -187,6 +199,8 @@ class Runner:
 def cache_bytes(case):
     if case.kind == "tiered":
         arrs = (case.k_hot, case.v_hot, case.k_cold, case.v_cold, case.k_scale, case.v_scale)
+    elif case.kind == "tiered_f16":
+        arrs = (case.k_hot, case.v_hot, case.k_cold, case.v_cold)
     else:
         arrs = (case.k_cache, case.v_cache)
     return sum(a.nbytes for a in arrs)
@@ -373,6 +387,15 @@ def line_for(case, steps, warmup, check=True):
     return res, m
 
 
+def workload(idx, window=0):
+    """Workloads 1-5 of the input generators, and 6: the tiered workload's shape
+    with an f16 cold tier."""
+    import synth
+    if idx == 6:
+        return synth.tiered_f16_workload(window)
+    return synth.config(idx, window=window)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -380,7 +403,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--all", action="store_true", help="also measure the other workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", type=int, default=2, help="headline workload index (default 2)")
+    ap.add_argument("--workload", type=int, default=2,
+                    help="headline workload index (default 2; 6 = the tiered workload with an f16 cold tier)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run 5 device copies of MIB MiB (for scaling memory counters)")
     args = ap.parse_args()
@@ -400,7 +424,7 @@ def main():
         copy_calibration(args.copy_calibration)
 
     log("generating headline workload ...")
-    case = synth.config(args.workload)
+    case = workload(args.workload)
     log(f"workload {case.name}: KV bytes {kv_bytes(case)}")
     head, m = line_for(case, args.steps, args.warmup)
     log(json.dumps(head))
@@ -410,7 +434,8 @@ def main():
     B, H, D = case.q.shape
     G = H // case.params["num_kv_heads"]
     kind = {"paged": "paged f16" if case.k_cache is not None and case.k_cache.dtype == np.float16 else "paged f32",
-            "tiered": "tiered int8 + f16 ring", "sparse": "block-sparse f16"}[case.kind]
+            "tiered": "tiered int8 + f16 ring", "tiered_f16": "tiered f16 + f16 ring",
+            "sparse": "block-sparse f16"}[case.kind]
     lens = case.seq_lens
     out = {
         "metric": "KV-read HBM GB/s (% of peak) and decode queries/sec, 1 MI355X",
@@ -447,9 +472,10 @@ def main():
         out["cpu_baseline"] = cpu_baseline(case, kvb)
     if args.all:
         extra = []
-        for idx, kw in ((1, {}), (3, dict(window=0)), (3, dict(window=4096)), (4, {}), (5, {})):
+        for idx, kw in ((1, {}), (3, dict(window=0)), (3, dict(window=4096)), (4, {}), (5, {}),
+                        (6, dict(window=0)), (6, dict(window=4096))):
             log(f"generating workload {idx} {kw} ...")
-            c = synth.config(idx, **kw)
+            c = workload(idx, **kw)
             res, _ = line_for(c, max(20, args.steps // 4), max(5, args.warmup // 4))
             log(json.dumps(res))
             extra.append(res)
