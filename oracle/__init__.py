@@ -104,7 +104,8 @@ def load(path: str = _LIB):
                                             i32, P, i32, i32, P, P]
     lib.orc_decode_tiered_f16.argtypes = [ctypes.POINTER(_Params), P, P, P, i32, P, P, P, P, P, P, P, i32, i32,
                                           P, P]
-    for f in (lib.orc_decode_paged, lib.orc_decode_tiered_int8, lib.orc_decode_tiered_f16,
+    lib.orc_decode_ring_f16.argtypes = [ctypes.POINTER(_Params), P, P, P, P, P, P, i32, i32, P, P]
+    for f in (lib.orc_decode_paged, lib.orc_decode_tiered_int8, lib.orc_decode_tiered_f16, lib.orc_decode_ring_f16,
               lib.orc_decode_block_sparse):
         f.restype = ctypes.c_int
     lib.orc_f32_to_f16.argtypes = [ctypes.c_float]
@@ -248,6 +249,24 @@ def decode_tiered_f16(p: Params, q, k_hot, v_hot, hot_window, k_cold, v_cold, co
     return out, lse
 
 
+def decode_ring_f16(p: Params, q, k_ring, v_ring, seq_lens, q_pos=None, pairs=None, nthreads=0, lib=None):
+    """Ring [B, W, Hkv, D] f16 with W = p.sliding_window: token t at slot t mod W, the last W resident."""
+    lib = _load(lib)
+    q = _arr(q, np.float32)
+    kr = _arr(k_ring, np.float16)
+    vr = _arr(v_ring, np.float16)
+    sl = _arr(seq_lens, np.int32)
+    qp = _arr(q_pos, np.int32)
+    pa, n = _pairs(p, pairs)
+    out = np.zeros((n, p.head_dim), np.float64)
+    lse = np.zeros((n,), np.float64)
+    cp = p.c()
+    rc = lib.orc_decode_ring_f16(ctypes.byref(cp), _ptr(q), _ptr(kr), _ptr(vr), _ptr(sl), _ptr(qp), _ptr(pa), n,
+                                 nthreads, _ptr(out), _ptr(lse))
+    _check(rc, "orc_decode_ring_f16")
+    return out, lse
+
+
 def decode_block_sparse(p: Params, q, k_cache, v_cache, block_table, seq_lens, sparse_block, num_layouts,
                         row_ptr, col_idx, q_pos=None, pairs=None, nthreads=0, lib=None):
     """CSR row_ptr [NL, R+1], col_idx [NL, col_stride]; paged f16 cache."""
@@ -285,6 +304,8 @@ def run(case, pairs=None, nthreads=0, lib=None):
         return decode_tiered_f16(p, case.q, case.k_hot, case.v_hot, case.hot_window, case.k_cold, case.v_cold,
                                  case.cold_block_table, case.seq_lens, case.cold_lens, case.q_pos, pairs, nthreads,
                                  lib)
+    if case.kind == "ring":
+        return decode_ring_f16(p, case.q, case.k_hot, case.v_hot, case.seq_lens, case.q_pos, pairs, nthreads, lib)
     if case.kind == "sparse":
         return decode_block_sparse(p, case.q, case.k_cache, case.v_cache, case.block_table, case.seq_lens,
                                    case.sparse_block, case.num_layouts, case.row_ptr, case.col_idx, case.q_pos,

@@ -47,6 +47,12 @@
  *           layout of the paged cache read through cold_block_table
  *           (attention.js executeAttentionTiered: f16 hot and cold buffers,
  *           the cold tier paged by default).
+ *   window ring: a per-sequence ring of W = sliding_window slots holding
+ *           the last W tokens, token t at slot t mod W (doppler
+ *           attention_f16kv.wgsl, get_kv_pos with the ring layout); only
+ *           t in [max(0, L-W), L) is resident, so the visible set is
+ *           intersected with that range (the kv_start / kv_len range of the
+ *           same kernel).
  *   sparse: the paged cache, and t is visible to head h only if its sparse
  *           block j = t / SB is a column of row r = q / SB of CSR layout
  *           (h mod NL) and j <= r; repeated columns count once
@@ -221,6 +227,22 @@ static void tiered_f16_fetch(const void* vsrc, int32_t b, int32_t g, int64_t t, 
   for (int32_t d = 0; d < D; ++d) dst[d] = orc_f16_to_f64(rows[base + d]);
 }
 
+/* Window ring: ring[b][t mod W][g][0..D) in f16. */
+typedef struct {
+  const orc_params* p;
+  const uint16_t* k;
+  const uint16_t* v;
+  int32_t ring;
+} ring_src;
+
+static void ring_fetch(const void* vsrc, int32_t b, int32_t g, int64_t t, int32_t is_v, double* dst) {
+  const ring_src* s = (const ring_src*)vsrc;
+  const orc_params* p = s->p;
+  const int64_t base = (((int64_t)b * s->ring + t % s->ring) * p->num_kv_heads + g) * p->head_dim;
+  const uint16_t* rows = is_v ? s->v : s->k;
+  for (int32_t d = 0; d < p->head_dim; ++d) dst[d] = orc_f16_to_f64(rows[base + d]);
+}
+
 /* -------------------------------------------------------------- attention */
 
 /* Attention of one query head over an explicit list of visible tokens. */
@@ -319,9 +341,10 @@ static int sparse_select(const sparse_csr* c, int32_t h, int64_t q, unsigned cha
 }
 
 /* Shared driver: for each requested flat pair b*H+h, enumerate the visible
- * tokens and attend.  pairs == NULL means every pair in order. */
+ * tokens and attend.  pairs == NULL means every pair in order.  resident > 0
+ * keeps only the last `resident` tokens of each sequence (a ring). */
 static int run_pairs(const orc_params* p, const float* q, const int32_t* seq_lens, const int32_t* q_pos,
-                     const sparse_csr* csr, row_fn fetch, const void* src, const int32_t* pairs,
+                     const sparse_csr* csr, int32_t resident, row_fn fetch, const void* src, const int32_t* pairs,
                      int32_t npairs, int32_t nthreads, double* out, double* lse) {
   int64_t total = (int64_t)p->num_seqs * p->num_heads;
   if (!pairs) npairs = (int32_t)total;
@@ -348,6 +371,7 @@ static int run_pairs(const orc_params* p, const float* q, const int32_t* seq_len
     int64_t n = 0;
     if (local == ORC_OK) {
       for (int64_t t = 0; t < L; ++t) {
+        if (resident > 0 && t < L - resident) continue;
         if (!orc_key_visible(t, qp, L, p->causal, p->sliding_window)) continue;
         if (csr && !sel[t / csr->sparse_block]) continue;
         toks[n++] = t;
@@ -379,7 +403,7 @@ int orc_decode_paged(const orc_params* p, const float* q, const void* k_cache, c
     if ((rc = check_table(p, block_table, b, seq_lens[b]))) return rc;
   }
   paged_src src = {p, k_cache, v_cache, kv_dtype, block_table};
-  return run_pairs(p, q, seq_lens, q_pos, NULL, paged_fetch, &src, pairs, npairs, nthreads, out, lse);
+  return run_pairs(p, q, seq_lens, q_pos, NULL, 0, paged_fetch, &src, pairs, npairs, nthreads, out, lse);
 }
 
 /* Tiered cache: paged int8 cold history + f16 hot ring. */
@@ -397,7 +421,7 @@ int orc_decode_tiered_int8(const orc_params* p, const float* q, const uint16_t* 
     if ((rc = check_table(p, cold_block_table, b, cold_lens[b]))) return rc;
   }
   tiered_src src = {p, k_hot, v_hot, hot_window, k_cold, v_cold, k_scale, v_scale, cold_block_table, cold_lens};
-  return run_pairs(p, q, seq_lens, q_pos, NULL, tiered_fetch, &src, pairs, npairs, nthreads, out, lse);
+  return run_pairs(p, q, seq_lens, q_pos, NULL, 0, tiered_fetch, &src, pairs, npairs, nthreads, out, lse);
 }
 
 /* Tiered cache with an f16 cold tier: paged f16 cold history + f16 hot ring.
@@ -418,7 +442,22 @@ int orc_decode_tiered_f16(const orc_params* p, const float* q, const uint16_t* k
   /* the cold words/scales fields carry the f16 rows; the scales are unused */
   tiered_src src = {p, k_hot, v_hot, hot_window, (const uint32_t*)(const void*)k_cold,
                     (const uint32_t*)(const void*)v_cold, NULL, NULL, cold_block_table, cold_lens};
-  return run_pairs(p, q, seq_lens, q_pos, NULL, tiered_f16_fetch, &src, pairs, npairs, nthreads, out, lse);
+  return run_pairs(p, q, seq_lens, q_pos, NULL, 0, tiered_f16_fetch, &src, pairs, npairs, nthreads, out, lse);
+}
+
+/* Sliding-window ring f16 cache: ring [B, W, Hkv, D], W = sliding_window >= 1;
+ * token t of sequence b at slot t mod W, the last W tokens resident. */
+int orc_decode_ring_f16(const orc_params* p, const float* q, const uint16_t* k_ring, const uint16_t* v_ring,
+                        const int32_t* seq_lens, const int32_t* q_pos, const int32_t* pairs, int32_t npairs,
+                        int32_t nthreads, double* out, double* lse) {
+  int rc = check_common(p);
+  if (rc) return rc;
+  if (p->sliding_window <= 0) return ORC_EINVAL;
+  for (int32_t b = 0; b < p->num_seqs; ++b)
+    if (seq_lens[b] < 0) return ORC_EINVAL;
+  ring_src src = {p, k_ring, v_ring, p->sliding_window};
+  return run_pairs(p, q, seq_lens, q_pos, NULL, p->sliding_window, ring_fetch, &src, pairs, npairs, nthreads, out,
+                   lse);
 }
 
 /* Block-sparse CSR selection over the paged f16 cache. */
@@ -437,7 +476,7 @@ int orc_decode_block_sparse(const orc_params* p, const float* q, const uint16_t*
   }
   paged_src src = {p, k_cache, v_cache, ORC_F16, block_table};
   sparse_csr csr = {sparse_block, num_layouts, row_stride, col_stride, row_ptr, col_idx};
-  return run_pairs(p, q, seq_lens, q_pos, &csr, paged_fetch, &src, pairs, npairs, nthreads, out, lse);
+  return run_pairs(p, q, seq_lens, q_pos, &csr, 0, paged_fetch, &src, pairs, npairs, nthreads, out, lse);
 }
 
 int orc_max_threads(void) {

@@ -17,6 +17,7 @@ Cache layouts (all C-contiguous numpy arrays):
   cold pool       k_cold, v_cold    [num_cold_blocks, bs, Hkv, D/4]  u32, 4 x int8 LSB-first
   cold scales     k_scale, v_scale  [num_cold_blocks, bs, Hkv]       f16
   f16 cold pool   k_cold, v_cold    [num_cold_blocks, bs, Hkv, D]    f16 (the tiered f16 kind)
+  window ring     k_hot, v_hot      [B, W, Hkv, D]                   f16 (the ring kind, W = sliding_window)
   CSR             row_ptr [NL, R+1], col_idx [NL, col_stride]        i32
 """
 from __future__ import annotations
@@ -39,7 +40,7 @@ def _params(B, H, Hkv, D, bs, max_blocks, num_blocks, scale=0.0, causal=1, windo
 @dataclass
 class Case:
     """Every array a decode call needs, plus the scalar parameters."""
-    kind: str                      # "paged", "tiered", "tiered_f16" or "sparse"
+    kind: str                      # "paged", "tiered", "tiered_f16", "ring" or "sparse"
     params: dict
     q: np.ndarray
     seq_lens: np.ndarray
@@ -262,6 +263,41 @@ def tiered_f16_case(seed, B, H, Hkv, D, bs, lens, cold_lens, hot_window, permute
                 cold_block_table=table, cold_lens=cold_lens, name=name)
 
 
+def ring_case(seed, B, H, Hkv, D, W, lens, q_pos=None, causal=1, softcap=0.0, scale=0.0, history=True,
+              name="") -> Case:
+    """Sliding-window ring of W slots per sequence: token t of sequence b sits at slot
+    t mod W and only the last W tokens are resident.  With ``history`` the whole token
+    history K/V[b, t] is drawn (float32 N(0,1) -> f16, kept in ``extra``) and its last W
+    tokens are written to the ring; otherwise the resident rows are drawn directly.
+    Slots that hold no resident token carry +-300."""
+    rng = np.random.default_rng(seed)
+    lens = np.asarray(lens, np.int32)
+    q = rng.standard_normal((B, H, D), dtype=np.float32)
+    hk = np.full((B, W, Hkv, D), 300.0, np.float16)
+    hv = np.full((B, W, Hkv, D), -300.0, np.float16)
+    extra = {}
+    if history:
+        Lmax = max(1, int(lens.max()))
+        k_log = _normal(rng, (B, Lmax, Hkv, D), F16)
+        v_log = _normal(rng, (B, Lmax, Hkv, D), F16)
+        for b, L in enumerate(lens):
+            t = np.arange(max(0, int(L) - W), int(L))
+            hk[b, t % W] = k_log[b, t]
+            hv[b, t % W] = v_log[b, t]
+        extra = dict(k_history=k_log, v_history=v_log)
+    else:
+        full = lens >= W
+        hk[full] = _normal(rng, (int(full.sum()), W, Hkv, D), F16)
+        hv[full] = _normal(rng, (int(full.sum()), W, Hkv, D), F16)
+        for b in np.nonzero(~full)[0]:
+            L = int(lens[b])
+            hk[b, :L] = rng.standard_normal((L, Hkv, D), dtype=np.float32).astype(np.float16)
+            hv[b, :L] = rng.standard_normal((L, Hkv, D), dtype=np.float32).astype(np.float16)
+    qp = None if q_pos is None else np.asarray(q_pos, np.int32)
+    return Case("ring", _params(B, H, Hkv, D, 1, 1, 1, scale, causal, W, softcap), q, lens, qp, k_hot=hk, v_hot=hv,
+                hot_window=int(W), name=name, extra=extra)
+
+
 # ------------------------------------------------------------------- sparse
 
 def csr_from_rows(rows_per_layout):
@@ -371,6 +407,15 @@ def config(i: int, window: int = 0) -> Case:
         return sparse_case(5, 8, 32, 8, 128, 64, 64, 4, lens=[16384] * 8,
                            scale=float(np.float32(1.0 / math.sqrt(128))), name="sparse_f16_B8_H32x8_D128_L16384")
     raise ValueError(i)
+
+
+def ring_workload() -> Case:
+    """Sliding-window ring f16: B=32, 32/8 heads, D=128, window (= ring) 4096,
+    L ~ U{4096..32768} (every ring full), causal, scale 1/sqrt(128)."""
+    rng = np.random.default_rng(7)
+    lens = rng.integers(4096, 32769, size=32)
+    return ring_case(7, 32, 32, 8, 128, 4096, lens, history=False, scale=float(np.float32(1.0 / math.sqrt(128))),
+                     name="ring_f16_B32_H32x8_D128_W4096")
 
 
 def tiered_f16_workload(window: int = 0) -> Case:

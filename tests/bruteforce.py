@@ -28,6 +28,16 @@ def logical_rows(case, b):
         V = case.v_cache[blk, t % bs].astype(np.float64)
         return K, V
     Hkv, D = p["num_kv_heads"], p["head_dim"]
+    if case.kind == "ring":
+        # only the last W tokens are resident; older positions get NaN rows, which the
+        # visibility matrix below never selects
+        W = case.hot_window
+        K = np.full((L, Hkv, D), np.nan)
+        V = np.full((L, Hkv, D), np.nan)
+        tr = t[max(0, L - W):]
+        K[tr] = case.k_hot[b, tr % W]
+        V[tr] = case.v_hot[b, tr % W]
+        return K, V
     c = int(case.cold_lens[b])
     if case.kind == "tiered_f16":
         tc, th = t[:c], t[c:]
@@ -63,6 +73,8 @@ def visible_matrix(case, b):
     W = p["sliding_window"]
     if W > 0 and q >= W:
         ok &= t >= q - W + 1
+    if case.kind == "ring":
+        ok &= t >= L - case.hot_window
     vis = np.repeat(ok[None, :], H, axis=0)
     if case.kind == "sparse":
         SB = case.sparse_block

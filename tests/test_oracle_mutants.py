@@ -49,8 +49,14 @@ MUTANTS = {
     "f16_hot_slot_from_hot_start": (
         "base = (((int64_t)b * s->hot_window + orc_ring_slot(t, s->hot_window)) * p->num_kv_heads + g) * D;",
         "base = (((int64_t)b * s->hot_window + (t - s->cold_lens[b])) * p->num_kv_heads + g) * D;"),
+    "window_ring_slot_shifted": ("const int64_t base = (((int64_t)b * s->ring + t % s->ring)",
+                          "const int64_t base = (((int64_t)b * s->ring + (t + 1) % s->ring)"),
+    "ring_keeps_one_more": ("if (resident > 0 && t < L - resident) continue;",
+                            "if (resident > 0 && t < L - resident - 1) continue;"),
+    "ring_residency_ignored": ("if (resident > 0 && t < L - resident) continue;", "(void)resident;"),
 }
-PIN_FILES = ["test_oracle_pins.py", "test_oracle_append_pins.py", "test_oracle_tiered_f16_pins.py"]
+PIN_FILES = ["test_oracle_pins.py", "test_oracle_append_pins.py", "test_oracle_tiered_f16_pins.py",
+             "test_oracle_ring_pins.py"]
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
