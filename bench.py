@@ -50,6 +50,8 @@ def visible_range(case, b):
     hi = min(q, L - 1) if p["causal"] else L - 1
     W = p["sliding_window"]
     lo = q - W + 1 if (W > 0 and q >= W) else 0
+    if case.kind == "ring":
+        lo = max(lo, L - case.hot_window)
     return lo, hi, q
 
 
@@ -68,7 +70,7 @@ def kv_bytes(case) -> int:
         if case.kind == "paged":
             esz = case.k_cache.dtype.itemsize
             total += (hi - lo + 1) * Hkv * 2 * D * esz
-        elif case.kind == "tiered_f16":
+        elif case.kind in ("tiered_f16", "ring"):
             total += (hi - lo + 1) * Hkv * 2 * D * 2
         elif case.kind == "tiered":
             c = int(case.cold_lens[b])
@@ -123,6 +125,8 @@ class Runner:
             NB, bs = c.k_cold.shape[0], c.k_cold.shape[1]
             mb = c.cold_block_table.shape[1]
             kind = dk.KIND_TIERED_INT8 if c.kind == "tiered" else dk.KIND_TIERED_F16
+        elif c.kind == "ring":
+            NB, bs, mb, kind = 1, 1, 1, dk.KIND_RING_F16
         else:
             NB, bs = c.k_cache.shape[0], c.k_cache.shape[1]
             mb = c.block_table.shape[1]
@@ -160,6 +164,14 @@ class Runner:
                             P(self.lse), P(self.ws), self.ws.numel(), self.stream)
                     self.calls.append(rest)
                 self.fn = L.dattn_decode_block_sparse
+        elif c.kind == "ring":
+            kr0, vr0 = T(c.k_hot), T(c.v_hot)
+            reps = [(kr0, vr0)] + [(kr0.clone(), vr0.clone()) for _ in range(copies - 1)]
+            self.keep = reps
+            for (kr, vr) in reps:
+                self.calls.append((P(self.q), P(kr), P(vr), P(self.seq_lens), P(self.q_pos), P(self.out),
+                                   P(self.lse), P(self.ws), self.ws.numel(), self.stream))
+            self.fn = L.dattn_decode_ring_f16
         elif c.kind == "tiered_f16":
             kh, vh, kc0, vc0 = T(c.k_hot), T(c.v_hot), T(c.k_cold), T(c.v_cold)
             tbl, cl = T(c.cold_block_table), T(c.cold_lens)
@@ -201,6 +213,8 @@ def cache_bytes(case):
         arrs = (case.k_hot, case.v_hot, case.k_cold, case.v_cold, case.k_scale, case.v_scale)
     elif case.kind == "tiered_f16":
         arrs = (case.k_hot, case.v_hot, case.k_cold, case.v_cold)
+    elif case.kind == "ring":
+        arrs = (case.k_hot, case.v_hot)
     else:
         arrs = (case.k_cache, case.v_cache)
     return sum(a.nbytes for a in arrs)
@@ -388,11 +402,13 @@ def line_for(case, steps, warmup, check=True):
 
 
 def workload(idx, window=0):
-    """Workloads 1-5 of the input generators, and 6: the tiered workload's shape
-    with an f16 cold tier."""
+    """Workloads 1-5 of the input generators, 6: the tiered workload's shape
+    with an f16 cold tier, 7: a sliding-window ring f16 cache."""
     import synth
     if idx == 6:
         return synth.tiered_f16_workload(window)
+    if idx == 7:
+        return synth.ring_workload()
     return synth.config(idx, window=window)
 
 
@@ -404,7 +420,8 @@ def main():
     ap.add_argument("--all", action="store_true", help="also measure the other workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", type=int, default=2,
-                    help="headline workload index (default 2; 6 = the tiered workload with an f16 cold tier)")
+                    help="headline workload index (default 2; 6 = the tiered workload with an f16 cold tier, "
+                         "7 = a sliding-window ring f16 cache)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run 5 device copies of MIB MiB (for scaling memory counters)")
     args = ap.parse_args()
@@ -434,7 +451,7 @@ def main():
     B, H, D = case.q.shape
     G = H // case.params["num_kv_heads"]
     kind = {"paged": "paged f16" if case.k_cache is not None and case.k_cache.dtype == np.float16 else "paged f32",
-            "tiered": "tiered int8 + f16 ring", "tiered_f16": "tiered f16 + f16 ring",
+            "tiered": "tiered int8 + f16 ring", "tiered_f16": "tiered f16 + f16 ring", "ring": "window ring f16",
             "sparse": "block-sparse f16"}[case.kind]
     lens = case.seq_lens
     out = {
@@ -473,7 +490,7 @@ def main():
     if args.all:
         extra = []
         for idx, kw in ((1, {}), (3, dict(window=0)), (3, dict(window=4096)), (4, {}), (5, {}),
-                        (6, dict(window=0)), (6, dict(window=4096))):
+                        (6, dict(window=0)), (6, dict(window=4096)), (7, {})):
             log(f"generating workload {idx} {kw} ...")
             c = workload(idx, **kw)
             res, _ = line_for(c, max(20, args.steps // 4), max(5, args.warmup // 4))

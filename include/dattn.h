@@ -63,6 +63,7 @@ extern "C" {
 #define DATTN_KIND_TIERED_INT8 1
 #define DATTN_KIND_BLOCK_SPARSE 2
 #define DATTN_KIND_TIERED_F16 3
+#define DATTN_KIND_RING_F16 4
 
 /*
  * Scalar parameters (doppler attention_f16kv.wgsl Uniforms and boostr
@@ -180,6 +181,23 @@ int dattn_decode_tiered_f16(const dattn_params* p, const float* q, const uint16_
                             const int32_t* cold_block_table, const int32_t* seq_lens, const int32_t* cold_lens,
                             const int32_t* q_pos, void* out, float* lse, void* workspace, size_t workspace_bytes,
                             void* stream);
+
+/*
+ * Sliding-window ring f16 cache (doppler attention_f16kv.wgsl, get_kv_pos
+ * with the ring layout): each sequence owns W = p->sliding_window slots and
+ * token t lives at slot t % W, so only the last W tokens,
+ * [max(0, seq_lens[b] - W), seq_lens[b]), are resident; the visible keys are
+ * those resident keys that pass the causal / window masks (a query before the
+ * last token cannot see keys the ring has already overwritten).
+ *   k_ring, v_ring  [B, W, Hkv, D] f16 (bit patterns); W = p->sliding_window >= 1
+ *   seq_lens        [B] i32, tokens written so far (may exceed W)
+ *   q_pos, out, lse as for dattn_decode_paged
+ * block_size, max_blocks_per_seq and num_blocks in p are ignored.  Workspace
+ * size: kind DATTN_KIND_RING_F16.
+ */
+int dattn_decode_ring_f16(const dattn_params* p, const float* q, const uint16_t* k_ring, const uint16_t* v_ring,
+                          const int32_t* seq_lens, const int32_t* q_pos, void* out, float* lse, void* workspace,
+                          size_t workspace_bytes, void* stream);
 
 /*
  * Block-sparse selection over the paged f16 cache (com.microsoft.SparseAttention

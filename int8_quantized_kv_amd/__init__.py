@@ -16,6 +16,7 @@ Cache layouts (C-contiguous):
   k_cold, v_cold    [num_blocks, bs, Hkv, D/4] int32/uint32 words of 4 int8, LSB first
   k_scale, v_scale  [num_blocks, bs, Hkv]      float16
   k_cold, v_cold    [num_blocks, bs, Hkv, D]   float16 (the tiered f16 cache)
+  k_ring, v_ring    [B, W, Hkv, D]             float16 (the window ring, W = sliding window)
   row_ptr           [num_layouts, rows + 1]    int32
   col_idx           [num_layouts, col_stride]  int32
 Outputs: out [B, H, D] float32 or float16 (out_dtype), lse [B, H] float32;
@@ -30,9 +31,9 @@ from typing import Optional
 
 __all__ = [
     "DattnError", "DattnParams", "lib", "library_path", "dattn_workspace_size", "dattn_decode_paged",
-    "dattn_decode_tiered_int8", "dattn_decode_tiered_f16", "dattn_decode_block_sparse", "dattn_append_tiered_int8", "dattn_last_error",
+    "dattn_decode_tiered_int8", "dattn_decode_tiered_f16", "dattn_decode_ring_f16", "dattn_decode_block_sparse", "dattn_append_tiered_int8", "dattn_last_error",
     "dattn_version",
-    "KIND_PAGED", "KIND_TIERED_INT8", "KIND_BLOCK_SPARSE", "KIND_TIERED_F16", "F32", "F16", "PHASE_ALL", "PHASE_SPLIT",
+    "KIND_PAGED", "KIND_TIERED_INT8", "KIND_BLOCK_SPARSE", "KIND_TIERED_F16", "KIND_RING_F16", "F32", "F16", "PHASE_ALL", "PHASE_SPLIT",
     "PHASE_COMBINE",
 ]
 
@@ -42,7 +43,7 @@ library_path = os.path.join(_HERE, "libdattn.so")
 OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_LAUNCH = 0, -1, -2, -3, -4
 F32, F16 = 0, 1
 PHASE_ALL, PHASE_SPLIT, PHASE_COMBINE = 0, 1, 2
-KIND_PAGED, KIND_TIERED_INT8, KIND_BLOCK_SPARSE, KIND_TIERED_F16 = 0, 1, 2, 3
+KIND_PAGED, KIND_TIERED_INT8, KIND_BLOCK_SPARSE, KIND_TIERED_F16, KIND_RING_F16 = 0, 1, 2, 3, 4
 
 
 class DattnParams(ctypes.Structure):
@@ -90,10 +91,12 @@ def lib():
         L.dattn_decode_paged.argtypes = [PP, P, P, P, i32, P, P, P, P, P, P, sz, P]
         L.dattn_decode_tiered_int8.argtypes = [PP, P, P, P, i32, P, P, P, P, P, P, P, P, P, P, P, sz, P]
         L.dattn_decode_tiered_f16.argtypes = [PP, P, P, P, i32, P, P, P, P, P, P, P, P, P, sz, P]
+        L.dattn_decode_ring_f16.argtypes = [PP, P, P, P, P, P, P, P, P, sz, P]
         L.dattn_decode_block_sparse.argtypes = [PP, P, P, P, P, P, P, i32, i32, P, i32, P, i32, P, P, P, sz, P]
         L.dattn_append_tiered_int8.argtypes = [PP, P, P, P, P, i32, P, P, P, P, P, P, P, P]
         for f in (L.dattn_workspace_size, L.dattn_decode_paged, L.dattn_decode_tiered_int8,
-                  L.dattn_decode_tiered_f16, L.dattn_decode_block_sparse, L.dattn_append_tiered_int8):
+                  L.dattn_decode_tiered_f16, L.dattn_decode_ring_f16, L.dattn_decode_block_sparse,
+                  L.dattn_append_tiered_int8):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -298,6 +301,34 @@ def dattn_decode_tiered_f16(q, k_hot, v_hot, k_cold, v_cold, cold_block_table, s
                                          _ptr(k_cold), _ptr(v_cold), _ptr(cold_block_table), _ptr(seq_lens),
                                          _ptr(cold_lens), _ptr(q_pos), _ptr(out), _ptr(lse), _ptr(workspace),
                                          workspace.numel(), _stream(stream)))
+    return out, lse
+
+
+def dattn_decode_ring_f16(q, k_ring, v_ring, seq_lens, *, q_pos=None, scale: float = 0.0, causal: bool = True,
+                          softcap: float = 0.0, max_seq_len: Optional[int] = None, split_tokens: int = 0, out=None,
+                          lse=None, want_lse: bool = True, workspace=None, stream=None, phases: int = PHASE_ALL,
+                          out_dtype=None, want_out: bool = True):
+    """Decode attention over a sliding-window ring [B, W, Hkv, D] f16 (the window is W,
+    the ring's slot count); returns (out, lse)."""
+    torch = _torch()
+    dev = q.device
+    _need(q, "q", (torch.float32,), 3, dev)
+    _need(k_ring, "k_ring", (torch.float16,), 4, dev)
+    _need(v_ring, "v_ring", (torch.float16,), 4, dev)
+    _need(seq_lens, "seq_lens", (torch.int32,), 1, dev)
+    if q_pos is not None:
+        _need(q_pos, "q_pos", (torch.int32,), 1, dev)
+    B, H, D = q.shape
+    Bk, W, Hkv, Dk = k_ring.shape
+    if Bk != B or Dk != D or tuple(v_ring.shape) != tuple(k_ring.shape) or seq_lens.shape[0] != B:
+        raise ValueError("ring tensors disagree on shape")
+    p = _params(q, Hkv, D, 1, 1, 1, _max_len(seq_lens, max_seq_len), scale, causal, W, softcap, split_tokens,
+                phases, out_dtype)
+    ws = dattn_workspace_size(p, KIND_RING_F16)
+    out, lse, workspace = _outputs(q, out, lse, want_lse, workspace, ws, out_dtype, want_out)
+    _check(lib().dattn_decode_ring_f16(ctypes.byref(p), _ptr(q), _ptr(k_ring), _ptr(v_ring), _ptr(seq_lens),
+                                       _ptr(q_pos), _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
+                                       _stream(stream)))
     return out, lse
 
 

@@ -40,6 +40,7 @@ struct Plan {
   int num_splits = 0;
   int sparse_nblk = 0;       // sparse
   int waves = 0;             // kv heads per workgroup
+  bool no_table = false;     // the cache has no block table to stage (window ring)
   size_t lds = 0;
   size_t acc_bytes = 0, ml_bytes = 0;  // static-split layout
   bool balanced_ok = false;            // the balanced schedule may be used (decided at launch)
@@ -80,7 +81,19 @@ int device_cus() {
   return it->second;
 }
 
-bool is_tiered(int kind) { return kind == DATTN_KIND_TIERED_INT8 || kind == DATTN_KIND_TIERED_F16; }
+// Kinds whose block table (if any) maps only part of the sequence.
+bool is_tiered(int kind) {
+  return kind == DATTN_KIND_TIERED_INT8 || kind == DATTN_KIND_TIERED_F16 || kind == DATTN_KIND_RING_F16;
+}
+
+// The ring has no pool or block table: its fields in p are ignored.
+dattn_params ring_params(const dattn_params* p) {
+  dattn_params r = *p;
+  r.block_size = 1;
+  r.max_blocks_per_seq = 1;
+  r.num_blocks = 1;
+  return r;
+}
 
 int check_params(const dattn_params* p, int kind) {
   if (!p) return fail(DATTN_ERR_INVALID, "params is NULL");
@@ -153,7 +166,8 @@ int make_plan(const dattn_params* p, int kind, int32_t sparse_block, Plan& pl) {
     pl.split_tokens = choose_split(p, L);
     pl.num_splits = (int)((L + pl.split_tokens - 1) / pl.split_tokens);
     if (pl.num_splits < 1) pl.num_splits = 1;
-    pl.lds = ((size_t)pl.split_tokens / p->block_size + 2) * sizeof(int32_t);
+    pl.no_table = kind == DATTN_KIND_RING_F16;
+    pl.lds = pl.no_table ? 16 : ((size_t)pl.split_tokens / p->block_size + 2) * sizeof(int32_t);
   } else if (kind == DATTN_KIND_BLOCK_SPARSE) {
     if (sparse_block < 1 || sparse_block % p->block_size)
       return fail(DATTN_ERR_INVALID, "sparse_block (%d) must be a positive multiple of block_size (%d)", sparse_block,
@@ -245,7 +259,7 @@ Balanced plan_balanced(const dattn_params* p, const Plan& pl, const void* fn) {
   const int64_t tmax = ((int64_t)p->max_seq_len + 15) / 16 + 1;
   const int64_t nmax = (int64_t)p->num_seqs * (2 * tmax + dattn::kSeqUnits);
   const int64_t cmax = (nmax + bl.workers - 1) / bl.workers;
-  const int64_t entries = cmax * 16 / p->block_size + 2;
+  const int64_t entries = pl.no_table ? 0 : cmax * 16 / p->block_size + 2;
   bl.lds = (size_t)(((p->num_seqs + 4) & ~3) + entries) * sizeof(int32_t);
   bl.on = bl.lds <= kMaxBalancedLds;
   return bl;
@@ -356,6 +370,11 @@ int dattn_workspace_size(const dattn_params* p, int32_t kind, int32_t sparse_blo
   g_err.clear();
   if (!bytes) return fail(DATTN_ERR_INVALID, "bytes is NULL");
   Plan pl;
+  dattn_params rp;
+  if (p && kind == DATTN_KIND_RING_F16) {
+    rp = ring_params(p);
+    p = &rp;
+  }
   int rc = make_plan(p, kind, sparse_block, pl);
   if (rc) return rc;
   *bytes = pl.workspace;
@@ -455,6 +474,37 @@ int dattn_decode_tiered_f16(const dattn_params* p, const float* q, const uint16_
   a.q_pos = q_pos;
   const bool cap = p->softcap > 0.0f;
   const bool contig = p->block_size % 16 == 0 && hot_window % 16 == 0;
+  return launch(dattn::split_kernel(dattn::kTieredF16, p->head_dim, cap, pl.G, contig),
+                dattn::split_kernel(dattn::kBalTieredF16, p->head_dim, cap, pl.G, contig), p, pl, a, out, lse,
+                (hipStream_t)stream);
+}
+
+int dattn_decode_ring_f16(const dattn_params* p_in, const float* q, const uint16_t* k_ring, const uint16_t* v_ring,
+                          const int32_t* seq_lens, const int32_t* q_pos, void* out, float* lse, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  if (!p_in) return fail(DATTN_ERR_INVALID, "params is NULL");
+  const dattn_params rp = ring_params(p_in);
+  const dattn_params* p = &rp;
+  Plan pl;
+  int rc = make_plan(p, DATTN_KIND_RING_F16, 0, pl);
+  if (rc) return rc;
+  const int W = p->sliding_window;
+  if (W < 1) return fail(DATTN_ERR_INVALID, "the window ring needs sliding_window >= 1 (its slot count)");
+  if ((int64_t)p->num_seqs * W > INT32_MAX) return fail(DATTN_ERR_UNSUPPORTED, "num_seqs * sliding_window must fit in int32");
+  if (p->num_seqs == 0) return DATTN_OK;
+  if ((rc = check_io(p, q && k_ring && v_ring && seq_lens, out, lse))) return rc;
+  if ((rc = check_workspace(pl, workspace, workspace_bytes))) return rc;
+  dattn::DecodeArgs a = base_args(p, pl, q, workspace);
+  a.k_hot = k_ring;
+  a.v_hot = v_ring;
+  a.hot_window = W;
+  a.hw = dattn::make_fastdiv((uint32_t)W);
+  a.ring = 1;
+  a.seq_lens = seq_lens;
+  a.q_pos = q_pos;
+  const bool cap = p->softcap > 0.0f;
+  const bool contig = W % 16 == 0;
   return launch(dattn::split_kernel(dattn::kTieredF16, p->head_dim, cap, pl.G, contig),
                 dattn::split_kernel(dattn::kBalTieredF16, p->head_dim, cap, pl.G, contig), p, pl, a, out, lse,
                 (hipStream_t)stream);

@@ -84,6 +84,7 @@ struct DecodeArgs {
   int32_t* sched;            // balanced: N, C, P[0..B]
   int32_t num_seqs, num_heads, num_kv_heads, max_blocks, num_splits, split_tokens;
   int32_t causal, window, hot_window;
+  int32_t ring;   // 1: the ring holds only the last hot_window tokens (no cold tier)
   int32_t sparse_block, num_layouts, row_stride, col_stride, sparse_nblk;
   float qmul;    // scale * log2(e) without softcap, 2 log2(e) * scale / cap with softcap
   float capl2;   // cap * log2(e), 0 without softcap
@@ -152,12 +153,14 @@ __device__ __forceinline__ float softcap_l2(float y, float capl2) {
 
 // Visible absolute key range [lo, hi] of sequence b (hi < lo when empty):
 // causal keeps t <= q, a window W keeps t >= q-W+1 once q >= W
-// (doppler is_masked), and keys exist only below seq_lens[b].
+// (doppler is_masked), and keys exist only below seq_lens[b] -- in a window
+// ring only the last hot_window of them (the ring layout's kv_start).
 __device__ __forceinline__ void visible_range(const DecodeArgs& a, int b, int& lo, int& hi, int& qpos) {
   int L = a.seq_lens[b];
   int q = a.q_pos ? a.q_pos[b] : L - 1;
   hi = a.causal ? min(q, L - 1) : L - 1;
   lo = (a.window > 0 && q >= a.window) ? q - a.window + 1 : 0;
+  if (a.ring) lo = max(lo, L - a.hot_window);   // older tokens were overwritten
   qpos = q;
 }
 
@@ -1000,7 +1003,7 @@ __device__ __forceinline__ void paged_segment(const DecodeArgs& a, int b, int kv
 template <int D, int G, bool CAP, bool FM, bool CF16>
 __device__ __forceinline__ void tiered_segment(const DecodeArgs& a, int b, int kvh, int lane, int tb, int te,
                                                int32_t* lds_tbl, const PartialDst& dst) {
-  const int C = a.cold_lens[b];
+  const int C = a.cold_lens ? a.cold_lens[b] : 0;   // no cold tier: a window ring
   const int ce = min(te, C);   // cold part [tb, ce)
   const int hb = max(tb, C);   // hot part  [hb, te)
   QRaw16<D> qraw;              // int8 cold keys use the int8 dim map, f16 keys the f16 one

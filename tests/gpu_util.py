@@ -47,6 +47,9 @@ class DeviceCase:
             self.v_cold = dev(c.v_cold, device)
             self.cold_block_table = dev(c.cold_block_table, device)
             self.cold_lens = dev(c.cold_lens, device)
+        if c.kind == "ring":
+            self.k_ring = dev(c.k_hot, device)
+            self.v_ring = dev(c.v_hot, device)
         if c.kind == "tiered":
             self.k_scale = dev(c.k_scale, device)
             self.v_scale = dev(c.v_scale, device)
@@ -71,6 +74,9 @@ class DeviceCase:
             return dk.dattn_decode_tiered_int8(self.q, self.k_hot, self.v_hot, self.k_cold, self.v_cold,
                                                self.k_scale, self.v_scale, self.cold_block_table, self.seq_lens,
                                                self.cold_lens, **kw)
+        if c.kind == "ring":
+            kw.pop("sliding_window")
+            return dk.dattn_decode_ring_f16(self.q, self.k_ring, self.v_ring, self.seq_lens, **kw)
         if c.kind == "tiered_f16":
             return dk.dattn_decode_tiered_f16(self.q, self.k_hot, self.v_hot, self.k_cold, self.v_cold,
                                               self.cold_block_table, self.seq_lens, self.cold_lens, **kw)

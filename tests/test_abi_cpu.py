@@ -30,7 +30,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("dattn_decode_paged", "dattn_decode_tiered_int8", "dattn_decode_tiered_f16", "dattn_decode_block_sparse",
+    for n in ("dattn_decode_paged", "dattn_decode_tiered_int8", "dattn_decode_tiered_f16", "dattn_decode_ring_f16",
+              "dattn_decode_block_sparse",
               "dattn_append_tiered_int8", "dattn_workspace_size", "dattn_last_error", "dattn_version"):
         assert n in names
 
@@ -193,6 +194,16 @@ def test_decode_calls_validate_before_any_hip_call(lib):
     assert rc == dk.ERR_INVALID and "hot_window" in dk.dattn_last_error()
     rc = lib.dattn_decode_tiered_f16(ctypes.byref(p), fake, fake, fake, 16, None, fake, fake, fake, fake, None, fake,
                                      None, fake, 1 << 20, None)
+    assert rc == dk.ERR_INVALID and "NULL" in dk.dattn_last_error()
+    # window ring: needs a window (its slot count); pool fields are ignored
+    for kw, word in ((dict(sliding_window=0), "sliding_window"), (dict(sliding_window=64, head_dim=80), "head_dim")):
+        pr = good_params(**kw)
+        rc = lib.dattn_decode_ring_f16(ctypes.byref(pr), fake, fake, fake, fake, None, fake, None, fake, 1 << 20, None)
+        assert rc in (dk.ERR_INVALID, dk.ERR_UNSUPPORTED) and word in dk.dattn_last_error(), kw
+    pr = good_params(sliding_window=64, block_size=0, num_blocks=0, max_blocks_per_seq=0, max_seq_len=5000)
+    rc, n, _ = ws_size(lib, pr, kind=dk.KIND_RING_F16)
+    assert rc == 0 and n > 0
+    rc = lib.dattn_decode_ring_f16(ctypes.byref(pr), fake, None, fake, fake, None, fake, None, fake, 1 << 30, None)
     assert rc == dk.ERR_INVALID and "NULL" in dk.dattn_last_error()
     # combine-only phase does not need the inputs, but needs out or lse
     pc = good_params(phases=dk.PHASE_COMBINE)
