@@ -53,6 +53,7 @@ class _Params(ctypes.Structure):
         ("block_size", ctypes.c_int32),
         ("max_blocks_per_seq", ctypes.c_int32),
         ("num_blocks", ctypes.c_int32),
+        ("query_len", ctypes.c_int32),
     ]
 
 
@@ -69,11 +70,12 @@ class Params:
     block_size: int = 16
     max_blocks_per_seq: int = 0
     num_blocks: int = 0
+    query_len: int = 1
 
     def c(self) -> _Params:
         return _Params(self.num_seqs, self.num_heads, self.num_kv_heads, self.head_dim,
                        self.scale, self.causal, self.sliding_window, self.softcap,
-                       self.block_size, self.max_blocks_per_seq, self.num_blocks)
+                       self.block_size, self.max_blocks_per_seq, self.num_blocks, self.query_len)
 
 
 _libs = {}
@@ -140,7 +142,7 @@ def _arr(a, dtype):
 
 def _pairs(p: Params, pairs):
     if pairs is None:
-        return None, p.num_seqs * p.num_heads
+        return None, p.num_seqs * max(1, p.query_len) * p.num_heads
     pa = np.ascontiguousarray(np.asarray(pairs, dtype=np.int32))
     return pa, int(pa.size)
 

@@ -28,6 +28,13 @@
  *                                             lse write of paged_attention_fwd_f32
  *   empty V: out = 0, lse = -inf.
  *
+ * Multi-query decode (query_len = Qn > 1): q holds Qn query rows per
+ * sequence, [B, Qn, H, D]; query i of sequence b sits at absolute position
+ * q0 + i with q0 = q_pos[b], or L - Qn when q_pos is not given (the queries
+ * are the last Qn tokens of the cache), and each query has its own visible
+ * set (doppler attention_f16kv.wgsl: abs_query = query_pos + start_pos in
+ * is_masked).  Outputs are [B, Qn, H, D] and [B, Qn, H].
+ *
  * The softmax is evaluated as the plain two-pass definition (max, then
  * exp-sum and weighted sum), in double precision, with no online rescaling.
  *
@@ -101,6 +108,7 @@ typedef struct {
   int32_t block_size;
   int32_t max_blocks_per_seq;
   int32_t num_blocks;     /* rows of the physical pool, for bounds checks */
+  int32_t query_len;      /* queries per sequence; 0 or 1 => one */
 } orc_params;
 
 /* ---------------------------------------------------------------- scalars */
@@ -246,7 +254,8 @@ static void ring_fetch(const void* vsrc, int32_t b, int32_t g, int64_t t, int32_
 /* -------------------------------------------------------------- attention */
 
 /* Attention of one query head over an explicit list of visible tokens. */
-static int head_attend(const orc_params* p, const float* q, int32_t b, int32_t h, const int64_t* toks,
+/* q row `qrow` (flat index into [B, Qn, H]) of sequence b and query head h. */
+static int head_attend(const orc_params* p, const float* q, int64_t qrow, int32_t b, int32_t h, const int64_t* toks,
                        int64_t n, row_fn fetch, const void* src, double* out, double* lse) {
   int32_t D = p->head_dim;
   int32_t g = h / (p->num_heads / p->num_kv_heads);
@@ -265,7 +274,7 @@ static int head_attend(const orc_params* p, const float* q, int32_t b, int32_t h
     free(qv), free(row), free(acc), free(s);
     return ORC_ENOMEM;
   }
-  for (int32_t d = 0; d < D; ++d) qv[d] = (double)q[((int64_t)b * p->num_heads + h) * D + d];
+  for (int32_t d = 0; d < D; ++d) qv[d] = (double)q[qrow * D + d];
 
   /* pass 1: scores, then their maximum */
   double M = -INFINITY;
@@ -297,7 +306,7 @@ static int check_common(const orc_params* p) {
   if (p->num_seqs < 0 || p->num_heads <= 0 || p->num_kv_heads <= 0 || p->head_dim <= 0) return ORC_EINVAL;
   if (p->num_heads % p->num_kv_heads) return ORC_EINVAL;
   if (p->block_size <= 0 || p->max_blocks_per_seq < 0 || p->num_blocks < 0) return ORC_EINVAL;
-  if (p->sliding_window < 0) return ORC_EINVAL;
+  if (p->sliding_window < 0 || p->query_len < 0) return ORC_EINVAL;
   return ORC_OK;
 }
 
@@ -313,8 +322,11 @@ static int check_table(const orc_params* p, const int32_t* table, int32_t b, int
   return ORC_OK;
 }
 
-static int64_t query_pos(const int32_t* q_pos, const int32_t* seq_lens, int32_t b) {
-  return q_pos ? (int64_t)q_pos[b] : (int64_t)seq_lens[b] - 1;
+static int32_t queries(const orc_params* p) { return p->query_len > 1 ? p->query_len : 1; }
+
+/* Absolute position of query i of sequence b. */
+static int64_t query_pos(const orc_params* p, const int32_t* q_pos, const int32_t* seq_lens, int32_t b, int32_t i) {
+  return (q_pos ? (int64_t)q_pos[b] : (int64_t)seq_lens[b] - queries(p)) + i;
 }
 
 /* Sparse selection for one head: sel[j] = 1 iff block j <= r is a column of
@@ -346,7 +358,8 @@ static int sparse_select(const sparse_csr* c, int32_t h, int64_t q, unsigned cha
 static int run_pairs(const orc_params* p, const float* q, const int32_t* seq_lens, const int32_t* q_pos,
                      const sparse_csr* csr, int32_t resident, row_fn fetch, const void* src, const int32_t* pairs,
                      int32_t npairs, int32_t nthreads, double* out, double* lse) {
-  int64_t total = (int64_t)p->num_seqs * p->num_heads;
+  const int32_t Qn = queries(p);
+  int64_t total = (int64_t)p->num_seqs * Qn * p->num_heads;
   if (!pairs) npairs = (int32_t)total;
   for (int32_t i = 0; i < npairs; ++i)
     if (pairs && (pairs[i] < 0 || pairs[i] >= total)) return ORC_EINVAL;
@@ -356,10 +369,11 @@ static int run_pairs(const orc_params* p, const float* q, const int32_t* seq_len
 #pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
 #endif
   for (int32_t i = 0; i < npairs; ++i) {
-    int32_t flat = pairs ? pairs[i] : i;
-    int32_t b = flat / p->num_heads, h = flat % p->num_heads;
+    int32_t flat = pairs ? pairs[i] : i;   /* (b * Qn + query) * H + h */
+    int32_t h = flat % p->num_heads, bq = flat / p->num_heads;
+    int32_t b = bq / Qn, qi = bq % Qn;
     int64_t L = seq_lens[b];
-    int64_t qp = query_pos(q_pos, seq_lens, b);
+    int64_t qp = query_pos(p, q_pos, seq_lens, b, qi);
     int64_t* toks = (int64_t*)malloc(sizeof(int64_t) * (size_t)(L > 0 ? L : 1));
     unsigned char* sel = NULL;
     int local = toks ? ORC_OK : ORC_ENOMEM;
@@ -376,7 +390,7 @@ static int run_pairs(const orc_params* p, const float* q, const int32_t* seq_len
         if (csr && !sel[t / csr->sparse_block]) continue;
         toks[n++] = t;
       }
-      local = head_attend(p, q, b, h, toks, n, fetch, src, out + (int64_t)i * p->head_dim, lse + i);
+      local = head_attend(p, q, flat, b, h, toks, n, fetch, src, out + (int64_t)i * p->head_dim, lse + i);
     }
     free(toks);
     free(sel);

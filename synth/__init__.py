@@ -31,10 +31,10 @@ import numpy as np
 F32, F16 = "f32", "f16"
 
 
-def _params(B, H, Hkv, D, bs, max_blocks, num_blocks, scale=0.0, causal=1, window=0, softcap=0.0):
+def _params(B, H, Hkv, D, bs, max_blocks, num_blocks, scale=0.0, causal=1, window=0, softcap=0.0, query_len=1):
     return dict(num_seqs=int(B), num_heads=int(H), num_kv_heads=int(Hkv), head_dim=int(D), scale=float(scale),
                 causal=int(causal), sliding_window=int(window), softcap=float(softcap), block_size=int(bs),
-                max_blocks_per_seq=int(max_blocks), num_blocks=int(num_blocks))
+                max_blocks_per_seq=int(max_blocks), num_blocks=int(num_blocks), query_len=int(query_len))
 
 
 @dataclass
@@ -112,21 +112,23 @@ def pool_table(rng, lens, bs, permute=True, extra_blocks=0):
 
 
 def paged_case(seed, B, H, Hkv, D, bs, lens=None, kv_dtype=F16, permute=True, q_pos=None, causal=1, window=0,
-               softcap=0.0, scale=0.0, extra_blocks=0, len_range=None, name="") -> Case:
+               softcap=0.0, scale=0.0, extra_blocks=0, len_range=None, name="", query_len=1) -> Case:
+    """query_len > 1: q is [B, query_len, H, D], query i of sequence b at position
+    q_pos[b] + i (q_pos[b] defaults to seq_lens[b] - query_len)."""
     rng = np.random.default_rng(seed)
     if lens is None:
         lo, hi = len_range
         lens = rng.integers(lo, hi + 1, size=B)
     lens = np.asarray(lens, np.int32)
-    q = rng.standard_normal((B, H, D), dtype=np.float32)
+    q = rng.standard_normal((B, H, D) if query_len == 1 else (B, query_len, H, D), dtype=np.float32)
     nblk = (lens.astype(np.int64) + bs - 1) // bs
     pool = max(int(nblk.sum()) + extra_blocks, 1)
     k = _normal(rng, (pool, bs, Hkv, D), kv_dtype)
     v = _normal(rng, (pool, bs, Hkv, D), kv_dtype)
     table, _ = pool_table(rng, lens, bs, permute, extra_blocks)
     qp = None if q_pos is None else np.asarray(q_pos, np.int32)
-    return Case("paged", _params(B, H, Hkv, D, bs, table.shape[1], pool, scale, causal, window, softcap), q, lens,
-                qp, k_cache=k, v_cache=v, block_table=table, name=name)
+    return Case("paged", _params(B, H, Hkv, D, bs, table.shape[1], pool, scale, causal, window, softcap, query_len),
+                q, lens, qp, k_cache=k, v_cache=v, block_table=table, name=name)
 
 
 # ------------------------------------------------------------------ int8 tier
@@ -416,6 +418,15 @@ def ring_workload() -> Case:
     lens = rng.integers(4096, 32769, size=32)
     return ring_case(7, 32, 32, 8, 128, 4096, lens, history=False, scale=float(np.float32(1.0 / math.sqrt(128))),
                      name="ring_f16_B32_H32x8_D128_W4096")
+
+
+def multi_query_workload(query_len: int = 4) -> Case:
+    """Multi-query (speculative) decode over workload 2's paged f16 cache shape:
+    B=32, 32/8 heads, D=128, bs=16, L ~ U{512..4096}, permuted pool, causal; the
+    last query_len tokens of each sequence are the queries."""
+    return paged_case(8, 32, 32, 8, 128, 16, len_range=(512, 4096), kv_dtype=F16, query_len=query_len,
+                      scale=float(np.float32(1.0 / math.sqrt(128))),
+                      name=f"paged_f16_mq{query_len}_B32_H32x8_D128_L512-4096")
 
 
 def tiered_f16_workload(window: int = 0) -> Case:

@@ -60,12 +60,17 @@ def logical_rows(case, b):
     return K, V
 
 
-def visible_matrix(case, b):
-    """bool [H, L]: which keys each query head of sequence b attends to."""
+def query_len(case):
+    return max(1, int(case.params.get("query_len", 1)))
+
+
+def visible_matrix(case, b, i=0):
+    """bool [H, L]: which keys each head of query i of sequence b attends to (query i
+    at position q_pos[b] + i, q_pos[b] defaulting to L - query_len)."""
     p = case.params
     H = p["num_heads"]
     L = int(case.seq_lens[b])
-    q = int(case.q_pos[b]) if case.q_pos is not None else L - 1
+    q = (int(case.q_pos[b]) if case.q_pos is not None else L - query_len(case)) + i
     t = np.arange(L)
     ok = np.ones(L, bool)
     if p["causal"]:
@@ -90,29 +95,35 @@ def visible_matrix(case, b):
 
 
 def attend(case):
-    """(out [B, H, D], lse [B, H]) in float64."""
+    """(out [B, H, D], lse [B, H]) in float64; with query_len Qn > 1,
+    (out [B, Qn, H, D], lse [B, Qn, H])."""
     p = case.params
     B, H, Hkv, D = p["num_seqs"], p["num_heads"], p["num_kv_heads"], p["head_dim"]
+    Qn = query_len(case)
     G = H // Hkv
     sc = scale_of(p)
     cap = float(p["softcap"])
-    out = np.zeros((B, H, D))
-    lse = np.full((B, H), -np.inf)
+    qs = case.q.reshape(B, Qn, H, D)
+    out = np.zeros((B, Qn, H, D))
+    lse = np.full((B, Qn, H), -np.inf)
     for b in range(B):
         K, V = logical_rows(case, b)
-        vis = visible_matrix(case, b)
-        qb = case.q[b].astype(np.float64)                     # [H, D]
         Kh = np.repeat(K, G, axis=1).transpose(1, 0, 2)       # [H, L, D]
         Vh = np.repeat(V, G, axis=1).transpose(1, 0, 2)
-        s = sc * np.einsum("hd,hld->hl", qb, Kh)
-        if cap > 0:
-            s = cap * np.tanh(s / cap)
-        for h in range(H):
-            if not vis[h].any():
-                continue
-            sv = s[h][vis[h]]
-            out[b, h] = softmax(sv) @ Vh[h][vis[h]]
-            lse[b, h] = logsumexp(sv)
+        for i in range(Qn):
+            vis = visible_matrix(case, b, i)
+            qb = qs[b, i].astype(np.float64)                  # [H, D]
+            s = sc * np.einsum("hd,hld->hl", qb, Kh)
+            if cap > 0:
+                s = cap * np.tanh(s / cap)
+            for h in range(H):
+                if not vis[h].any():
+                    continue
+                sv = s[h][vis[h]]
+                out[b, i, h] = softmax(sv) @ Vh[h][vis[h]]
+                lse[b, i, h] = logsumexp(sv)
+    if Qn == 1:
+        return out[:, 0], lse[:, 0]
     return out, lse
 
 

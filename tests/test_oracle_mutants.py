@@ -54,9 +54,15 @@ MUTANTS = {
     "ring_keeps_one_more": ("if (resident > 0 && t < L - resident) continue;",
                             "if (resident > 0 && t < L - resident - 1) continue;"),
     "ring_residency_ignored": ("if (resident > 0 && t < L - resident) continue;", "(void)resident;"),
+    "mq_all_queries_at_first_position": (
+        "return (q_pos ? (int64_t)q_pos[b] : (int64_t)seq_lens[b] - queries(p)) + i;",
+        "return (q_pos ? (int64_t)q_pos[b] : (int64_t)seq_lens[b] - queries(p)) + 0 * i;"),
+    "mq_default_start_at_last_token": ("(int64_t)seq_lens[b] - queries(p)) + i;", "(int64_t)seq_lens[b] - 1) + i;"),
+    "mq_query_rows_transposed": ("int32_t b = bq / Qn, qi = bq % Qn;",
+                                 "int32_t b = bq % p->num_seqs, qi = bq / p->num_seqs;"),
 }
 PIN_FILES = ["test_oracle_pins.py", "test_oracle_append_pins.py", "test_oracle_tiered_f16_pins.py",
-             "test_oracle_ring_pins.py"]
+             "test_oracle_ring_pins.py", "test_oracle_multi_query_pins.py"]
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
