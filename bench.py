@@ -46,8 +46,9 @@ def log(msg):
 def visible_range(case, b):
     p = case.params
     L = int(case.seq_lens[b])
-    q = int(case.q_pos[b]) if case.q_pos is not None else L - 1
-    hi = min(q, L - 1) if p["causal"] else L - 1
+    qn = max(1, p.get("query_len", 1))
+    q = int(case.q_pos[b]) if case.q_pos is not None else L - qn
+    hi = min(q + qn - 1, L - 1) if p["causal"] else L - 1
     W = p["sliding_window"]
     lo = q - W + 1 if (W > 0 and q >= W) else 0
     if case.kind == "ring":
@@ -57,8 +58,9 @@ def visible_range(case, b):
 
 def kv_bytes(case) -> int:
     """Algorithmic KV bytes of one decode call: K + V (+ int8 scales) of each visible
-    (token, kv head) row once per (sequence, kv head); for the block-sparse cache a row
-    counts once for the union of the blocks its GQA group selects."""
+    (token, kv head) row once per (sequence, kv head) -- with several queries per
+    sequence, a row visible to any of them; for the block-sparse cache a row counts
+    once for the union of the blocks its GQA group selects."""
     p = case.params
     B, H, Hkv, D = p["num_seqs"], p["num_heads"], p["num_kv_heads"], p["head_dim"]
     G = H // Hkv
@@ -117,9 +119,10 @@ class Runner:
         self.q = T(c.q)
         self.seq_lens = T(c.seq_lens)
         self.q_pos = T(c.q_pos) if c.q_pos is not None else None
-        B, H, D = c.q.shape
-        self.out = torch.empty((B, H, D), dtype=torch.float32, device=dev)
-        self.lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+        B, H, D = c.q.shape[0], c.q.shape[-2], c.q.shape[-1]
+        qn = max(1, p.get("query_len", 1))
+        self.out = torch.empty(c.q.shape, dtype=torch.float32, device=dev)
+        self.lse = torch.empty(c.q.shape[:-1], dtype=torch.float32, device=dev)
         max_len = int(c.seq_lens.max())
         if c.kind in ("tiered", "tiered_f16"):
             NB, bs = c.k_cold.shape[0], c.k_cold.shape[1]
@@ -134,7 +137,7 @@ class Runner:
 
         def params(phases):
             return dk.DattnParams(B, H, p["num_kv_heads"], D, p["scale"], p["causal"], p["sliding_window"],
-                                  p["softcap"], bs, mb, NB, max_len, 0, phases)
+                                  p["softcap"], bs, mb, NB, max_len, 0, phases, dk.F32, qn)
 
         self.p_all, self.p_split, self.p_comb = params(0), params(dk.PHASE_SPLIT), params(dk.PHASE_COMBINE)
         ws = dk.dattn_workspace_size(self.p_all, kind, c.sparse_block)
@@ -377,7 +380,7 @@ def line_for(case, steps, warmup, check=True):
     import synth  # noqa: F401
     kvb = kv_bytes(case)
     r, m = measure(case, steps, warmup)
-    B = case.params["num_seqs"]
+    B = case.params["num_seqs"] * max(1, case.params.get("query_len", 1))   # query tokens per call
     res = dict(workload=case.name, kv_bytes=kvb, ms_per_call=round(m["wall_s"] * 1e3, 5),
                kv_gbs=round(kvb / m["wall_s"] / 1e9, 2), pct_peak=round(100 * kvb / m["wall_s"] / 1e9 / HBM_PEAK_GBS, 2),
                queries_per_s=round(B / m["wall_s"], 1), split_ms=round(m["split_ms"], 5),
@@ -389,7 +392,7 @@ def line_for(case, steps, warmup, check=True):
         out, lse = r.result()
         p = case.params
         rng = np.random.default_rng(0)
-        nb = p["num_seqs"] * p["num_heads"]
+        nb = p["num_seqs"] * max(1, p.get("query_len", 1)) * p["num_heads"]
         pairs = np.unique(np.concatenate([[0, nb - 1], rng.integers(0, nb, 14)])).astype(np.int32)
         ro, rl = oracle.run(case, pairs=pairs)
         go = out.reshape(nb, -1)[pairs]
@@ -403,12 +406,15 @@ def line_for(case, steps, warmup, check=True):
 
 def workload(idx, window=0):
     """Workloads 1-5 of the input generators, 6: the tiered workload's shape
-    with an f16 cold tier, 7: a sliding-window ring f16 cache."""
+    with an f16 cold tier, 7: a sliding-window ring f16 cache, 8: four queries
+    per sequence over a paged f16 cache of workload 2's shape."""
     import synth
     if idx == 6:
         return synth.tiered_f16_workload(window)
     if idx == 7:
         return synth.ring_workload()
+    if idx == 8:
+        return synth.multi_query_workload(4)
     return synth.config(idx, window=window)
 
 
@@ -421,7 +427,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", type=int, default=2,
                     help="headline workload index (default 2; 6 = the tiered workload with an f16 cold tier, "
-                         "7 = a sliding-window ring f16 cache)")
+                         "7 = a sliding-window ring f16 cache, 8 = four queries per sequence)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run 5 device copies of MIB MiB (for scaling memory counters)")
     args = ap.parse_args()
@@ -448,7 +454,7 @@ def main():
     kvb = head["kv_bytes"]
     split_s = m["split_ms"] / 1e3
     achieved = kvb / split_s / 1e9
-    B, H, D = case.q.shape
+    B, H, D = case.q.shape[0], case.q.shape[-2], case.q.shape[-1]
     G = H // case.params["num_kv_heads"]
     kind = {"paged": "paged f16" if case.k_cache is not None and case.k_cache.dtype == np.float16 else "paged f32",
             "tiered": "tiered int8 + f16 ring", "tiered_f16": "tiered f16 + f16 ring", "ring": "window ring f16",
@@ -490,7 +496,7 @@ def main():
     if args.all:
         extra = []
         for idx, kw in ((1, {}), (3, dict(window=0)), (3, dict(window=4096)), (4, {}), (5, {}),
-                        (6, dict(window=0)), (6, dict(window=4096)), (7, {})):
+                        (6, dict(window=0)), (6, dict(window=4096)), (7, {}), (8, {})):
             log(f"generating workload {idx} {kw} ...")
             c = workload(idx, **kw)
             res, _ = line_for(c, max(20, args.steps // 4), max(5, args.warmup // 4))

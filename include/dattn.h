@@ -88,6 +88,9 @@ typedef struct dattn_params {
   int32_t out_dtype;          /* storage type of out: DATTN_F32 (0) or DATTN_F16, the f32
                                  result rounded to nearest even (attention.js sizes its output
                                  by the kernel variant's outputDtype, f16 or f32) */
+  int32_t query_len;          /* queries per sequence, 0 or 1 => one; > 1: multi-query decode
+                                 (paged cache only; query_len * GQA group <= 16); see
+                                 dattn_decode_paged */
 } dattn_params;
 
 /*
@@ -131,6 +134,12 @@ int dattn_workspace_size(const dattn_params* p, int32_t kind, int32_t sparse_blo
  *   out          [B, H, D] f32 or f16 per p->out_dtype (written), or NULL to
  *                write lse only (the split kernel still reads K and V)
  *   lse          [B, H] f32 (written), or NULL; out and lse are not both NULL
+ * Multi-query decode (p->query_len = Qn > 1; doppler attention_f16kv.wgsl,
+ * query rows at abs_query = query_pos + start_pos): q is [B, Qn, H, D], query
+ * i of sequence b sits at position q_pos[b] + i (q_pos NULL: seq_lens[b] - Qn,
+ * the last Qn tokens of the cache) with its own causal / window bound; out is
+ * [B, Qn, H, D] and lse [B, Qn, H].  Each K/V row is still read once per
+ * (sequence, kv head), for all Qn * G query rows of the group.
  */
 int dattn_decode_paged(const dattn_params* p, const float* q, const void* k_cache, const void* v_cache,
                        int32_t kv_dtype, const int32_t* block_table, const int32_t* seq_lens,

@@ -64,6 +64,7 @@ class DattnParams(ctypes.Structure):
         ("split_tokens", ctypes.c_int32),
         ("phases", ctypes.c_int32),
         ("out_dtype", ctypes.c_int32),
+        ("query_len", ctypes.c_int32),
     ]
 
 
@@ -158,15 +159,17 @@ def _out_code(out_dtype):
 
 def _params(q, Hkv, D, bs, max_blocks, num_blocks, max_seq_len, scale, causal, sliding_window, softcap,
             split_tokens, phases=PHASE_ALL, out_dtype=None):
-    B, H, _ = q.shape
+    """q is [B, H, D], or [B, Qn, H, D] for Qn queries per sequence."""
+    B, H = q.shape[0], q.shape[-2]
+    qn = q.shape[1] if q.dim() == 4 else 1
     code = F32 if out_dtype is None else _out_code(out_dtype)
     return DattnParams(B, H, Hkv, D, float(scale), int(causal), int(sliding_window), float(softcap), bs, max_blocks,
-                       num_blocks, int(max_seq_len), int(split_tokens), int(phases), code)
+                       num_blocks, int(max_seq_len), int(split_tokens), int(phases), code, qn)
 
 
 def _outputs(q, out, lse, want_lse, workspace, ws_bytes, out_dtype=None, want_out=True):
     torch = _torch()
-    B, H, D = q.shape
+    oshape, lshape = tuple(q.shape), tuple(q.shape[:-1])
     out_dtype = torch.float32 if out_dtype is None else out_dtype
     if not want_out:
         if out is not None:
@@ -174,13 +177,17 @@ def _outputs(q, out, lse, want_lse, workspace, ws_bytes, out_dtype=None, want_ou
         if lse is None and not want_lse:
             raise ValueError("want_out=False needs lse")
     elif out is None:
-        out = torch.empty((B, H, D), dtype=out_dtype, device=q.device)
+        out = torch.empty(oshape, dtype=out_dtype, device=q.device)
     else:
-        _need(out, "out", (out_dtype,), 3, q.device)
+        _need(out, "out", (out_dtype,), len(oshape), q.device)
+        if tuple(out.shape) != oshape:
+            raise ValueError(f"out must have shape {oshape}")
     if lse is None and want_lse:
-        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+        lse = torch.empty(lshape, dtype=torch.float32, device=q.device)
     elif lse is not None:
-        _need(lse, "lse", (torch.float32,), 2, q.device)
+        _need(lse, "lse", (torch.float32,), len(lshape), q.device)
+        if tuple(lse.shape) != lshape:
+            raise ValueError(f"lse must have shape {lshape}")
     if workspace is None:
         workspace = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device=q.device)
     return out, lse, workspace
@@ -204,10 +211,12 @@ def dattn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, *, q_pos=None
                        max_seq_len: Optional[int] = None, split_tokens: int = 0, out=None, lse=None,
                        want_lse: bool = True, workspace=None, stream=None, phases: int = PHASE_ALL,
                        out_dtype=None, want_out: bool = True):
-    """Decode attention over a paged f16/f32 cache; returns (out, lse)."""
+    """Decode attention over a paged f16/f32 cache; returns (out, lse).  q [B, Qn, H, D]
+    asks for Qn queries per sequence (query i at q_pos[b] + i, q_pos defaulting to
+    seq_lens - Qn); out and lse then carry the Qn axis too."""
     torch = _torch()
     dev = q.device
-    _need(q, "q", (torch.float32,), 3, dev)
+    _need(q, "q", (torch.float32,), q.dim() if q.dim() in (3, 4) else 3, dev)
     _need(k_cache, "k_cache", (torch.float16, torch.float32), 4, dev)
     _need(v_cache, "v_cache", (k_cache.dtype,), 4, dev)
     _need(block_table, "block_table", (torch.int32,), 2, dev)
@@ -215,7 +224,7 @@ def dattn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, *, q_pos=None
     if q_pos is not None:
         _need(q_pos, "q_pos", (torch.int32,), 1, dev)
     NB, bs, Hkv, D = k_cache.shape
-    if tuple(v_cache.shape) != tuple(k_cache.shape) or q.shape[2] != D:
+    if tuple(v_cache.shape) != tuple(k_cache.shape) or q.shape[-1] != D:
         raise ValueError("k_cache, v_cache and q disagree on shape")
     if block_table.shape[0] != q.shape[0] or seq_lens.shape[0] != q.shape[0]:
         raise ValueError("block_table / seq_lens must have one row per sequence")

@@ -130,6 +130,13 @@ int check_params(const dattn_params* p, int kind) {
     return fail(DATTN_ERR_INVALID, "phases must be 0..3 (got %d)", p->phases);
   if (p->out_dtype != DATTN_F32 && p->out_dtype != DATTN_F16)
     return fail(DATTN_ERR_INVALID, "out_dtype must be DATTN_F32 or DATTN_F16 (got %d)", p->out_dtype);
+  if (p->query_len < 0) return fail(DATTN_ERR_INVALID, "query_len must be >= 0 (got %d)", p->query_len);
+  if (p->query_len > 1) {
+    if (kind != DATTN_KIND_PAGED)
+      return fail(DATTN_ERR_UNSUPPORTED, "query_len > 1 is built for the paged cache only");
+    if (G * p->query_len > 16)
+      return fail(DATTN_ERR_UNSUPPORTED, "query_len (%d) * GQA group (%d) must be <= 16", p->query_len, G);
+  }
   if (p->split_tokens < 0 || p->split_tokens % 16)
     return fail(DATTN_ERR_INVALID, "split_tokens must be 0 or a positive multiple of 16 (got %d)", p->split_tokens);
   return DATTN_OK;
@@ -197,7 +204,8 @@ int make_plan(const dattn_params* p, int kind, int32_t sparse_block, Plan& pl) {
     return fail(DATTN_ERR_INVALID, "unknown kind %d", kind);
   }
   if (pl.lds > 65536) return fail(DATTN_ERR_UNSUPPORTED, "LDS need %zu exceeds 64 KiB", pl.lds);
-  const size_t heads = (size_t)p->num_seqs * p->num_heads;
+  const size_t qn = p->query_len > 1 ? (size_t)p->query_len : 1;
+  const size_t heads = (size_t)p->num_seqs * p->num_heads * qn;
   pl.acc_bytes = align_up(heads * pl.num_splits * p->head_dim * sizeof(float));
   pl.ml_bytes = align_up(heads * pl.num_splits * sizeof(float2));
   pl.workspace = pl.acc_bytes + pl.ml_bytes;
@@ -205,8 +213,8 @@ int make_plan(const dattn_params* p, int kind, int32_t sparse_block, Plan& pl) {
                    p->num_seqs <= kMaxBalancedSeqs;
   if (pl.balanced_ok) {
     const size_t slots = (size_t)kMaxWorkers + p->num_seqs;
-    pl.bal_acc_bytes = align_up(slots * p->num_heads * p->head_dim * sizeof(float));
-    pl.bal_ml_bytes = align_up(slots * p->num_heads * sizeof(float2));
+    pl.bal_acc_bytes = align_up(slots * p->num_heads * qn * p->head_dim * sizeof(float));
+    pl.bal_ml_bytes = align_up(slots * p->num_heads * qn * sizeof(float2));
     pl.bal_sched_bytes = align_up((size_t)(p->num_seqs + 3) * sizeof(int32_t));
     const size_t bal = pl.bal_acc_bytes + pl.bal_ml_bytes + pl.bal_sched_bytes;
     if (bal > pl.workspace) pl.workspace = bal;
@@ -278,6 +286,9 @@ dattn::DecodeArgs base_args(const dattn_params* p, const Plan& pl, const float* 
   a.split_tokens = pl.split_tokens;
   a.causal = p->causal;
   a.window = p->sliding_window;
+  a.qn = p->query_len > 1 ? p->query_len : 1;
+  a.grp = p->num_heads / p->num_kv_heads;
+  a.heads_out = a.qn * p->num_heads;
   const double scale = p->scale != 0.0f ? (double)p->scale : (double)(float)(1.0 / sqrt((double)p->head_dim));
   const double log2e = 1.4426950408889634;
   if (p->softcap > 0.0f) {
@@ -337,16 +348,16 @@ int launch(void* split_fn, void* bal_fn, const dattn_params* p, const Plan& pl, 
     if (rc) return rc;
   }
   if (!run_combine(p)) return DATTN_OK;
-  const int nbh = p->num_seqs * p->num_heads;
-  const dim3 cgrid(nbh);   // one workgroup per (sequence, head)
+  const int nbh = p->num_seqs * a.heads_out;
+  const dim3 cgrid(nbh);   // one workgroup per (sequence, query, head)
   const int f16 = p->out_dtype == DATTN_F16;
   if (bl.on) {
     if (p->head_dim == 64)
       hipLaunchKernelGGL(dattn::combine_balanced_kernel<64>, cgrid, dim3(256), 0, st, a.part_acc, a.part_ml,
-                         a.sched, out, f16, lse, p->num_heads, nbh);
+                         a.sched, out, f16, lse, a.heads_out, nbh);
     else
       hipLaunchKernelGGL(dattn::combine_balanced_kernel<128>, cgrid, dim3(256), 0, st, a.part_acc, a.part_ml,
-                         a.sched, out, f16, lse, p->num_heads, nbh);
+                         a.sched, out, f16, lse, a.heads_out, nbh);
   } else {
     if (p->head_dim == 64)
       hipLaunchKernelGGL(dattn::combine_kernel<64>, cgrid, dim3(256), 0, st, a.part_acc, a.part_ml, out, f16, lse,
@@ -402,8 +413,15 @@ int dattn_decode_paged(const dattn_params* p, const float* q, const void* k_cach
   const bool cap = p->softcap > 0.0f;
   const bool f16 = kv_dtype == DATTN_F16;
   const bool contig = p->block_size % 16 == 0;
-  void* fn = dattn::split_kernel(f16 ? dattn::kPagedF16 : dattn::kPagedF32, p->head_dim, cap, pl.G, contig);
-  void* bal = dattn::split_kernel(f16 ? dattn::kBalF16 : dattn::kBalF32, p->head_dim, cap, pl.G, contig);
+  void* fn;
+  void* bal;
+  if (a.qn > 1) {   // several queries per sequence: MFMA columns are (query, head) pairs
+    fn = dattn::split_kernel(f16 ? dattn::kPagedF16MQ : dattn::kPagedF32MQ, p->head_dim, cap, 16, contig);
+    bal = dattn::split_kernel(f16 ? dattn::kBalF16MQ : dattn::kBalF32MQ, p->head_dim, cap, 16, contig);
+  } else {
+    fn = dattn::split_kernel(f16 ? dattn::kPagedF16 : dattn::kPagedF32, p->head_dim, cap, pl.G, contig);
+    bal = dattn::split_kernel(f16 ? dattn::kBalF16 : dattn::kBalF32, p->head_dim, cap, pl.G, contig);
+  }
   return launch(fn, bal, p, pl, a, out, lse, (hipStream_t)stream);
 }
 

@@ -85,6 +85,9 @@ struct DecodeArgs {
   int32_t num_seqs, num_heads, num_kv_heads, max_blocks, num_splits, split_tokens;
   int32_t causal, window, hot_window;
   int32_t ring;   // 1: the ring holds only the last hot_window tokens (no cold tier)
+  int32_t qn;         // queries per sequence (multi-query decode), >= 1
+  int32_t grp;        // GQA group size H / Hkv
+  int32_t heads_out;  // qn * num_heads: rows per slot of the partials and of out
   int32_t sparse_block, num_layouts, row_stride, col_stride, sparse_nblk;
   float qmul;    // scale * log2(e) without softcap, 2 log2(e) * scale / cap with softcap
   float capl2;   // cap * log2(e), 0 without softcap
@@ -155,10 +158,12 @@ __device__ __forceinline__ float softcap_l2(float y, float capl2) {
 // causal keeps t <= q, a window W keeps t >= q-W+1 once q >= W
 // (doppler is_masked), and keys exist only below seq_lens[b] -- in a window
 // ring only the last hot_window of them (the ring layout's kv_start).
+// With qn queries per sequence, query i sits at q0 + i (q0 = q_pos[b], or
+// L - qn) and the range is the union over the queries.
 __device__ __forceinline__ void visible_range(const DecodeArgs& a, int b, int& lo, int& hi, int& qpos) {
   int L = a.seq_lens[b];
-  int q = a.q_pos ? a.q_pos[b] : L - 1;
-  hi = a.causal ? min(q, L - 1) : L - 1;
+  int q = a.q_pos ? a.q_pos[b] : L - a.qn;
+  hi = a.causal ? min(q + a.qn - 1, L - 1) : L - 1;
   lo = (a.window > 0 && q >= a.window) ? q - a.window + 1 : 0;
   if (a.ring) lo = max(lo, L - a.hot_window);   // older tokens were overwritten
   qpos = q;
@@ -242,10 +247,25 @@ struct QF16 {
   h8 hi[D / 32], lo[D / 32];
 };
 
-template <int D, int G, bool I8MAP>
+// Row of q (in units of D) for MFMA column j of kv head kvh.  One query per
+// sequence: column j < G is head kvh*G + j.  With qn queries (MQ), column
+// j < grp*qn is query j / grp, head kvh*grp + j % grp, of q [B, qn, H, D].
+// Columns beyond those read row 0 of the group (their Q is zeroed).
+template <int G, bool MQ>
+__device__ __forceinline__ size_t q_row(const DecodeArgs& a, int b, int kvh, int j) {
+  if constexpr (MQ) {
+    const int jj = j < a.grp * a.qn ? j : 0;
+    const int i = jj / a.grp;
+    return ((size_t)b * a.qn + i) * a.num_heads + (size_t)kvh * a.grp + (jj - i * a.grp);
+  } else {
+    return (size_t)b * a.num_heads + (size_t)kvh * G + (j < G ? j : 0);
+  }
+}
+
+template <int D, int G, bool I8MAP, bool MQ = false>
 __device__ __forceinline__ void load_q_raw16(const DecodeArgs& a, int b, int kvh, int lane, QRaw16<D>& r) {
   const int j = lane & 15, g = lane >> 4;
-  const float* qrow = a.q + ((size_t)b * a.num_heads + (size_t)kvh * G + (j < G ? j : 0)) * D;
+  const float* qrow = a.q + q_row<G, MQ>(a, b, kvh, j) * D;
 #pragma unroll
   for (int c = 0; c < D / 32; ++c) {
     const int d0 = qdim<I8MAP>(c, g);
@@ -254,9 +274,9 @@ __device__ __forceinline__ void load_q_raw16(const DecodeArgs& a, int b, int kvh
   }
 }
 
-template <int D, int G>
+template <int D, int G, bool MQ = false>
 __device__ __forceinline__ void convert_q(const DecodeArgs& a, int lane, const QRaw16<D>& r, QF16<D>& qf) {
-  const bool live = (lane & 15) < G;
+  const bool live = (lane & 15) < (MQ ? a.grp * a.qn : G);
 #pragma unroll
   for (int c = 0; c < D / 32; ++c) {
     const float x[8] = {r.x[2 * c].x, r.x[2 * c].y, r.x[2 * c].z, r.x[2 * c].w,
@@ -281,17 +301,17 @@ struct QF32 {
   float v[D / 4];
 };
 
-template <int D, int G>
+template <int D, int G, bool MQ = false>
 __device__ __forceinline__ void load_q_raw32(const DecodeArgs& a, int b, int kvh, int lane, QRaw32<D>& r) {
   const int j = lane & 15, g = lane >> 4;
-  const float* qrow = a.q + ((size_t)b * a.num_heads + (size_t)kvh * G + (j < G ? j : 0)) * D;
+  const float* qrow = a.q + q_row<G, MQ>(a, b, kvh, j) * D;
 #pragma unroll
   for (int m = 0; m < D / 16; ++m) r.x[m] = *(const f4*)(qrow + 16 * m + 4 * g);
 }
 
-template <int D, int G>
+template <int D, int G, bool MQ = false>
 __device__ __forceinline__ void convert_q(const DecodeArgs& a, int lane, const QRaw32<D>& r, QF32<D>& qf) {
-  const bool live = (lane & 15) < G;
+  const bool live = (lane & 15) < (MQ ? a.grp * a.qn : G);
 #pragma unroll
   for (int m = 0; m < D / 16; ++m) {
     qf.v[4 * m + 0] = live ? r.x[m].x * a.qmul : 0.0f;
@@ -769,16 +789,17 @@ struct PartialDst {
   size_t ml_hstride;
 };
 
-// Static splits: partials [B, H, S, D] and [B, H, S].
+// Static splits: partials [B, H, S, D] and [B, H, S] (H -> qn*H with several
+// queries per sequence; G is the GQA group, the column count of one query).
 __device__ __forceinline__ PartialDst split_dst(const DecodeArgs& a, int b, int kvh, int G, int split, int D) {
   const size_t S = (size_t)a.num_splits;
-  const size_t head0 = (size_t)b * a.num_heads + (size_t)kvh * G;
+  const size_t head0 = (size_t)b * a.heads_out + (size_t)kvh * G;
   return PartialDst{a.part_acc + (head0 * S + split) * D, S * D, a.part_ml + head0 * S + split, S};
 }
 
 // Balanced schedule: partials [slots, H, D] and [slots, H].
 __device__ __forceinline__ PartialDst slot_dst(const DecodeArgs& a, int slot, int kvh, int G, int D) {
-  const size_t head0 = (size_t)slot * a.num_heads + (size_t)kvh * G;
+  const size_t head0 = (size_t)slot * a.heads_out + (size_t)kvh * G;
   return PartialDst{a.part_acc + head0 * D, (size_t)D, a.part_ml + head0, 1};
 }
 
@@ -851,11 +872,39 @@ struct Online {
     }
     if (lane < G) dst.ml[lane * dst.ml_hstride] = make_float2(m, lt);
   }
+  // Several queries per sequence: column r < grp*qn is query r / grp, head
+  // r % grp, stored at row (r / grp) * H + r % grp of the partials.
+  __device__ __forceinline__ void finish_mq(const PartialDst& dst, int lane, int grp, int qn, int H) {
+    const float lt = rows_sum(l);
+    const int g = lane >> 4, c = lane & 15, ncols = grp * qn;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 4 * g + e;
+      if (r < ncols) {
+        const int i = r / grp;
+        float* out = dst.acc + (size_t)(i * H + r - i * grp) * dst.acc_hstride + NT * c;
+#pragma unroll
+        for (int t4 = 0; t4 < NT / 4; ++t4)
+          *(f4*)(out + 4 * t4) = f4{o[4 * t4][e], o[4 * t4 + 1][e], o[4 * t4 + 2][e], o[4 * t4 + 3][e]};
+      }
+    }
+    if (lane < ncols) {
+      const int i = lane / grp;
+      dst.ml[(size_t)(i * H + lane - i * grp) * dst.ml_hstride] = make_float2(m, lt);
+    }
+  }
 };
 
 template <int G>
 __device__ __forceinline__ void write_empty(const PartialDst& dst, int lane) {
   if (lane < G) dst.ml[lane * dst.ml_hstride] = make_float2(-__builtin_inff(), 0.f);
+}
+
+__device__ __forceinline__ void write_empty_mq(const PartialDst& dst, int lane, int grp, int qn, int H) {
+  if (lane < grp * qn) {
+    const int i = lane / grp;
+    dst.ml[(size_t)(i * H + lane - i * grp) * dst.ml_hstride] = make_float2(-__builtin_inff(), 0.f);
+  }
 }
 
 // ------------------------------------------------------------ tile engine
@@ -872,10 +921,13 @@ __device__ __forceinline__ void write_empty(const PartialDst& dst, int lane) {
 // products costs accumulator copies at the join).  The Q fragments are
 // prepared after the first loads are on their way.
 
-template <int D, int G, bool CAP, int NBUF, bool FAST, class Store, class Map, class QF, class QPrep>
+//
+// MQ (several queries per sequence): each lane's score column belongs to one
+// query, whose visible keys are [qlo, qhi]; keys outside are masked per lane.
+template <int D, int G, bool CAP, int NBUF, bool FAST, bool MQ = false, class Store, class Map, class QF, class QPrep>
 __device__ __forceinline__ void run_tiles(const DecodeArgs& a, const Store& st, const Map& map, QF& qf,
                                           QPrep&& prep_q, const LaneGeo& lg, Online<D, G, CAP>& on, int tfirst,
-                                          int tend, int lane) {
+                                          int tend, int lane, int qlo = 0, int qhi = 0) {
   using KFrag = typename Store::KFrag;
   using VFrag = typename Store::VFrag;
   KFrag kb[NBUF];
@@ -901,6 +953,13 @@ __device__ __forceinline__ void run_tiles(const DecodeArgs& a, const Store& st, 
     const f4 raw = st.scores(kb[slot], qf);
     bool valid[4], kvalid[4];
     map.tile_valid(t0, lg, valid, kvalid);
+    if constexpr (MQ) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = t0 + 4 * lg.g + e;
+        valid[e] = valid[e] && t >= qlo && t <= qhi;
+      }
+    }
     float p[4];
     if (on.softmax_tile(a.capl2, raw, valid, p)) on.rescale(lane);
     st.template pv<FAST>(kb[slot], vb[slot], p, kvalid, on.o);
@@ -960,23 +1019,37 @@ __device__ __forceinline__ void table_span(const DecodeArgs& a, int t0, int t1, 
 // Sweep keys [tb, te) of sequence b for one kv head of a paged cache and write
 // the partial to dst.  Every wave of the workgroup calls it with the same
 // (b, tb, te): the block-table staging is shared.
-template <int D, int G, bool CAP, class T, bool FM>
+// MQ: several queries per sequence (G = 16 columns, a.grp * a.qn of them
+// used); the lane's query bounds [qlo, qhi] mask its column.
+template <int D, int G, bool CAP, class T, bool FM, bool MQ = false>
 __device__ __forceinline__ void paged_segment(const DecodeArgs& a, int b, int kvh, int lane, int tb, int te,
                                               int32_t* lds_tbl, const PartialDst& dst) {
   using QRaw = std::conditional_t<std::is_same_v<T, float>, QRaw32<D>, QRaw16<D>>;
   QRaw qraw;
   if (tb < te) {
     if constexpr (std::is_same_v<T, float>)
-      load_q_raw32<D, G>(a, b, kvh, lane, qraw);
+      load_q_raw32<D, G, MQ>(a, b, kvh, lane, qraw);
     else
-      load_q_raw16<D, G, false>(a, b, kvh, lane, qraw);
+      load_q_raw16<D, G, false, MQ>(a, b, kvh, lane, qraw);
   }
   int blk0, nblk;
   table_span(a, tb, te, blk0, nblk);
   stage_table(a, b, blk0, nblk, lds_tbl);
   if (tb >= te) {
-    write_empty<G>(dst, lane);
+    if constexpr (MQ)
+      write_empty_mq(dst, lane, a.grp, a.qn, a.num_heads);
+    else
+      write_empty<G>(dst, lane);
     return;
+  }
+  int qlo = 0, qhi = 0;
+  if constexpr (MQ) {
+    const int L = a.seq_lens[b];
+    const int c = lane & 15;
+    const int q = (a.q_pos ? a.q_pos[b] : L - a.qn) + c / a.grp;
+    qhi = a.causal ? min(q, L - 1) : L - 1;
+    qlo = (a.window > 0 && q >= a.window) ? q - a.window + 1 : 0;
+    if (c >= a.grp * a.qn) qlo = qhi + 1;   // unused column: nothing visible
   }
   LaneGeo lg;
   lg.init(lane);
@@ -986,15 +1059,18 @@ __device__ __forceinline__ void paged_segment(const DecodeArgs& a, int b, int kv
   if constexpr (std::is_same_v<T, float>) {
     QF32<D> qf;
     StoreF32<D> st{(const float*)a.k, (const float*)a.v, a.num_kv_heads, kvh};
-    run_tiles<D, G, CAP, kPipe, FM>(a, st, map, qf, [&](QF32<D>& q) { convert_q<D, G>(a, lane, qraw, q); }, lg, on,
-                                tb & ~(kTile - 1), te, lane);
+    run_tiles<D, G, CAP, kPipe, FM, MQ>(a, st, map, qf, [&](QF32<D>& q) { convert_q<D, G, MQ>(a, lane, qraw, q); },
+                                        lg, on, tb & ~(kTile - 1), te, lane, qlo, qhi);
   } else {
     QF16<D> qf;
     StoreF16<D> st{(const _Float16*)a.k, (const _Float16*)a.v, a.num_kv_heads, kvh};
-    run_tiles<D, G, CAP, kPipe, FM>(a, st, map, qf, [&](QF16<D>& q) { convert_q<D, G>(a, lane, qraw, q); }, lg, on,
-                                tb & ~(kTile - 1), te, lane);
+    run_tiles<D, G, CAP, kPipe, FM, MQ>(a, st, map, qf, [&](QF16<D>& q) { convert_q<D, G, MQ>(a, lane, qraw, q); },
+                                        lg, on, tb & ~(kTile - 1), te, lane, qlo, qhi);
   }
-  on.finish(dst, lane);
+  if constexpr (MQ)
+    on.finish_mq(dst, lane, a.grp, a.qn, a.num_heads);
+  else
+    on.finish(dst, lane);
 }
 
 // The same for the tiered cache: keys below cold_lens[b] from the paged cold
@@ -1051,7 +1127,7 @@ __device__ __forceinline__ void tiered_segment(const DecodeArgs& a, int b, int k
 
 // Static splits: workgroup (split, b, z) sweeps keys [split*T, (split+1)*T)
 // of sequence b for kv heads z*waves + [0, waves).
-template <int D, int G, bool CAP, class T, bool FM>
+template <int D, int G, bool CAP, class T, bool FM, bool MQ = false>
 __global__ __launch_bounds__(DATTN_MAX_THREADS) __attribute__((amdgpu_waves_per_eu(2))) void paged_split_kernel(DecodeArgs a) {
   extern __shared__ int32_t lds_tbl[];
   const int split = blockIdx.x, b = blockIdx.y;
@@ -1061,7 +1137,8 @@ __global__ __launch_bounds__(DATTN_MAX_THREADS) __attribute__((amdgpu_waves_per_
   visible_range(a, b, lo, hi, qp);
   const int tb = max(split * a.split_tokens, lo);
   const int te = min((split + 1) * a.split_tokens, hi + 1);
-  paged_segment<D, G, CAP, T, FM>(a, b, kvh, lane, tb, te, lds_tbl, split_dst(a, b, kvh, G, split, D));
+  paged_segment<D, G, CAP, T, FM, MQ>(a, b, kvh, lane, tb, te, lds_tbl,
+                                      split_dst(a, b, kvh, MQ ? a.grp : G, split, D));
 }
 
 template <int D, int G, bool CAP, bool FM, bool CF16>
@@ -1158,7 +1235,8 @@ __device__ __forceinline__ int unit_prefix(const DecodeArgs& a, int32_t* P) {
   return P[B];
 }
 
-// KIND: 0 paged f16, 1 paged f32, 2 tiered int8, 3 tiered f16.  Registers are capped for two
+// KIND: 0 paged f16, 1 paged f32, 2 tiered int8, 3 tiered f16, 4 / 5 paged
+// f16 / f32 with several queries per sequence (G = 16 columns).  Registers are capped for two
 // waves per SIMD: measured, a third wave (with Q moved to LDS to make room)
 // and a third tile of loads in flight per wave are both slower -- about
 // 32 KiB of loads in flight per SIMD is what HBM rewards here.
@@ -1199,13 +1277,17 @@ void balanced_kernel(DecodeArgs a) {
     sc.init(a, b);
     const int tb = max(sc.lo, sc.base + kTile * sc.tile_at(x0 - P[b]));
     const int te = min(sc.hi + 1, sc.base + kTile * sc.tile_at(seg_end - P[b]));
-    const PartialDst dst = slot_dst(a, w + b, kvh, G, D);
+    const PartialDst dst = slot_dst(a, w + b, kvh, KIND >= 4 ? a.grp : G, D);
     if constexpr (KIND == 2)
       tiered_segment<D, G, CAP, FM, false>(a, b, kvh, lane, tb, te, tbl, dst);
     else if constexpr (KIND == 3)
       tiered_segment<D, G, CAP, FM, true>(a, b, kvh, lane, tb, te, tbl, dst);
     else if constexpr (KIND == 1)
       paged_segment<D, G, CAP, float, FM>(a, b, kvh, lane, tb, te, tbl, dst);
+    else if constexpr (KIND == 4)
+      paged_segment<D, G, CAP, _Float16, FM, true>(a, b, kvh, lane, tb, te, tbl, dst);
+    else if constexpr (KIND == 5)
+      paged_segment<D, G, CAP, float, FM, true>(a, b, kvh, lane, tb, te, tbl, dst);
     else
       paged_segment<D, G, CAP, _Float16, FM>(a, b, kvh, lane, tb, te, tbl, dst);
     x0 = seg_end;

@@ -16,10 +16,14 @@ enum SplitKind : int {
   kBalTiered,      // balanced schedule, tiered
   kTieredF16,      // static splits, f16 cold pool + f16 hot ring
   kBalTieredF16,   // balanced schedule, tiered f16
+  kPagedF16MQ,     // static splits, paged f16, several queries per sequence (G = 16 columns)
+  kPagedF32MQ,
+  kBalF16MQ,       // balanced schedule, the same
+  kBalF32MQ,
 };
 
 // Split kernel for (kind, GQA group G in {1, 2, 4, 8}, contiguous 16-row
-// tiles); nullptr for an unknown kind.
+// tiles); the multi-query kinds take G = 16.  nullptr for an unknown pair.
 void* split_kernel_d64_cap0(int kind, int G, bool contig);
 void* split_kernel_d64_cap1(int kind, int G, bool contig);
 void* split_kernel_d128_cap0(int kind, int G, bool contig);

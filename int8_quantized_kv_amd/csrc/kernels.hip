@@ -14,17 +14,27 @@ template <int G, bool FM>
 void* instance(int kind) {
   constexpr int D = DATTN_D;
   constexpr bool CAP = DATTN_CAP != 0;
-  switch (kind) {
-    case kPagedF16: return (void*)&paged_split_kernel<D, G, CAP, _Float16, FM>;
-    case kPagedF32: return (void*)&paged_split_kernel<D, G, CAP, float, FM>;
-    case kTiered: return (void*)&tiered_split_kernel<D, G, CAP, FM, false>;
-    case kTieredF16: return (void*)&tiered_split_kernel<D, G, CAP, FM, true>;
-    case kSparse: return (void*)&sparse_split_kernel<D, G, CAP, FM>;
-    case kBalF16: return (void*)&balanced_kernel<D, G, CAP, 0, FM>;
-    case kBalF32: return (void*)&balanced_kernel<D, G, CAP, 1, FM>;
-    case kBalTiered: return (void*)&balanced_kernel<D, G, CAP, 2, FM>;
-    case kBalTieredF16: return (void*)&balanced_kernel<D, G, CAP, 3, FM>;
-    default: return nullptr;
+  if constexpr (G == 16) {   // multi-query kinds only
+    switch (kind) {
+      case kPagedF16MQ: return (void*)&paged_split_kernel<D, 16, CAP, _Float16, FM, true>;
+      case kPagedF32MQ: return (void*)&paged_split_kernel<D, 16, CAP, float, FM, true>;
+      case kBalF16MQ: return (void*)&balanced_kernel<D, 16, CAP, 4, FM>;
+      case kBalF32MQ: return (void*)&balanced_kernel<D, 16, CAP, 5, FM>;
+      default: return nullptr;
+    }
+  } else {
+    switch (kind) {
+      case kPagedF16: return (void*)&paged_split_kernel<D, G, CAP, _Float16, FM>;
+      case kPagedF32: return (void*)&paged_split_kernel<D, G, CAP, float, FM>;
+      case kTiered: return (void*)&tiered_split_kernel<D, G, CAP, FM, false>;
+      case kTieredF16: return (void*)&tiered_split_kernel<D, G, CAP, FM, true>;
+      case kSparse: return (void*)&sparse_split_kernel<D, G, CAP, FM>;
+      case kBalF16: return (void*)&balanced_kernel<D, G, CAP, 0, FM>;
+      case kBalF32: return (void*)&balanced_kernel<D, G, CAP, 1, FM>;
+      case kBalTiered: return (void*)&balanced_kernel<D, G, CAP, 2, FM>;
+      case kBalTieredF16: return (void*)&balanced_kernel<D, G, CAP, 3, FM>;
+      default: return nullptr;
+    }
   }
 }
 
@@ -34,7 +44,9 @@ void* by_group(int kind, int G) {
     case 1: return instance<1, FM>(kind);
     case 2: return instance<2, FM>(kind);
     case 4: return instance<4, FM>(kind);
-    default: return instance<8, FM>(kind);
+    case 8: return instance<8, FM>(kind);
+    case 16: return instance<16, FM>(kind);
+    default: return nullptr;
   }
 }
 

@@ -95,8 +95,9 @@ def oracle_run(case, pairs=None):
     out, lse = oracle.run(case, pairs=pairs)
     if pairs is None:
         p = case.params
-        out = out.reshape(p["num_seqs"], p["num_heads"], p["head_dim"])
-        lse = lse.reshape(p["num_seqs"], p["num_heads"])
+        lead = (p["num_seqs"],) if p.get("query_len", 1) <= 1 else (p["num_seqs"], p["query_len"])
+        out = out.reshape(*lead, p["num_heads"], p["head_dim"])
+        lse = lse.reshape(*lead, p["num_heads"])
     return out, lse
 
 

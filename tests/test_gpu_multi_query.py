@@ -1,0 +1,96 @@
+"""GPU parity of multi-query decode over the paged cache (Qn query rows per
+sequence, query i at q_pos[b] + i; the MFMA columns hold the Qn * G
+(query, head) pairs of a kv head) against the fp64 oracle."""
+import numpy as np
+import pytest
+
+import synth
+from gpu_util import DeviceCase, compare, log, oracle_run
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import int8_quantized_kv_amd as dk
+    dk.lib()   # fail loudly if the library is missing
+    yield
+
+
+def _check(case, split_tokens=0, what="", **over):
+    log(f"case mq {what} split_tokens={split_tokens}")
+    og, lg = DeviceCase(case).run_np(split_tokens, **over)
+    orf, lrf = oracle_run(case)
+    return compare(og, lg, orf, lrf, what=what)
+
+
+@pytest.mark.parametrize("qn", [2, 4])
+@pytest.mark.parametrize("split_tokens", [0, 64])
+def test_mq_paged_f16_small(qn, split_tokens):
+    c = synth.paged_case(501, 4, 32, 8, 128, 16, len_range=(512, 1200), kv_dtype=synth.F16, query_len=qn)
+    _check(c, split_tokens, what=f"paged f16 G4 Qn{qn}")
+
+
+@pytest.mark.parametrize("G,qn", [(8, 2), (1, 16), (2, 8), (4, 3)])
+def test_mq_column_limits(G, qn):
+    c = synth.paged_case(502 + G, 3, 4 * G, 4, 128, 16, lens=[700, 33, 5], kv_dtype=synth.F16, query_len=qn,
+                         softcap=30.0, window=200)
+    _check(c, what=f"G{G} Qn{qn} window 200 cap 30")
+
+
+def test_mq_paged_f32_d64():
+    c = synth.paged_case(503, 2, 8, 2, 64, 5, lens=[300, 47], kv_dtype=synth.F32, query_len=3, causal=1)
+    _check(c, what="paged f32 D64 bs5 Qn3")
+
+
+def test_mq_sequences_shorter_than_the_queries():
+    # q_pos defaults to L - Qn: queries before position 0 see nothing (causal)
+    c = synth.paged_case(504, 4, 16, 4, 128, 16, lens=[2, 0, 1, 40], kv_dtype=synth.F16, query_len=4)
+    _check(c, what="L < Qn")
+
+
+def _rand_case(seed):
+    rng = np.random.default_rng(95_000 + seed)
+    D = int(rng.choice([64, 128]))
+    G = int(rng.choice([1, 2, 4, 8]))
+    qn = int(rng.choice([q for q in (2, 3, 4, 5, 8, 16) if q * G <= 16]))
+    Hkv = int(rng.choice([1, 2, 3, 4, 8]))
+    B = int(rng.integers(1, 4))
+    lens = rng.integers(0, 900, size=B)
+    qp = None
+    if rng.random() < 0.4:
+        qp = np.array([int(rng.integers(0, max(1, L))) for L in lens], np.int32)
+    bs = int(rng.choice([1, 3, 16, 64]))
+    return synth.paged_case(seed, B, Hkv * G, Hkv, D, bs, lens=lens, query_len=qn, q_pos=qp,
+                            kv_dtype=synth.F32 if rng.random() < 0.25 else synth.F16,
+                            causal=int(rng.random() < 0.85), window=int(rng.choice([0, 0, 1, 17, 200])),
+                            softcap=float(rng.choice([0.0, 0.0, 5.0, 50.0])),
+                            scale=float(rng.choice([0.0, np.float32(rng.uniform(0.03, 0.3))])))
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_mq_random_sweep(seed):
+    case = _rand_case(seed)
+    st = int(np.random.default_rng(seed).choice([0, 0, 16, 48, 256]))
+    p = case.params
+    _check(case, split_tokens=st,
+           what=f"seed{seed} B{p['num_seqs']} Qn{p['query_len']} H{p['num_heads']}/{p['num_kv_heads']} "
+                f"D{p['head_dim']} bs{p['block_size']} W{p['sliding_window']} cap{p['softcap']}")
+
+
+def test_mq_f16_output_and_lse_only():
+    import torch
+    c = synth.paged_case(505, 2, 32, 8, 128, 16, lens=[900, 300], kv_dtype=synth.F16, query_len=4)
+    dc = DeviceCase(c)
+    o32, l32 = dc.run()
+    o16, l16 = dc.run(out_dtype=torch.float16)
+    o_none, l_only = dc.run(want_out=False)
+    torch.cuda.synchronize()
+    assert tuple(o16.shape) == (2, 4, 32, 128) and tuple(l_only.shape) == (2, 4, 32) and o_none is None
+    assert torch.equal(o16, o32.to(torch.float16))
+    assert torch.equal(l16, l32) and torch.equal(l_only, l32)
+    orf, lrf = oracle_run(c)
+    compare(o32.cpu().numpy(), l32.cpu().numpy(), orf, lrf, what="mq f32 out")
