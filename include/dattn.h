@@ -89,8 +89,8 @@ typedef struct dattn_params {
                                  result rounded to nearest even (attention.js sizes its output
                                  by the kernel variant's outputDtype, f16 or f32) */
   int32_t query_len;          /* queries per sequence, 0 or 1 => one; > 1: multi-query decode
-                                 (paged cache only; query_len * GQA group <= 16); see
-                                 dattn_decode_paged */
+                                 (paged, tiered and window-ring caches; query_len * GQA group
+                                 <= 16); see dattn_decode_paged */
 } dattn_params;
 
 /*
@@ -139,7 +139,8 @@ int dattn_workspace_size(const dattn_params* p, int32_t kind, int32_t sparse_blo
  * i of sequence b sits at position q_pos[b] + i (q_pos NULL: seq_lens[b] - Qn,
  * the last Qn tokens of the cache) with its own causal / window bound; out is
  * [B, Qn, H, D] and lse [B, Qn, H].  Each K/V row is still read once per
- * (sequence, kv head), for all Qn * G query rows of the group.
+ * (sequence, kv head), for all Qn * G query rows of the group.  The tiered and
+ * window-ring entry points take query_len the same way.
  */
 int dattn_decode_paged(const dattn_params* p, const float* q, const void* k_cache, const void* v_cache,
                        int32_t kv_dtype, const int32_t* block_table, const int32_t* seq_lens,

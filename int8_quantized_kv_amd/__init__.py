@@ -244,10 +244,11 @@ def dattn_decode_tiered_int8(q, k_hot, v_hot, k_cold, v_cold, k_scale, v_scale, 
                              sliding_window: int = 0, softcap: float = 0.0, max_seq_len: Optional[int] = None,
                              split_tokens: int = 0, out=None, lse=None, want_lse: bool = True, workspace=None,
                              stream=None, phases: int = PHASE_ALL, out_dtype=None, want_out: bool = True):
-    """Decode attention over an int8 cold pool + f16 hot ring; returns (out, lse)."""
+    """Decode attention over an int8 cold pool + f16 hot ring; returns (out, lse).
+    q [B, Qn, H, D] asks for Qn queries per sequence, as for dattn_decode_paged."""
     torch = _torch()
     dev = q.device
-    _need(q, "q", (torch.float32,), 3, dev)
+    _need(q, "q", (torch.float32,), q.dim() if q.dim() in (3, 4) else 3, dev)
     _need(k_hot, "k_hot", (torch.float16,), 4, dev)
     _need(v_hot, "v_hot", (torch.float16,), 4, dev)
     _need(k_cold, "k_cold", (torch.int32, torch.uint32), 4, dev)
@@ -259,7 +260,7 @@ def dattn_decode_tiered_int8(q, k_hot, v_hot, k_cold, v_cold, k_scale, v_scale, 
     _need(cold_lens, "cold_lens", (torch.int32,), 1, dev)
     if q_pos is not None:
         _need(q_pos, "q_pos", (torch.int32,), 1, dev)
-    B, H, D = q.shape
+    B, D = q.shape[0], q.shape[-1]
     _, hot_window, Hkv, Dh = k_hot.shape
     NB, bs, Hkv2, W4 = k_cold.shape
     if Dh != D or Hkv2 != Hkv or W4 * 4 != D or tuple(v_hot.shape) != tuple(k_hot.shape) \
@@ -283,10 +284,11 @@ def dattn_decode_tiered_f16(q, k_hot, v_hot, k_cold, v_cold, cold_block_table, s
                             max_seq_len: Optional[int] = None, split_tokens: int = 0, out=None, lse=None,
                             want_lse: bool = True, workspace=None, stream=None, phases: int = PHASE_ALL,
                             out_dtype=None, want_out: bool = True):
-    """Decode attention over an f16 paged cold pool + f16 hot ring; returns (out, lse)."""
+    """Decode attention over an f16 paged cold pool + f16 hot ring; returns (out, lse).
+    q [B, Qn, H, D] asks for Qn queries per sequence, as for dattn_decode_paged."""
     torch = _torch()
     dev = q.device
-    _need(q, "q", (torch.float32,), 3, dev)
+    _need(q, "q", (torch.float32,), q.dim() if q.dim() in (3, 4) else 3, dev)
     _need(k_hot, "k_hot", (torch.float16,), 4, dev)
     _need(v_hot, "v_hot", (torch.float16,), 4, dev)
     _need(k_cold, "k_cold", (torch.float16,), 4, dev)
@@ -296,7 +298,7 @@ def dattn_decode_tiered_f16(q, k_hot, v_hot, k_cold, v_cold, cold_block_table, s
     _need(cold_lens, "cold_lens", (torch.int32,), 1, dev)
     if q_pos is not None:
         _need(q_pos, "q_pos", (torch.int32,), 1, dev)
-    B, H, D = q.shape
+    B, D = q.shape[0], q.shape[-1]
     _, hot_window, Hkv, Dh = k_hot.shape
     NB, bs, Hkv2, Dc = k_cold.shape
     if Dh != D or Dc != D or Hkv2 != Hkv or tuple(v_hot.shape) != tuple(k_hot.shape) \
@@ -318,16 +320,17 @@ def dattn_decode_ring_f16(q, k_ring, v_ring, seq_lens, *, q_pos=None, scale: flo
                           lse=None, want_lse: bool = True, workspace=None, stream=None, phases: int = PHASE_ALL,
                           out_dtype=None, want_out: bool = True):
     """Decode attention over a sliding-window ring [B, W, Hkv, D] f16 (the window is W,
-    the ring's slot count); returns (out, lse)."""
+    the ring's slot count); returns (out, lse).  q [B, Qn, H, D] asks for Qn queries
+    per sequence, as for dattn_decode_paged."""
     torch = _torch()
     dev = q.device
-    _need(q, "q", (torch.float32,), 3, dev)
+    _need(q, "q", (torch.float32,), q.dim() if q.dim() in (3, 4) else 3, dev)
     _need(k_ring, "k_ring", (torch.float16,), 4, dev)
     _need(v_ring, "v_ring", (torch.float16,), 4, dev)
     _need(seq_lens, "seq_lens", (torch.int32,), 1, dev)
     if q_pos is not None:
         _need(q_pos, "q_pos", (torch.int32,), 1, dev)
-    B, H, D = q.shape
+    B, D = q.shape[0], q.shape[-1]
     Bk, W, Hkv, Dk = k_ring.shape
     if Bk != B or Dk != D or tuple(v_ring.shape) != tuple(k_ring.shape) or seq_lens.shape[0] != B:
         raise ValueError("ring tensors disagree on shape")

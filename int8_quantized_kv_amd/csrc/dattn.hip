@@ -132,8 +132,8 @@ int check_params(const dattn_params* p, int kind) {
     return fail(DATTN_ERR_INVALID, "out_dtype must be DATTN_F32 or DATTN_F16 (got %d)", p->out_dtype);
   if (p->query_len < 0) return fail(DATTN_ERR_INVALID, "query_len must be >= 0 (got %d)", p->query_len);
   if (p->query_len > 1) {
-    if (kind != DATTN_KIND_PAGED)
-      return fail(DATTN_ERR_UNSUPPORTED, "query_len > 1 is built for the paged cache only");
+    if (kind == DATTN_KIND_BLOCK_SPARSE)
+      return fail(DATTN_ERR_UNSUPPORTED, "query_len > 1 is not built for the block-sparse cache");
     if (G * p->query_len > 16)
       return fail(DATTN_ERR_UNSUPPORTED, "query_len (%d) * GQA group (%d) must be <= 16", p->query_len, G);
   }
@@ -457,6 +457,10 @@ int dattn_decode_tiered_int8(const dattn_params* p, const float* q, const uint16
   a.q_pos = q_pos;
   const bool cap = p->softcap > 0.0f;
   const bool contig = p->block_size % 16 == 0 && hot_window % 16 == 0;
+  if (a.qn > 1)   // several queries per sequence: MFMA columns are (query, head) pairs
+    return launch(dattn::split_kernel(dattn::kTieredMQ, p->head_dim, cap, 16, contig),
+                  dattn::split_kernel(dattn::kBalTieredMQ, p->head_dim, cap, 16, contig), p, pl, a, out, lse,
+                  (hipStream_t)stream);
   return launch(dattn::split_kernel(dattn::kTiered, p->head_dim, cap, pl.G, contig),
                 dattn::split_kernel(dattn::kBalTiered, p->head_dim, cap, pl.G, contig), p, pl, a, out, lse,
                 (hipStream_t)stream);
@@ -492,9 +496,12 @@ int dattn_decode_tiered_f16(const dattn_params* p, const float* q, const uint16_
   a.q_pos = q_pos;
   const bool cap = p->softcap > 0.0f;
   const bool contig = p->block_size % 16 == 0 && hot_window % 16 == 0;
-  return launch(dattn::split_kernel(dattn::kTieredF16, p->head_dim, cap, pl.G, contig),
-                dattn::split_kernel(dattn::kBalTieredF16, p->head_dim, cap, pl.G, contig), p, pl, a, out, lse,
-                (hipStream_t)stream);
+  const bool mq = a.qn > 1;
+  return launch(dattn::split_kernel(mq ? dattn::kTieredF16MQ : dattn::kTieredF16, p->head_dim, cap, mq ? 16 : pl.G,
+                                    contig),
+                dattn::split_kernel(mq ? dattn::kBalTieredF16MQ : dattn::kBalTieredF16, p->head_dim, cap,
+                                    mq ? 16 : pl.G, contig),
+                p, pl, a, out, lse, (hipStream_t)stream);
 }
 
 int dattn_decode_ring_f16(const dattn_params* p_in, const float* q, const uint16_t* k_ring, const uint16_t* v_ring,
@@ -523,9 +530,12 @@ int dattn_decode_ring_f16(const dattn_params* p_in, const float* q, const uint16
   a.q_pos = q_pos;
   const bool cap = p->softcap > 0.0f;
   const bool contig = W % 16 == 0;
-  return launch(dattn::split_kernel(dattn::kTieredF16, p->head_dim, cap, pl.G, contig),
-                dattn::split_kernel(dattn::kBalTieredF16, p->head_dim, cap, pl.G, contig), p, pl, a, out, lse,
-                (hipStream_t)stream);
+  const bool mq = a.qn > 1;
+  return launch(dattn::split_kernel(mq ? dattn::kTieredF16MQ : dattn::kTieredF16, p->head_dim, cap, mq ? 16 : pl.G,
+                                    contig),
+                dattn::split_kernel(mq ? dattn::kBalTieredF16MQ : dattn::kBalTieredF16, p->head_dim, cap,
+                                    mq ? 16 : pl.G, contig),
+                p, pl, a, out, lse, (hipStream_t)stream);
 }
 
 int dattn_decode_block_sparse(const dattn_params* p, const float* q, const uint16_t* k_cache,

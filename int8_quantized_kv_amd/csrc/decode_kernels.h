@@ -1019,6 +1019,18 @@ __device__ __forceinline__ void table_span(const DecodeArgs& a, int t0, int t1, 
 // Sweep keys [tb, te) of sequence b for one kv head of a paged cache and write
 // the partial to dst.  Every wave of the workgroup calls it with the same
 // (b, tb, te): the block-table staging is shared.
+// Several queries per sequence: the visible keys [qlo, qhi] of the query whose
+// (query, head) pair is this lane's score column (column r: query r / grp);
+// an unused column (r >= grp * qn) sees nothing.
+__device__ __forceinline__ void query_bounds(const DecodeArgs& a, int b, int lane, int& qlo, int& qhi) {
+  const int L = a.seq_lens[b];
+  const int c = lane & 15;
+  const int q = (a.q_pos ? a.q_pos[b] : L - a.qn) + c / a.grp;
+  qhi = a.causal ? min(q, L - 1) : L - 1;
+  qlo = (a.window > 0 && q >= a.window) ? q - a.window + 1 : 0;
+  if (c >= a.grp * a.qn) qlo = qhi + 1;
+}
+
 // MQ: several queries per sequence (G = 16 columns, a.grp * a.qn of them
 // used); the lane's query bounds [qlo, qhi] mask its column.
 template <int D, int G, bool CAP, class T, bool FM, bool MQ = false>
@@ -1043,14 +1055,7 @@ __device__ __forceinline__ void paged_segment(const DecodeArgs& a, int b, int kv
     return;
   }
   int qlo = 0, qhi = 0;
-  if constexpr (MQ) {
-    const int L = a.seq_lens[b];
-    const int c = lane & 15;
-    const int q = (a.q_pos ? a.q_pos[b] : L - a.qn) + c / a.grp;
-    qhi = a.causal ? min(q, L - 1) : L - 1;
-    qlo = (a.window > 0 && q >= a.window) ? q - a.window + 1 : 0;
-    if (c >= a.grp * a.qn) qlo = qhi + 1;   // unused column: nothing visible
-  }
+  if constexpr (MQ) query_bounds(a, b, lane, qlo, qhi);
   LaneGeo lg;
   lg.init(lane);
   PagedMap map{lds_tbl, blk0, tb, te - 1, a.bs, FM};
@@ -1076,7 +1081,7 @@ __device__ __forceinline__ void paged_segment(const DecodeArgs& a, int b, int kv
 // The same for the tiered cache: keys below cold_lens[b] from the paged cold
 // pool (int8 words with f16 scales, or f16 rows when CF16), the rest from the
 // f16 ring.
-template <int D, int G, bool CAP, bool FM, bool CF16>
+template <int D, int G, bool CAP, bool FM, bool CF16, bool MQ = false>
 __device__ __forceinline__ void tiered_segment(const DecodeArgs& a, int b, int kvh, int lane, int tb, int te,
                                                int32_t* lds_tbl, const PartialDst& dst) {
   const int C = a.cold_lens ? a.cold_lens[b] : 0;   // no cold tier: a window ring
@@ -1084,16 +1089,21 @@ __device__ __forceinline__ void tiered_segment(const DecodeArgs& a, int b, int k
   const int hb = max(tb, C);   // hot part  [hb, te)
   QRaw16<D> qraw;              // int8 cold keys use the int8 dim map, f16 keys the f16 one
   if (tb < ce)
-    load_q_raw16<D, G, !CF16>(a, b, kvh, lane, qraw);
+    load_q_raw16<D, G, !CF16, MQ>(a, b, kvh, lane, qraw);
   else if (tb < te)
-    load_q_raw16<D, G, false>(a, b, kvh, lane, qraw);
+    load_q_raw16<D, G, false, MQ>(a, b, kvh, lane, qraw);
   int blk0, nblk;
   table_span(a, tb, ce, blk0, nblk);
   stage_table(a, b, blk0, nblk, lds_tbl);
   if (tb >= te) {
-    write_empty<G>(dst, lane);
+    if constexpr (MQ)
+      write_empty_mq(dst, lane, a.grp, a.qn, a.num_heads);
+    else
+      write_empty<G>(dst, lane);
     return;
   }
+  int qlo = 0, qhi = 0;
+  if constexpr (MQ) query_bounds(a, b, lane, qlo, qhi);
   LaneGeo lg;
   lg.init(lane);
   QF16<D> qf;
@@ -1103,26 +1113,29 @@ __device__ __forceinline__ void tiered_segment(const DecodeArgs& a, int b, int k
     PagedMap map{lds_tbl, blk0, tb, ce - 1, a.bs, FM};
     if constexpr (CF16) {
       StoreF16<D> st{(const _Float16*)a.k, (const _Float16*)a.v, a.num_kv_heads, kvh};
-      run_tiles<D, G, CAP, kPipe, FM>(a, st, map, qf, [&](QF16<D>& q) { convert_q<D, G>(a, lane, qraw, q); }, lg,
-                                      on, tb & ~(kTile - 1), ce, lane);
+      run_tiles<D, G, CAP, kPipe, FM, MQ>(a, st, map, qf, [&](QF16<D>& q) { convert_q<D, G, MQ>(a, lane, qraw, q); },
+                                          lg, on, tb & ~(kTile - 1), ce, lane, qlo, qhi);
     } else {
       StoreI8<D> st{(const uint32_t*)a.k, (const uint32_t*)a.v, a.k_scale, a.v_scale, a.num_kv_heads, kvh};
-      run_tiles<D, G, CAP, kPipe, FM>(a, st, map, qf, [&](QF16<D>& q) { convert_q<D, G>(a, lane, qraw, q); }, lg,
-                                      on, tb & ~(kTile - 1), ce, lane);
+      run_tiles<D, G, CAP, kPipe, FM, MQ>(a, st, map, qf, [&](QF16<D>& q) { convert_q<D, G, MQ>(a, lane, qraw, q); },
+                                          lg, on, tb & ~(kTile - 1), ce, lane, qlo, qhi);
     }
   }
   if (hb < te) {
     RingMap map{b, hb, te - 1, a.hw, FM};
     StoreF16<D> st{(const _Float16*)a.k_hot, (const _Float16*)a.v_hot, a.num_kv_heads, kvh};
     const bool had_cold = !CF16 && tb < ce;   // Q was laid out for int8 keys
-    run_tiles<D, G, CAP, kPipe, FM>(a, st, map, qf,
-                                [&](QF16<D>& q) {
-                                  if (had_cold) load_q_raw16<D, G, false>(a, b, kvh, lane, qraw);
-                                  convert_q<D, G>(a, lane, qraw, q);
-                                },
-                                lg, on, hb & ~(kTile - 1), te, lane);
+    run_tiles<D, G, CAP, kPipe, FM, MQ>(a, st, map, qf,
+                                        [&](QF16<D>& q) {
+                                          if (had_cold) load_q_raw16<D, G, false, MQ>(a, b, kvh, lane, qraw);
+                                          convert_q<D, G, MQ>(a, lane, qraw, q);
+                                        },
+                                        lg, on, hb & ~(kTile - 1), te, lane, qlo, qhi);
   }
-  on.finish(dst, lane);
+  if constexpr (MQ)
+    on.finish_mq(dst, lane, a.grp, a.qn, a.num_heads);
+  else
+    on.finish(dst, lane);
 }
 
 // Static splits: workgroup (split, b, z) sweeps keys [split*T, (split+1)*T)
@@ -1141,7 +1154,7 @@ __global__ __launch_bounds__(DATTN_MAX_THREADS) __attribute__((amdgpu_waves_per_
                                       split_dst(a, b, kvh, MQ ? a.grp : G, split, D));
 }
 
-template <int D, int G, bool CAP, bool FM, bool CF16>
+template <int D, int G, bool CAP, bool FM, bool CF16, bool MQ = false>
 __global__ __launch_bounds__(DATTN_MAX_THREADS) __attribute__((amdgpu_waves_per_eu(2))) void tiered_split_kernel(DecodeArgs a) {
   extern __shared__ int32_t lds_tbl[];
   const int split = blockIdx.x, b = blockIdx.y;
@@ -1151,7 +1164,8 @@ __global__ __launch_bounds__(DATTN_MAX_THREADS) __attribute__((amdgpu_waves_per_
   visible_range(a, b, lo, hi, qp);
   const int tb = max(split * a.split_tokens, lo);
   const int te = min((split + 1) * a.split_tokens, hi + 1);
-  tiered_segment<D, G, CAP, FM, CF16>(a, b, kvh, lane, tb, te, lds_tbl, split_dst(a, b, kvh, G, split, D));
+  tiered_segment<D, G, CAP, FM, CF16, MQ>(a, b, kvh, lane, tb, te, lds_tbl,
+                                          split_dst(a, b, kvh, MQ ? a.grp : G, split, D));
 }
 
 // ------------------------------------------------------- balanced schedule
@@ -1194,7 +1208,7 @@ struct SeqCost {
     base = lo & ~(kTile - 1);
     ntiles = hi < lo ? 0 : (hi >> 4) - (lo >> 4) + 1;
     ncold = ntiles;
-    if constexpr (KIND == 2) ncold = min(ntiles, max(0, (a.cold_lens[b] - base + kTile - 1) / kTile));
+    if constexpr (KIND == 2 || KIND == 6) ncold = min(ntiles, max(0, (a.cold_lens[b] - base + kTile - 1) / kTile));
     head = ntiles > 0 ? kSeqUnits : 0;
   }
   __device__ __forceinline__ int units() const { return head + ncold + 2 * (ntiles - ncold); }
@@ -1235,8 +1249,9 @@ __device__ __forceinline__ int unit_prefix(const DecodeArgs& a, int32_t* P) {
   return P[B];
 }
 
-// KIND: 0 paged f16, 1 paged f32, 2 tiered int8, 3 tiered f16, 4 / 5 paged
-// f16 / f32 with several queries per sequence (G = 16 columns).  Registers are capped for two
+// KIND: 0 paged f16, 1 paged f32, 2 tiered int8, 3 tiered f16 (and the window
+// ring); 4, 5, 6, 7: paged f16, paged f32, tiered int8, tiered f16 with
+// several queries per sequence (G = 16 columns).  Registers are capped for two
 // waves per SIMD: measured, a third wave (with Q moved to LDS to make room)
 // and a third tile of loads in flight per wave are both slower -- about
 // 32 KiB of loads in flight per SIMD is what HBM rewards here.
@@ -1288,6 +1303,10 @@ void balanced_kernel(DecodeArgs a) {
       paged_segment<D, G, CAP, _Float16, FM, true>(a, b, kvh, lane, tb, te, tbl, dst);
     else if constexpr (KIND == 5)
       paged_segment<D, G, CAP, float, FM, true>(a, b, kvh, lane, tb, te, tbl, dst);
+    else if constexpr (KIND == 6)
+      tiered_segment<D, G, CAP, FM, false, true>(a, b, kvh, lane, tb, te, tbl, dst);
+    else if constexpr (KIND == 7)
+      tiered_segment<D, G, CAP, FM, true, true>(a, b, kvh, lane, tb, te, tbl, dst);
     else
       paged_segment<D, G, CAP, _Float16, FM>(a, b, kvh, lane, tb, te, tbl, dst);
     x0 = seg_end;

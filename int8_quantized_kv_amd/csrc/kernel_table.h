@@ -20,6 +20,10 @@ enum SplitKind : int {
   kPagedF32MQ,
   kBalF16MQ,       // balanced schedule, the same
   kBalF32MQ,
+  kTieredMQ,       // static splits, tiered int8, several queries per sequence
+  kTieredF16MQ,    // static splits, tiered f16 / window ring, several queries per sequence
+  kBalTieredMQ,    // balanced schedule, the same
+  kBalTieredF16MQ,
 };
 
 // Split kernel for (kind, GQA group G in {1, 2, 4, 8}, contiguous 16-row

@@ -20,6 +20,10 @@ void* instance(int kind) {
       case kPagedF32MQ: return (void*)&paged_split_kernel<D, 16, CAP, float, FM, true>;
       case kBalF16MQ: return (void*)&balanced_kernel<D, 16, CAP, 4, FM>;
       case kBalF32MQ: return (void*)&balanced_kernel<D, 16, CAP, 5, FM>;
+      case kTieredMQ: return (void*)&tiered_split_kernel<D, 16, CAP, FM, false, true>;
+      case kTieredF16MQ: return (void*)&tiered_split_kernel<D, 16, CAP, FM, true, true>;
+      case kBalTieredMQ: return (void*)&balanced_kernel<D, 16, CAP, 6, FM>;
+      case kBalTieredF16MQ: return (void*)&balanced_kernel<D, 16, CAP, 7, FM>;
       default: return nullptr;
     }
   } else {

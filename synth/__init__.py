@@ -186,7 +186,7 @@ def exact_rows(rng, shape):
 
 
 def tiered_case(seed, B, H, Hkv, D, bs, lens, cold_lens, hot_window, permute=True, q_pos=None, causal=1, window=0,
-                softcap=0.0, scale=0.0, exact=False, extra_blocks=0, name="") -> Case:
+                softcap=0.0, scale=0.0, exact=False, extra_blocks=0, name="", query_len=1) -> Case:
     """Logical token rows K/V[b, t] are drawn first (float32 N(0,1), or ``exact_rows``); token
     t < cold_lens[b] is stored as int8 codes + f16 scale in the paged cold pool, token
     t >= cold_lens[b] as f16 in the ring at slot t mod hot_window.  Ring slots and pool rows
@@ -195,7 +195,7 @@ def tiered_case(seed, B, H, Hkv, D, bs, lens, cold_lens, hot_window, permute=Tru
     lens = np.asarray(lens, np.int32)
     cold_lens = np.asarray(cold_lens, np.int32)
     assert np.all(cold_lens <= lens) and np.all(lens - cold_lens <= hot_window)
-    q = rng.standard_normal((B, H, D), dtype=np.float32)
+    q = rng.standard_normal((B, H, D) if query_len == 1 else (B, query_len, H, D), dtype=np.float32)
     Lmax = max(1, int(lens.max()))
     draw = exact_rows if exact else (lambda r, shp: _normal(r, shp, F32))
     k_log = draw(rng, (B, Lmax, Hkv, D))
@@ -222,14 +222,14 @@ def tiered_case(seed, B, H, Hkv, D, bs, lens, cold_lens, hot_window, permute=Tru
         hv[hb, ht % hot_window] = v_log[hb, ht].astype(np.float16)
     del k_log, v_log
     qp = None if q_pos is None else np.asarray(q_pos, np.int32)
-    return Case("tiered", _params(B, H, Hkv, D, bs, table.shape[1], pool, scale, causal, window, softcap), q, lens,
-                qp, k_hot=hk, v_hot=hv, hot_window=int(hot_window), k_cold=pack_int8(kc), v_cold=pack_int8(vc),
+    return Case("tiered", _params(B, H, Hkv, D, bs, table.shape[1], pool, scale, causal, window, softcap, query_len),
+                q, lens, qp, k_hot=hk, v_hot=hv, hot_window=int(hot_window), k_cold=pack_int8(kc), v_cold=pack_int8(vc),
                 k_scale=ks, v_scale=vs, cold_block_table=table, cold_lens=cold_lens, name=name,
                 extra=dict(k_codes=kc, v_codes=vc))
 
 
 def tiered_f16_case(seed, B, H, Hkv, D, bs, lens, cold_lens, hot_window, permute=True, q_pos=None, causal=1,
-                    window=0, softcap=0.0, scale=0.0, extra_blocks=0, name="") -> Case:
+                    window=0, softcap=0.0, scale=0.0, extra_blocks=0, name="", query_len=1) -> Case:
     """As ``tiered_case`` with an f16 cold tier: token t < cold_lens[b] is stored as f16 in the
     paged cold pool [pool, bs, Hkv, D], token t >= cold_lens[b] as f16 in the ring at slot
     t mod hot_window.  Pool rows and ring slots that hold no live token carry +-300."""
@@ -237,7 +237,7 @@ def tiered_f16_case(seed, B, H, Hkv, D, bs, lens, cold_lens, hot_window, permute
     lens = np.asarray(lens, np.int32)
     cold_lens = np.asarray(cold_lens, np.int32)
     assert np.all(cold_lens <= lens) and np.all(lens - cold_lens <= hot_window)
-    q = rng.standard_normal((B, H, D), dtype=np.float32)
+    q = rng.standard_normal((B, H, D) if query_len == 1 else (B, query_len, H, D), dtype=np.float32)
     Lmax = max(1, int(lens.max()))
     k_log = _normal(rng, (B, Lmax, Hkv, D), F16)
     v_log = _normal(rng, (B, Lmax, Hkv, D), F16)
@@ -260,13 +260,13 @@ def tiered_f16_case(seed, B, H, Hkv, D, bs, lens, cold_lens, hot_window, permute
         hv[hb, ht % hot_window] = v_log[hb, ht]
     del k_log, v_log
     qp = None if q_pos is None else np.asarray(q_pos, np.int32)
-    return Case("tiered_f16", _params(B, H, Hkv, D, bs, table.shape[1], pool, scale, causal, window, softcap), q,
-                lens, qp, k_hot=hk, v_hot=hv, hot_window=int(hot_window), k_cold=kc, v_cold=vc,
+    return Case("tiered_f16", _params(B, H, Hkv, D, bs, table.shape[1], pool, scale, causal, window, softcap,
+                                      query_len), q, lens, qp, k_hot=hk, v_hot=hv, hot_window=int(hot_window), k_cold=kc, v_cold=vc,
                 cold_block_table=table, cold_lens=cold_lens, name=name)
 
 
 def ring_case(seed, B, H, Hkv, D, W, lens, q_pos=None, causal=1, softcap=0.0, scale=0.0, history=True,
-              name="") -> Case:
+              name="", query_len=1) -> Case:
     """Sliding-window ring of W slots per sequence: token t of sequence b sits at slot
     t mod W and only the last W tokens are resident.  With ``history`` the whole token
     history K/V[b, t] is drawn (float32 N(0,1) -> f16, kept in ``extra``) and its last W
@@ -274,7 +274,7 @@ def ring_case(seed, B, H, Hkv, D, W, lens, q_pos=None, causal=1, softcap=0.0, sc
     Slots that hold no resident token carry +-300."""
     rng = np.random.default_rng(seed)
     lens = np.asarray(lens, np.int32)
-    q = rng.standard_normal((B, H, D), dtype=np.float32)
+    q = rng.standard_normal((B, H, D) if query_len == 1 else (B, query_len, H, D), dtype=np.float32)
     hk = np.full((B, W, Hkv, D), 300.0, np.float16)
     hv = np.full((B, W, Hkv, D), -300.0, np.float16)
     extra = {}
@@ -296,8 +296,8 @@ def ring_case(seed, B, H, Hkv, D, W, lens, q_pos=None, causal=1, softcap=0.0, sc
             hk[b, :L] = rng.standard_normal((L, Hkv, D), dtype=np.float32).astype(np.float16)
             hv[b, :L] = rng.standard_normal((L, Hkv, D), dtype=np.float32).astype(np.float16)
     qp = None if q_pos is None else np.asarray(q_pos, np.int32)
-    return Case("ring", _params(B, H, Hkv, D, 1, 1, 1, scale, causal, W, softcap), q, lens, qp, k_hot=hk, v_hot=hv,
-                hot_window=int(W), name=name, extra=extra)
+    return Case("ring", _params(B, H, Hkv, D, 1, 1, 1, scale, causal, W, softcap, query_len), q, lens, qp, k_hot=hk,
+                v_hot=hv, hot_window=int(W), name=name, extra=extra)
 
 
 # ------------------------------------------------------------------- sparse

@@ -94,3 +94,38 @@ def test_mq_f16_output_and_lse_only():
     assert torch.equal(l16, l32) and torch.equal(l_only, l32)
     orf, lrf = oracle_run(c)
     compare(o32.cpu().numpy(), l32.cpu().numpy(), orf, lrf, what="mq f32 out")
+
+
+@pytest.mark.parametrize("kind", ["tiered", "tiered_f16", "ring"])
+@pytest.mark.parametrize("split_tokens", [0, 48])
+def test_mq_other_caches(kind, split_tokens):
+    kw = dict(query_len=4, softcap=50.0)
+    if kind == "ring":
+        c = synth.ring_case(510, 3, 32, 8, 128, 256, [1000, 100, 257], **kw)
+    else:
+        make = synth.tiered_case if kind == "tiered" else synth.tiered_f16_case
+        c = make(511, 2, 32, 8, 128, 16, [700, 613], [450, 420], 256, window=300, **kw)
+    _check(c, split_tokens, what=f"{kind} Qn4")
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_mq_other_caches_sweep(seed):
+    rng = np.random.default_rng(97_000 + seed)
+    kind = ["tiered", "tiered_f16", "ring"][seed % 3]
+    G = int(rng.choice([1, 2, 4, 8]))
+    qn = int(rng.choice([q for q in (2, 3, 4, 8) if q * G <= 16]))
+    Hkv = int(rng.choice([1, 2, 4, 8]))
+    D = int(rng.choice([64, 128]))
+    B = int(rng.integers(1, 4))
+    lens = rng.integers(0, 900, size=B)
+    kw = dict(query_len=qn, causal=int(rng.random() < 0.85), softcap=float(rng.choice([0.0, 5.0, 50.0])))
+    if kind == "ring":
+        case = synth.ring_case(seed, B, Hkv * G, Hkv, D, int(rng.choice([16, 50, 128])), lens, **kw)
+    else:
+        hw = int(rng.choice([16, 50, 128]))
+        cold = np.array([max(0, int(L) - int(rng.integers(0, hw + 1))) for L in lens])
+        make = synth.tiered_case if kind == "tiered" else synth.tiered_f16_case
+        case = make(seed, B, Hkv * G, Hkv, D, int(rng.choice([5, 16])), lens, cold, hw,
+                    window=int(rng.choice([0, 0, 17, 200])), **kw)
+    st = int(np.random.default_rng(seed).choice([0, 0, 16, 256]))
+    _check(case, st, what=f"seed{seed} {kind} B{B} Qn{qn} G{G} Hkv{Hkv} D{D}")

@@ -93,3 +93,23 @@ def test_causal_counts_grow_by_one_per_query():
     for b, L in enumerate([40, 17]):
         assert list(counts[b, :, 0]) == [L - 4 + i for i in range(5)]
     assert np.allclose(out, 1.0)
+
+
+@pytest.mark.parametrize("kind,seed", [(k, s) for k in ("tiered", "tiered_f16", "ring") for s in range(8)])
+def test_multi_query_other_caches_match_bruteforce(kind, seed):
+    rng = np.random.default_rng(9700 + seed)
+    Hkv, G, Qn = int(rng.choice([1, 2])), int(rng.choice([1, 2, 4])), int(rng.choice([2, 3, 4]))
+    B, D = 2, 16
+    lens = rng.integers(0, 200, size=B)
+    kw = dict(query_len=Qn, causal=int(rng.integers(0, 2)), softcap=float(rng.choice([0.0, 5.0])))
+    if kind == "ring":
+        case = synth.ring_case(seed, B, Hkv * G, Hkv, D, int(rng.choice([5, 16, 64])), lens, **kw)
+    else:
+        hw = int(rng.choice([7, 32]))
+        cold = np.array([max(0, int(L) - int(rng.integers(0, hw + 1))) for L in lens])
+        make = synth.tiered_case if kind == "tiered" else synth.tiered_f16_case
+        case = make(seed, B, Hkv * G, Hkv, D, 3, lens, cold, hw, window=int(rng.choice([0, 20])), **kw)
+    out, lse = _run(case)
+    ref_out, ref_lse = attend(case)
+    _close(out, ref_out)
+    _close(lse, ref_lse)
