@@ -12,6 +12,9 @@ from gpu_util import DeviceCase, compare, log, oracle_run
 pytestmark = pytest.mark.gpu
 
 WORKLOADS = [(2, {}), (3, {"window": 0}), (3, {"window": 4096}), (4, {}), (5, {})]
+# the tiered workload's shape with an f16 cold tier, the window ring, four queries per sequence
+EXTRA = {"tiered_f16": lambda: synth.tiered_f16_workload(0), "ring": synth.ring_workload,
+         "multi_query": lambda: synth.multi_query_workload(4)}
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -24,19 +27,27 @@ def _gpu():
     yield
 
 
-@pytest.mark.parametrize("idx,kw", WORKLOADS, ids=["paged", "tiered_w0", "tiered_w4096", "long", "sparse"])
-def test_full_size_sampled(idx, kw):
+def _sampled(case, seed):
     import torch
-    case = synth.config(idx, **kw)
     log(f"full-size {case.name}")
     dc = DeviceCase(case)
     out, lse = dc.run_np()
     del dc
     torch.cuda.empty_cache()
     p = case.params
-    nbh = p["num_seqs"] * p["num_heads"]
+    nbh = p["num_seqs"] * max(1, p.get("query_len", 1)) * p["num_heads"]
     assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
-    rng = np.random.default_rng(idx)
+    rng = np.random.default_rng(seed)
     pairs = np.unique(np.concatenate([[0, nbh - 1, p["num_heads"] - 1], rng.integers(0, nbh, 21)])).astype(np.int32)
     ref_o, ref_l = oracle_run(case, pairs=pairs)
     compare(out.reshape(nbh, -1)[pairs], lse.reshape(nbh)[pairs], ref_o, ref_l, what=f"{case.name} sampled")
+
+
+@pytest.mark.parametrize("idx,kw", WORKLOADS, ids=["paged", "tiered_w0", "tiered_w4096", "long", "sparse"])
+def test_full_size_sampled(idx, kw):
+    _sampled(synth.config(idx, **kw), idx)
+
+
+@pytest.mark.parametrize("name", sorted(EXTRA))
+def test_full_size_sampled_other_caches(name):
+    _sampled(EXTRA[name](), 11)
