@@ -33,6 +33,14 @@
 // Loads are 128-bit where the row allows; each K instruction reads whole
 // 64-byte pieces of 16 K rows, each V instruction (D/2) contiguous bytes of
 // 4 V rows per 16 lanes.
+//
+// Caches: paged (f16 or f32 pool through a block table), tiered (a paged int8
+// or f16 cold tier below cold_lens[b], then an f16 ring), window ring (the
+// tiered path with no cold tier: the last hot_window tokens), block-sparse
+// (the union of the GQA group's CSR rows over the paged f16 pool).  With
+// several queries per sequence the 16 score columns hold (query, head)
+// pairs -- column r is query r / G, head r % G -- and each lane masks its
+// column with its own query's causal / window bound.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
