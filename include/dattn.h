@@ -91,6 +91,9 @@ typedef struct dattn_params {
   int32_t query_len;          /* queries per sequence, 0 or 1 => one; > 1: multi-query decode
                                  (paged, tiered and window-ring caches; query_len * GQA group
                                  <= 16); see dattn_decode_paged */
+  int32_t q_dtype;            /* storage type of q: DATTN_F32 (0) or DATTN_F16 (converted to f32
+                                 exactly); with DATTN_F16 and out_dtype DATTN_F16 this is the f16
+                                 Q/K/V, f16 output variant (doppler attention_f16.wgsl) */
 } dattn_params;
 
 /*
@@ -125,7 +128,7 @@ int dattn_workspace_size(const dattn_params* p, int32_t kind, int32_t sparse_blo
 /*
  * Paged cache (boostr paged_attention.wgsl: token t of sequence b lives in
  * physical block block_table[b][t / block_size] at offset t % block_size).
- *   q            [B, H, D] f32
+ *   q            [B, H, D] f32, or f16 per p->q_dtype; 16-byte aligned
  *   k_cache,
  *   v_cache      [num_blocks, block_size, Hkv, D], f32 or f16 per kv_dtype
  *   block_table  [B, max_blocks_per_seq] i32
@@ -142,7 +145,7 @@ int dattn_workspace_size(const dattn_params* p, int32_t kind, int32_t sparse_blo
  * (sequence, kv head), for all Qn * G query rows of the group.  The tiered and
  * window-ring entry points take query_len the same way.
  */
-int dattn_decode_paged(const dattn_params* p, const float* q, const void* k_cache, const void* v_cache,
+int dattn_decode_paged(const dattn_params* p, const void* q, const void* k_cache, const void* v_cache,
                        int32_t kv_dtype, const int32_t* block_table, const int32_t* seq_lens,
                        const int32_t* q_pos, void* out, float* lse, void* workspace, size_t workspace_bytes,
                        void* stream);
@@ -164,7 +167,7 @@ int dattn_decode_paged(const dattn_params* p, const float* q, const void* k_cach
  *   seq_lens, cold_lens   [B] i32
  *   q_pos, out, lse       as for dattn_decode_paged
  */
-int dattn_decode_tiered_int8(const dattn_params* p, const float* q, const uint16_t* k_hot,
+int dattn_decode_tiered_int8(const dattn_params* p, const void* q, const uint16_t* k_hot,
                              const uint16_t* v_hot, int32_t hot_window, const uint32_t* k_cold,
                              const uint32_t* v_cold, const uint16_t* k_scale, const uint16_t* v_scale,
                              const int32_t* cold_block_table, const int32_t* seq_lens, const int32_t* cold_lens,
@@ -186,7 +189,7 @@ int dattn_decode_tiered_int8(const dattn_params* p, const float* q, const uint16
  *   q_pos, out, lse       as for dattn_decode_paged
  * Workspace size: kind DATTN_KIND_TIERED_F16.
  */
-int dattn_decode_tiered_f16(const dattn_params* p, const float* q, const uint16_t* k_hot, const uint16_t* v_hot,
+int dattn_decode_tiered_f16(const dattn_params* p, const void* q, const uint16_t* k_hot, const uint16_t* v_hot,
                             int32_t hot_window, const uint16_t* k_cold, const uint16_t* v_cold,
                             const int32_t* cold_block_table, const int32_t* seq_lens, const int32_t* cold_lens,
                             const int32_t* q_pos, void* out, float* lse, void* workspace, size_t workspace_bytes,
@@ -205,7 +208,7 @@ int dattn_decode_tiered_f16(const dattn_params* p, const float* q, const uint16_
  * block_size, max_blocks_per_seq and num_blocks in p are ignored.  Workspace
  * size: kind DATTN_KIND_RING_F16.
  */
-int dattn_decode_ring_f16(const dattn_params* p, const float* q, const uint16_t* k_ring, const uint16_t* v_ring,
+int dattn_decode_ring_f16(const dattn_params* p, const void* q, const uint16_t* k_ring, const uint16_t* v_ring,
                           const int32_t* seq_lens, const int32_t* q_pos, void* out, float* lse, void* workspace,
                           size_t workspace_bytes, void* stream);
 
@@ -222,7 +225,7 @@ int dattn_decode_ring_f16(const dattn_params* p, const float* q, const uint16_t*
  *   other arrays  as for dattn_decode_paged with kv_dtype = DATTN_F16
  * Needs q / sparse_block < row_stride - 1 (rows beyond select nothing).
  */
-int dattn_decode_block_sparse(const dattn_params* p, const float* q, const uint16_t* k_cache,
+int dattn_decode_block_sparse(const dattn_params* p, const void* q, const uint16_t* k_cache,
                               const uint16_t* v_cache, const int32_t* block_table, const int32_t* seq_lens,
                               const int32_t* q_pos, int32_t sparse_block, int32_t num_layouts,
                               const int32_t* row_ptr, int32_t row_stride, const int32_t* col_idx,

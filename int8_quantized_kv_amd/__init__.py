@@ -19,6 +19,7 @@ Cache layouts (C-contiguous):
   k_ring, v_ring    [B, W, Hkv, D]             float16 (the window ring, W = sliding window)
   row_ptr           [num_layouts, rows + 1]    int32
   col_idx           [num_layouts, col_stride]  int32
+q may also be float16 (converted exactly).
 Outputs: out [B, H, D] float32 or float16 (out_dtype), lse [B, H] float32;
 want_out=False writes lse only.
 """
@@ -65,6 +66,7 @@ class DattnParams(ctypes.Structure):
         ("phases", ctypes.c_int32),
         ("out_dtype", ctypes.c_int32),
         ("query_len", ctypes.c_int32),
+        ("q_dtype", ctypes.c_int32),
     ]
 
 
@@ -163,8 +165,10 @@ def _params(q, Hkv, D, bs, max_blocks, num_blocks, max_seq_len, scale, causal, s
     B, H = q.shape[0], q.shape[-2]
     qn = q.shape[1] if q.dim() == 4 else 1
     code = F32 if out_dtype is None else _out_code(out_dtype)
+    torch = _torch()
     return DattnParams(B, H, Hkv, D, float(scale), int(causal), int(sliding_window), float(softcap), bs, max_blocks,
-                       num_blocks, int(max_seq_len), int(split_tokens), int(phases), code, qn)
+                       num_blocks, int(max_seq_len), int(split_tokens), int(phases), code, qn,
+                       F16 if q.dtype == torch.float16 else F32)
 
 
 def _outputs(q, out, lse, want_lse, workspace, ws_bytes, out_dtype=None, want_out=True):
@@ -216,7 +220,7 @@ def dattn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, *, q_pos=None
     seq_lens - Qn); out and lse then carry the Qn axis too."""
     torch = _torch()
     dev = q.device
-    _need(q, "q", (torch.float32,), q.dim() if q.dim() in (3, 4) else 3, dev)
+    _need(q, "q", (torch.float32, torch.float16), q.dim() if q.dim() in (3, 4) else 3, dev)
     _need(k_cache, "k_cache", (torch.float16, torch.float32), 4, dev)
     _need(v_cache, "v_cache", (k_cache.dtype,), 4, dev)
     _need(block_table, "block_table", (torch.int32,), 2, dev)
@@ -248,7 +252,7 @@ def dattn_decode_tiered_int8(q, k_hot, v_hot, k_cold, v_cold, k_scale, v_scale, 
     q [B, Qn, H, D] asks for Qn queries per sequence, as for dattn_decode_paged."""
     torch = _torch()
     dev = q.device
-    _need(q, "q", (torch.float32,), q.dim() if q.dim() in (3, 4) else 3, dev)
+    _need(q, "q", (torch.float32, torch.float16), q.dim() if q.dim() in (3, 4) else 3, dev)
     _need(k_hot, "k_hot", (torch.float16,), 4, dev)
     _need(v_hot, "v_hot", (torch.float16,), 4, dev)
     _need(k_cold, "k_cold", (torch.int32, torch.uint32), 4, dev)
@@ -288,7 +292,7 @@ def dattn_decode_tiered_f16(q, k_hot, v_hot, k_cold, v_cold, cold_block_table, s
     q [B, Qn, H, D] asks for Qn queries per sequence, as for dattn_decode_paged."""
     torch = _torch()
     dev = q.device
-    _need(q, "q", (torch.float32,), q.dim() if q.dim() in (3, 4) else 3, dev)
+    _need(q, "q", (torch.float32, torch.float16), q.dim() if q.dim() in (3, 4) else 3, dev)
     _need(k_hot, "k_hot", (torch.float16,), 4, dev)
     _need(v_hot, "v_hot", (torch.float16,), 4, dev)
     _need(k_cold, "k_cold", (torch.float16,), 4, dev)
@@ -324,7 +328,7 @@ def dattn_decode_ring_f16(q, k_ring, v_ring, seq_lens, *, q_pos=None, scale: flo
     per sequence, as for dattn_decode_paged."""
     torch = _torch()
     dev = q.device
-    _need(q, "q", (torch.float32,), q.dim() if q.dim() in (3, 4) else 3, dev)
+    _need(q, "q", (torch.float32, torch.float16), q.dim() if q.dim() in (3, 4) else 3, dev)
     _need(k_ring, "k_ring", (torch.float16,), 4, dev)
     _need(v_ring, "v_ring", (torch.float16,), 4, dev)
     _need(seq_lens, "seq_lens", (torch.int32,), 1, dev)
@@ -385,7 +389,7 @@ def dattn_decode_block_sparse(q, k_cache, v_cache, block_table, seq_lens, sparse
     """Decode attention over the paged f16 cache restricted by per-head CSR block masks."""
     torch = _torch()
     dev = q.device
-    _need(q, "q", (torch.float32,), 3, dev)
+    _need(q, "q", (torch.float32, torch.float16), 3, dev)
     _need(k_cache, "k_cache", (torch.float16,), 4, dev)
     _need(v_cache, "v_cache", (torch.float16,), 4, dev)
     _need(block_table, "block_table", (torch.int32,), 2, dev)

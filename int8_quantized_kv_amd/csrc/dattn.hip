@@ -131,6 +131,8 @@ int check_params(const dattn_params* p, int kind) {
   if (p->out_dtype != DATTN_F32 && p->out_dtype != DATTN_F16)
     return fail(DATTN_ERR_INVALID, "out_dtype must be DATTN_F32 or DATTN_F16 (got %d)", p->out_dtype);
   if (p->query_len < 0) return fail(DATTN_ERR_INVALID, "query_len must be >= 0 (got %d)", p->query_len);
+  if (p->q_dtype != DATTN_F32 && p->q_dtype != DATTN_F16)
+    return fail(DATTN_ERR_INVALID, "q_dtype must be DATTN_F32 or DATTN_F16 (got %d)", p->q_dtype);
   if (p->query_len > 1) {
     if (kind == DATTN_KIND_BLOCK_SPARSE)
       return fail(DATTN_ERR_UNSUPPORTED, "query_len > 1 is not built for the block-sparse cache");
@@ -273,7 +275,7 @@ Balanced plan_balanced(const dattn_params* p, const Plan& pl, const void* fn) {
   return bl;
 }
 
-dattn::DecodeArgs base_args(const dattn_params* p, const Plan& pl, const float* q, void* ws) {
+dattn::DecodeArgs base_args(const dattn_params* p, const Plan& pl, const void* q, void* ws) {
   dattn::DecodeArgs a{};
   a.q = q;
   a.part_acc = (float*)ws;
@@ -289,6 +291,7 @@ dattn::DecodeArgs base_args(const dattn_params* p, const Plan& pl, const float* 
   a.qn = p->query_len > 1 ? p->query_len : 1;
   a.grp = p->num_heads / p->num_kv_heads;
   a.heads_out = a.qn * p->num_heads;
+  a.q_f16 = p->q_dtype == DATTN_F16;
   const double scale = p->scale != 0.0f ? (double)p->scale : (double)(float)(1.0 / sqrt((double)p->head_dim));
   const double log2e = 1.4426950408889634;
   if (p->softcap > 0.0f) {
@@ -392,7 +395,7 @@ int dattn_workspace_size(const dattn_params* p, int32_t kind, int32_t sparse_blo
   return DATTN_OK;
 }
 
-int dattn_decode_paged(const dattn_params* p, const float* q, const void* k_cache, const void* v_cache,
+int dattn_decode_paged(const dattn_params* p, const void* q, const void* k_cache, const void* v_cache,
                        int32_t kv_dtype, const int32_t* block_table, const int32_t* seq_lens, const int32_t* q_pos,
                        void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
   g_err.clear();
@@ -425,7 +428,7 @@ int dattn_decode_paged(const dattn_params* p, const float* q, const void* k_cach
   return launch(fn, bal, p, pl, a, out, lse, (hipStream_t)stream);
 }
 
-int dattn_decode_tiered_int8(const dattn_params* p, const float* q, const uint16_t* k_hot, const uint16_t* v_hot,
+int dattn_decode_tiered_int8(const dattn_params* p, const void* q, const uint16_t* k_hot, const uint16_t* v_hot,
                              int32_t hot_window, const uint32_t* k_cold, const uint32_t* v_cold,
                              const uint16_t* k_scale, const uint16_t* v_scale, const int32_t* cold_block_table,
                              const int32_t* seq_lens, const int32_t* cold_lens, const int32_t* q_pos, void* out,
@@ -466,7 +469,7 @@ int dattn_decode_tiered_int8(const dattn_params* p, const float* q, const uint16
                 (hipStream_t)stream);
 }
 
-int dattn_decode_tiered_f16(const dattn_params* p, const float* q, const uint16_t* k_hot, const uint16_t* v_hot,
+int dattn_decode_tiered_f16(const dattn_params* p, const void* q, const uint16_t* k_hot, const uint16_t* v_hot,
                             int32_t hot_window, const uint16_t* k_cold, const uint16_t* v_cold,
                             const int32_t* cold_block_table, const int32_t* seq_lens, const int32_t* cold_lens,
                             const int32_t* q_pos, void* out, float* lse, void* workspace, size_t workspace_bytes,
@@ -504,7 +507,7 @@ int dattn_decode_tiered_f16(const dattn_params* p, const float* q, const uint16_
                 p, pl, a, out, lse, (hipStream_t)stream);
 }
 
-int dattn_decode_ring_f16(const dattn_params* p_in, const float* q, const uint16_t* k_ring, const uint16_t* v_ring,
+int dattn_decode_ring_f16(const dattn_params* p_in, const void* q, const uint16_t* k_ring, const uint16_t* v_ring,
                           const int32_t* seq_lens, const int32_t* q_pos, void* out, float* lse, void* workspace,
                           size_t workspace_bytes, void* stream) {
   g_err.clear();
@@ -538,7 +541,7 @@ int dattn_decode_ring_f16(const dattn_params* p_in, const float* q, const uint16
                 p, pl, a, out, lse, (hipStream_t)stream);
 }
 
-int dattn_decode_block_sparse(const dattn_params* p, const float* q, const uint16_t* k_cache,
+int dattn_decode_block_sparse(const dattn_params* p, const void* q, const uint16_t* k_cache,
                               const uint16_t* v_cache, const int32_t* block_table, const int32_t* seq_lens,
                               const int32_t* q_pos, int32_t sparse_block, int32_t num_layouts,
                               const int32_t* row_ptr, int32_t row_stride, const int32_t* col_idx, int32_t col_stride,

@@ -74,7 +74,7 @@ constexpr float kLn2 = 0.69314718055994531f;
 
 // Kernel arguments (one struct for every kind; unused fields are zero).
 struct DecodeArgs {
-  const float* q;            // [B, H, D]
+  const void* q;             // [B, H, D] (or [B, qn, H, D]) f32, or f16 when q_f16
   const void* k;             // paged pool [NB, bs, Hkv, D] (f16/f32) or cold words [NB, bs, Hkv, D/4]
   const void* v;
   const uint16_t* k_scale;   // cold scales [NB, bs, Hkv]
@@ -96,6 +96,7 @@ struct DecodeArgs {
   int32_t qn;         // queries per sequence (multi-query decode), >= 1
   int32_t grp;        // GQA group size H / Hkv
   int32_t heads_out;  // qn * num_heads: rows per slot of the partials and of out
+  int32_t q_f16;      // 1: q holds f16 values (converted to f32 exactly)
   int32_t sparse_block, num_layouts, row_stride, col_stride, sparse_nblk;
   float qmul;    // scale * log2(e) without softcap, 2 log2(e) * scale / cap with softcap
   float capl2;   // cap * log2(e), 0 without softcap
@@ -246,6 +247,12 @@ __device__ __forceinline__ int qdim(int c, int g) {
   return I8MAP ? 64 * (c >> 1) + 16 * g + 8 * (c & 1) : 32 * c + 8 * g;
 }
 
+// Half `i` (0: low, 1: high) of the 32-bit pattern in w, as a float.
+__device__ __forceinline__ float half_at(float w, int i) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, w);
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(i ? u >> 16 : u & 0xFFFFu));
+}
+
 template <int D>
 struct QRaw16 {
   f4 x[D / 16];
@@ -273,12 +280,22 @@ __device__ __forceinline__ size_t q_row(const DecodeArgs& a, int b, int kvh, int
 template <int D, int G, bool I8MAP, bool MQ = false>
 __device__ __forceinline__ void load_q_raw16(const DecodeArgs& a, int b, int kvh, int lane, QRaw16<D>& r) {
   const int j = lane & 15, g = lane >> 4;
-  const float* qrow = a.q + q_row<G, MQ>(a, b, kvh, j) * D;
+  const size_t row = q_row<G, MQ>(a, b, kvh, j) * D;
+  if (a.q_f16) {   // the 8 halves stay raw in x[2c] until convert_q
+    const _Float16* qrow = (const _Float16*)a.q + row;
 #pragma unroll
-  for (int c = 0; c < D / 32; ++c) {
-    const int d0 = qdim<I8MAP>(c, g);
-    r.x[2 * c] = *(const f4*)(qrow + d0);
-    r.x[2 * c + 1] = *(const f4*)(qrow + d0 + 4);
+    for (int c = 0; c < D / 32; ++c) {
+      r.x[2 * c] = __builtin_bit_cast(f4, *(const u4*)(qrow + qdim<I8MAP>(c, g)));
+      r.x[2 * c + 1] = f4{0.f, 0.f, 0.f, 0.f};   // defined on both paths: keeps r in registers
+    }
+  } else {
+    const float* qrow = (const float*)a.q + row;
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c) {
+      const int d0 = qdim<I8MAP>(c, g);
+      r.x[2 * c] = *(const f4*)(qrow + d0);
+      r.x[2 * c + 1] = *(const f4*)(qrow + d0 + 4);
+    }
   }
 }
 
@@ -287,8 +304,12 @@ __device__ __forceinline__ void convert_q(const DecodeArgs& a, int lane, const Q
   const bool live = (lane & 15) < (MQ ? a.grp * a.qn : G);
 #pragma unroll
   for (int c = 0; c < D / 32; ++c) {
-    const float x[8] = {r.x[2 * c].x, r.x[2 * c].y, r.x[2 * c].z, r.x[2 * c].w,
-                        r.x[2 * c + 1].x, r.x[2 * c + 1].y, r.x[2 * c + 1].z, r.x[2 * c + 1].w};
+    const f4 x0 = r.x[2 * c], x1 = r.x[2 * c + 1];
+    const float f[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+    const float w[4] = {x0.x, x0.y, x0.z, x0.w};   // the raw halves, two per word, when q is f16
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = a.q_f16 ? half_at(w[e >> 1], e & 1) : f[e];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float v = live ? x[e] * a.qmul : 0.0f;
@@ -312,9 +333,20 @@ struct QF32 {
 template <int D, int G, bool MQ = false>
 __device__ __forceinline__ void load_q_raw32(const DecodeArgs& a, int b, int kvh, int lane, QRaw32<D>& r) {
   const int j = lane & 15, g = lane >> 4;
-  const float* qrow = a.q + q_row<G, MQ>(a, b, kvh, j) * D;
+  const size_t row = q_row<G, MQ>(a, b, kvh, j) * D;
+  if (a.q_f16) {   // 4 halves raw in the low half of x[m] until convert_q
+    const _Float16* qrow = (const _Float16*)a.q + row;
 #pragma unroll
-  for (int m = 0; m < D / 16; ++m) r.x[m] = *(const f4*)(qrow + 16 * m + 4 * g);
+    for (int m = 0; m < D / 16; ++m) {
+      const u2v w = *(const u2v*)(qrow + 16 * m + 4 * g);
+      const uint32_t w0 = w.x, w1 = w.y;   // bit casts take whole values, not vector elements
+      r.x[m] = f4{__builtin_bit_cast(float, w0), __builtin_bit_cast(float, w1), 0.0f, 0.0f};
+    }
+  } else {
+    const float* qrow = (const float*)a.q + row;
+#pragma unroll
+    for (int m = 0; m < D / 16; ++m) r.x[m] = *(const f4*)(qrow + 16 * m + 4 * g);
+  }
 }
 
 template <int D, int G, bool MQ = false>
@@ -322,10 +354,12 @@ __device__ __forceinline__ void convert_q(const DecodeArgs& a, int lane, const Q
   const bool live = (lane & 15) < (MQ ? a.grp * a.qn : G);
 #pragma unroll
   for (int m = 0; m < D / 16; ++m) {
-    qf.v[4 * m + 0] = live ? r.x[m].x * a.qmul : 0.0f;
-    qf.v[4 * m + 1] = live ? r.x[m].y * a.qmul : 0.0f;
-    qf.v[4 * m + 2] = live ? r.x[m].z * a.qmul : 0.0f;
-    qf.v[4 * m + 3] = live ? r.x[m].w * a.qmul : 0.0f;
+    const f4 y = r.x[m];   // the raw halves, two per word in .x and .y, when q is f16
+    const f4 x = a.q_f16 ? f4{half_at(y.x, 0), half_at(y.x, 1), half_at(y.y, 0), half_at(y.y, 1)} : y;
+    qf.v[4 * m + 0] = live ? x.x * a.qmul : 0.0f;
+    qf.v[4 * m + 1] = live ? x.y * a.qmul : 0.0f;
+    qf.v[4 * m + 2] = live ? x.z * a.qmul : 0.0f;
+    qf.v[4 * m + 3] = live ? x.w * a.qmul : 0.0f;
   }
 }
 

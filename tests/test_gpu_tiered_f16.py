@@ -167,3 +167,29 @@ def test_lse_only(idx):
     lg = lse.cpu().numpy()
     assert np.all(lg[~full] == -np.inf)
     assert np.max(np.abs(lg[full] - lrf[full])) <= 1e-3
+
+
+def _f16_q_cases():
+    return _mode_cases() + [
+        synth.paged_case(316, 2, 32, 8, 128, 16, lens=[700, 90], query_len=4),
+        synth.ring_case(317, 2, 32, 8, 128, 256, [600, 100], softcap=20.0),
+    ]
+
+
+@pytest.mark.parametrize("idx", range(7))
+def test_f16_q_input_equals_its_f32_copy(idx):
+    """q stored as f16 is converted to f32 exactly, so the result must equal, bit for
+    bit, the call on the f32 copy of the same values (and match the oracle on them)."""
+    import torch
+    case = _f16_q_cases()[idx]
+    dc = DeviceCase(case)
+    q16 = dc.q.half()
+    dc.q = q16.float()
+    o32, l32 = dc.run()
+    dc.q = q16
+    o16, l16 = dc.run(out_dtype=torch.float16)
+    torch.cuda.synchronize()
+    assert torch.equal(o16, o32.to(torch.float16)) and torch.equal(l16, l32), f"case {idx}"
+    case.q = q16.float().cpu().numpy()
+    orf, lrf = oracle_run(case)
+    compare(o32.cpu().numpy(), l32.cpu().numpy(), orf, lrf, what=f"f16 q case {idx}")
