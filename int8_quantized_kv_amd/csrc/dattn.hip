@@ -54,6 +54,7 @@ struct Plan {
 constexpr int kMaxWorkers = 1024;
 constexpr int kMaxBalancedSeqs = 4096;
 constexpr size_t kMaxBalancedLds = 16384;
+constexpr int64_t kMinWorkerUnits = 16;   // about 128 keys of the bound below per worker
 
 // Per-device cache of the CU count and of kernel occupancies.
 std::mutex g_mu;
@@ -268,6 +269,11 @@ Balanced plan_balanced(const dattn_params* p, const Plan& pl, const void* fn) {
   // tile plus the start-up units of every sequence.
   const int64_t tmax = ((int64_t)p->max_seq_len + 15) / 16 + 1;
   const int64_t nmax = (int64_t)p->num_seqs * (2 * tmax + dattn::kSeqUnits);
+  // A small call gets no more workers than it can feed with kMinWorkerUnits
+  // units each (by the bound nmax): a resident round of mostly idle workers
+  // costs more than the work itself.
+  const int64_t feed = (nmax + kMinWorkerUnits - 1) / kMinWorkerUnits;
+  if (feed < bl.workers) bl.workers = (int)(feed > 0 ? feed : 1);
   const int64_t cmax = (nmax + bl.workers - 1) / bl.workers;
   const int64_t entries = pl.no_table ? 0 : cmax * 16 / p->block_size + 2;
   bl.lds = (size_t)(((p->num_seqs + 4) & ~3) + entries) * sizeof(int32_t);
