@@ -1,7 +1,7 @@
 // dattn.hip -- host side of the C ABI declared in include/dattn.h:
 // argument validation (before any HIP call), split planning, workspace
-// layout and the two launches (split kernel, combine kernel) on the caller's
-// stream.
+// layout and the launches on the caller's stream: split kernel and combine
+// kernel for a decode call, one kernel for the tiered write path.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdarg.h>
@@ -54,7 +54,7 @@ struct Plan {
 constexpr int kMaxWorkers = 1024;
 constexpr int kMaxBalancedSeqs = 4096;
 constexpr size_t kMaxBalancedLds = 16384;
-constexpr int64_t kMinWorkerUnits = 16;   // about 128 keys of the bound below per worker
+constexpr int64_t kMinWorkerUnits = 16;   // units of the host-side work bound per worker (about 8 tiles)
 
 // Per-device cache of the CU count and of kernel occupancies.
 std::mutex g_mu;

@@ -1058,9 +1058,6 @@ __device__ __forceinline__ void table_span(const DecodeArgs& a, int t0, int t1, 
   }
 }
 
-// Sweep keys [tb, te) of sequence b for one kv head of a paged cache and write
-// the partial to dst.  Every wave of the workgroup calls it with the same
-// (b, tb, te): the block-table staging is shared.
 // Several queries per sequence: the visible keys [qlo, qhi] of the query whose
 // (query, head) pair is this lane's score column (column r: query r / grp);
 // an unused column (r >= grp * qn) sees nothing.
@@ -1073,8 +1070,11 @@ __device__ __forceinline__ void query_bounds(const DecodeArgs& a, int b, int lan
   if (c >= a.grp * a.qn) qlo = qhi + 1;
 }
 
-// MQ: several queries per sequence (G = 16 columns, a.grp * a.qn of them
-// used); the lane's query bounds [qlo, qhi] mask its column.
+// Sweep keys [tb, te) of sequence b for one kv head of a paged cache and write
+// the partial to dst.  Every wave of the workgroup calls it with the same
+// (b, tb, te): the block-table staging is shared.  MQ: several queries per
+// sequence (G = 16 columns, a.grp * a.qn of them used); the lane's query
+// bounds [qlo, qhi] mask its column.
 template <int D, int G, bool CAP, class T, bool FM, bool MQ = false>
 __device__ __forceinline__ void paged_segment(const DecodeArgs& a, int b, int kvh, int lane, int tb, int te,
                                               int32_t* lds_tbl, const PartialDst& dst) {
