@@ -116,6 +116,8 @@ def load(path: str = _LIB):
     lib.orc_quantize_row.restype = None
     lib.orc_append_tiered_int8.argtypes = [ctypes.POINTER(_Params), P, P, P, P, i32, P, P, P, P, P, P, P]
     lib.orc_append_tiered_int8.restype = ctypes.c_int
+    lib.orc_append_ring_f16.argtypes = [ctypes.POINTER(_Params), P, P, P, P, P]
+    lib.orc_append_ring_f16.restype = ctypes.c_int
     _libs[path] = lib
     return lib
 
@@ -352,3 +354,16 @@ def append_tiered_int8(p: Params, k_new, v_new, k_hot, v_hot, hot_window, k_cold
                                     _ptr(kc), _ptr(vc), _ptr(ks), _ptr(vs), _ptr(bt), _ptr(sl), _ptr(cl))
     _check(rc, "orc_append_tiered_int8")
     return kh, vh, kc, vc, ks, vs, sl, cl
+
+
+def append_ring_f16(p: Params, k_new, v_new, k_ring, v_ring, seq_lens, lib=None):
+    """One token per sequence into a window ring [B, W, Hkv, D] f16 (W = p.sliding_window),
+    at slot seq_len mod W; returns copies (k_ring, v_ring, seq_lens)."""
+    lib = _load(lib)
+    kn, vn = _arr(k_new, np.float16), _arr(v_new, np.float16)
+    kr, vr = np.array(k_ring, np.float16, copy=True), np.array(v_ring, np.float16, copy=True)
+    sl = np.array(seq_lens, np.int32, copy=True)
+    cp = p.c()
+    _check(lib.orc_append_ring_f16(ctypes.byref(cp), _ptr(kn), _ptr(vn), _ptr(kr), _ptr(vr), _ptr(sl)),
+           "orc_append_ring_f16")
+    return kr, vr, sl

@@ -78,6 +78,9 @@
  * i = clamp(rint(x / f32(s)), -127, 127) in f32, an all-zero row giving
  * s = 0 and i = 0.
  *
+ * The window ring's write path (orc_append_ring_f16) stores the new token at
+ * slot seq_len[b] mod W, overwriting the token that leaves the window.
+ *
  * Every function validates its inputs enough never to read out of bounds and
  * returns a negative code otherwise.
  */
@@ -600,6 +603,32 @@ int orc_append_tiered_int8(const orc_params* p, const uint16_t* k_new, const uin
     }
     seq_lens[b] = (int32_t)(L + 1);
     cold_lens[b] = (int32_t)C;
+  }
+  return ORC_OK;
+}
+
+/* Window-ring write path: the new token of sequence b goes to slot
+ * seq_len[b] mod W (W = sliding_window), overwriting the token W positions
+ * older -- the one that leaves the window -- and seq_len[b] grows by one
+ * (the slot rule of doppler attention_f16kv.wgsl, get_kv_pos with the ring
+ * layout).  Refuses the call, nothing written, if W < 1 or a seq_len is
+ * negative. */
+int orc_append_ring_f16(const orc_params* p, const uint16_t* k_new, const uint16_t* v_new, uint16_t* k_ring,
+                        uint16_t* v_ring, int32_t* seq_lens) {
+  const int32_t B = p->num_seqs, Hkv = p->num_kv_heads, D = p->head_dim, W = p->sliding_window;
+  if (B < 0 || Hkv < 1 || D < 1 || W < 1) return ORC_EINVAL;
+  for (int32_t b = 0; b < B; ++b)
+    if (seq_lens[b] < 0 || seq_lens[b] >= INT32_MAX) return ORC_EINVAL;
+  for (int32_t b = 0; b < B; ++b) {
+    const int64_t L = seq_lens[b];
+    const int64_t slot = L % W;
+    for (int32_t g = 0; g < Hkv; ++g) {
+      const size_t dst = (((size_t)b * W + slot) * Hkv + g) * D;
+      const size_t src = ((size_t)b * Hkv + g) * D;
+      memcpy(k_ring + dst, k_new + src, (size_t)D * sizeof(uint16_t));
+      memcpy(v_ring + dst, v_new + src, (size_t)D * sizeof(uint16_t));
+    }
+    seq_lens[b] = (int32_t)(L + 1);
   }
   return ORC_OK;
 }

@@ -54,6 +54,9 @@ MUTANTS = {
     "ring_keeps_one_more": ("if (resident > 0 && t < L - resident) continue;",
                             "if (resident > 0 && t < L - resident - 1) continue;"),
     "ring_residency_ignored": ("if (resident > 0 && t < L - resident) continue;", "(void)resident;"),
+    "ring_append_next_slot": ("const int64_t slot = L % W;", "const int64_t slot = (L + 1) % W;"),
+    "ring_append_length_kept": ("    seq_lens[b] = (int32_t)(L + 1);\n  }\n  return ORC_OK;\n}\n",
+                                "    seq_lens[b] = (int32_t)(L + 0);\n  }\n  return ORC_OK;\n}\n"),
     "mq_all_queries_at_first_position": (
         "return (q_pos ? (int64_t)q_pos[b] : (int64_t)seq_lens[b] - queries(p)) + i;",
         "return (q_pos ? (int64_t)q_pos[b] : (int64_t)seq_lens[b] - queries(p)) + 0 * i;"),

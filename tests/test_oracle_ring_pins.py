@@ -106,3 +106,46 @@ def test_ring_needs_a_window():
     rc.params["sliding_window"] = 0
     with pytest.raises(oracle.OracleError):
         _run(rc)
+
+
+# ----------------------------------------------------------- the write path
+
+def _ring_of_history(k_hist, v_hist, lens, W):
+    """The ring a token history must leave: slot t mod W holds token t for the last W
+    tokens of each sequence; slots no token reached keep their initial +-300."""
+    B, _, Hkv, D = k_hist.shape
+    kr = np.full((B, W, Hkv, D), 300.0, np.float16)
+    vr = np.full((B, W, Hkv, D), -300.0, np.float16)
+    for b, L in enumerate(lens):
+        for t in range(max(0, L - W), L):
+            kr[b, t % W] = k_hist[b, t]
+            vr[b, t % W] = v_hist[b, t]
+    return kr, vr
+
+
+@pytest.mark.parametrize("W,start,steps", [(4, [0, 3], 9), (16, [20, 0], 20), (1, [2, 5], 3), (7, [7, 6], 1)])
+def test_ring_appends_leave_the_ring_of_the_history(W, start, steps):
+    rng = np.random.default_rng(W * 31 + steps)
+    B, Hkv, D = 2, 2, 16
+    T = [s + steps for s in start]
+    k = rng.standard_normal((B, max(T), Hkv, D)).astype(np.float16)
+    v = rng.standard_normal((B, max(T), Hkv, D)).astype(np.float16)
+    kr, vr = _ring_of_history(k, v, start, W)
+    sl = np.array(start, np.int32)
+    p = oracle.Params(B, 2 * Hkv, Hkv, D, sliding_window=W, block_size=1, max_blocks_per_seq=1, num_blocks=1)
+    for i in range(steps):
+        kn = np.stack([k[b, start[b] + i] for b in range(B)])
+        vn = np.stack([v[b, start[b] + i] for b in range(B)])
+        kr, vr, sl = oracle.append_ring_f16(p, kn, vn, kr, vr, sl)
+    want_k, want_v = _ring_of_history(k, v, T, W)
+    assert np.array_equal(kr.view(np.uint16), want_k.view(np.uint16))
+    assert np.array_equal(vr.view(np.uint16), want_v.view(np.uint16))
+    assert list(sl) == T
+
+
+def test_ring_append_rejects_a_missing_window():
+    p = oracle.Params(1, 2, 1, 16, sliding_window=0, block_size=1, max_blocks_per_seq=1, num_blocks=1)
+    z = np.zeros((1, 1, 16), np.float16)
+    with pytest.raises(oracle.OracleError):
+        oracle.append_ring_f16(p, z, z, np.zeros((1, 4, 1, 16), np.float16), np.zeros((1, 4, 1, 16), np.float16),
+                               np.int32([3]))
