@@ -267,6 +267,22 @@ int dattn_append_tiered_int8(const dattn_params* p, const uint16_t* k_new, const
                              uint16_t* k_scale, uint16_t* v_scale, const int32_t* cold_block_table,
                              int32_t* seq_lens, int32_t* cold_lens, void* stream);
 
+/*
+ * Write path of the window ring: append one token per sequence.  The new
+ * token k_new[b], v_new[b] goes to slot seq_lens[b] % W (W =
+ * p->sliding_window >= 1), overwriting the token that leaves the window, and
+ * seq_lens[b] becomes seq_lens[b] + 1 (the slot rule of
+ * dattn_decode_ring_f16).
+ *   k_new, v_new    [B, Hkv, D] f16 (bit patterns), read
+ *   k_ring, v_ring  [B, W, Hkv, D] f16, updated
+ *   seq_lens        [B] i32 on the device, advanced in place
+ * Reads num_seqs, num_kv_heads, head_dim (64 or 128) and sliding_window from
+ * p.  Needs no workspace.  A sequence with a negative length is left
+ * unchanged.  Overlapping calls on the same ring race.
+ */
+int dattn_append_ring_f16(const dattn_params* p, const uint16_t* k_new, const uint16_t* v_new, uint16_t* k_ring,
+                          uint16_t* v_ring, int32_t* seq_lens, void* stream);
+
 /* Message for the last non-zero return on this thread ("" if none). */
 const char* dattn_last_error(void);
 

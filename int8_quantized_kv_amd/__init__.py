@@ -31,11 +31,12 @@ import os
 from typing import Optional
 
 __all__ = [
-    "DattnError", "DattnParams", "lib", "library_path", "dattn_workspace_size", "dattn_decode_paged",
-    "dattn_decode_tiered_int8", "dattn_decode_tiered_f16", "dattn_decode_ring_f16", "dattn_decode_block_sparse", "dattn_append_tiered_int8", "dattn_last_error",
-    "dattn_version",
-    "KIND_PAGED", "KIND_TIERED_INT8", "KIND_BLOCK_SPARSE", "KIND_TIERED_F16", "KIND_RING_F16", "F32", "F16", "PHASE_ALL", "PHASE_SPLIT",
-    "PHASE_COMBINE",
+    "DattnError", "DattnParams", "lib", "library_path", "dattn_workspace_size",
+    "dattn_decode_paged", "dattn_decode_tiered_int8", "dattn_decode_tiered_f16", "dattn_decode_ring_f16",
+    "dattn_decode_block_sparse", "dattn_append_tiered_int8", "dattn_append_ring_f16",
+    "dattn_last_error", "dattn_version",
+    "KIND_PAGED", "KIND_TIERED_INT8", "KIND_BLOCK_SPARSE", "KIND_TIERED_F16", "KIND_RING_F16",
+    "F32", "F16", "PHASE_ALL", "PHASE_SPLIT", "PHASE_COMBINE",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -97,9 +98,10 @@ def lib():
         L.dattn_decode_ring_f16.argtypes = [PP, P, P, P, P, P, P, P, P, sz, P]
         L.dattn_decode_block_sparse.argtypes = [PP, P, P, P, P, P, P, i32, i32, P, i32, P, i32, P, P, P, sz, P]
         L.dattn_append_tiered_int8.argtypes = [PP, P, P, P, P, i32, P, P, P, P, P, P, P, P]
+        L.dattn_append_ring_f16.argtypes = [PP, P, P, P, P, P, P]
         for f in (L.dattn_workspace_size, L.dattn_decode_paged, L.dattn_decode_tiered_int8,
                   L.dattn_decode_tiered_f16, L.dattn_decode_ring_f16, L.dattn_decode_block_sparse,
-                  L.dattn_append_tiered_int8):
+                  L.dattn_append_tiered_int8, L.dattn_append_ring_f16):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -417,3 +419,22 @@ def default_scale(head_dim: int) -> float:
     """1/sqrt(head_dim) rounded to f32, the value scale=0 selects."""
     import struct
     return struct.unpack("f", struct.pack("f", 1.0 / math.sqrt(head_dim)))[0]
+
+
+def dattn_append_ring_f16(k_new, v_new, k_ring, v_ring, seq_lens, *, stream=None):
+    """Append one token per sequence (k_new, v_new [B, Hkv, D] f16) to a window ring
+    [B, W, Hkv, D] in place, at slot seq_len mod W; seq_lens (device int32) advance in place."""
+    torch = _torch()
+    dev = k_new.device
+    _need(k_new, "k_new", (torch.float16,), 3, dev)
+    _need(v_new, "v_new", (torch.float16,), 3, dev)
+    _need(k_ring, "k_ring", (torch.float16,), 4, dev)
+    _need(v_ring, "v_ring", (torch.float16,), 4, dev)
+    _need(seq_lens, "seq_lens", (torch.int32,), 1, dev)
+    B, Hkv, D = k_new.shape
+    if tuple(v_new.shape) != (B, Hkv, D) or tuple(v_ring.shape) != tuple(k_ring.shape) or k_ring.shape[0] != B \
+            or k_ring.shape[2] != Hkv or k_ring.shape[3] != D or seq_lens.shape[0] != B:
+        raise ValueError("ring tensors disagree on shape")
+    p = DattnParams(B, Hkv, Hkv, D, 0.0, 0, int(k_ring.shape[1]), 0.0, 1, 1, 1, 0, 0, 0)
+    _check(lib().dattn_append_ring_f16(ctypes.byref(p), _ptr(k_new), _ptr(v_new), _ptr(k_ring), _ptr(v_ring),
+                                       _ptr(seq_lens), _stream(stream)))

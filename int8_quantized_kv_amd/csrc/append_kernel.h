@@ -1,6 +1,7 @@
-// append_kernel.h -- gfx950 write path of the tiered cache: append one token
-// per sequence to the f16 hot ring, first moving the oldest hot token to the
-// paged int8 cold tier when the ring is full (quantise on evict).
+// append_kernel.h -- gfx950 write paths: append one token per sequence to the
+// tiered cache's f16 hot ring, first moving the oldest hot token to the paged
+// int8 cold tier when the ring is full (quantise on evict); and append one
+// token per sequence to a window ring.
 //
 // The ring and the paged cold tier are the layouts the tiered decode reads
 // (doppler attention_decode_tiered_int8_f16kv.wgsl: hot slot = absolute
@@ -136,6 +137,32 @@ __global__ __launch_bounds__(1024) void append_tiered_int8_kernel(AppendArgs a) 
     a.seq_lens[b] = (int32_t)(L + 1);
     a.cold_lens[b] = (int32_t)(evict ? C + 1 : C);
   }
+}
+
+// Window-ring write path: the new token of sequence b goes to slot
+// seq_lens[b] mod W, overwriting the token that leaves the window, and
+// seq_lens[b] grows by one.  One workgroup per sequence, a wave per kv head
+// (strided), lane l < D/4 copying elements 4l .. 4l+3.  A negative length
+// leaves the sequence unchanged.
+template <int D>
+__global__ __launch_bounds__(1024) void append_ring_f16_kernel(const uint16_t* k_new, const uint16_t* v_new,
+                                                               uint16_t* k_ring, uint16_t* v_ring, int32_t* seq_lens,
+                                                               int Hkv, int W) {
+  const int b = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, waves = blockDim.x >> 6;
+  const int64_t L = seq_lens[b];
+  if (L < 0 || L >= 0x7FFFFFFF) return;   // uniform over the workgroup
+  const int64_t slot = L % W;
+  if (lane < D / 4) {
+    for (int g = wave; g < Hkv; g += waves) {
+      const int64_t src = ((int64_t)b * Hkv + g) * D + 4 * lane;
+      const int64_t dst = (((int64_t)b * W + slot) * Hkv + g) * D + 4 * lane;
+      *(uint2*)(k_ring + dst) = *(const uint2*)(k_new + src);
+      *(uint2*)(v_ring + dst) = *(const uint2*)(v_new + src);
+    }
+  }
+  __syncthreads();   // every thread has read seq_lens[b]
+  if (threadIdx.x == 0) seq_lens[b] = (int32_t)(L + 1);
 }
 
 }  // namespace dattn

@@ -614,4 +614,27 @@ int dattn_append_tiered_int8(const dattn_params* p, const uint16_t* k_new, const
   return check_launch("append kernel");
 }
 
+int dattn_append_ring_f16(const dattn_params* p, const uint16_t* k_new, const uint16_t* v_new, uint16_t* k_ring,
+                          uint16_t* v_ring, int32_t* seq_lens, void* stream) {
+  g_err.clear();
+  if (!p) return fail(DATTN_ERR_INVALID, "params is NULL");
+  if (p->num_seqs < 0) return fail(DATTN_ERR_INVALID, "num_seqs must be >= 0 (got %d)", p->num_seqs);
+  if (p->num_kv_heads < 1) return fail(DATTN_ERR_INVALID, "num_kv_heads must be >= 1 (got %d)", p->num_kv_heads);
+  if (p->head_dim != 64 && p->head_dim != 128)
+    return fail(DATTN_ERR_UNSUPPORTED, "head_dim %d not built (64, 128)", p->head_dim);
+  if (p->sliding_window < 1)
+    return fail(DATTN_ERR_INVALID, "the window ring needs sliding_window >= 1 (its slot count)");
+  if (p->num_seqs == 0) return DATTN_OK;
+  if (!k_new || !v_new || !k_ring || !v_ring || !seq_lens) return fail(DATTN_ERR_INVALID, "an array argument is NULL");
+  const int waves = p->num_kv_heads < 16 ? p->num_kv_heads : 16;
+  const dim3 grid(p->num_seqs), block(64 * waves);
+  if (p->head_dim == 64)
+    hipLaunchKernelGGL(dattn::append_ring_f16_kernel<64>, grid, block, 0, (hipStream_t)stream, k_new, v_new, k_ring,
+                       v_ring, seq_lens, p->num_kv_heads, p->sliding_window);
+  else
+    hipLaunchKernelGGL(dattn::append_ring_f16_kernel<128>, grid, block, 0, (hipStream_t)stream, k_new, v_new, k_ring,
+                       v_ring, seq_lens, p->num_kv_heads, p->sliding_window);
+  return check_launch("append kernel");
+}
+
 }  // extern "C"

@@ -32,7 +32,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("dattn_decode_paged", "dattn_decode_tiered_int8", "dattn_decode_tiered_f16", "dattn_decode_ring_f16",
               "dattn_decode_block_sparse",
-              "dattn_append_tiered_int8", "dattn_workspace_size", "dattn_last_error", "dattn_version"):
+              "dattn_append_tiered_int8", "dattn_append_ring_f16", "dattn_workspace_size", "dattn_last_error",
+              "dattn_version"):
         assert n in names
 
 
@@ -259,3 +260,20 @@ def test_append_validates_before_any_hip_call(lib):
     p0 = good_params(num_seqs=0)
     rc = lib.dattn_append_tiered_int8(ctypes.byref(p0), *([None] * 4 + [8] + [None] * 8))
     assert rc == 0 and dk.dattn_last_error() == ""
+
+
+def test_ring_append_validates_before_any_hip_call(lib):
+    P = ctypes.c_void_p
+    fake = P(0x1000)   # never dereferenced: every call below fails validation or is empty
+    for kw, code, word in ((dict(sliding_window=0), dk.ERR_INVALID, "sliding_window"),
+                           (dict(sliding_window=8, head_dim=96), dk.ERR_UNSUPPORTED, "head_dim"),
+                           (dict(sliding_window=8, num_kv_heads=0), dk.ERR_INVALID, "num_kv_heads")):
+        p = good_params(**kw)
+        rc = lib.dattn_append_ring_f16(ctypes.byref(p), fake, fake, fake, fake, fake, None)
+        assert rc == code and word in dk.dattn_last_error(), kw
+    p = good_params(sliding_window=8)
+    rc = lib.dattn_append_ring_f16(ctypes.byref(p), fake, fake, None, fake, fake, None)
+    assert rc == dk.ERR_INVALID and "NULL" in dk.dattn_last_error()
+    rc = lib.dattn_append_ring_f16(ctypes.byref(good_params(num_seqs=0, sliding_window=8)), None, None, None, None,
+                                   None, None)
+    assert rc == 0

@@ -143,3 +143,40 @@ def test_append_leaves_broken_sequences_unchanged():
     assert list(got[6]) == [9, 8, 9] and list(got[7]) == [5, 4, 4]
     assert np.array_equal(got[0][1:].view(np.uint16), k_hot[1:].view(np.uint16))
     assert np.array_equal(got[0][0, 0].view(np.uint16), kn[0].view(np.uint16))   # slot 8 % 4 = 0
+
+
+@pytest.mark.parametrize("D,Hkv,W,start,steps", [(128, 8, 16, [0, 20, 37], 24), (64, 20, 5, [3, 0], 11),
+                                                 (128, 1, 1, [4, 0], 3)])
+def test_ring_append_bit_exact_then_decode(D, Hkv, W, start, steps):
+    import torch
+
+    import int8_quantized_kv_amd as dk
+    import synth
+    rng = np.random.default_rng(D + Hkv * 7 + W)
+    B = len(start)
+    kr = rng.standard_normal((B, W, Hkv, D)).astype(np.float16)
+    vr = rng.standard_normal((B, W, Hkv, D)).astype(np.float16)
+    sl = np.array(start, np.int32)
+    p = oracle.Params(B, Hkv, Hkv, D, sliding_window=W, block_size=1, max_blocks_per_seq=1, num_blocks=1)
+    dkr, dvr, dsl = _dev(kr), _dev(vr), _dev(sl)
+    log(f"ring append D={D} Hkv={Hkv} W={W} start={start} steps={steps}")
+    for i in range(steps):
+        kn = rng.standard_normal((B, Hkv, D)).astype(np.float16)
+        vn = rng.standard_normal((B, Hkv, D)).astype(np.float16)
+        kr, vr, sl = oracle.append_ring_f16(p, kn, vn, kr, vr, sl)
+        dk.dattn_append_ring_f16(_dev(kn), _dev(vn), dkr, dvr, dsl)
+        torch.cuda.synchronize()
+        assert np.array_equal(_host(dkr, kr).view(np.uint16), kr.view(np.uint16)), i
+        assert np.array_equal(_host(dvr, vr).view(np.uint16), vr.view(np.uint16)), i
+        assert np.array_equal(dsl.cpu().numpy(), sl), i
+    # decode over the appended ring
+    G = 4
+    q = rng.standard_normal((B, Hkv * G, D)).astype(np.float32)
+    case = synth.Case("ring", dict(num_seqs=B, num_heads=Hkv * G, num_kv_heads=Hkv, head_dim=D, scale=0.0, causal=1,
+                                   sliding_window=W, softcap=0.0, block_size=1, max_blocks_per_seq=1, num_blocks=1,
+                                   query_len=1), q, sl, None, k_hot=kr, v_hot=vr, hot_window=W)
+    out, lse = dk.dattn_decode_ring_f16(_dev(q), dkr, dvr, dsl, max_seq_len=int(sl.max()))
+    torch.cuda.synchronize()
+    ro, rl = oracle.run(case)
+    compare(out.cpu().numpy(), lse.cpu().numpy(), ro.reshape(B, Hkv * G, D), rl.reshape(B, Hkv * G),
+            what="decode over the appended ring")
