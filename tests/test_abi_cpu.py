@@ -5,6 +5,7 @@ import ctypes
 import os
 import re
 import subprocess
+import sys
 
 import numpy as np
 import pytest
@@ -277,3 +278,9 @@ def test_ring_append_validates_before_any_hip_call(lib):
     rc = lib.dattn_append_ring_f16(ctypes.byref(good_params(num_seqs=0, sliding_window=8)), None, None, None, None,
                                    None, None)
     assert rc == 0
+
+
+def test_bench_refuses_more_than_one_gpu():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr

@@ -1,0 +1,72 @@
+"""GPU parity at the edges of the plans: batches larger than the balanced
+schedule takes (static splits), the largest GQA group and head counts, one
+kv head, head_dim 64 on every cache, and sequences of one key -- checked
+against the oracle on sampled (sequence, head) pairs."""
+import numpy as np
+import pytest
+
+import synth
+from gpu_util import DeviceCase, compare, log, oracle_run
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import int8_quantized_kv_amd as dk
+    dk.lib()
+    yield
+
+
+def _sampled(case, what, n=40):
+    log(f"edge {what}")
+    og, lg = DeviceCase(case).run_np()
+    p = case.params
+    nbh = p["num_seqs"] * max(1, p.get("query_len", 1)) * p["num_heads"]
+    rng = np.random.default_rng(nbh)
+    pairs = np.unique(np.concatenate([[0, nbh - 1], rng.integers(0, nbh, n)])).astype(np.int32)
+    ro, rl = oracle_run(case, pairs=pairs)
+    compare(og.reshape(nbh, -1)[pairs], lg.reshape(nbh)[pairs], ro, rl, what=what)
+
+
+@pytest.mark.parametrize("B", [4096, 5000])
+def test_many_short_sequences(B):
+    # 4096 sequences still fit the balanced schedule's sequence limit; 5000 go to static splits
+    rng = np.random.default_rng(B)
+    lens = rng.integers(1, 65, size=B)
+    c = synth.paged_case(700 + B % 7, B, 32, 8, 128, 16, lens=lens, kv_dtype=synth.F16)
+    _sampled(c, f"paged f16 B{B} L 1-64")
+
+
+def test_largest_group_and_many_heads():
+    c = synth.paged_case(711, 3, 128, 16, 128, 16, lens=[2000, 1, 777], kv_dtype=synth.F16, softcap=30.0)
+    _sampled(c, "H128 / Hkv16 (G8)")
+
+
+def test_one_kv_head_mha_and_gqa():
+    c = synth.paged_case(712, 2, 8, 1, 128, 64, lens=[3000, 100], kv_dtype=synth.F16, window=1000)
+    _sampled(c, "Hkv1 G8 bs64 window 1000")
+    c = synth.paged_case(713, 2, 16, 16, 64, 16, lens=[900, 33], kv_dtype=synth.F16)
+    _sampled(c, "MHA G1 D64")
+
+
+@pytest.mark.parametrize("kind", ["tiered", "tiered_f16", "ring", "sparse"])
+def test_head_dim_64(kind):
+    if kind == "tiered":
+        c = synth.tiered_case(714, 2, 32, 8, 64, 16, [900, 300], [700, 250], 256, softcap=50.0)
+    elif kind == "tiered_f16":
+        c = synth.tiered_f16_case(715, 2, 32, 8, 64, 16, [900, 300], [700, 250], 256)
+    elif kind == "ring":
+        c = synth.ring_case(716, 2, 32, 8, 64, 128, [900, 50])
+    else:
+        c = synth.sparse_case(717, 2, 32, 8, 64, 64, 64, 4, [2048, 700])
+    _sampled(c, f"{kind} D64")
+
+
+def test_single_key_sequences_everywhere():
+    B = 300
+    c = synth.tiered_case(718, B, 32, 8, 128, 16, [1] * B, [i % 2 for i in range(B)], 16)
+    _sampled(c, "tiered, one key per sequence (hot or cold)")
