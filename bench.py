@@ -252,7 +252,8 @@ def measure(case, steps, warmup, copies=None):
     torch.cuda.synchronize()
     split_ms = ev[0].elapsed_time(ev[1]) / steps
     comb_ms = ev[1].elapsed_time(ev[2]) / steps
-    return r, dict(wall_s=wall, split_ms=split_ms, combine_ms=comb_ms, copies=copies)
+    graph_ms = graph_call_ms(r)
+    return r, dict(wall_s=wall, split_ms=split_ms, combine_ms=comb_ms, copies=copies, graph_ms=graph_ms)
 
 
 def measure_append(B=16, Hkv=8, D=128, hot_window=512, bs=16, calls=200, warmup=20):
@@ -342,6 +343,58 @@ def copy_calibration(mib):
     log(f"copy calibration: 5 x torch.neg over {mib} MiB float32")
 
 
+def graph_call_ms(r, reps=20):
+    """Full calls (split + combine), one per cache copy, captured into a HIP graph and
+    replayed `reps` times back to back: a call's GPU time without host-side enqueue
+    cost.  Runs last: afterwards the runner's calls name the capture stream."""
+    import torch
+    n = min(r.copies, 64)   # the tiny workload has thousands of copies; 64 calls per graph suffice
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        r.stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        r.calls = [c[:-1] + (r.stream,) for c in r.calls]
+        for i in range(n):
+            r.call(i, "all")
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / (reps * n)
+
+
+def read_reference(nbytes=300 << 20, copies=4, reps=20):
+    """Read GB/s of the library's plain streaming-read kernel (128-bit nontemporal
+    loads) over buffers rotated past the Infinity Cache: the measured read ceiling."""
+    import torch
+    import int8_quantized_kv_amd as dk
+    srcs = [torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0") for _ in range(copies)]
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    for x in srcs:
+        dk.dattn_stream_read(x, sink)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(reps):
+        dk.dattn_stream_read(srcs[i % copies], sink)
+    e1.record()
+    torch.cuda.synchronize()
+    return round(nbytes * reps / (e0.elapsed_time(e1) / 1e3) / 1e9, 1)
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def copy_reference(nbytes=300 << 20, copies=4, reps=20):
     """Read + write GB/s of torch.neg over float32 buffers rotated past the Infinity
     Cache: what a plain streaming elementwise kernel reaches on this GPU."""
@@ -372,6 +425,7 @@ def cpu_baseline(case, kvb, min_seconds=10.0):
         if el >= min_seconds:
             break
     return dict(value=round(kvb * reps / el / 1e9, 4), unit="GB/s", cores=int(oracle.max_threads()), kind="oracle",
+                cpu_model=cpu_model(),
                 sample=f"whole workload ({case.name}), {reps} run(s) in {el:.1f} s, fp64, OpenMP over (seq, head)",
                 seconds_per_call=round(el / reps, 4))
 
@@ -385,6 +439,7 @@ def line_for(case, steps, warmup, check=True):
                kv_gbs=round(kvb / m["wall_s"] / 1e9, 2), pct_peak=round(100 * kvb / m["wall_s"] / 1e9 / HBM_PEAK_GBS, 2),
                queries_per_s=round(B / m["wall_s"], 1), split_ms=round(m["split_ms"], 5),
                combine_ms=round(m["combine_ms"], 5), split_gbs=round(kvb / (m["split_ms"] / 1e3) / 1e9, 2),
+               graph_ms_per_call=round(m["graph_ms"], 5),
                cache_copies=m["copies"])
     if check:
         # sampled parity of the timed launch configuration against the oracle
@@ -480,7 +535,8 @@ def main():
                    "total_tokens": int(lens.sum()), "parallelism": "single GPU"},
         "pct_of_hbm_peak": head["pct_peak"],
         "queries_per_s": head["queries_per_s"],
-        "kernels": {"split_ms": head["split_ms"], "combine_ms": head["combine_ms"]},
+        "kernels": {"split_ms": head["split_ms"], "combine_ms": head["combine_ms"],
+                    "graph_ms_per_call": head["graph_ms_per_call"]},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(case.name),
                      "kernel": f"split kernel <D={D}, G={G}, {kind}>",
@@ -488,6 +544,9 @@ def main():
         "parity_sample": {k: head[k] for k in ("sample_max_abs_err", "sample_rel_err", "sample_lse_err")},
         "copy_reference_gbs": copy_reference(),
     }
+    ceiling = read_reference()
+    out["roofline"]["measured_read_ceiling_gbs"] = ceiling
+    out["roofline"]["frac_of_measured_ceiling"] = round(achieved / ceiling, 4)
     log("timing the tiered write path ...")
     out["write_path"] = measure_append()
     if not args.no_cpu_baseline:

@@ -283,6 +283,16 @@ int dattn_append_tiered_int8(const dattn_params* p, const uint16_t* k_new, const
 int dattn_append_ring_f16(const dattn_params* p, const uint16_t* k_new, const uint16_t* v_new, uint16_t* k_ring,
                           uint16_t* v_ring, int32_t* seq_lens, void* stream);
 
+/*
+ * Measurement helper, not part of the attention method: a plain streaming
+ * read of `bytes` bytes (a multiple of 16, src 16-byte aligned) with 128-bit
+ * nontemporal loads (4 workgroups of 1024 threads per CU).  It gives the
+ * measured read ceiling that kernel rates are reported against.  *sink
+ * (device, 4 bytes) is written only if the data fold to one particular 32-bit
+ * value.  Enqueued on `stream`.
+ */
+int dattn_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream);
+
 /* Message for the last non-zero return on this thread ("" if none). */
 const char* dattn_last_error(void);
 

@@ -34,7 +34,7 @@ __all__ = [
     "DattnError", "DattnParams", "lib", "library_path", "dattn_workspace_size",
     "dattn_decode_paged", "dattn_decode_tiered_int8", "dattn_decode_tiered_f16", "dattn_decode_ring_f16",
     "dattn_decode_block_sparse", "dattn_append_tiered_int8", "dattn_append_ring_f16",
-    "dattn_last_error", "dattn_version",
+    "dattn_stream_read", "dattn_last_error", "dattn_version",
     "KIND_PAGED", "KIND_TIERED_INT8", "KIND_BLOCK_SPARSE", "KIND_TIERED_F16", "KIND_RING_F16",
     "F32", "F16", "PHASE_ALL", "PHASE_SPLIT", "PHASE_COMBINE",
 ]
@@ -99,9 +99,10 @@ def lib():
         L.dattn_decode_block_sparse.argtypes = [PP, P, P, P, P, P, P, i32, i32, P, i32, P, i32, P, P, P, sz, P]
         L.dattn_append_tiered_int8.argtypes = [PP, P, P, P, P, i32, P, P, P, P, P, P, P, P]
         L.dattn_append_ring_f16.argtypes = [PP, P, P, P, P, P, P]
+        L.dattn_stream_read.argtypes = [P, sz, P, P]
         for f in (L.dattn_workspace_size, L.dattn_decode_paged, L.dattn_decode_tiered_int8,
                   L.dattn_decode_tiered_f16, L.dattn_decode_ring_f16, L.dattn_decode_block_sparse,
-                  L.dattn_append_tiered_int8, L.dattn_append_ring_f16):
+                  L.dattn_append_tiered_int8, L.dattn_append_ring_f16, L.dattn_stream_read):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -438,3 +439,13 @@ def dattn_append_ring_f16(k_new, v_new, k_ring, v_ring, seq_lens, *, stream=None
     p = DattnParams(B, Hkv, Hkv, D, 0.0, 0, int(k_ring.shape[1]), 0.0, 1, 1, 1, 0, 0, 0)
     _check(lib().dattn_append_ring_f16(ctypes.byref(p), _ptr(k_new), _ptr(v_new), _ptr(k_ring), _ptr(v_ring),
                                        _ptr(seq_lens), _stream(stream)))
+
+
+def dattn_stream_read(src, sink, *, stream=None):
+    """Measurement helper: stream-read the bytes of the contiguous GPU tensor `src`
+    (sink: a 1-element int32 GPU tensor) -- the measured read ceiling."""
+    torch = _torch()
+    _need(sink, "sink", (torch.int32,), 1, src.device)
+    if not src.is_contiguous() or src.device.type != "cuda":
+        raise ValueError("src must be a contiguous GPU tensor")
+    _check(lib().dattn_stream_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink), _stream(stream)))

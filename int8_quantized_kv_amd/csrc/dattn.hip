@@ -378,6 +378,22 @@ int launch(void* split_fn, void* bal_fn, const dattn_params* p, const Plan& pl, 
   return check_launch("combine kernel");
 }
 
+// Measured read ceiling: a grid-stride loop of 128-bit nontemporal loads,
+// unrolled four times, folded with XOR; the result is stored only if it
+// equals a constant no benchmark buffer produces, so the loads stay live
+// without a store per lane.  Launched as 4 workgroups of 1024 threads per CU,
+// the fastest shape of a sweep on MI355X (6.6-6.9 TB/s).
+__global__ __launch_bounds__(1024) void stream_read_kernel(const dattn::u4* __restrict__ src, size_t n,
+                                                           uint32_t* sink) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  dattn::u4 acc = {0u, 0u, 0u, 0u};
+#pragma unroll 4
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
+    acc ^= __builtin_nontemporal_load(src + i);
+  const uint32_t x = acc.x ^ acc.y ^ acc.z ^ acc.w;
+  if (x == 0x9E3779B9u) sink[0] = x;
+}
+
 }  // namespace
 
 extern "C" {
@@ -385,6 +401,17 @@ extern "C" {
 const char* dattn_last_error(void) { return g_err.c_str(); }
 
 const char* dattn_version(void) { return "dattn 0.1.0 gfx950"; }
+
+int dattn_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream) {
+  g_err.clear();
+  if (!src || !sink) return fail(DATTN_ERR_INVALID, "src and sink must be non-NULL");
+  if (bytes % 16 || (uintptr_t)src % 16) return fail(DATTN_ERR_INVALID, "bytes and src must be multiples of 16");
+  if (bytes == 0) return DATTN_OK;
+  const int blocks = device_cus() * 4;
+  hipLaunchKernelGGL(stream_read_kernel, dim3(blocks), dim3(1024), 0, (hipStream_t)stream, (const dattn::u4*)src,
+                     bytes / 16, sink);
+  return check_launch("stream read kernel");
+}
 
 int dattn_workspace_size(const dattn_params* p, int32_t kind, int32_t sparse_block, size_t* bytes) {
   g_err.clear();

@@ -284,3 +284,11 @@ def test_bench_refuses_more_than_one_gpu():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True, text=True,
                        timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_stream_read_validates(lib):
+    P = ctypes.c_void_p
+    assert lib.dattn_stream_read(None, 64, P(0x1000), None) == dk.ERR_INVALID
+    assert lib.dattn_stream_read(P(0x1000), 60, P(0x1000), None) == dk.ERR_INVALID
+    assert lib.dattn_stream_read(P(0x1004), 64, P(0x1000), None) == dk.ERR_INVALID
+    assert lib.dattn_stream_read(P(0x1000), 0, P(0x1000), None) == 0

@@ -70,3 +70,17 @@ def test_single_key_sequences_everywhere():
     B = 300
     c = synth.tiered_case(718, B, 32, 8, 128, 16, [1] * B, [i % 2 for i in range(B)], 16)
     _sampled(c, "tiered, one key per sequence (hot or cold)")
+
+
+@pytest.mark.parametrize("nbytes,pos", [(1 << 20, 12345), ((64 << 20) + 48, (16 << 20) + 3)])
+def test_stream_read_touches_every_word(nbytes, pos):
+    """The measured read ceiling must read the whole buffer: one marked word among
+    zeros reaches the sink."""
+    import torch
+    import int8_quantized_kv_amd as dk
+    buf = torch.zeros(nbytes // 4, dtype=torch.int32, device="cuda")
+    buf[pos] = np.int32(np.uint32(0x9E3779B9).view(np.int32))
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    dk.dattn_stream_read(buf, sink)
+    torch.cuda.synchronize()
+    assert np.uint32(sink.cpu().numpy()[0]) == 0x9E3779B9
