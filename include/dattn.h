@@ -1,8 +1,9 @@
 /*
  * dattn.h -- C ABI of the MI355X (gfx950) split-KV decode-attention library.
  *
- * One query token per sequence ("decode"), grouped-query attention (GQA):
- * query head h reads kv head h / (num_heads / num_kv_heads)
+ * One query token per sequence ("decode"), or a few (multi-query decode, see
+ * dattn_params.query_len), with grouped-query attention (GQA): query head h
+ * reads kv head h / (num_heads / num_kv_heads)
  * (doppler attention_decode_tiered_int8_f16kv.wgsl, get_kv_head_idx).
  * For every sequence b and query head h the library computes
  *
@@ -17,6 +18,13 @@
  * seq_lens[b]-1 when q_pos is NULL.  A query with no visible key gets out = 0
  * and lse = -inf.  lse is the natural log-sum-exp of the capped scores
  * (boostr paged_attention.wgsl, paged_attention_fwd_f32's lse output).
+ *
+ * Caches: paged f16/f32 (dattn_decode_paged), tiered int8 cold + f16 ring
+ * (dattn_decode_tiered_int8), tiered f16 cold + f16 ring
+ * (dattn_decode_tiered_f16), sliding-window ring (dattn_decode_ring_f16),
+ * block-sparse CSR over the paged f16 cache (dattn_decode_block_sparse).
+ * Write paths: dattn_append_tiered_int8 (quantise on evict) and
+ * dattn_append_ring_f16.
  *
  * Conventions shared by every entry point
  *   - All array arguments are DEVICE pointers on the current HIP device,
@@ -54,7 +62,7 @@ extern "C" {
 #define DATTN_ERR_WORKSPACE (-3)   /* workspace NULL, misaligned or too small */
 #define DATTN_ERR_LAUNCH (-4)      /* a HIP call failed; see dattn_last_error() */
 
-/* storage type of the paged K/V pool and of out */
+/* storage types: paged K/V pool (kv_dtype), out (out_dtype), q (q_dtype) */
 #define DATTN_F32 0
 #define DATTN_F16 1
 
