@@ -84,3 +84,41 @@ def test_stream_read_touches_every_word(nbytes, pos):
     dk.dattn_stream_read(buf, sink)
     torch.cuda.synchronize()
     assert np.uint32(sink.cpu().numpy()[0]) == 0x9E3779B9
+
+
+@pytest.mark.parametrize("qmul", [40.0, 1e-4])
+@pytest.mark.parametrize("kind", ["paged", "tiered", "multi_query"])
+def test_score_dynamic_range(kind, qmul):
+    """Scores of hundreds (the running max moves by far more than its lazy slack, so
+    the accumulator is rescaled many times) or nearly flat (weights all ~1)."""
+    if kind == "paged":
+        c = synth.paged_case(720, 3, 32, 8, 128, 16, lens=[3000, 100, 1000], kv_dtype=synth.F16)
+    elif kind == "tiered":
+        c = synth.tiered_case(721, 2, 32, 8, 128, 16, [2000, 700], [1800, 600], 256)
+    else:
+        c = synth.paged_case(722, 2, 32, 8, 128, 16, lens=[2000, 300], kv_dtype=synth.F16, query_len=4)
+    # sort keys so that later tiles hold ever larger scores for the first head: increasing max
+    c.q = (c.q * np.float32(qmul)).astype(np.float32)
+    _sampled(c, f"{kind} q x {qmul}")
+
+
+def test_extreme_int8_scales():
+    """Zero, subnormal and large f16 scales.  Key scales stay below 0.05 so the
+    scores keep the O(1) magnitude the absolute tolerance is stated for; value
+    scales go up to 60000, so outputs reach ~1e6 and are held to the normwise
+    criterion (max |g - r| <= 1e-3 max |r|) alone, as f32 cannot hold 1e-3
+    absolute at that size."""
+    import torch
+    c = synth.tiered_case(723, 2, 32, 8, 128, 16, [900, 400], [800, 300], 128)
+    rng = np.random.default_rng(5)
+    for sc, choices in ((c.k_scale, [0.0, 1e-4, 6e-5, 3e-3, 0.05]), (c.v_scale, [0.0, 1e-4, 6e-5, 3e-3, 60000.0])):
+        pick = rng.random(sc.shape) < 0.3
+        sc[pick] = rng.choice(np.array(choices, np.float16), size=int(pick.sum()))
+    log("edge int8 scales 0 .. 60000")
+    og, lg = DeviceCase(c).run_np()
+    ro, rl = oracle_run(c)
+    assert np.all(np.isfinite(og)) and np.all(np.isfinite(lg))
+    err = np.max(np.abs(og - ro))
+    log(f"  max abs {err:.3e}, max |ref| {np.max(np.abs(ro)):.3e}, lse {np.max(np.abs(lg - rl)):.3e}")
+    assert err <= 1e-3 * np.max(np.abs(ro))
+    assert np.max(np.abs(lg - rl)) <= 1e-3
