@@ -48,10 +48,11 @@ struct Plan {
   size_t workspace = 0;
 };
 
-// Balanced schedule bounds: at most kMaxWorkers workgroups, so at most
-// kMaxWorkers + B partial slots; sequences up to kMaxBalancedSeqs (their tile
-// prefix lives in LDS).
-constexpr int kMaxWorkers = 1024;
+// Balanced schedule bounds: one resident round of at most kMaxWaves waves,
+// i.e. at most kMaxWaves / Hkv workgroups per kv-head group (a workgroup holds
+// one wave per kv head of its group), so at most kMaxWaves / Hkv + B partial
+// slots; sequences up to kMaxBalancedSeqs (their tile prefix lives in LDS).
+constexpr int kMaxWaves = 4096;
 constexpr int kMaxBalancedSeqs = 4096;
 constexpr size_t kMaxBalancedLds = 16384;
 constexpr int64_t kMinWorkerUnits = 16;   // units of the host-side work bound per worker (about 8 tiles)
@@ -166,6 +167,8 @@ int waves_per_group(int Hkv) {
   return 1;
 }
 
+int max_workers_per_group(int Hkv) { return Hkv < kMaxWaves ? kMaxWaves / Hkv : 1; }
+
 int make_plan(const dattn_params* p, int kind, int32_t sparse_block, Plan& pl) {
   int rc = check_params(p, kind);
   if (rc) return rc;
@@ -215,7 +218,7 @@ int make_plan(const dattn_params* p, int kind, int32_t sparse_block, Plan& pl) {
   pl.balanced_ok = p->split_tokens == 0 && kind != DATTN_KIND_BLOCK_SPARSE && p->num_seqs >= 1 &&
                    p->num_seqs <= kMaxBalancedSeqs;
   if (pl.balanced_ok) {
-    const size_t slots = (size_t)kMaxWorkers + p->num_seqs;
+    const size_t slots = (size_t)max_workers_per_group(p->num_kv_heads) + p->num_seqs;
     pl.bal_acc_bytes = align_up(slots * p->num_heads * qn * p->head_dim * sizeof(float));
     pl.bal_ml_bytes = align_up(slots * p->num_heads * qn * sizeof(float2));
     pl.bal_sched_bytes = align_up((size_t)(p->num_seqs + 3) * sizeof(int32_t));
@@ -261,9 +264,8 @@ Balanced plan_balanced(const dattn_params* p, const Plan& pl, const void* fn) {
     return bl;
   }
   const int groups = p->num_kv_heads / pl.waves;
-  int total = cus * per_cu;
-  if (total > kMaxWorkers) total = kMaxWorkers;
-  bl.workers = total / groups > 0 ? total / groups : 1;
+  bl.workers = cus * per_cu / groups > 0 ? cus * per_cu / groups : 1;
+  if (bl.workers > max_workers_per_group(p->num_kv_heads)) bl.workers = max_workers_per_group(p->num_kv_heads);
   // A worker's piece of one sequence has at most C tiles (every tile costs at
   // least one unit); C <= ceil(N / workers) with N bounded by two units per
   // tile plus the start-up units of every sequence.

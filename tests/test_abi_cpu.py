@@ -139,10 +139,12 @@ def test_workspace_size_null_arguments(lib):
 
 def test_workspace_size_values(lib):
     # the library-chosen split (split_tokens = 0) also sizes the balanced schedule's slots
-    rc, n0, _ = ws_size(lib, good_params())
     up = lambda x: (x + 255) // 256 * 256  # noqa: E731
-    slots = 1024 + 2
-    assert rc == 0 and n0 >= up(slots * 8 * 128 * 4) + up(slots * 8 * 8) + up(5 * 4)
+    # slots: one resident round of at most 4096 waves, i.e. 4096 / Hkv workers per kv-head group, plus B
+    for hkv, n_heads in ((2, 8), (1, 8), (8, 32)):
+        rc, n0, _ = ws_size(lib, good_params(num_kv_heads=hkv, num_heads=n_heads))
+        slots = 4096 // hkv + 2
+        assert rc == 0 and n0 == up(slots * n_heads * 128 * 4) + up(slots * n_heads * 8) + up(5 * 4), hkv
     rc, n, _ = ws_size(lib, good_params(split_tokens=32))
     assert rc == 0
     S, B, H, D = 4, 2, 8, 128          # ceil(100 / 32) splits
