@@ -461,8 +461,9 @@ def line_for(case, steps, warmup, check=True):
 
 def workload(idx, window=0):
     """Workloads 1-5 of the input generators, 6: the tiered workload's shape
-    with an f16 cold tier, 7: a sliding-window ring f16 cache, 8: four queries
-    per sequence over a paged f16 cache of workload 2's shape."""
+    with an f16 cold tier, 7: a sliding-window ring f16 cache, 8 and 9: four
+    and sixteen queries per sequence over a paged f16 cache of workload 2's
+    shape."""
     import synth
     if idx == 6:
         return synth.tiered_f16_workload(window)
@@ -470,6 +471,8 @@ def workload(idx, window=0):
         return synth.ring_workload()
     if idx == 8:
         return synth.multi_query_workload(4)
+    if idx == 9:
+        return synth.multi_query_workload(16)
     return synth.config(idx, window=window)
 
 
@@ -482,7 +485,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", type=int, default=2,
                     help="headline workload index (default 2; 6 = the tiered workload with an f16 cold tier, "
-                         "7 = a sliding-window ring f16 cache, 8 = four queries per sequence)")
+                         "7 = a sliding-window ring f16 cache, 8 = four queries per sequence, 9 = sixteen)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run 5 device copies of MIB MiB (for scaling memory counters)")
     args = ap.parse_args()
@@ -555,7 +558,7 @@ def main():
     if args.all:
         extra = []
         for idx, kw in ((1, {}), (3, dict(window=0)), (3, dict(window=4096)), (4, {}), (5, {}),
-                        (6, dict(window=0)), (6, dict(window=4096)), (7, {}), (8, {})):
+                        (6, dict(window=0)), (6, dict(window=4096)), (7, {}), (8, {}), (9, {})):
             log(f"generating workload {idx} {kw} ...")
             c = workload(idx, **kw)
             res, _ = line_for(c, max(20, args.steps // 4), max(5, args.warmup // 4))

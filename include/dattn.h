@@ -98,7 +98,7 @@ typedef struct dattn_params {
                                  by the kernel variant's outputDtype, f16 or f32) */
   int32_t query_len;          /* queries per sequence, 0 or 1 => one; > 1: multi-query decode
                                  (paged, tiered and window-ring caches; query_len * GQA group
-                                 <= 16); see dattn_decode_paged */
+                                 <= 128, else DATTN_ERR_UNSUPPORTED); see dattn_decode_paged */
   int32_t q_dtype;            /* storage type of q: DATTN_F32 (0) or DATTN_F16 (converted to f32
                                  exactly); with DATTN_F16 and out_dtype DATTN_F16 this is the f16
                                  Q/K/V, f16 output variant (doppler attention_f16.wgsl) */
@@ -149,8 +149,10 @@ int dattn_workspace_size(const dattn_params* p, int32_t kind, int32_t sparse_blo
  * query rows at abs_query = query_pos + start_pos): q is [B, Qn, H, D], query
  * i of sequence b sits at position q_pos[b] + i (q_pos NULL: seq_lens[b] - Qn,
  * the last Qn tokens of the cache) with its own causal / window bound; out is
- * [B, Qn, H, D] and lse [B, Qn, H].  Each K/V row is still read once per
- * (sequence, kv head), for all Qn * G query rows of the group.  The tiered and
+ * [B, Qn, H, D] and lse [B, Qn, H].  The Qn * G (query, head) rows of a kv
+ * head (at most 128) are taken 16 at a time by the waves of one workgroup,
+ * which sweep the same keys side by side, so each K/V row is fetched from HBM
+ * about once per (sequence, kv head) for all of them.  The tiered and
  * window-ring entry points take query_len the same way.
  */
 int dattn_decode_paged(const dattn_params* p, const void* q, const void* k_cache, const void* v_cache,

@@ -23,6 +23,9 @@ ARCH = os.environ.get("DATTN_OFFLOAD_ARCH", "gfx950")
 UNITS = [("dattn", "dattn.hip", [])] + [
     (f"kernels_d{d}_cap{c}", "kernels.hip", [f"-DDATTN_D={d}", f"-DDATTN_CAP={c}"])
     for d in (64, 128) for c in (0, 1)
+] + [
+    (f"shared_d{d}_cap{c}", "kernels.hip", [f"-DDATTN_D={d}", f"-DDATTN_CAP={c}", "-DDATTN_SHARED=1"])
+    for d in (64, 128) for c in (0, 1)
 ]
 
 

@@ -39,7 +39,9 @@ struct Plan {
   int split_tokens = 0;  // keys (or sparse slots) per split
   int num_splits = 0;
   int sparse_nblk = 0;       // sparse
-  int waves = 0;             // kv heads per workgroup
+  int waves = 0;             // waves per workgroup: kv heads, times rbk row blocks each
+  int rbk = 1;               // multi-query: waves (16-column row blocks) per kv head, 1, 2, 4 or 8
+  int vheads = 0;            // num_kv_heads * rbk: waves per (sequence, split)
   bool no_table = false;     // the cache has no block table to stage (window ring)
   size_t lds = 0;
   size_t acc_bytes = 0, ml_bytes = 0;  // static-split layout
@@ -53,6 +55,9 @@ struct Plan {
 // one wave per kv head of its group), so at most kMaxWaves / Hkv + B partial
 // slots; sequences up to kMaxBalancedSeqs (their tile prefix lives in LDS).
 constexpr int kMaxWaves = 4096;
+// Multi-query decode: query_len * GQA group (query, head) rows per kv head, 16
+// per wave, at most 8 waves (one workgroup) per kv head.
+constexpr int kMaxQueryRows = 128;
 constexpr int kMaxBalancedSeqs = 4096;
 constexpr size_t kMaxBalancedLds = 16384;
 constexpr int64_t kMinWorkerUnits = 16;   // units of the host-side work bound per worker (about 8 tiles)
@@ -60,7 +65,7 @@ constexpr int64_t kMinWorkerUnits = 16;   // units of the host-side work bound p
 // Per-device cache of the CU count and of kernel occupancies.
 std::mutex g_mu;
 std::map<int, int> g_cus;
-std::map<std::tuple<int, const void*, int>, int> g_occ;
+std::map<std::tuple<int, const void*, int, size_t>, int> g_occ;
 
 // CU count of the current device; 256 (MI355X) when no device can be queried,
 // so that host-only callers of dattn_workspace_size get the same answer.
@@ -138,8 +143,9 @@ int check_params(const dattn_params* p, int kind) {
   if (p->query_len > 1) {
     if (kind == DATTN_KIND_BLOCK_SPARSE)
       return fail(DATTN_ERR_UNSUPPORTED, "query_len > 1 is not built for the block-sparse cache");
-    if (G * p->query_len > 16)
-      return fail(DATTN_ERR_UNSUPPORTED, "query_len (%d) * GQA group (%d) must be <= 16", p->query_len, G);
+    if ((int64_t)G * p->query_len > kMaxQueryRows)
+      return fail(DATTN_ERR_UNSUPPORTED, "query_len (%d) * GQA group (%d) must be <= %d", p->query_len, G,
+                  kMaxQueryRows);
   }
   if (p->split_tokens < 0 || p->split_tokens % 16)
     return fail(DATTN_ERR_INVALID, "split_tokens must be 0 or a positive multiple of 16 (got %d)", p->split_tokens);
@@ -167,13 +173,23 @@ int waves_per_group(int Hkv) {
   return 1;
 }
 
-int max_workers_per_group(int Hkv) { return Hkv < kMaxWaves ? kMaxWaves / Hkv : 1; }
+// vheads: waves per (sequence, split), num_kv_heads * rbk
+int max_workers_per_group(int vheads) { return vheads < kMaxWaves ? kMaxWaves / vheads : 1; }
 
 int make_plan(const dattn_params* p, int kind, int32_t sparse_block, Plan& pl) {
   int rc = check_params(p, kind);
   if (rc) return rc;
   pl.G = p->num_heads / p->num_kv_heads;
   pl.waves = waves_per_group(p->num_kv_heads);
+  if (p->query_len > 1) {
+    // blocks of 16 (query, head) columns, rounded up to 1, 2, 4 or 8 (the
+    // shared-tile sweep splits a tile into equal shares); the row blocks of a
+    // kv head fill one workgroup
+    const int need = (pl.G * p->query_len + 15) / 16;
+    while (pl.rbk < need) pl.rbk *= 2;
+    if (pl.rbk > 1) pl.waves = pl.rbk;
+  }
+  pl.vheads = p->num_kv_heads * pl.rbk;
   const int64_t L = p->max_seq_len;
   if (kind == DATTN_KIND_PAGED || is_tiered(kind)) {
     pl.split_tokens = choose_split(p, L);
@@ -218,7 +234,7 @@ int make_plan(const dattn_params* p, int kind, int32_t sparse_block, Plan& pl) {
   pl.balanced_ok = p->split_tokens == 0 && kind != DATTN_KIND_BLOCK_SPARSE && p->num_seqs >= 1 &&
                    p->num_seqs <= kMaxBalancedSeqs;
   if (pl.balanced_ok) {
-    const size_t slots = (size_t)max_workers_per_group(p->num_kv_heads) + p->num_seqs;
+    const size_t slots = (size_t)max_workers_per_group(pl.vheads) + p->num_seqs;
     pl.bal_acc_bytes = align_up(slots * p->num_heads * qn * p->head_dim * sizeof(float));
     pl.bal_ml_bytes = align_up(slots * p->num_heads * qn * sizeof(float2));
     pl.bal_sched_bytes = align_up((size_t)(p->num_seqs + 3) * sizeof(int32_t));
@@ -230,17 +246,18 @@ int make_plan(const dattn_params* p, int kind, int32_t sparse_block, Plan& pl) {
 
 // ---- device properties (cached per device) for sizing the balanced grid
 
-// Workgroups of `fn` (block threads, 16 KiB LDS) resident per CU; 0 on error.
-int resident_groups(const void* fn, int block, int& cus) {
+// Workgroups of `fn` (block threads, lds bytes of dynamic LDS) resident per
+// CU; 0 on error.
+int resident_groups(const void* fn, int block, size_t lds, int& cus) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   cus = device_cus();
   std::lock_guard<std::mutex> lk(g_mu);
-  const auto key = std::make_tuple(dev, fn, block);
+  const auto key = std::make_tuple(dev, fn, block, lds);
   auto jt = g_occ.find(key);
   if (jt == g_occ.end()) {
     int nb = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, block, kMaxBalancedLds) != hipSuccess) return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, block, lds) != hipSuccess) return 0;
     jt = g_occ.emplace(key, nb).first;
   }
   return jt->second;
@@ -254,18 +271,18 @@ struct Balanced {
 
 // Use the balanced schedule when allowed and it fits: one round of resident
 // workgroups, and the per-worker block-table staging within kMaxBalancedLds.
-Balanced plan_balanced(const dattn_params* p, const Plan& pl, const void* fn) {
+Balanced plan_balanced(const dattn_params* p, const Plan& pl, const void* fn, size_t tile_lds) {
   Balanced bl;
   if (!pl.balanced_ok) return bl;
   int cus = 0;
-  const int per_cu = resident_groups(fn, 64 * pl.waves, cus);
+  const int per_cu = resident_groups(fn, 64 * pl.waves, kMaxBalancedLds + tile_lds, cus);
   if (per_cu <= 0 || cus <= 0) {
     (void)hipGetLastError();
     return bl;
   }
-  const int groups = p->num_kv_heads / pl.waves;
+  const int groups = pl.vheads / pl.waves;
   bl.workers = cus * per_cu / groups > 0 ? cus * per_cu / groups : 1;
-  if (bl.workers > max_workers_per_group(p->num_kv_heads)) bl.workers = max_workers_per_group(p->num_kv_heads);
+  if (bl.workers > max_workers_per_group(pl.vheads)) bl.workers = max_workers_per_group(pl.vheads);
   // A worker's piece of one sequence has at most C tiles (every tile costs at
   // least one unit); C <= ceil(N / workers) with N bounded by two units per
   // tile plus the start-up units of every sequence.
@@ -299,6 +316,7 @@ dattn::DecodeArgs base_args(const dattn_params* p, const Plan& pl, const void* q
   a.qn = p->query_len > 1 ? p->query_len : 1;
   a.grp = p->num_heads / p->num_kv_heads;
   a.heads_out = a.qn * p->num_heads;
+  a.rbk = pl.rbk;
   a.q_f16 = p->q_dtype == DATTN_F16;
   const double scale = p->scale != 0.0f ? (double)p->scale : (double)(float)(1.0 / sqrt((double)p->head_dim));
   const double log2e = 1.4426950408889634;
@@ -341,19 +359,28 @@ int check_io(const dattn_params* p, bool split_inputs_ok, void* out, float* lse)
   return DATTN_OK;
 }
 
+// shared_tiles: the kernels are the shared-tile instances (several row-block
+// waves per kv head sweeping contiguous tiles through LDS buffers).
 int launch(void* split_fn, void* bal_fn, const dattn_params* p, const Plan& pl, dattn::DecodeArgs& a, void* out,
-           float* lse, hipStream_t st) {
-  const Balanced bl = bal_fn ? plan_balanced(p, pl, bal_fn) : Balanced{};
+           float* lse, hipStream_t st, bool shared_tiles = false) {
+  if (!split_fn) return fail(DATTN_ERR_UNSUPPORTED, "no kernel instance for this configuration");
+  // two tile buffers of 16 f16 K rows + 16 f16 V rows (int8 rows and scales fit)
+  const size_t tile_lds = shared_tiles ? (size_t)128 * p->head_dim : 0;
+  const Balanced bl = bal_fn ? plan_balanced(p, pl, bal_fn, tile_lds) : Balanced{};
+  a.tile_lds = (int32_t)tile_lds;
+  if (!bl.on && pl.lds + tile_lds > 65536)
+    return fail(DATTN_ERR_UNSUPPORTED, "LDS need %zu exceeds 64 KiB", pl.lds + tile_lds);
   if (bl.on) {
     a.part_ml = (float2*)((char*)a.part_acc + pl.bal_acc_bytes);
     a.sched = (int32_t*)((char*)a.part_acc + pl.bal_acc_bytes + pl.bal_ml_bytes);
   }
   if (run_split(p)) {
-    const dim3 grid = bl.on ? dim3(bl.workers, 1, p->num_kv_heads / pl.waves)
-                            : dim3(pl.num_splits, p->num_seqs, p->num_kv_heads / pl.waves);
+    const dim3 grid = bl.on ? dim3(bl.workers, 1, pl.vheads / pl.waves)
+                            : dim3(pl.num_splits, p->num_seqs, pl.vheads / pl.waves);
     const dim3 block(64 * pl.waves);
     void* args[] = {&a};
-    hipError_t e = hipLaunchKernel(bl.on ? bal_fn : split_fn, grid, block, args, bl.on ? bl.lds : pl.lds, st);
+    hipError_t e = hipLaunchKernel(bl.on ? bal_fn : split_fn, grid, block, args,
+                                   (bl.on ? bl.lds : pl.lds) + (size_t)a.tile_lds, st);
     if (e != hipSuccess) return fail(DATTN_ERR_LAUNCH, "split kernel launch failed: %s", hipGetErrorString(e));
     int rc = check_launch("split kernel");
     if (rc) return rc;
@@ -453,14 +480,18 @@ int dattn_decode_paged(const dattn_params* p, const void* q, const void* k_cache
   const bool contig = p->block_size % 16 == 0;
   void* fn;
   void* bal;
-  if (a.qn > 1) {   // several queries per sequence: MFMA columns are (query, head) pairs
+  const bool shared = f16 && contig && pl.rbk > 1;   // row-block waves share tiles
+  if (shared) {
+    fn = dattn::shared_kernel(dattn::kPagedF16MQ, p->head_dim, cap, pl.rbk);
+    bal = dattn::shared_kernel(dattn::kBalF16MQ, p->head_dim, cap, pl.rbk);
+  } else if (a.qn > 1) {   // several queries per sequence: MFMA columns are (query, head) pairs
     fn = dattn::split_kernel(f16 ? dattn::kPagedF16MQ : dattn::kPagedF32MQ, p->head_dim, cap, 16, contig);
     bal = dattn::split_kernel(f16 ? dattn::kBalF16MQ : dattn::kBalF32MQ, p->head_dim, cap, 16, contig);
   } else {
     fn = dattn::split_kernel(f16 ? dattn::kPagedF16 : dattn::kPagedF32, p->head_dim, cap, pl.G, contig);
     bal = dattn::split_kernel(f16 ? dattn::kBalF16 : dattn::kBalF32, p->head_dim, cap, pl.G, contig);
   }
-  return launch(fn, bal, p, pl, a, out, lse, (hipStream_t)stream);
+  return launch(fn, bal, p, pl, a, out, lse, (hipStream_t)stream, shared);
 }
 
 int dattn_decode_tiered_int8(const dattn_params* p, const void* q, const uint16_t* k_hot, const uint16_t* v_hot,
@@ -495,6 +526,10 @@ int dattn_decode_tiered_int8(const dattn_params* p, const void* q, const uint16_
   a.q_pos = q_pos;
   const bool cap = p->softcap > 0.0f;
   const bool contig = p->block_size % 16 == 0 && hot_window % 16 == 0;
+  if (contig && pl.rbk > 1)   // row-block waves share tiles
+    return launch(dattn::shared_kernel(dattn::kTieredMQ, p->head_dim, cap, pl.rbk),
+                  dattn::shared_kernel(dattn::kBalTieredMQ, p->head_dim, cap, pl.rbk), p, pl, a, out, lse,
+                  (hipStream_t)stream, true);
   if (a.qn > 1)   // several queries per sequence: MFMA columns are (query, head) pairs
     return launch(dattn::split_kernel(dattn::kTieredMQ, p->head_dim, cap, 16, contig),
                   dattn::split_kernel(dattn::kBalTieredMQ, p->head_dim, cap, 16, contig), p, pl, a, out, lse,
@@ -535,6 +570,10 @@ int dattn_decode_tiered_f16(const dattn_params* p, const void* q, const uint16_t
   const bool cap = p->softcap > 0.0f;
   const bool contig = p->block_size % 16 == 0 && hot_window % 16 == 0;
   const bool mq = a.qn > 1;
+  if (contig && pl.rbk > 1)   // row-block waves share tiles
+    return launch(dattn::shared_kernel(dattn::kTieredF16MQ, p->head_dim, cap, pl.rbk),
+                  dattn::shared_kernel(dattn::kBalTieredF16MQ, p->head_dim, cap, pl.rbk), p, pl, a, out, lse,
+                  (hipStream_t)stream, true);
   return launch(dattn::split_kernel(mq ? dattn::kTieredF16MQ : dattn::kTieredF16, p->head_dim, cap, mq ? 16 : pl.G,
                                     contig),
                 dattn::split_kernel(mq ? dattn::kBalTieredF16MQ : dattn::kBalTieredF16, p->head_dim, cap,
@@ -569,6 +608,10 @@ int dattn_decode_ring_f16(const dattn_params* p_in, const void* q, const uint16_
   const bool cap = p->softcap > 0.0f;
   const bool contig = W % 16 == 0;
   const bool mq = a.qn > 1;
+  if (contig && pl.rbk > 1)   // row-block waves share tiles
+    return launch(dattn::shared_kernel(dattn::kTieredF16MQ, p->head_dim, cap, pl.rbk),
+                  dattn::shared_kernel(dattn::kBalTieredF16MQ, p->head_dim, cap, pl.rbk), p, pl, a, out, lse,
+                  (hipStream_t)stream, true);
   return launch(dattn::split_kernel(mq ? dattn::kTieredF16MQ : dattn::kTieredF16, p->head_dim, cap, mq ? 16 : pl.G,
                                     contig),
                 dattn::split_kernel(mq ? dattn::kBalTieredF16MQ : dattn::kBalTieredF16, p->head_dim, cap,

@@ -96,6 +96,8 @@ struct DecodeArgs {
   int32_t qn;         // queries per sequence (multi-query decode), >= 1
   int32_t grp;        // GQA group size H / Hkv
   int32_t heads_out;  // qn * num_heads: rows per slot of the partials and of out
+  int32_t rbk;        // multi-query: blocks of 16 (query, head) columns per kv head, one wave each
+  int32_t tile_lds;   // bytes of shared-tile buffers at the start of dynamic LDS (rbk > 1), else 0
   int32_t q_f16;      // 1: q holds f16 values (converted to f32 exactly)
   int32_t sparse_block, num_layouts, row_stride, col_stride, sparse_nblk;
   float qmul;    // scale * log2(e) without softcap, 2 log2(e) * scale / cap with softcap
@@ -264,8 +266,9 @@ struct QF16 {
 
 // Row of q (in units of D) for MFMA column j of kv head kvh.  One query per
 // sequence: column j < G is head kvh*G + j.  With qn queries (MQ), column
-// j < grp*qn is query j / grp, head kvh*grp + j % grp, of q [B, qn, H, D].
-// Columns beyond those read row 0 of the group (their Q is zeroed).
+// j < grp*qn is query j / grp, head kvh*grp + j % grp, of q [B, qn, H, D];
+// the wave of row block rb holds columns 16*rb + [0, 16).  Columns beyond
+// those read row 0 of the group (their Q is zeroed).
 template <int G, bool MQ>
 __device__ __forceinline__ size_t q_row(const DecodeArgs& a, int b, int kvh, int j) {
   if constexpr (MQ) {
@@ -278,8 +281,9 @@ __device__ __forceinline__ size_t q_row(const DecodeArgs& a, int b, int kvh, int
 }
 
 template <int D, int G, bool I8MAP, bool MQ = false>
-__device__ __forceinline__ void load_q_raw16(const DecodeArgs& a, int b, int kvh, int lane, QRaw16<D>& r) {
-  const int j = lane & 15, g = lane >> 4;
+__device__ __forceinline__ void load_q_raw16(const DecodeArgs& a, int b, int kvh, int lane, QRaw16<D>& r,
+                                             int col0 = 0) {
+  const int j = col0 + (lane & 15), g = lane >> 4;
   const size_t row = q_row<G, MQ>(a, b, kvh, j) * D;
   if (a.q_f16) {   // the 8 halves stay raw in x[2c] until convert_q
     const _Float16* qrow = (const _Float16*)a.q + row;
@@ -300,8 +304,9 @@ __device__ __forceinline__ void load_q_raw16(const DecodeArgs& a, int b, int kvh
 }
 
 template <int D, int G, bool MQ = false>
-__device__ __forceinline__ void convert_q(const DecodeArgs& a, int lane, const QRaw16<D>& r, QF16<D>& qf) {
-  const bool live = (lane & 15) < (MQ ? a.grp * a.qn : G);
+__device__ __forceinline__ void convert_q(const DecodeArgs& a, int lane, const QRaw16<D>& r, QF16<D>& qf,
+                                          int col0 = 0) {
+  const bool live = col0 + (lane & 15) < (MQ ? a.grp * a.qn : G);
 #pragma unroll
   for (int c = 0; c < D / 32; ++c) {
     const f4 x0 = r.x[2 * c], x1 = r.x[2 * c + 1];
@@ -331,8 +336,9 @@ struct QF32 {
 };
 
 template <int D, int G, bool MQ = false>
-__device__ __forceinline__ void load_q_raw32(const DecodeArgs& a, int b, int kvh, int lane, QRaw32<D>& r) {
-  const int j = lane & 15, g = lane >> 4;
+__device__ __forceinline__ void load_q_raw32(const DecodeArgs& a, int b, int kvh, int lane, QRaw32<D>& r,
+                                             int col0 = 0) {
+  const int j = col0 + (lane & 15), g = lane >> 4;
   const size_t row = q_row<G, MQ>(a, b, kvh, j) * D;
   if (a.q_f16) {   // 4 halves raw in the low half of x[m] until convert_q
     const _Float16* qrow = (const _Float16*)a.q + row;
@@ -350,8 +356,9 @@ __device__ __forceinline__ void load_q_raw32(const DecodeArgs& a, int b, int kvh
 }
 
 template <int D, int G, bool MQ = false>
-__device__ __forceinline__ void convert_q(const DecodeArgs& a, int lane, const QRaw32<D>& r, QF32<D>& qf) {
-  const bool live = (lane & 15) < (MQ ? a.grp * a.qn : G);
+__device__ __forceinline__ void convert_q(const DecodeArgs& a, int lane, const QRaw32<D>& r, QF32<D>& qf,
+                                          int col0 = 0) {
+  const bool live = col0 + (lane & 15) < (MQ ? a.grp * a.qn : G);
 #pragma unroll
   for (int m = 0; m < D / 16; ++m) {
     const f4 y = r.x[m];   // the raw halves, two per word in .x and .y, when q is f16
@@ -915,13 +922,14 @@ struct Online {
     if (lane < G) dst.ml[lane * dst.ml_hstride] = make_float2(m, lt);
   }
   // Several queries per sequence: column r < grp*qn is query r / grp, head
-  // r % grp, stored at row (r / grp) * H + r % grp of the partials.
-  __device__ __forceinline__ void finish_mq(const PartialDst& dst, int lane, int grp, int qn, int H) {
+  // r % grp, stored at row (r / grp) * H + r % grp of the partials; this
+  // wave holds columns col0 + [0, 16).
+  __device__ __forceinline__ void finish_mq(const PartialDst& dst, int lane, int grp, int qn, int H, int col0) {
     const float lt = rows_sum(l);
     const int g = lane >> 4, c = lane & 15, ncols = grp * qn;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int r = 4 * g + e;
+      const int r = col0 + 4 * g + e;
       if (r < ncols) {
         const int i = r / grp;
         float* out = dst.acc + (size_t)(i * H + r - i * grp) * dst.acc_hstride + NT * c;
@@ -930,9 +938,9 @@ struct Online {
           *(f4*)(out + 4 * t4) = f4{o[4 * t4][e], o[4 * t4 + 1][e], o[4 * t4 + 2][e], o[4 * t4 + 3][e]};
       }
     }
-    if (lane < ncols) {
-      const int i = lane / grp;
-      dst.ml[(size_t)(i * H + lane - i * grp) * dst.ml_hstride] = make_float2(m, lt);
+    if (lane < 16 && col0 + lane < ncols) {
+      const int r = col0 + lane, i = r / grp;
+      dst.ml[(size_t)(i * H + r - i * grp) * dst.ml_hstride] = make_float2(m, lt);
     }
   }
 };
@@ -942,10 +950,10 @@ __device__ __forceinline__ void write_empty(const PartialDst& dst, int lane) {
   if (lane < G) dst.ml[lane * dst.ml_hstride] = make_float2(-__builtin_inff(), 0.f);
 }
 
-__device__ __forceinline__ void write_empty_mq(const PartialDst& dst, int lane, int grp, int qn, int H) {
-  if (lane < grp * qn) {
-    const int i = lane / grp;
-    dst.ml[(size_t)(i * H + lane - i * grp) * dst.ml_hstride] = make_float2(-__builtin_inff(), 0.f);
+__device__ __forceinline__ void write_empty_mq(const PartialDst& dst, int lane, int grp, int qn, int H, int col0) {
+  if (lane < 16 && col0 + lane < grp * qn) {
+    const int r = col0 + lane, i = r / grp;
+    dst.ml[(size_t)(i * H + r - i * grp) * dst.ml_hstride] = make_float2(-__builtin_inff(), 0.f);
   }
 }
 
@@ -1030,6 +1038,171 @@ __device__ __forceinline__ void run_tiles(const DecodeArgs& a, const Store& st, 
   });
 }
 
+// ------------------------------------------------------------ shared tiles
+//
+// Multi-query decode with more than 16 (query, head) columns per kv head: the
+// RBK row-block waves of a kv head sit in one workgroup and need the same
+// tiles.  Fetching every tile in every wave would leave each wave's stream
+// latency-bound at a quarter of the streams.  Instead wave w fetches a 1/RBK
+// share of each tile (1 KB blocks j*RBK + w of 16-byte chunks) into
+// registers, NS tiles ahead, and writes it into one of two LDS buffers just
+// before the tile is used; after a barrier every wave reads its MFMA
+// fragments from the buffer.  Each byte is fetched once per workgroup and
+// each wave keeps 4-8 KB of loads in flight, as the one-query kernels do.
+// A buffer holds the 16 K rows, the 16 V rows and, for int8 rows, the 16 K
+// and 16 V scales; chunk c of row r sits at position r*CPR + (c ^ (r % CPR))
+// (CPR chunks per row) so that the fragment reads of 16 rows fall into
+// distinct banks.  Contiguous tiles only.
+template <class Store>
+struct ShareGeo;
+template <int D>
+struct ShareGeo<StoreF16<D>> {
+  static constexpr int RB = 2 * D;   // bytes per row
+  static constexpr bool kScaled = false;
+};
+template <int D>
+struct ShareGeo<StoreI8<D>> {
+  static constexpr int RB = D;
+  static constexpr bool kScaled = true;
+};
+
+template <class Store, int RBK>
+struct Share {
+  static constexpr int RB = ShareGeo<Store>::RB;
+  static constexpr bool kScaled = ShareGeo<Store>::kScaled;
+  static constexpr int CPR = RB / 16;                  // 16-byte chunks per row
+  static constexpr int KCH = 16 * CPR;                 // chunks of the K rows (a multiple of 64)
+  static constexpr int NBLK = 2 * KCH / 64;            // 1 KB blocks per tile
+  static constexpr int PER = (NBLK + RBK - 1) / RBK;   // blocks per wave
+  static constexpr int NS = 2;                         // tiles of shares in flight
+  static constexpr int kScaleOff = 2 * KCH * 16;
+  static constexpr int kBytes = kScaleOff + (kScaled ? 64 : 0);
+  struct Regs {
+    u4 r[PER];
+    uint16_t sc;
+  };
+  __device__ static __forceinline__ int pos(int row, int chunk) { return row * CPR + (chunk ^ (row & (CPR - 1))); }
+
+  // Block j of wave wv: j*RBK + wv, wrapped into the tile's NBLK blocks (both
+  // powers of two), so every load and store is unconditional: with fewer
+  // blocks than waves, two waves move the same block (equal bytes to equal
+  // addresses).  Likewise every lane moves one scale (lane % 32 < 16: K).
+  __device__ static __forceinline__ int block(int j, int wv) { return (j * RBK + wv) & (NBLK - 1); }
+  __device__ static __forceinline__ void load(const Store& st, uint32_t row0, int wv, int lane, Regs& s) {
+    const uint32_t rs = (uint32_t)st.Hkv * RB;   // bytes per row of the pool
+    const size_t head = (size_t)row0 * rs + (size_t)st.kvh * RB;
+    const char* kt = (const char*)st.kbase + head;
+    const char* vt = (const char*)st.vbase + head;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int blk = block(j, wv);
+      const int q = (blk & (NBLK / 2 - 1)) * 64 + lane;   // chunk within the K (or V) rows
+      const int row = q / CPR, c = (q & (CPR - 1)) ^ (row & (CPR - 1));
+      const char* base = blk >= NBLK / 2 ? vt : kt;
+      s.r[j] = load_at<u4>(base, tie((uint32_t)row * rs + 16u * (uint32_t)c, base));
+    }
+    if constexpr (kScaled) {
+      const uint16_t* sc = (lane & 16) ? st.vsc : st.ksc;
+      s.sc = ntload<uint16_t>(sc + ((size_t)row0 + (lane & 15)) * (uint32_t)st.Hkv + st.kvh);
+    }
+  }
+  __device__ static __forceinline__ void store(const Regs& s, int wv, int lane, char* buf) {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) *(u4*)(buf + 16 * (block(j, wv) * 64 + lane)) = s.r[j];
+    if constexpr (kScaled) *(uint16_t*)(buf + kScaleOff + 2 * (lane & 31)) = s.sc;
+  }
+  // the fragments Store::load_tile would have loaded
+  __device__ static __forceinline__ void read(const char* buf, const LaneGeo& lg, typename Store::KFrag& k,
+                                              typename Store::VFrag& v) {
+    constexpr int KQ = RB / 64;   // 16-byte K pieces per lane
+#pragma unroll
+    for (int c = 0; c < KQ; ++c) k.r[c] = *(const u4*)(buf + 16 * pos(lg.kkey, lg.g + 4 * c));
+    using VW = std::remove_reference_t<decltype(v.r[0])>;
+    constexpr int VB = sizeof(VW);   // V bytes per lane and key
+    const int vbyte = VB * lg.kkey;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      v.r[e] = *(const VW*)(buf + 16 * (KCH + pos(4 * lg.g + e, vbyte / 16)) + (vbyte & 15));
+    if constexpr (kScaled) {
+      const int key = 4 * lg.g + (lg.kkey & 3);
+      k.ks = *(const uint16_t*)(buf + kScaleOff + 2 * key);
+      k.vs = *(const uint16_t*)(buf + kScaleOff + 32 + 2 * key);
+    }
+  }
+};
+
+// The sweep of run_tiles (contiguous tiles, several queries) through shared
+// tiles; ring holds two buffers of Share::kBytes.  Every wave of the
+// workgroup calls it with the same range: each tile costs one barrier.
+template <int D, int G, bool CAP, int RBK, class Store, class Map, class QF, class QPrep>
+__device__ __forceinline__ void run_tiles_shared(const DecodeArgs& a, const Store& st, const Map& map, QF& qf,
+                                                 QPrep&& prep_q, const LaneGeo& lg, Online<D, G, CAP>& on,
+                                                 int tfirst, int tend, int lane, int qlo, int qhi, int wv,
+                                                 char* ring) {
+  using SH = Share<Store, RBK>;
+  constexpr int NS = SH::NS;
+  typename SH::Regs sh[NS];
+  auto issue = [&](int t0, auto slotc) { SH::load(st, map.tile_row0(t0), wv, lane, sh[decltype(slotc)::value]); };
+  auto consume = [&](int t0, int i, auto slotc) {
+    constexpr int slot = decltype(slotc)::value;
+    char* buf = ring + (i & 1) * SH::kBytes;
+    SH::store(sh[slot], wv, lane, buf);   // the other waves left this buffer two barriers ago
+    issue(t0 + NS * kTile, slotc);
+    __syncthreads();
+    typename Store::KFrag kf;
+    typename Store::VFrag vf;
+    SH::read(buf, lg, kf, vf);
+    const f4 raw = st.scores(kf, qf);
+    bool valid[4], kvalid[4];
+    map.tile_valid(t0, lg, valid, kvalid);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = t0 + 4 * lg.g + e;
+      valid[e] = valid[e] && t >= qlo && t <= qhi;
+    }
+    float p[4];
+    if (on.softmax_tile(a.capl2, raw, valid, p)) on.rescale(lane);
+    st.template pv<true>(kf, vf, p, kvalid, on.o);
+  };
+
+  if (tfirst >= tend) {
+    prep_q(qf);
+    return;
+  }
+  const int ntiles = (tend - tfirst + kTile - 1) / kTile;
+  static_for<0, NS>([&](auto u) { issue(tfirst + decltype(u)::value * kTile, u); });
+  prep_q(qf);
+  int i = 0;
+  for (; i + NS <= ntiles; i += NS) {
+    static_for<0, NS>([&](auto u) {
+      constexpr int U = decltype(u)::value;
+      consume(tfirst + (i + U) * kTile, i + U, u);
+    });
+  }
+  static_for<0, NS - 1>([&](auto u) {
+    constexpr int U = decltype(u)::value;
+    if (i + U < ntiles) consume(tfirst + (i + U) * kTile, i + U, u);
+  });
+  __syncthreads();   // every wave is done with the buffers
+}
+
+// One sweep of a segment: through shared tiles by the RBK row-block waves of
+// the kv head (RBK > 1: multi-query kernels built for contiguous tiles, with
+// 2 * Share::kBytes of LDS at the start of dynamic LDS), else each wave on
+// its own.
+template <int D, int G, bool CAP, bool FM, bool MQ, int RBK, class Store, class Map, class QF, class QPrep>
+__device__ __forceinline__ void sweep(const DecodeArgs& a, const Store& st, const Map& map, QF& qf, QPrep&& prep_q,
+                                      const LaneGeo& lg, Online<D, G, CAP>& on, int tfirst, int tend, int lane,
+                                      int qlo, int qhi, int col0, char* ring) {
+  if constexpr (RBK > 1) {
+    static_assert(MQ && FM, "shared tiles are built for contiguous multi-query sweeps");
+    const int wv = __builtin_amdgcn_readfirstlane((col0 >> 4) & (RBK - 1));   // row block of this wave
+    run_tiles_shared<D, G, CAP, RBK>(a, st, map, qf, prep_q, lg, on, tfirst, tend, lane, qlo, qhi, wv, ring);
+  } else {
+    run_tiles<D, G, CAP, kPipe, FM, MQ>(a, st, map, qf, prep_q, lg, on, tfirst, tend, lane, qlo, qhi);
+  }
+}
+
 // ---------------------------------------------------------------- kernels
 //
 // FM (chosen by the host): every cache the kernel sweeps is contiguous in
@@ -1059,11 +1232,11 @@ __device__ __forceinline__ void table_span(const DecodeArgs& a, int t0, int t1, 
 }
 
 // Several queries per sequence: the visible keys [qlo, qhi] of the query whose
-// (query, head) pair is this lane's score column (column r: query r / grp);
-// an unused column (r >= grp * qn) sees nothing.
-__device__ __forceinline__ void query_bounds(const DecodeArgs& a, int b, int lane, int& qlo, int& qhi) {
+// (query, head) pair is this lane's score column (column r = col0 + lane % 16:
+// query r / grp); an unused column (r >= grp * qn) sees nothing.
+__device__ __forceinline__ void query_bounds(const DecodeArgs& a, int b, int lane, int col0, int& qlo, int& qhi) {
   const int L = a.seq_lens[b];
-  const int c = lane & 15;
+  const int c = col0 + (lane & 15);
   const int q = (a.q_pos ? a.q_pos[b] : L - a.qn) + c / a.grp;
   qhi = a.causal ? min(q, L - 1) : L - 1;
   qlo = (a.window > 0 && q >= a.window) ? q - a.window + 1 : 0;
@@ -1075,29 +1248,30 @@ __device__ __forceinline__ void query_bounds(const DecodeArgs& a, int b, int lan
 // (b, tb, te): the block-table staging is shared.  MQ: several queries per
 // sequence (G = 16 columns, a.grp * a.qn of them used); the lane's query
 // bounds [qlo, qhi] mask its column.
-template <int D, int G, bool CAP, class T, bool FM, bool MQ = false>
+template <int D, int G, bool CAP, class T, bool FM, bool MQ = false, int RBK = 1>
 __device__ __forceinline__ void paged_segment(const DecodeArgs& a, int b, int kvh, int lane, int tb, int te,
-                                              int32_t* lds_tbl, const PartialDst& dst) {
+                                              int32_t* lds_tbl, const PartialDst& dst, int col0 = 0,
+                                              char* ring = nullptr) {
   using QRaw = std::conditional_t<std::is_same_v<T, float>, QRaw32<D>, QRaw16<D>>;
   QRaw qraw;
   if (tb < te) {
     if constexpr (std::is_same_v<T, float>)
-      load_q_raw32<D, G, MQ>(a, b, kvh, lane, qraw);
+      load_q_raw32<D, G, MQ>(a, b, kvh, lane, qraw, col0);
     else
-      load_q_raw16<D, G, false, MQ>(a, b, kvh, lane, qraw);
+      load_q_raw16<D, G, false, MQ>(a, b, kvh, lane, qraw, col0);
   }
   int blk0, nblk;
   table_span(a, tb, te, blk0, nblk);
   stage_table(a, b, blk0, nblk, lds_tbl);
   if (tb >= te) {
     if constexpr (MQ)
-      write_empty_mq(dst, lane, a.grp, a.qn, a.num_heads);
+      write_empty_mq(dst, lane, a.grp, a.qn, a.num_heads, col0);
     else
       write_empty<G>(dst, lane);
     return;
   }
   int qlo = 0, qhi = 0;
-  if constexpr (MQ) query_bounds(a, b, lane, qlo, qhi);
+  if constexpr (MQ) query_bounds(a, b, lane, col0, qlo, qhi);
   LaneGeo lg;
   lg.init(lane);
   PagedMap map{lds_tbl, blk0, tb, te - 1, a.bs, FM};
@@ -1106,16 +1280,16 @@ __device__ __forceinline__ void paged_segment(const DecodeArgs& a, int b, int kv
   if constexpr (std::is_same_v<T, float>) {
     QF32<D> qf;
     StoreF32<D> st{(const float*)a.k, (const float*)a.v, a.num_kv_heads, kvh};
-    run_tiles<D, G, CAP, kPipe, FM, MQ>(a, st, map, qf, [&](QF32<D>& q) { convert_q<D, G, MQ>(a, lane, qraw, q); },
+    run_tiles<D, G, CAP, kPipe, FM, MQ>(a, st, map, qf, [&](QF32<D>& q) { convert_q<D, G, MQ>(a, lane, qraw, q, col0); },
                                         lg, on, tb & ~(kTile - 1), te, lane, qlo, qhi);
   } else {
     QF16<D> qf;
     StoreF16<D> st{(const _Float16*)a.k, (const _Float16*)a.v, a.num_kv_heads, kvh};
-    run_tiles<D, G, CAP, kPipe, FM, MQ>(a, st, map, qf, [&](QF16<D>& q) { convert_q<D, G, MQ>(a, lane, qraw, q); },
-                                        lg, on, tb & ~(kTile - 1), te, lane, qlo, qhi);
+    sweep<D, G, CAP, FM, MQ, RBK>(a, st, map, qf, [&](QF16<D>& q) { convert_q<D, G, MQ>(a, lane, qraw, q, col0); }, lg,
+                             on, tb & ~(kTile - 1), te, lane, qlo, qhi, col0, ring);
   }
   if constexpr (MQ)
-    on.finish_mq(dst, lane, a.grp, a.qn, a.num_heads);
+    on.finish_mq(dst, lane, a.grp, a.qn, a.num_heads, col0);
   else
     on.finish(dst, lane);
 }
@@ -1123,29 +1297,30 @@ __device__ __forceinline__ void paged_segment(const DecodeArgs& a, int b, int kv
 // The same for the tiered cache: keys below cold_lens[b] from the paged cold
 // pool (int8 words with f16 scales, or f16 rows when CF16), the rest from the
 // f16 ring.
-template <int D, int G, bool CAP, bool FM, bool CF16, bool MQ = false>
+template <int D, int G, bool CAP, bool FM, bool CF16, bool MQ = false, int RBK = 1>
 __device__ __forceinline__ void tiered_segment(const DecodeArgs& a, int b, int kvh, int lane, int tb, int te,
-                                               int32_t* lds_tbl, const PartialDst& dst) {
+                                               int32_t* lds_tbl, const PartialDst& dst, int col0 = 0,
+                                               char* ring = nullptr) {
   const int C = a.cold_lens ? a.cold_lens[b] : 0;   // no cold tier: a window ring
   const int ce = min(te, C);   // cold part [tb, ce)
   const int hb = max(tb, C);   // hot part  [hb, te)
   QRaw16<D> qraw;              // int8 cold keys use the int8 dim map, f16 keys the f16 one
   if (tb < ce)
-    load_q_raw16<D, G, !CF16, MQ>(a, b, kvh, lane, qraw);
+    load_q_raw16<D, G, !CF16, MQ>(a, b, kvh, lane, qraw, col0);
   else if (tb < te)
-    load_q_raw16<D, G, false, MQ>(a, b, kvh, lane, qraw);
+    load_q_raw16<D, G, false, MQ>(a, b, kvh, lane, qraw, col0);
   int blk0, nblk;
   table_span(a, tb, ce, blk0, nblk);
   stage_table(a, b, blk0, nblk, lds_tbl);
   if (tb >= te) {
     if constexpr (MQ)
-      write_empty_mq(dst, lane, a.grp, a.qn, a.num_heads);
+      write_empty_mq(dst, lane, a.grp, a.qn, a.num_heads, col0);
     else
       write_empty<G>(dst, lane);
     return;
   }
   int qlo = 0, qhi = 0;
-  if constexpr (MQ) query_bounds(a, b, lane, qlo, qhi);
+  if constexpr (MQ) query_bounds(a, b, lane, col0, qlo, qhi);
   LaneGeo lg;
   lg.init(lane);
   QF16<D> qf;
@@ -1155,59 +1330,83 @@ __device__ __forceinline__ void tiered_segment(const DecodeArgs& a, int b, int k
     PagedMap map{lds_tbl, blk0, tb, ce - 1, a.bs, FM};
     if constexpr (CF16) {
       StoreF16<D> st{(const _Float16*)a.k, (const _Float16*)a.v, a.num_kv_heads, kvh};
-      run_tiles<D, G, CAP, kPipe, FM, MQ>(a, st, map, qf, [&](QF16<D>& q) { convert_q<D, G, MQ>(a, lane, qraw, q); },
-                                          lg, on, tb & ~(kTile - 1), ce, lane, qlo, qhi);
+      sweep<D, G, CAP, FM, MQ, RBK>(a, st, map, qf, [&](QF16<D>& q) { convert_q<D, G, MQ>(a, lane, qraw, q, col0); },
+                               lg, on, tb & ~(kTile - 1), ce, lane, qlo, qhi, col0, ring);
     } else {
       StoreI8<D> st{(const uint32_t*)a.k, (const uint32_t*)a.v, a.k_scale, a.v_scale, a.num_kv_heads, kvh};
-      run_tiles<D, G, CAP, kPipe, FM, MQ>(a, st, map, qf, [&](QF16<D>& q) { convert_q<D, G, MQ>(a, lane, qraw, q); },
-                                          lg, on, tb & ~(kTile - 1), ce, lane, qlo, qhi);
+      sweep<D, G, CAP, FM, MQ, RBK>(a, st, map, qf, [&](QF16<D>& q) { convert_q<D, G, MQ>(a, lane, qraw, q, col0); },
+                               lg, on, tb & ~(kTile - 1), ce, lane, qlo, qhi, col0, ring);
     }
   }
   if (hb < te) {
     RingMap map{b, hb, te - 1, a.hw, FM};
     StoreF16<D> st{(const _Float16*)a.k_hot, (const _Float16*)a.v_hot, a.num_kv_heads, kvh};
     const bool had_cold = !CF16 && tb < ce;   // Q was laid out for int8 keys
-    run_tiles<D, G, CAP, kPipe, FM, MQ>(a, st, map, qf,
-                                        [&](QF16<D>& q) {
-                                          if (had_cold) load_q_raw16<D, G, false, MQ>(a, b, kvh, lane, qraw);
-                                          convert_q<D, G, MQ>(a, lane, qraw, q);
-                                        },
-                                        lg, on, hb & ~(kTile - 1), te, lane, qlo, qhi);
+    sweep<D, G, CAP, FM, MQ, RBK>(a, st, map, qf,
+                             [&](QF16<D>& q) {
+                               if (had_cold) load_q_raw16<D, G, false, MQ>(a, b, kvh, lane, qraw, col0);
+                               convert_q<D, G, MQ>(a, lane, qraw, q, col0);
+                             },
+                             lg, on, hb & ~(kTile - 1), te, lane, qlo, qhi, col0, ring);
   }
   if constexpr (MQ)
-    on.finish_mq(dst, lane, a.grp, a.qn, a.num_heads);
+    on.finish_mq(dst, lane, a.grp, a.qn, a.num_heads, col0);
   else
     on.finish(dst, lane);
 }
 
-// Static splits: workgroup (split, b, z) sweeps keys [split*T, (split+1)*T)
-// of sequence b for kv heads z*waves + [0, waves).
-template <int D, int G, bool CAP, class T, bool FM, bool MQ = false>
-__global__ __launch_bounds__(DATTN_MAX_THREADS) __attribute__((amdgpu_waves_per_eu(2))) void paged_split_kernel(DecodeArgs a) {
-  extern __shared__ int32_t lds_tbl[];
-  const int split = blockIdx.x, b = blockIdx.y;
-  const int lane = threadIdx.x & 63;
-  const int kvh = blockIdx.z * (blockDim.x >> 6) + (threadIdx.x >> 6);
-  int lo, hi, qp;
-  visible_range(a, b, lo, hi, qp);
-  const int tb = max(split * a.split_tokens, lo);
-  const int te = min((split + 1) * a.split_tokens, hi + 1);
-  paged_segment<D, G, CAP, T, FM, MQ>(a, b, kvh, lane, tb, te, lds_tbl,
-                                      split_dst(a, b, kvh, MQ ? a.grp : G, split, D));
+// The wave's kv head and first score column.  One query per sequence: wave v
+// of workgroup z is kv head z*waves + v.  Several queries (MQ): the (kv head,
+// row block) pairs are numbered kv-head-major, a.rbk row blocks of 16
+// columns per kv head, so the row blocks of a kv head sit in one workgroup
+// and sweep the same keys side by side.
+template <bool MQ>
+__device__ __forceinline__ void wave_head(const DecodeArgs& a, int& kvh, int& col0) {
+  const int v = blockIdx.z * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  if constexpr (MQ) {
+    kvh = v / a.rbk;
+    col0 = 16 * (v - kvh * a.rbk);
+  } else {
+    kvh = v;
+    col0 = 0;
+  }
 }
 
-template <int D, int G, bool CAP, bool FM, bool CF16, bool MQ = false>
-__global__ __launch_bounds__(DATTN_MAX_THREADS) __attribute__((amdgpu_waves_per_eu(2))) void tiered_split_kernel(DecodeArgs a) {
-  extern __shared__ int32_t lds_tbl[];
+// Multi-query workgroups hold up to 8 row-block waves of one kv head.
+#define DATTN_BOUNDS(MQ) __launch_bounds__((MQ) ? 2 * DATTN_MAX_THREADS : DATTN_MAX_THREADS)
+
+// Static splits: workgroup (split, b, z) sweeps keys [split*T, (split+1)*T)
+// of sequence b for its waves' kv heads.
+template <int D, int G, bool CAP, class T, bool FM, bool MQ = false, int RBK = 1>
+__global__ DATTN_BOUNDS(MQ) __attribute__((amdgpu_waves_per_eu(2))) void paged_split_kernel(DecodeArgs a) {
+  extern __shared__ int32_t lds_all[];
+  int32_t* lds_tbl = MQ ? lds_all + a.tile_lds / 4 : lds_all;
   const int split = blockIdx.x, b = blockIdx.y;
   const int lane = threadIdx.x & 63;
-  const int kvh = blockIdx.z * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  int kvh, col0;
+  wave_head<MQ>(a, kvh, col0);
   int lo, hi, qp;
   visible_range(a, b, lo, hi, qp);
   const int tb = max(split * a.split_tokens, lo);
   const int te = min((split + 1) * a.split_tokens, hi + 1);
-  tiered_segment<D, G, CAP, FM, CF16, MQ>(a, b, kvh, lane, tb, te, lds_tbl,
-                                          split_dst(a, b, kvh, MQ ? a.grp : G, split, D));
+  paged_segment<D, G, CAP, T, FM, MQ, RBK>(a, b, kvh, lane, tb, te, lds_tbl,
+                                      split_dst(a, b, kvh, MQ ? a.grp : G, split, D), col0, (char*)lds_all);
+}
+
+template <int D, int G, bool CAP, bool FM, bool CF16, bool MQ = false, int RBK = 1>
+__global__ DATTN_BOUNDS(MQ) __attribute__((amdgpu_waves_per_eu(2))) void tiered_split_kernel(DecodeArgs a) {
+  extern __shared__ int32_t lds_all[];
+  int32_t* lds_tbl = MQ ? lds_all + a.tile_lds / 4 : lds_all;
+  const int split = blockIdx.x, b = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  int kvh, col0;
+  wave_head<MQ>(a, kvh, col0);
+  int lo, hi, qp;
+  visible_range(a, b, lo, hi, qp);
+  const int tb = max(split * a.split_tokens, lo);
+  const int te = min((split + 1) * a.split_tokens, hi + 1);
+  tiered_segment<D, G, CAP, FM, CF16, MQ, RBK>(a, b, kvh, lane, tb, te, lds_tbl,
+                                          split_dst(a, b, kvh, MQ ? a.grp : G, split, D), col0, (char*)lds_all);
 }
 
 // ------------------------------------------------------- balanced schedule
@@ -1293,20 +1492,24 @@ __device__ __forceinline__ int unit_prefix(const DecodeArgs& a, int32_t* P) {
 
 // KIND: 0 paged f16, 1 paged f32, 2 tiered int8, 3 tiered f16 (and the window
 // ring); 4, 5, 6, 7: paged f16, paged f32, tiered int8, tiered f16 with
-// several queries per sequence (G = 16 columns).  Registers are capped for two
+// several queries per sequence (G = 16 columns per wave, a.rbk waves per kv
+// head).  Registers are capped for two
 // waves per SIMD: measured, a third wave (with Q moved to LDS to make room)
 // and a third tile of loads in flight per wave are both slower -- about
 // 32 KiB of loads in flight per SIMD is what HBM rewards here.
-template <int D, int G, bool CAP, int KIND, bool FM>
-__global__ __launch_bounds__(DATTN_MAX_THREADS) __attribute__((amdgpu_waves_per_eu(2)))
+template <int D, int G, bool CAP, int KIND, bool FM, int RBK = 1>
+__global__ DATTN_BOUNDS(KIND >= 4) __attribute__((amdgpu_waves_per_eu(2)))
 void balanced_kernel(DecodeArgs a) {
-  extern __shared__ int32_t lds[];
+  extern __shared__ int32_t lds_all[];
+  int32_t* lds = KIND >= 4 ? lds_all + a.tile_lds / 4 : lds_all;
+  char* ring = (char*)lds_all;
   const int B = a.num_seqs;
   int32_t* P = lds;
   int32_t* tbl = lds + ((B + 4) & ~3);
   const int w = blockIdx.x, nw = gridDim.x;
   const int lane = threadIdx.x & 63;
-  const int kvh = blockIdx.z * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  int kvh, col0;
+  wave_head<(KIND >= 4)>(a, kvh, col0);
   const int N = unit_prefix<KIND>(a, P);
   const int C = (N + nw - 1) / nw;
   if (w == 0 && blockIdx.z == 0) {
@@ -1342,13 +1545,13 @@ void balanced_kernel(DecodeArgs a) {
     else if constexpr (KIND == 1)
       paged_segment<D, G, CAP, float, FM>(a, b, kvh, lane, tb, te, tbl, dst);
     else if constexpr (KIND == 4)
-      paged_segment<D, G, CAP, _Float16, FM, true>(a, b, kvh, lane, tb, te, tbl, dst);
+      paged_segment<D, G, CAP, _Float16, FM, true, RBK>(a, b, kvh, lane, tb, te, tbl, dst, col0, ring);
     else if constexpr (KIND == 5)
-      paged_segment<D, G, CAP, float, FM, true>(a, b, kvh, lane, tb, te, tbl, dst);
+      paged_segment<D, G, CAP, float, FM, true>(a, b, kvh, lane, tb, te, tbl, dst, col0, ring);
     else if constexpr (KIND == 6)
-      tiered_segment<D, G, CAP, FM, false, true>(a, b, kvh, lane, tb, te, tbl, dst);
+      tiered_segment<D, G, CAP, FM, false, true, RBK>(a, b, kvh, lane, tb, te, tbl, dst, col0, ring);
     else if constexpr (KIND == 7)
-      tiered_segment<D, G, CAP, FM, true, true>(a, b, kvh, lane, tb, te, tbl, dst);
+      tiered_segment<D, G, CAP, FM, true, true, RBK>(a, b, kvh, lane, tb, te, tbl, dst, col0, ring);
     else
       paged_segment<D, G, CAP, _Float16, FM>(a, b, kvh, lane, tb, te, tbl, dst);
     x0 = seg_end;

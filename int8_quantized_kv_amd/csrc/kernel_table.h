@@ -38,4 +38,18 @@ inline void* split_kernel(int kind, int D, bool cap, int G, bool contig) {
   return cap ? split_kernel_d128_cap1(kind, G, contig) : split_kernel_d128_cap0(kind, G, contig);
 }
 
+// Multi-query kernels (kPagedF16MQ, kBalF16MQ, kTieredMQ, kTieredF16MQ,
+// kBalTieredMQ, kBalTieredF16MQ) for contiguous tiles whose rbk in {2, 4, 8}
+// row-block waves per kv head share each tile through LDS (2 * 64 * D bytes
+// at the start of dynamic LDS).  nullptr for other kinds.
+void* shared_kernel_d64_cap0(int kind, int rbk);
+void* shared_kernel_d64_cap1(int kind, int rbk);
+void* shared_kernel_d128_cap0(int kind, int rbk);
+void* shared_kernel_d128_cap1(int kind, int rbk);
+
+inline void* shared_kernel(int kind, int D, bool cap, int rbk) {
+  if (D == 64) return cap ? shared_kernel_d64_cap1(kind, rbk) : shared_kernel_d64_cap0(kind, rbk);
+  return cap ? shared_kernel_d128_cap1(kind, rbk) : shared_kernel_d128_cap0(kind, rbk);
+}
+
 }  // namespace dattn

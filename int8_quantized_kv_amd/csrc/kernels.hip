@@ -1,5 +1,6 @@
 // kernels.hip -- the split-kernel instances of one (head_dim, softcap) pair,
-// chosen with -DDATTN_D=<64|128> -DDATTN_CAP=<0|1>.
+// chosen with -DDATTN_D=<64|128> -DDATTN_CAP=<0|1>; with -DDATTN_SHARED=1 the
+// multi-query instances whose row-block waves share tiles through LDS.
 #include "decode_kernels.h"
 #include "kernel_table.h"
 
@@ -10,6 +11,7 @@
 namespace dattn {
 namespace {
 
+#if !DATTN_SHARED
 template <int G, bool FM>
 void* instance(int kind) {
   constexpr int D = DATTN_D;
@@ -42,6 +44,26 @@ void* instance(int kind) {
   }
 }
 
+#endif
+
+#if DATTN_SHARED
+// Multi-query kinds over contiguous tiles whose RBK row-block waves per kv
+// head share each tile through LDS.
+template <int RBK>
+void* shared_instance(int kind) {
+  constexpr int D = DATTN_D;
+  constexpr bool CAP = DATTN_CAP != 0;
+  switch (kind) {
+    case kPagedF16MQ: return (void*)&paged_split_kernel<D, 16, CAP, _Float16, true, true, RBK>;
+    case kBalF16MQ: return (void*)&balanced_kernel<D, 16, CAP, 4, true, RBK>;
+    case kTieredMQ: return (void*)&tiered_split_kernel<D, 16, CAP, true, false, true, RBK>;
+    case kTieredF16MQ: return (void*)&tiered_split_kernel<D, 16, CAP, true, true, true, RBK>;
+    case kBalTieredMQ: return (void*)&balanced_kernel<D, 16, CAP, 6, true, RBK>;
+    case kBalTieredF16MQ: return (void*)&balanced_kernel<D, 16, CAP, 7, true, RBK>;
+    default: return nullptr;
+  }
+}
+#else
 template <bool FM>
 void* by_group(int kind, int G) {
   switch (G) {
@@ -54,13 +76,29 @@ void* by_group(int kind, int G) {
   }
 }
 
+#endif
+
 }  // namespace
 
+#if DATTN_SHARED
+#define DATTN_NAME2(d, c) shared_kernel_d##d##_cap##c
+#define DATTN_NAME(d, c) DATTN_NAME2(d, c)
+
+void* DATTN_NAME(DATTN_D, DATTN_CAP)(int kind, int rbk) {
+  switch (rbk) {
+    case 2: return shared_instance<2>(kind);
+    case 4: return shared_instance<4>(kind);
+    case 8: return shared_instance<8>(kind);
+    default: return nullptr;
+  }
+}
+#else
 #define DATTN_NAME2(d, c) split_kernel_d##d##_cap##c
 #define DATTN_NAME(d, c) DATTN_NAME2(d, c)
 
 void* DATTN_NAME(DATTN_D, DATTN_CAP)(int kind, int G, bool contig) {
   return contig ? by_group<true>(kind, G) : by_group<false>(kind, G);
 }
+#endif
 
 }  // namespace dattn

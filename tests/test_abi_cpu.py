@@ -120,6 +120,9 @@ BAD = [
     (dict(phases=7), dk.ERR_INVALID, "phases"),
     (dict(out_dtype=2), dk.ERR_INVALID, "out_dtype"),
     (dict(num_seqs=70000), dk.ERR_UNSUPPORTED, "num_seqs"),
+    (dict(query_len=-1), dk.ERR_INVALID, "query_len"),
+    (dict(query_len=33), dk.ERR_UNSUPPORTED, "128"),           # 33 queries x group 4 = 132 rows
+    (dict(query_len=129, num_heads=2, num_kv_heads=2), dk.ERR_UNSUPPORTED, "128"),
 ]
 
 
@@ -157,6 +160,13 @@ def test_workspace_size_values(lib):
     assert ws_size(lib, good_params(max_seq_len=500), kind=dk.KIND_TIERED_F16)[0] == 0
     assert ws_size(lib, good_params(), kind=dk.KIND_TIERED_F16)[1] == ws_size(lib, good_params(),
                                                                               kind=dk.KIND_TIERED_INT8)[1]
+    # multi-query: slots and rows grow with the row blocks (query_len * group / 16 waves per kv head)
+    for qn, hkv, n_heads in ((32, 2, 8), (8, 8, 32), (128, 1, 1)):
+        rc, n0, _ = ws_size(lib, good_params(num_kv_heads=hkv, num_heads=n_heads, query_len=qn))
+        slots = 4096 // (hkv * -(-qn * n_heads // hkv // 16)) + 2
+        rows = slots * n_heads * qn
+        assert rc == 0 and n0 == up(rows * 128 * 4) + up(rows * 8) + up(5 * 4), (qn, hkv)
+    assert ws_size(lib, good_params(query_len=32), kind=dk.KIND_BLOCK_SPARSE, sb=32)[0] == dk.ERR_UNSUPPORTED
     # sparse: sparse_block must be a positive multiple of block_size
     assert ws_size(lib, good_params(), kind=dk.KIND_BLOCK_SPARSE, sb=24)[0] == dk.ERR_INVALID
     assert ws_size(lib, good_params(), kind=dk.KIND_BLOCK_SPARSE, sb=32)[0] == 0

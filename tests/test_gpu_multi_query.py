@@ -1,6 +1,6 @@
-"""GPU parity of multi-query decode over the paged cache (Qn query rows per
-sequence, query i at q_pos[b] + i; the MFMA columns hold the Qn * G
-(query, head) pairs of a kv head) against the fp64 oracle."""
+"""GPU parity of multi-query decode (Qn query rows per sequence, query i at
+q_pos[b] + i; the MFMA columns hold the Qn * G (query, head) pairs of a kv
+head, 16 per wave) against the fp64 oracle."""
 import numpy as np
 import pytest
 
@@ -129,3 +129,79 @@ def test_mq_other_caches_sweep(seed):
                     window=int(rng.choice([0, 0, 17, 200])), **kw)
     st = int(np.random.default_rng(seed).choice([0, 0, 16, 256]))
     _check(case, st, what=f"seed{seed} {kind} B{B} Qn{qn} G{G} Hkv{Hkv} D{D}")
+
+
+# More than 16 (query, head) rows per kv head: the rows are cut into blocks of
+# 16, one wave each, and the row blocks of a kv head share a workgroup.
+@pytest.mark.parametrize("G,qn,Hkv", [(4, 5, 8), (4, 8, 2), (4, 12, 1), (4, 16, 8), (8, 16, 4), (1, 100, 2),
+                                      (2, 40, 3), (8, 9, 1), (1, 128, 1)])
+@pytest.mark.parametrize("split_tokens", [0, 64])
+def test_mq_row_blocks(G, qn, Hkv, split_tokens):
+    c = synth.paged_case(520 + qn, 2, Hkv * G, Hkv, 128, 16, lens=[900, qn + 37], kv_dtype=synth.F16, query_len=qn,
+                         softcap=30.0 if qn % 2 else 0.0, window=300 if G == 4 else 0)
+    _check(c, split_tokens, what=f"rows {G * qn} G{G} Qn{qn} Hkv{Hkv}")
+
+
+@pytest.mark.parametrize("kind", ["tiered", "tiered_f16", "ring"])
+@pytest.mark.parametrize("split_tokens", [0, 48])
+def test_mq_row_blocks_other_caches(kind, split_tokens):
+    kw = dict(query_len=12, softcap=50.0)
+    if kind == "ring":
+        c = synth.ring_case(530, 3, 32, 8, 128, 256, [1000, 100, 257], **kw)
+    else:
+        make = synth.tiered_case if kind == "tiered" else synth.tiered_f16_case
+        c = make(531, 2, 32, 8, 128, 16, [700, 613], [450, 420], 256, window=300, **kw)
+    _check(c, split_tokens, what=f"{kind} Qn12 (48 rows)")
+
+
+def test_mq_row_blocks_f32_d64_and_short_sequences():
+    # q_pos defaults to L - Qn: the early queries of a short sequence see nothing
+    c = synth.paged_case(532, 4, 32, 8, 64, 5, lens=[3, 0, 1, 70], kv_dtype=synth.F32, query_len=20)
+    _check(c, what="paged f32 D64 Qn20 (80 rows), L < Qn")
+
+
+def test_mq_row_blocks_f16_q_and_output_modes():
+    import torch
+    c = synth.paged_case(533, 2, 32, 8, 128, 16, lens=[900, 300], kv_dtype=synth.F16, query_len=16)
+    dc = DeviceCase(c)
+    q16 = dc.q.half()
+    dc.q = q16.float()           # the f32 copy of f16 values: an f16 q must give the same bits
+    o32, l32 = dc.run()
+    o16, l16 = dc.run(out_dtype=torch.float16)
+    o_none, l_only = dc.run(want_out=False)
+    dc.q = q16
+    oq, lq = dc.run()
+    torch.cuda.synchronize()
+    assert tuple(o16.shape) == (2, 16, 32, 128) and o_none is None
+    assert torch.equal(o16, o32.to(torch.float16)) and torch.equal(l16, l32) and torch.equal(l_only, l32)
+    assert torch.equal(oq, o32) and torch.equal(lq, l32)
+    c.q = q16.float().cpu().numpy()
+    orf, lrf = oracle_run(c)
+    compare(o32.cpu().numpy(), l32.cpu().numpy(), orf, lrf, what="Qn16 (64 rows) f16 q")
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_mq_row_blocks_random_sweep(seed):
+    rng = np.random.default_rng(99_000 + seed)
+    kind = ["paged", "tiered", "tiered_f16", "ring"][seed % 4]
+    G = int(rng.choice([1, 2, 4, 8]))
+    qn = int(rng.integers(16 // G + 1, 128 // G + 1))
+    Hkv = int(rng.choice([1, 2, 3, 4, 8]))
+    D = int(rng.choice([64, 128]))
+    B = int(rng.integers(1, 4))
+    lens = rng.integers(0, 700, size=B)
+    kw = dict(query_len=qn, causal=int(rng.random() < 0.85), softcap=float(rng.choice([0.0, 5.0, 50.0])))
+    if kind == "paged":
+        case = synth.paged_case(seed, B, Hkv * G, Hkv, D, int(rng.choice([3, 16])), lens=lens,
+                                kv_dtype=synth.F32 if rng.random() < 0.25 else synth.F16,
+                                window=int(rng.choice([0, 0, 17, 200])), **kw)
+    elif kind == "ring":
+        case = synth.ring_case(seed, B, Hkv * G, Hkv, D, int(rng.choice([16, 50, 128])), lens, **kw)
+    else:
+        hw = int(rng.choice([16, 50, 128]))
+        cold = np.array([max(0, int(L) - int(rng.integers(0, hw + 1))) for L in lens])
+        make = synth.tiered_case if kind == "tiered" else synth.tiered_f16_case
+        case = make(seed, B, Hkv * G, Hkv, D, int(rng.choice([5, 16])), lens, cold, hw,
+                    window=int(rng.choice([0, 0, 17, 200])), **kw)
+    st = int(np.random.default_rng(seed).choice([0, 0, 16, 256]))
+    _check(case, st, what=f"seed{seed} {kind} B{B} Qn{qn} G{G} rows {qn * G} Hkv{Hkv} D{D}")
