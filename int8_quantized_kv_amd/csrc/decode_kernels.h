@@ -1720,6 +1720,78 @@ __device__ __forceinline__ void merge_partials(const Loc& loc, int n, const OutR
   if (tid == 0 && lse_out) *lse_out = Lt > 0.f ? (M + __builtin_log2f(Lt)) * kLn2 : -__builtin_inff();
 }
 
+// The same merge by 32 threads for one row with few partials: the partials
+// are folded in one at a time with a running max, four loads in flight;
+// thread c owns dims 4c + 128j.  No LDS and no barrier.
+template <int D, class Loc>
+__device__ __forceinline__ void merge_row(const Loc& loc, int n, const OutRow out, float* __restrict__ lse_out,
+                                          int c) {
+  constexpr int NJ = D / 128 > 0 ? D / 128 : 1;
+  constexpr int DC = D >= 128 ? 32 : D / 4;
+  constexpr int U = 4;
+  float m = -__builtin_inff(), L = 0.f;
+  f4 o[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) o[j] = f4{0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < n; s0 += U) {
+    float2 v[U];
+    f4 x[U][NJ];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int s = s0 + u;
+      v[u] = s < n ? loc.ml(s) : make_float2(-__builtin_inff(), 0.f);
+      if (s < n && c < DC && out.p) {
+        const float* row = loc.acc(s);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) x[u][j] = *(const f4*)(row + 128 * j + 4 * c);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (v[u].y > 0.f) {
+        const float m_new = fmaxf(m, v[u].x);
+        const float ca = fast_exp2(m - m_new), cb = fast_exp2(v[u].x - m_new);
+        L = L * ca + v[u].y * cb;
+        if (c < DC) {
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) o[j] = o[j] * ca + x[u][j] * cb;
+        }
+        m = m_new;
+      }
+    }
+  }
+  if (out.p && c < DC) {
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) out.store(128 * j + 4 * c + e, L > 0.f ? o[j][e] / L : 0.f);
+  }
+  if (c == 0 && lse_out) *lse_out = L > 0.f ? (m + __builtin_log2f(L)) * kLn2 : -__builtin_inff();
+}
+
+// Eight rows per workgroup: a row with at most kShortRow partials is merged
+// by its own 32 threads; a longer one (a long sequence in a batch of short
+// ones) by all 256 threads afterwards, one row at a time.  n_of(row) must give
+// every thread the same count.
+constexpr int kShortRow = 16;
+template <int D, class LocOf, class NOf>
+__device__ __forceinline__ void merge_rows(const LocOf& loc_of, const NOf& n_of, void* out, bool out_f16,
+                                           float* lse, int nbh) {
+  const int tid = threadIdx.x, row0 = blockIdx.x * 8;
+  const int row = row0 + (tid >> 5);
+  if (row < nbh) {
+    const int n = n_of(row);
+    if (n <= kShortRow) merge_row<D>(loc_of(row), n, out_row(out, out_f16, row, D), lse ? lse + row : nullptr, tid & 31);
+  }
+  for (int r = row0; r < min(row0 + 8, nbh); ++r) {
+    const int n = n_of(r);
+    if (n > kShortRow) {
+      merge_partials<D>(loc_of(r), n, out_row(out, out_f16, r, D), lse ? lse + r : nullptr);
+      __syncthreads();   // the LDS of the merge is reused by the next long row
+    }
+  }
+}
+
 // Static splits: partials of (b, h) at [bh, s] for s < S.
 struct SplitLoc {
   const float* acc0;
@@ -1767,6 +1839,52 @@ __global__ __launch_bounds__(256) void combine_balanced_kernel(const float* __re
   }
   const SlotLoc loc{part_acc + (slot0 * H + h) * D, part_ml + slot0 * H + h, H, D};
   merge_partials<D>(loc, n, out_row(out, out_f16 != 0, bh, D), lse ? lse + bh : nullptr);
+}
+
+// Balanced schedule, eight rows per workgroup (the partials of (b, h) found
+// as in combine_balanced_kernel); for calls whose rows have few partials.
+template <int D>
+__global__ __launch_bounds__(256) void combine_balanced_rows_kernel(const float* __restrict__ part_acc,
+                                                                    const float2* __restrict__ part_ml,
+                                                                    const int32_t* __restrict__ sched,
+                                                                    void* __restrict__ out, int out_f16,
+                                                                    float* __restrict__ lse, int H, int nbh) {
+  const int C = sched[1];
+  auto span = [&](int bh, int& n, size_t& slot0) {
+    const int b = bh / H;
+    const int p0 = sched[2 + b], p1 = sched[3 + b];
+    n = 0;
+    slot0 = 0;
+    if (p1 > p0 && C > 0) {
+      const int w0 = p0 / C, w1 = (p1 - 1) / C;
+      n = w1 - w0 + 1;
+      slot0 = (size_t)(w0 + b);
+    }
+  };
+  auto n_of = [&](int bh) {
+    int n;
+    size_t slot0;
+    span(bh, n, slot0);
+    return n;
+  };
+  auto loc_of = [&](int bh) {
+    int n;
+    size_t slot0;
+    span(bh, n, slot0);
+    const int h = bh - (bh / H) * H;
+    return SlotLoc{part_acc + (slot0 * H + h) * D, part_ml + slot0 * H + h, H, D};
+  };
+  merge_rows<D>(loc_of, n_of, out, out_f16 != 0, lse, nbh);
+}
+
+// Static splits with at most kShortRow splits, eight rows per workgroup.
+template <int D>
+__global__ __launch_bounds__(256) void combine_rows_kernel(const float* __restrict__ part_acc,
+                                                           const float2* __restrict__ part_ml, void* __restrict__ out,
+                                                           int out_f16, float* __restrict__ lse, int S, int nbh) {
+  auto n_of = [&](int) { return S; };
+  auto loc_of = [&](int bh) { return SplitLoc{part_acc + (size_t)bh * S * D, part_ml + (size_t)bh * S, D}; };
+  merge_rows<D>(loc_of, n_of, out, out_f16 != 0, lse, nbh);
 }
 
 }  // namespace dattn

@@ -41,6 +41,34 @@ def test_many_short_sequences(B):
     _sampled(c, f"paged f16 B{B} L 1-64")
 
 
+def test_combine_rows_with_one_long_sequence():
+    # 300 sequences share the workers, so the combine takes eight rows per
+    # workgroup; the one long sequence has far more partials than a row group
+    # merges alone and is merged by the whole workgroup
+    rng = np.random.default_rng(714)
+    lens = rng.integers(1, 65, size=300)
+    lens[137] = 40000
+    c = synth.paged_case(714, 300, 32, 8, 128, 16, lens=lens, kv_dtype=synth.F16, softcap=30.0)
+    log("edge combine rows, one long sequence")
+    og, lg = DeviceCase(c).run_np()
+    H = 32
+    pairs = np.unique(np.concatenate([137 * H + np.arange(0, H, 3), [0, 136 * H + 5, 138 * H + 7, 299 * H + 31],
+                                      rng.integers(0, 300 * H, 20)])).astype(np.int32)
+    ro, rl = oracle_run(c, pairs=pairs)
+    compare(og.reshape(300 * H, -1)[pairs], lg.reshape(300 * H)[pairs], ro, rl, what="combine rows, long row")
+
+
+@pytest.mark.parametrize("longest,split_tokens", [(1024, 64), (1100, 64), (1100, 128)])
+def test_combine_rows_static_splits(longest, split_tokens):
+    # 72 x 32 rows: with at most 16 splits per row the static path's combine takes
+    # eight rows per workgroup (1100 keys in splits of 64 make 18 and take the other)
+    rng = np.random.default_rng(715)
+    lens = rng.integers(0, 1025, size=72)
+    lens[5] = longest
+    c = synth.paged_case(715, 72, 32, 8, 128, 16, lens=lens, kv_dtype=synth.F16)
+    _sampled(c, f"static splits of {split_tokens}, longest {longest}", n=60)
+
+
 def test_largest_group_and_many_heads():
     c = synth.paged_case(711, 3, 128, 16, 128, 16, lens=[2000, 1, 777], kv_dtype=synth.F16, softcap=30.0)
     _sampled(c, "H128 / Hkv16 (G8)")
