@@ -341,13 +341,14 @@ typedef struct {
 } sparse_csr;
 
 static int sparse_select(const sparse_csr* c, int32_t h, int64_t q, unsigned char* sel, int64_t nsel) {
+  memset(sel, 0, (size_t)nsel);
+  if (q < 0) return ORC_OK;   /* a query before position 0 has no CSR row: it selects no block */
   int64_t r = q / c->sparse_block;
   if (r + 1 >= c->row_stride) return ORC_EINVAL;
   int32_t layout = h % c->num_layouts;
   const int32_t* rp = c->row_ptr + (int64_t)layout * c->row_stride;
   int32_t start = rp[r], end = rp[r + 1];
   if (start < 0 || end < start || end > c->col_stride) return ORC_EINVAL;
-  memset(sel, 0, (size_t)nsel);
   for (int32_t e = start; e < end; ++e) {
     int32_t j = c->col_idx[(int64_t)layout * c->col_stride + e];
     if (j >= 0 && j <= r && j < nsel) sel[j] = 1;

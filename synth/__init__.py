@@ -358,10 +358,13 @@ def random_rows(rng, R, NL, density=0.4, dup_frac=0.3, beyond=True):
 
 
 def sparse_case(seed, B, H, Hkv, D, bs, sparse_block, num_layouts, lens, rows=None, permute=True, q_pos=None,
-                causal=1, window=0, softcap=0.0, scale=0.0, name="", csr_kind="local_strided") -> Case:
+                causal=1, window=0, softcap=0.0, scale=0.0, name="", csr_kind="local_strided", query_len=1) -> Case:
+    """query_len > 1: q is [B, query_len, H, D], query i of sequence b at position
+    q_pos[b] + i (q_pos[b] defaults to seq_lens[b] - query_len), each with the CSR
+    row of its own position."""
     rng = np.random.default_rng(seed)
     lens = np.asarray(lens, np.int32)
-    q = rng.standard_normal((B, H, D), dtype=np.float32)
+    q = rng.standard_normal((B, H, D) if query_len == 1 else (B, query_len, H, D), dtype=np.float32)
     nblk = (lens.astype(np.int64) + bs - 1) // bs
     pool = max(int(nblk.sum()), 1)
     k = _normal(rng, (pool, bs, Hkv, D), F16)
@@ -373,7 +376,8 @@ def sparse_case(seed, B, H, Hkv, D, bs, sparse_block, num_layouts, lens, rows=No
                 else random_rows(rng, R, num_layouts))
     row_ptr, col_idx = csr_from_rows(rows)
     qp = None if q_pos is None else np.asarray(q_pos, np.int32)
-    return Case("sparse", _params(B, H, Hkv, D, bs, table.shape[1], pool, scale, causal, window, softcap), q, lens,
+    return Case("sparse", _params(B, H, Hkv, D, bs, table.shape[1], pool, scale, causal, window, softcap, query_len),
+                q, lens,
                 qp, k_cache=k, v_cache=v, block_table=table, sparse_block=int(sparse_block),
                 num_layouts=int(num_layouts), row_ptr=row_ptr, col_idx=col_idx, name=name, extra=dict(rows=rows))
 

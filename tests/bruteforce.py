@@ -81,7 +81,9 @@ def visible_matrix(case, b, i=0):
     if case.kind == "ring":
         ok &= t >= L - case.hot_window
     vis = np.repeat(ok[None, :], H, axis=0)
-    if case.kind == "sparse":
+    if case.kind == "sparse" and q < 0:
+        vis[:] = False   # a query before position 0 has no CSR row
+    elif case.kind == "sparse":
         SB = case.sparse_block
         r = q // SB
         for h in range(H):

@@ -113,3 +113,57 @@ def test_multi_query_other_caches_match_bruteforce(kind, seed):
     ref_out, ref_lse = attend(case)
     _close(out, ref_out)
     _close(lse, ref_lse)
+
+
+def _sparse_case(seed, rng):
+    Hkv, G, Qn = int(rng.choice([1, 2])), int(rng.choice([1, 2, 4])), int(rng.choice([2, 3, 4, 8]))
+    B, D, bs = 2, 16, int(rng.choice([4, 8]))
+    SB = bs * int(rng.choice([1, 2, 4]))
+    lens = rng.integers(0, 260, size=B)
+    q_pos = None
+    if rng.random() < 0.4:
+        q_pos = np.array([int(rng.integers(0, max(1, L))) for L in lens], np.int32)
+    return synth.sparse_case(seed, B, Hkv * G, Hkv, D, bs, SB, int(rng.choice([1, 3, 4])), lens, q_pos=q_pos,
+                             query_len=Qn, causal=int(rng.integers(0, 2)), window=int(rng.choice([0, 0, 30])),
+                             softcap=float(rng.choice([0.0, 5.0])),
+                             csr_kind=str(rng.choice(["local_strided", "random"])))
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_multi_query_block_sparse_matches_bruteforce(seed):
+    """Each query selects the blocks of its own CSR row (row q // SB of each
+    head's layout); a query before position 0 (L < Qn) selects none."""
+    case = _sparse_case(seed, np.random.default_rng(9800 + seed))
+    out, lse = _run(case)
+    ref_out, ref_lse = attend(case)
+    _close(out, ref_out)
+    _close(lse, ref_lse)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_multi_query_block_sparse_equals_single_queries(seed):
+    case = _sparse_case(seed, np.random.default_rng(9900 + seed))
+    out, lse = _run(case)
+    p = case.params
+    B, Qn, H = p["num_seqs"], p["query_len"], p["num_heads"]
+    q0 = case.q_pos if case.q_pos is not None else (case.seq_lens - Qn).astype(np.int32)
+    for i in range(Qn):
+        qi = (q0 + i).astype(np.int32)
+        if np.any(qi < 0):
+            continue   # the single-query call takes no position below 0
+        single = synth.Case("sparse", dict(p, query_len=1), np.ascontiguousarray(case.q[:, i]), case.seq_lens, qi,
+                            k_cache=case.k_cache, v_cache=case.v_cache, block_table=case.block_table,
+                            sparse_block=case.sparse_block, num_layouts=case.num_layouts, row_ptr=case.row_ptr,
+                            col_idx=case.col_idx)
+        o1, l1 = oracle.run(single)
+        assert np.array_equal(out[:, i], o1.reshape(B, H, -1)), i
+        assert np.array_equal(lse[:, i], l1.reshape(B, H)), i
+
+
+def test_multi_query_block_sparse_query_before_position_zero_sees_nothing():
+    # L = 3 < Qn = 5 without q_pos: the first two queries sit at -2 and -1; non-causal
+    # so that only the missing CSR row hides the keys
+    c = synth.sparse_case(5, 1, 4, 2, 16, 4, 8, 2, [3], query_len=5, causal=0)
+    out, lse = _run(c)
+    assert np.all(lse[0, :2] == -np.inf) and np.all(out[0, :2] == 0.0)
+    assert np.all(np.isfinite(lse[0, 2:]))
