@@ -81,13 +81,14 @@ def kv_bytes(case) -> int:
             total += ncold * Hkv * 2 * (D + 2) + nhot * Hkv * 2 * D * 2
         else:
             SB = case.sparse_block
-            r = q // SB
+            rows = sorted({(q + i) // SB for i in range(max(1, p.get("query_len", 1))) if q + i >= 0})
             for g in range(Hkv):
                 union = set()
                 for j in range(G):
                     lay = (g * G + j) % case.num_layouts
-                    s, e = case.row_ptr[lay, r], case.row_ptr[lay, r + 1]
-                    union |= {int(c) for c in case.col_idx[lay, s:e] if 0 <= c <= r}
+                    for r in rows:
+                        s, e = case.row_ptr[lay, r], case.row_ptr[lay, r + 1]
+                        union |= {int(c) for c in case.col_idx[lay, s:e] if 0 <= c <= r}
                 for blk in union:
                     t0, t1 = max(lo, blk * SB), min(hi, blk * SB + SB - 1)
                     if t1 >= t0:
@@ -463,7 +464,7 @@ def workload(idx, window=0):
     """Workloads 1-5 of the input generators, 6: the tiered workload's shape
     with an f16 cold tier, 7: a sliding-window ring f16 cache, 8 and 9: four
     and sixteen queries per sequence over a paged f16 cache of workload 2's
-    shape."""
+    shape, 10: four queries per sequence over the block-sparse workload."""
     import synth
     if idx == 6:
         return synth.tiered_f16_workload(window)
@@ -473,6 +474,8 @@ def workload(idx, window=0):
         return synth.multi_query_workload(4)
     if idx == 9:
         return synth.multi_query_workload(16)
+    if idx == 10:
+        return synth.sparse_multi_query_workload(4)
     return synth.config(idx, window=window)
 
 
@@ -485,7 +488,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", type=int, default=2,
                     help="headline workload index (default 2; 6 = the tiered workload with an f16 cold tier, "
-                         "7 = a sliding-window ring f16 cache, 8 = four queries per sequence, 9 = sixteen)")
+                         "7 = a sliding-window ring f16 cache, 8 = four queries per sequence, 9 = sixteen, "
+                         "10 = four over the block-sparse cache)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run 5 device copies of MIB MiB (for scaling memory counters)")
     args = ap.parse_args()
@@ -558,7 +562,7 @@ def main():
     if args.all:
         extra = []
         for idx, kw in ((1, {}), (3, dict(window=0)), (3, dict(window=4096)), (4, {}), (5, {}),
-                        (6, dict(window=0)), (6, dict(window=4096)), (7, {}), (8, {}), (9, {})):
+                        (6, dict(window=0)), (6, dict(window=4096)), (7, {}), (8, {}), (9, {}), (10, {})):
             log(f"generating workload {idx} {kw} ...")
             c = workload(idx, **kw)
             res, _ = line_for(c, max(20, args.steps // 4), max(5, args.warmup // 4))

@@ -389,10 +389,11 @@ def dattn_decode_block_sparse(q, k_cache, v_cache, block_table, seq_lens, sparse
                               softcap: float = 0.0, max_seq_len: Optional[int] = None, split_tokens: int = 0,
                               out=None, lse=None, want_lse: bool = True, workspace=None, stream=None,
                               phases: int = PHASE_ALL, out_dtype=None, want_out: bool = True):
-    """Decode attention over the paged f16 cache restricted by per-head CSR block masks."""
+    """Decode attention over the paged f16 cache restricted by per-head CSR block masks;
+    q [B, Qn, H, D] gives Qn queries per sequence, each with its own CSR row."""
     torch = _torch()
     dev = q.device
-    _need(q, "q", (torch.float32, torch.float16), 3, dev)
+    _need(q, "q", (torch.float32, torch.float16), q.dim() if q.dim() in (3, 4) else 3, dev)
     _need(k_cache, "k_cache", (torch.float16,), 4, dev)
     _need(v_cache, "v_cache", (torch.float16,), 4, dev)
     _need(block_table, "block_table", (torch.int32,), 2, dev)

@@ -149,8 +149,9 @@ int check_params(const dattn_params* p, int kind) {
   if (p->q_dtype != DATTN_F32 && p->q_dtype != DATTN_F16)
     return fail(DATTN_ERR_INVALID, "q_dtype must be DATTN_F32 or DATTN_F16 (got %d)", p->q_dtype);
   if (p->query_len > 1) {
-    if (kind == DATTN_KIND_BLOCK_SPARSE)
-      return fail(DATTN_ERR_UNSUPPORTED, "query_len > 1 is not built for the block-sparse cache");
+    if (kind == DATTN_KIND_BLOCK_SPARSE && (int64_t)G * p->query_len > 16)
+      return fail(DATTN_ERR_UNSUPPORTED, "query_len (%d) * GQA group (%d) must be <= 16 for the block-sparse cache",
+                  p->query_len, G);
     if ((int64_t)G * p->query_len > kMaxQueryRows)
       return fail(DATTN_ERR_UNSUPPORTED, "query_len (%d) * GQA group (%d) must be <= %d", p->query_len, G,
                   kMaxQueryRows);
@@ -683,8 +684,10 @@ int dattn_decode_block_sparse(const dattn_params* p, const void* q, const uint16
   a.sparse_nblk = pl.sparse_nblk;
   a.sb = dattn::make_fastdiv((uint32_t)sparse_block);
   const bool contig = p->block_size % 16 == 0 && sparse_block % 16 == 0;
-  return launch(dattn::split_kernel(dattn::kSparse, p->head_dim, p->softcap > 0.0f, pl.G, contig), nullptr, p, pl,
-                a, out, lse, (hipStream_t)stream);
+  const bool mq = a.qn > 1;   // several queries per sequence: MFMA columns are (query, head) pairs
+  return launch(dattn::split_kernel(mq ? dattn::kSparseMQ : dattn::kSparse, p->head_dim, p->softcap > 0.0f,
+                                    mq ? 16 : pl.G, contig),
+                nullptr, p, pl, a, out, lse, (hipStream_t)stream);
 }
 
 int dattn_append_tiered_int8(const dattn_params* p, const uint16_t* k_new, const uint16_t* v_new, uint16_t* k_hot,

@@ -828,6 +828,40 @@ struct SparseMap {
   }
 };
 
+// Several queries per sequence: the lane's score column is one (query, head)
+// pair, whose CSR row is its query's; the union list carries one mask bit per
+// column, and the lane also masks keys outside its query's bounds [qlo, qhi].
+struct SparseMapMQ : SparseMap {
+  int qlo, qhi;
+  __device__ __forceinline__ void tile_valid(int s0, const LaneGeo& lg, bool (&valid)[4], bool (&kvalid)[4]) const {
+    if (contig) {
+      int t;
+      uint32_t mk;
+      resolve(s0, t, mk);
+      t = __builtin_amdgcn_readfirstlane(t);
+      mk = (uint32_t)__builtin_amdgcn_readfirstlane((int)mk);
+      const bool head_on = (mk >> lg.kkey) & 1u;
+      const bool live = s0 < slot_end;
+      const uint32_t rel = (uint32_t)(t + 4 * lg.g - lo), span = (uint32_t)(hi - lo);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int k = t + 4 * lg.g + e;
+        kvalid[e] = live && rel + e <= span;
+        valid[e] = head_on && kvalid[e] && k >= qlo && k <= qhi;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        int t;
+        uint32_t mk;
+        resolve(s0 + 4 * lg.g + e, t, mk);
+        valid[e] = ((mk >> lg.kkey) & 1u) && t >= lo && t <= hi && t >= qlo && t <= qhi;
+        kvalid[e] = valid[e];
+      }
+    }
+  }
+};
+
 // ------------------------------------------------- online softmax state
 
 // Where the partial (acc[D], (m, l)) of heads kvh*G + h, h < G, goes.
@@ -1563,8 +1597,8 @@ void balanced_kernel(DecodeArgs a) {
 // LDS (a G-bit head mask per sparse block, then the blocks with a non-zero
 // mask compacted in increasing order), takes the slice of that list its
 // split owns and sweeps its keys.
-template <int D, int G, bool CAP, bool FM>
-__global__ __launch_bounds__(DATTN_MAX_THREADS) __attribute__((amdgpu_waves_per_eu(2))) void sparse_split_kernel(DecodeArgs a) {
+template <int D, int G, bool CAP, bool FM, bool MQ = false>
+__global__ DATTN_BOUNDS(MQ) __attribute__((amdgpu_waves_per_eu(2))) void sparse_split_kernel(DecodeArgs a) {
   extern __shared__ uint32_t lds_sp[];
   const int split = blockIdx.x, b = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -1575,13 +1609,21 @@ __global__ __launch_bounds__(DATTN_MAX_THREADS) __attribute__((amdgpu_waves_per_
   int lo, hi, qp;
   visible_range(a, b, lo, hi, qp);
   QRaw16<D> qraw;
-  load_q_raw16<D, G, false>(a, b, kvh, lane, qraw);
+  load_q_raw16<D, G, false, MQ>(a, b, kvh, lane, qraw);
   for (int i = lane; i < nb; i += 64) mask[i] = 0u;
   __syncthreads();
-  const uint32_t r = fdiv((uint32_t)max(qp, 0), a.sb);
-  if (lo <= hi && (int)r + 1 < a.row_stride) {
-    for (int j = 0; j < G; ++j) {
-      const int layout = (kvh * G + j) % a.num_layouts;
+  // Column j (a head of the group, or with several queries the (query j / grp,
+  // head j % grp) pair) selects the blocks of the CSR row of its query's
+  // position in its head's layout; a query before position 0 selects none.
+  const int ncols = MQ ? a.grp * a.qn : G;
+  if (lo <= hi) {
+    for (int j = 0; j < ncols; ++j) {
+      const int qj = MQ ? qp + j / a.grp : max(qp, 0);
+      if (qj < 0) continue;
+      const uint32_t r = fdiv((uint32_t)qj, a.sb);
+      if ((int)r + 1 >= a.row_stride) continue;
+      const int head = MQ ? kvh * a.grp + j % a.grp : kvh * G + j;
+      const int layout = head % a.num_layouts;
       const int32_t* rp = a.row_ptr + (size_t)layout * a.row_stride;
       const int start = max(rp[r], 0);
       const int end = min(rp[r + 1], a.col_stride);
@@ -1603,24 +1645,35 @@ __global__ __launch_bounds__(DATTN_MAX_THREADS) __attribute__((amdgpu_waves_per_
     count += __builtin_popcountll(bal);
   }
   __syncthreads();
-  const PartialDst dst = split_dst(a, b, kvh, G, split, D);
+  const PartialDst dst = split_dst(a, b, kvh, MQ ? a.grp : G, split, D);
   const int e0 = (int)((int64_t)split * count / a.num_splits);
   const int e1 = (int)((int64_t)(split + 1) * count / a.num_splits);
   if (e0 >= e1 || lo > hi) {
-    write_empty<G>(dst, lane);
+    if constexpr (MQ)
+      write_empty_mq(dst, lane, a.grp, a.qn, a.num_heads, 0);
+    else
+      write_empty<G>(dst, lane);
     return;
   }
   LaneGeo lg;
   lg.init(lane);
-  SparseMap map{list, a.table + (size_t)b * a.max_blocks, e1 * (int)a.sb.d, lo, hi, a.bs, a.sb,
-                FM, (1u << G) - 1u};
+  const SparseMap smap{list, a.table + (size_t)b * a.max_blocks, e1 * (int)a.sb.d, lo, hi, a.bs, a.sb,
+                       FM, (1u << G) - 1u};
   QF16<D> qf;
   StoreF16<D> st{(const _Float16*)a.k, (const _Float16*)a.v, a.num_kv_heads, kvh};
   Online<D, G, CAP> on;
   on.init();
-  run_tiles<D, G, CAP, kPipe, FM>(a, st, map, qf, [&](QF16<D>& q) { convert_q<D, G>(a, lane, qraw, q); }, lg, on,
-                              e0 * (int)a.sb.d, map.slot_end, lane);
-  on.finish(dst, lane);
+  auto prep = [&](QF16<D>& q) { convert_q<D, G, MQ>(a, lane, qraw, q); };
+  if constexpr (MQ) {
+    // the map applies each lane's query bounds to the resolved key positions
+    SparseMapMQ map{smap, 0, 0};
+    query_bounds(a, b, lane, 0, map.qlo, map.qhi);
+    run_tiles<D, G, CAP, kPipe, FM>(a, st, map, qf, prep, lg, on, e0 * (int)a.sb.d, map.slot_end, lane);
+    on.finish_mq(dst, lane, a.grp, a.qn, a.num_heads, 0);
+  } else {
+    run_tiles<D, G, CAP, kPipe, FM>(a, st, smap, qf, prep, lg, on, e0 * (int)a.sb.d, smap.slot_end, lane);
+    on.finish(dst, lane);
+  }
 }
 
 // ------------------------------------------------------------------ combine

@@ -24,6 +24,7 @@ enum SplitKind : int {
   kTieredF16MQ,    // static splits, tiered f16 / window ring, several queries per sequence
   kBalTieredMQ,    // balanced schedule, the same
   kBalTieredF16MQ,
+  kSparseMQ,       // static splits over the CSR union, several queries per sequence
 };
 
 // Split kernel for (kind, GQA group G in {1, 2, 4, 8}, contiguous 16-row

@@ -26,6 +26,7 @@ void* instance(int kind) {
       case kTieredF16MQ: return (void*)&tiered_split_kernel<D, 16, CAP, FM, true, true>;
       case kBalTieredMQ: return (void*)&balanced_kernel<D, 16, CAP, 6, FM>;
       case kBalTieredF16MQ: return (void*)&balanced_kernel<D, 16, CAP, 7, FM>;
+      case kSparseMQ: return (void*)&sparse_split_kernel<D, 16, CAP, FM, true>;
       default: return nullptr;
     }
   } else {

@@ -433,6 +433,15 @@ def multi_query_workload(query_len: int = 4) -> Case:
                       name=f"paged_f16_mq{query_len}_B32_H32x8_D128_L512-4096")
 
 
+def sparse_multi_query_workload(query_len: int = 4) -> Case:
+    """Multi-query decode over workload 5's block-sparse cache: B=8, 32/8 heads,
+    D=128, L=16384, SB=bs=64, 4 layouts; the last query_len tokens are the queries,
+    each with its own CSR row."""
+    return sparse_case(5, 8, 32, 8, 128, 64, 64, 4, lens=[16384] * 8, query_len=query_len,
+                       scale=float(np.float32(1.0 / math.sqrt(128))),
+                       name=f"sparse_f16_mq{query_len}_B8_H32x8_D128_L16384")
+
+
 def tiered_f16_workload(window: int = 0) -> Case:
     """The tiered workload's shape with an f16 cold tier: B=16, 32/8 heads, D=128,
     L=8192 = 7680 f16 cold (bs=16, permuted pool) + 512 f16 hot (ring of 512), softcap 50."""

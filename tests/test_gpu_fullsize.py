@@ -12,10 +12,12 @@ from gpu_util import DeviceCase, compare, log, oracle_run
 pytestmark = pytest.mark.gpu
 
 WORKLOADS = [(2, {}), (3, {"window": 0}), (3, {"window": 4096}), (4, {}), (5, {})]
-# the tiered workload's shape with an f16 cold tier, the window ring, four and sixteen queries per sequence
+# the tiered workload's shape with an f16 cold tier, the window ring, four and sixteen queries per sequence,
+# four queries over the block-sparse cache
 EXTRA = {"tiered_f16": lambda: synth.tiered_f16_workload(0), "ring": synth.ring_workload,
          "multi_query": lambda: synth.multi_query_workload(4),
-         "multi_query_16": lambda: synth.multi_query_workload(16)}
+         "multi_query_16": lambda: synth.multi_query_workload(16),
+         "sparse_multi_query": lambda: synth.sparse_multi_query_workload(4)}
 
 
 @pytest.fixture(scope="module", autouse=True)

@@ -205,3 +205,42 @@ def test_mq_row_blocks_random_sweep(seed):
                     window=int(rng.choice([0, 0, 17, 200])), **kw)
     st = int(np.random.default_rng(seed).choice([0, 0, 16, 256]))
     _check(case, st, what=f"seed{seed} {kind} B{B} Qn{qn} G{G} rows {qn * G} Hkv{Hkv} D{D}")
+
+
+# The block-sparse cache: each query takes the CSR row of its own position; the
+# union list carries one mask bit per (query, head) column.
+@pytest.mark.parametrize("G,qn", [(4, 4), (8, 2), (1, 16), (2, 3)])
+@pytest.mark.parametrize("split_tokens", [0, 128])
+def test_mq_block_sparse(G, qn, split_tokens):
+    c = synth.sparse_case(540 + qn, 2, 4 * G, 4, 128, 16, 64, 4, [2000, 700], query_len=qn, softcap=30.0,
+                          csr_kind="random" if qn % 2 else "local_strided")
+    _check(c, split_tokens, what=f"sparse G{G} Qn{qn}")
+
+
+def test_mq_block_sparse_gather_and_short_sequences():
+    # block size 5 (tiles gathered row by row), sparse blocks of 10, L < Qn: the
+    # first queries sit before position 0 and select no block
+    c = synth.sparse_case(545, 4, 16, 4, 64, 5, 10, 3, [3, 0, 250, 41], query_len=4, causal=0, window=0)
+    _check(c, what="sparse bs5 SB10 D64 non-causal, L < Qn")
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_mq_block_sparse_random_sweep(seed):
+    rng = np.random.default_rng(98_000 + seed)
+    G = int(rng.choice([1, 2, 4, 8]))
+    qn = int(rng.choice([q for q in (2, 3, 4, 8, 16) if q * G <= 16]))
+    Hkv = int(rng.choice([1, 2, 4, 8]))
+    D = int(rng.choice([64, 128]))
+    bs = int(rng.choice([5, 16, 32]))
+    sb = bs * int(rng.choice([1, 2, 4]))
+    B = int(rng.integers(1, 4))
+    lens = rng.integers(0, 1200, size=B)
+    qp = None
+    if rng.random() < 0.4:
+        qp = np.array([int(rng.integers(0, max(1, L))) for L in lens], np.int32)
+    c = synth.sparse_case(seed, B, Hkv * G, Hkv, D, bs, sb, int(rng.choice([1, 3, 4])), lens, q_pos=qp, query_len=qn,
+                          causal=int(rng.random() < 0.85), window=int(rng.choice([0, 0, 17, 300])),
+                          softcap=float(rng.choice([0.0, 5.0, 50.0])),
+                          csr_kind=str(rng.choice(["local_strided", "random"])))
+    st = int(np.random.default_rng(seed).choice([0, 0, 64, 256]))
+    _check(c, st, what=f"sparse seed{seed} B{B} Qn{qn} G{G} Hkv{Hkv} D{D} bs{bs} SB{sb}")
