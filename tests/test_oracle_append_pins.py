@@ -30,7 +30,8 @@ def test_f32_to_f16_ties_overflow_and_random_match_numpy():
     xs = np.concatenate([mids, edges, rand])
     xs = np.concatenate([xs, -xs])
     got = np.array([oracle.f32_to_f16(float(x)) for x in xs], np.uint16)
-    want = xs.astype(np.float16).view(np.uint16)
+    with np.errstate(over="ignore"):   # values past the f16 range round to inf on purpose
+        want = xs.astype(np.float16).view(np.uint16)
     assert np.array_equal(got, want)
 
 
