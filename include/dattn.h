@@ -97,9 +97,8 @@ typedef struct dattn_params {
                                  result rounded to nearest even (attention.js sizes its output
                                  by the kernel variant's outputDtype, f16 or f32) */
   int32_t query_len;          /* queries per sequence, 0 or 1 => one; > 1: multi-query decode
-                                 (every cache; query_len * GQA group <= 128, <= 16 for the
-                                 block-sparse cache, else DATTN_ERR_UNSUPPORTED); see
-                                 dattn_decode_paged */
+                                 (every cache; query_len * GQA group <= 128, else
+                                 DATTN_ERR_UNSUPPORTED); see dattn_decode_paged */
   int32_t q_dtype;            /* storage type of q: DATTN_F32 (0) or DATTN_F16 (converted to f32
                                  exactly); with DATTN_F16 and out_dtype DATTN_F16 this is the f16
                                  Q/K/V, f16 output variant (doppler attention_f16.wgsl) */
@@ -154,8 +153,9 @@ int dattn_workspace_size(const dattn_params* p, int32_t kind, int32_t sparse_blo
  * head (at most 128) are taken 16 at a time by the waves of one workgroup,
  * which sweep the same keys side by side, so each K/V row is fetched from HBM
  * about once per (sequence, kv head) for all of them.  The tiered and
- * window-ring entry points take query_len the same way, the block-sparse one
- * with at most 16 rows per kv head.
+ * window-ring entry points take query_len the same way, and so does the
+ * block-sparse one, whose waves each build the block union of their own 16
+ * rows.
  */
 int dattn_decode_paged(const dattn_params* p, const void* q, const void* k_cache, const void* v_cache,
                        int32_t kv_dtype, const int32_t* block_table, const int32_t* seq_lens,
@@ -236,9 +236,9 @@ int dattn_decode_ring_f16(const dattn_params* p, const void* q, const uint16_t* 
  *   col_idx       [num_layouts, col_stride] i32
  *   other arrays  as for dattn_decode_paged with kv_dtype = DATTN_F16
  * Needs q / sparse_block < row_stride - 1 (rows beyond select nothing).
- * Multi-query decode (p->query_len = Qn > 1, Qn * GQA group <= 16, else
- * DATTN_ERR_UNSUPPORTED): query i at position q_pos[b] + i takes the CSR row
- * of its own position; a query before position 0 selects no block.
+ * Multi-query decode (p->query_len = Qn > 1): query i at position q_pos[b] + i
+ * takes the CSR row of its own position; a query before position 0 selects
+ * no block.
  */
 int dattn_decode_block_sparse(const dattn_params* p, const void* q, const uint16_t* k_cache,
                               const uint16_t* v_cache, const int32_t* block_table, const int32_t* seq_lens,

@@ -149,9 +149,6 @@ int check_params(const dattn_params* p, int kind) {
   if (p->q_dtype != DATTN_F32 && p->q_dtype != DATTN_F16)
     return fail(DATTN_ERR_INVALID, "q_dtype must be DATTN_F32 or DATTN_F16 (got %d)", p->q_dtype);
   if (p->query_len > 1) {
-    if (kind == DATTN_KIND_BLOCK_SPARSE && (int64_t)G * p->query_len > 16)
-      return fail(DATTN_ERR_UNSUPPORTED, "query_len (%d) * GQA group (%d) must be <= 16 for the block-sparse cache",
-                  p->query_len, G);
     if ((int64_t)G * p->query_len > kMaxQueryRows)
       return fail(DATTN_ERR_UNSUPPORTED, "query_len (%d) * GQA group (%d) must be <= %d", p->query_len, G,
                   kMaxQueryRows);
@@ -222,7 +219,7 @@ int make_plan(const dattn_params* p, int kind, int32_t sparse_block, Plan& pl) {
       const int64_t per = p->split_tokens / sparse_block > 0 ? p->split_tokens / sparse_block : 1;
       pl.num_splits = (int)((pl.sparse_nblk + per - 1) / per);
     } else {
-      const int64_t pairs = (int64_t)p->num_seqs * p->num_kv_heads;
+      const int64_t pairs = (int64_t)p->num_seqs * pl.vheads;   // waves per split
       const int64_t target = (int64_t)device_cus() * 8;
       int64_t S = pairs > 0 ? (target + pairs - 1) / pairs : 1;
       if (S > pl.sparse_nblk) S = pl.sparse_nblk;

@@ -1602,27 +1602,30 @@ __global__ DATTN_BOUNDS(MQ) __attribute__((amdgpu_waves_per_eu(2))) void sparse_
   extern __shared__ uint32_t lds_sp[];
   const int split = blockIdx.x, b = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int kvh = blockIdx.z * (blockDim.x >> 6) + wave;
+  int kvh, col0;   // several queries: each wave builds the union of its own 16 columns
+  wave_head<MQ>(a, kvh, col0);
   const int nb = a.sparse_nblk;
   uint32_t* mask = lds_sp + (size_t)wave * 2 * nb;
   uint32_t* list = mask + nb;
   int lo, hi, qp;
   visible_range(a, b, lo, hi, qp);
   QRaw16<D> qraw;
-  load_q_raw16<D, G, false, MQ>(a, b, kvh, lane, qraw);
+  load_q_raw16<D, G, false, MQ>(a, b, kvh, lane, qraw, col0);
   for (int i = lane; i < nb; i += 64) mask[i] = 0u;
   __syncthreads();
-  // Column j (a head of the group, or with several queries the (query j / grp,
-  // head j % grp) pair) selects the blocks of the CSR row of its query's
-  // position in its head's layout; a query before position 0 selects none.
-  const int ncols = MQ ? a.grp * a.qn : G;
+  // Column j (a head of the group, or with several queries the (query c / grp,
+  // head c % grp) pair of column c = col0 + j) selects the blocks of the CSR
+  // row of its query's position in its head's layout; a query before
+  // position 0 selects none.
+  const int ncols = MQ ? min(16, a.grp * a.qn - col0) : G;
   if (lo <= hi) {
     for (int j = 0; j < ncols; ++j) {
-      const int qj = MQ ? qp + j / a.grp : max(qp, 0);
+      const int c = col0 + j;
+      const int qj = MQ ? qp + c / a.grp : max(qp, 0);
       if (qj < 0) continue;
       const uint32_t r = fdiv((uint32_t)qj, a.sb);
       if ((int)r + 1 >= a.row_stride) continue;
-      const int head = MQ ? kvh * a.grp + j % a.grp : kvh * G + j;
+      const int head = MQ ? kvh * a.grp + c % a.grp : kvh * G + j;
       const int layout = head % a.num_layouts;
       const int32_t* rp = a.row_ptr + (size_t)layout * a.row_stride;
       const int start = max(rp[r], 0);
@@ -1650,7 +1653,7 @@ __global__ DATTN_BOUNDS(MQ) __attribute__((amdgpu_waves_per_eu(2))) void sparse_
   const int e1 = (int)((int64_t)(split + 1) * count / a.num_splits);
   if (e0 >= e1 || lo > hi) {
     if constexpr (MQ)
-      write_empty_mq(dst, lane, a.grp, a.qn, a.num_heads, 0);
+      write_empty_mq(dst, lane, a.grp, a.qn, a.num_heads, col0);
     else
       write_empty<G>(dst, lane);
     return;
@@ -1663,13 +1666,13 @@ __global__ DATTN_BOUNDS(MQ) __attribute__((amdgpu_waves_per_eu(2))) void sparse_
   StoreF16<D> st{(const _Float16*)a.k, (const _Float16*)a.v, a.num_kv_heads, kvh};
   Online<D, G, CAP> on;
   on.init();
-  auto prep = [&](QF16<D>& q) { convert_q<D, G, MQ>(a, lane, qraw, q); };
+  auto prep = [&](QF16<D>& q) { convert_q<D, G, MQ>(a, lane, qraw, q, col0); };
   if constexpr (MQ) {
     // the map applies each lane's query bounds to the resolved key positions
     SparseMapMQ map{smap, 0, 0};
-    query_bounds(a, b, lane, 0, map.qlo, map.qhi);
+    query_bounds(a, b, lane, col0, map.qlo, map.qhi);
     run_tiles<D, G, CAP, kPipe, FM>(a, st, map, qf, prep, lg, on, e0 * (int)a.sb.d, map.slot_end, lane);
-    on.finish_mq(dst, lane, a.grp, a.qn, a.num_heads, 0);
+    on.finish_mq(dst, lane, a.grp, a.qn, a.num_heads, col0);
   } else {
     run_tiles<D, G, CAP, kPipe, FM>(a, st, smap, qf, prep, lg, on, e0 * (int)a.sb.d, smap.slot_end, lane);
     on.finish(dst, lane);

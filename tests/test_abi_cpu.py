@@ -166,7 +166,8 @@ def test_workspace_size_values(lib):
         slots = 4096 // (hkv * -(-qn * n_heads // hkv // 16)) + 2
         rows = slots * n_heads * qn
         assert rc == 0 and n0 == up(rows * 128 * 4) + up(rows * 8) + up(5 * 4), (qn, hkv)
-    assert ws_size(lib, good_params(query_len=32), kind=dk.KIND_BLOCK_SPARSE, sb=32)[0] == dk.ERR_UNSUPPORTED
+    assert ws_size(lib, good_params(query_len=32), kind=dk.KIND_BLOCK_SPARSE, sb=32)[0] == 0
+    assert ws_size(lib, good_params(query_len=33), kind=dk.KIND_BLOCK_SPARSE, sb=32)[0] == dk.ERR_UNSUPPORTED
     # sparse: sparse_block must be a positive multiple of block_size
     assert ws_size(lib, good_params(), kind=dk.KIND_BLOCK_SPARSE, sb=24)[0] == dk.ERR_INVALID
     assert ws_size(lib, good_params(), kind=dk.KIND_BLOCK_SPARSE, sb=32)[0] == 0

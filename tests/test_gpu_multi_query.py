@@ -244,3 +244,11 @@ def test_mq_block_sparse_random_sweep(seed):
                           csr_kind=str(rng.choice(["local_strided", "random"])))
     st = int(np.random.default_rng(seed).choice([0, 0, 64, 256]))
     _check(c, st, what=f"sparse seed{seed} B{B} Qn{qn} G{G} Hkv{Hkv} D{D} bs{bs} SB{sb}")
+
+
+@pytest.mark.parametrize("G,qn,split_tokens", [(4, 8, 0), (4, 16, 128), (8, 16, 0), (1, 100, 0), (2, 40, 64)])
+def test_mq_block_sparse_row_blocks(G, qn, split_tokens):
+    # more than 16 rows per kv head: each row-block wave builds the union of its own columns
+    c = synth.sparse_case(550 + qn, 2, 4 * G, 4, 128, 16, 64, 4, [2000, qn + 50], query_len=qn, softcap=30.0,
+                          csr_kind="random" if G % 2 else "local_strided")
+    _check(c, split_tokens, what=f"sparse rows {G * qn} G{G} Qn{qn}")
