@@ -58,6 +58,13 @@ class Step:
         }
         p = synth.paged_case(602, 4, 32, 8, 128, 16, lens=[700, 90, 1500, 3], query_len=2)
         self.p = {k: _dev(getattr(p, k)) for k in ("q", "k_cache", "v_cache", "block_table", "seq_lens")}
+        # sixteen queries per sequence: row-block waves sharing tiles through LDS, and the
+        # eight-rows-per-workgroup combine (8 x 16 x 32 rows)
+        w = synth.paged_case(603, 8, 32, 8, 128, 16, lens=[900, 40, 1300, 17, 600, 2000, 256, 5], query_len=16)
+        self.w = {k: _dev(getattr(w, k)) for k in ("q", "k_cache", "v_cache", "block_table", "seq_lens")}
+        self.out_w = torch.empty((8, 16, 32, 128), dtype=torch.float32, device="cuda")
+        self.lse_w = torch.empty((8, 16, 32), dtype=torch.float32, device="cuda")
+        self.ws3 = torch.empty((128 << 20,), dtype=torch.uint8, device="cuda")
         self.k_new = torch.zeros((B, Hkv, D), dtype=torch.float16, device="cuda")
         self.v_new = torch.zeros_like(self.k_new)
         self.out_t = torch.empty((B, 32, D), dtype=torch.float32, device="cuda")
@@ -76,13 +83,16 @@ class Step:
                                     max_seq_len=2048, out=self.out_t, lse=self.lse_t, workspace=self.ws)
         dk.dattn_decode_paged(p["q"], p["k_cache"], p["v_cache"], p["block_table"], p["seq_lens"], max_seq_len=1500,
                               out=self.out_p, lse=self.lse_p, out_dtype=self.out_p.dtype, workspace=self.ws2)
+        w = self.w
+        dk.dattn_decode_paged(w["q"], w["k_cache"], w["v_cache"], w["block_table"], w["seq_lens"], max_seq_len=2000,
+                              out=self.out_w, lse=self.lse_w, workspace=self.ws3)
 
     def snapshot(self):
         import torch
         torch.cuda.synchronize()
         keys = ("k_hot", "v_hot", "k_cold", "v_cold", "k_scale", "v_scale", "seq_lens", "cold_lens")
         return [self.t[k].clone() for k in keys] + [x.clone() for x in (self.out_t, self.lse_t, self.out_p,
-                                                                         self.lse_p)]
+                                                                         self.lse_p, self.out_w, self.lse_w)]
 
     def load(self, snap):
         keys = ("k_hot", "v_hot", "k_cold", "v_cold", "k_scale", "v_scale", "seq_lens", "cold_lens")
@@ -114,6 +124,7 @@ def test_decode_step_graph_replays_equal_eager_calls():
         st.v_new.copy_(torch.from_numpy(rng.standard_normal((4, 8, 128)).astype(np.float16)))
         st.t["q"].mul_(-1.0)
         st.p["q"].add_(0.25)
+        st.w["q"].mul_(0.75)
         start = st.snapshot()
         g.replay()
         got = st.snapshot()
