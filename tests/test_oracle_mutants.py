@@ -63,6 +63,10 @@ MUTANTS = {
     "mq_default_start_at_last_token": ("(int64_t)seq_lens[b] - queries(p)) + i;", "(int64_t)seq_lens[b] - 1) + i;"),
     "mq_query_rows_transposed": ("int32_t b = bq / Qn, qi = bq % Qn;",
                                  "int32_t b = bq % p->num_seqs, qi = bq / p->num_seqs;"),
+    "sparse_negative_query_takes_row_zero": ("if (q < 0) return ORC_OK;", "if (q < 0) q = 0;"),
+    "sparse_mq_rows_of_first_query": ("local = sel ? sparse_select(csr, h, qp, sel, nblk) : ORC_ENOMEM;",
+                                      "local = sel ? sparse_select(csr, h, query_pos(p, q_pos, seq_lens, b, 0), sel, "
+                                      "nblk) : ORC_ENOMEM;"),
 }
 PIN_FILES = ["test_oracle_pins.py", "test_oracle_append_pins.py", "test_oracle_tiered_f16_pins.py",
              "test_oracle_ring_pins.py", "test_oracle_multi_query_pins.py"]
