@@ -284,3 +284,26 @@ def test_sparse_nonlive_rows_hold_nan():
     c = synth.sparse_case(123, 2, 16, 4, 128, 16, 64, 3, [1000, 333])
     _poison_paged(c.k_cache, c.v_cache, c.block_table, c.seq_lens, 16)
     _check(c, what="sparse NaN/Inf outside the live rows")
+
+
+@pytest.mark.parametrize("qn", [4, 16])
+def test_multi_query_nonlive_rows_hold_nan(qn):
+    """The same with several queries per sequence; with 16 queries (64 rows per
+    kv head) the tiles go through the shared LDS buffers of the row-block waves."""
+    c = synth.paged_case(124 + qn, 3, 16, 4, 128, 16, lens=[77, 300, 1], kv_dtype=synth.F16, query_len=qn,
+                         q_pos=[60, 280, 0])
+    _poison_paged(c.k_cache, c.v_cache, c.block_table, c.seq_lens, 16)
+    _check(c, what=f"paged f16 Qn{qn} NaN/Inf outside the live rows")
+    t = synth.tiered_case(126 + qn, 3, 16, 4, 128, 16, [700, 300, 40], [450, 260, 0], 256, query_len=qn)
+    live = np.zeros(t.k_scale.shape[:2], bool)
+    for b, C in enumerate(t.cold_lens):
+        k = np.arange(int(C))
+        live[t.cold_block_table[b, k // 16], k % 16] = True
+    t.k_scale[~live] = np.float16(np.nan)
+    t.v_scale[~live] = np.float16(np.inf)
+    ring_live = np.zeros(t.k_hot.shape[:2], bool)
+    for b, (L, C) in enumerate(zip(t.seq_lens, t.cold_lens)):
+        ring_live[b, np.arange(int(C), int(L)) % t.hot_window] = True
+    t.k_hot[~ring_live] = np.float16(np.nan)
+    t.v_hot[~ring_live] = np.float16(np.inf)
+    _check(t, what=f"tiered Qn{qn} NaN/Inf outside the live rows and ring slots")
