@@ -33,7 +33,7 @@ import numpy as np  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
 MALL_BYTES = 1.0e9     # rotate cache copies until each step touches new memory
-KERNEL_SOURCE = os.path.join(ROOT, "int8_quantized_kv_amd", "csrc", "decode_kernels.h")
+KERNEL_SOURCES = [os.path.join(ROOT, "int8_quantized_kv_amd", "csrc", f) for f in ("decode_kernels.h", "dattn.hip")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_balanced_paged_f16_B32_H32x8_D128.txt")
 
 
@@ -314,8 +314,13 @@ def measure_append(B=16, Hkv=8, D=128, hot_window=512, bs=16, calls=200, warmup=
 
 
 def kernel_source_sha():
+    """sha256 over the kernel source and the host planner (worker counts and
+    splits change the bytes a launch moves), concatenated in that order."""
     import hashlib
-    return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        h.update(open(path, "rb").read())
+    return h.hexdigest()
 
 
 def measured_traffic(workload=None):

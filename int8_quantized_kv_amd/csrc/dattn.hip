@@ -43,6 +43,7 @@ struct Plan {
   int rbk = 1;               // multi-query: waves (16-column row blocks) per kv head, 1, 2, 4 or 8
   int vheads = 0;            // num_kv_heads * rbk: waves per (sequence, split)
   bool no_table = false;     // the cache has no block table to stage (window ring)
+  int waves_per_cu = 8;      // balanced schedule: resident waves per CU to use
   size_t lds = 0;
   size_t acc_bytes = 0, ml_bytes = 0;  // static-split layout
   bool balanced_ok = false;            // the balanced schedule may be used (decided at launch)
@@ -68,6 +69,20 @@ constexpr size_t kMaxBalancedLds = 16384;
 // 1024 rows of about 10 partials the one-row-per-workgroup merge is faster.
 constexpr int64_t kRowsMinRows = 2048;
 constexpr int64_t kRowsWorkersPerSeq = 8;
+#ifndef DATTN_F16_WAVES_PER_CU
+#define DATTN_F16_WAVES_PER_CU 4
+#endif
+#ifndef DATTN_I8_WAVES_PER_CU
+#define DATTN_I8_WAVES_PER_CU 8
+#endif
+// Waves per CU in the balanced schedule's round of workers.  f16 and f32
+// tiles (8 KB or more per wave in flight): one wave per SIMD streams faster
+// than two (paged f16 split 52.1 -> 50.5 us, long paged 328 -> 318 us, window
+// ring 93.3 -> 90 us, four queries per sequence 61 -> 54.6 us) and halves the
+// partials.  int8 tiles (4 KB) need both waves (halving them: 60 -> 68 us),
+// and so do row-block waves sharing tiles (sixteen queries: 101 -> 118 us).
+constexpr int kF16WavesPerCU = DATTN_F16_WAVES_PER_CU;
+constexpr int kI8WavesPerCU = DATTN_I8_WAVES_PER_CU;
 constexpr int64_t kMinWorkerUnits = 16;   // units of the host-side work bound per worker (about 8 tiles)
 
 // Per-device cache of the CU count and of kernel occupancies.
@@ -187,6 +202,7 @@ int make_plan(const dattn_params* p, int kind, int32_t sparse_block, Plan& pl) {
   if (rc) return rc;
   pl.G = p->num_heads / p->num_kv_heads;
   pl.waves = waves_per_group(p->num_kv_heads);
+  pl.waves_per_cu = kind == DATTN_KIND_TIERED_INT8 ? kI8WavesPerCU : kF16WavesPerCU;
   if (p->query_len > 1) {
     // blocks of 16 (query, head) columns, rounded up to 1, 2, 4 or 8 (the
     // shared-tile sweep splits a tile into equal shares); the row blocks of a
@@ -196,6 +212,7 @@ int make_plan(const dattn_params* p, int kind, int32_t sparse_block, Plan& pl) {
     if (pl.rbk > 1) pl.waves = pl.rbk;
   }
   pl.vheads = p->num_kv_heads * pl.rbk;
+  if (pl.rbk > 1) pl.waves_per_cu = 8;   // row-block waves sharing tiles keep two per SIMD
   const int64_t L = p->max_seq_len;
   if (kind == DATTN_KIND_PAGED || is_tiered(kind)) {
     pl.split_tokens = choose_split(p, L);
@@ -281,12 +298,14 @@ Balanced plan_balanced(const dattn_params* p, const Plan& pl, const void* fn, si
   Balanced bl;
   if (!pl.balanced_ok) return bl;
   int cus = 0;
-  const int per_cu = resident_groups(fn, 64 * pl.waves, kMaxBalancedLds + tile_lds, cus);
+  int per_cu = resident_groups(fn, 64 * pl.waves, kMaxBalancedLds + tile_lds, cus);
   if (per_cu <= 0 || cus <= 0) {
     (void)hipGetLastError();
     return bl;
   }
   const int groups = pl.vheads / pl.waves;
+  const int want = pl.waves_per_cu / pl.waves;   // workgroups per CU the cache's tiles stream best with
+  if (want >= 1 && per_cu > want) per_cu = want;
   bl.workers = cus * per_cu / groups > 0 ? cus * per_cu / groups : 1;
   if (bl.workers > max_workers_per_group(pl.vheads)) bl.workers = max_workers_per_group(pl.vheads);
   // A worker's piece of one sequence has at most C tiles (every tile costs at
