@@ -229,15 +229,17 @@ int make_plan(const dattn_params* p, int kind, int32_t sparse_block, Plan& pl) {
     if (nb > 8192) return fail(DATTN_ERR_UNSUPPORTED, "more than 8192 sparse blocks per sequence is not supported");
     pl.sparse_nblk = (int)(nb > 0 ? nb : 1);
     // Each split takes an equal share of the union list the kernel builds
-    // (its length is only known on the device).  By default the splits fill
-    // one round of resident waves (8 per CU); split_tokens > 0 asks for
-    // split_tokens / sparse_block union blocks per split at most.
+    // (its length is only known on the device).  By default the splits give
+    // kF16WavesPerCU waves per CU, one per SIMD, as the balanced schedule
+    // does for f16 tiles (against two per SIMD: workload 5 split 57 -> 50 us);
+    // split_tokens > 0 asks for split_tokens / sparse_block union blocks per
+    // split at most.
     if (p->split_tokens > 0) {
       const int64_t per = p->split_tokens / sparse_block > 0 ? p->split_tokens / sparse_block : 1;
       pl.num_splits = (int)((pl.sparse_nblk + per - 1) / per);
     } else {
       const int64_t pairs = (int64_t)p->num_seqs * pl.vheads;   // waves per split
-      const int64_t target = (int64_t)device_cus() * 8;
+      const int64_t target = (int64_t)device_cus() * kF16WavesPerCU;
       int64_t S = pairs > 0 ? (target + pairs - 1) / pairs : 1;
       if (S > pl.sparse_nblk) S = pl.sparse_nblk;
       pl.num_splits = (int)(S > 0 ? S : 1);
