@@ -481,7 +481,7 @@ def workload(idx, window=0):
         return synth.multi_query_workload(16)
     if idx == 10:
         return synth.sparse_multi_query_workload(4)
-    return synth.config(idx, window=window)
+    return synth.workload(idx, window=window)
 
 
 def main():

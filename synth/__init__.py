@@ -384,7 +384,7 @@ def sparse_case(seed, B, H, Hkv, D, bs, sparse_block, num_layouts, lens, rows=No
 
 # ------------------------------------------------------------ the workloads
 
-def config(i: int, window: int = 0) -> Case:
+def workload(i: int, window: int = 0) -> Case:
     """The five decode workloads, seeded with their index.
 
     1  tiny: B=1, H=4/Hkv=2, D=64, L=256, f32 KV, bs=16, identity table, causal at 255

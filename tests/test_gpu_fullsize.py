@@ -48,7 +48,7 @@ def _sampled(case, seed):
 
 @pytest.mark.parametrize("idx,kw", WORKLOADS, ids=["paged", "tiered_w0", "tiered_w4096", "long", "sparse"])
 def test_full_size_sampled(idx, kw):
-    _sampled(synth.config(idx, **kw), idx)
+    _sampled(synth.workload(idx, **kw), idx)
 
 
 @pytest.mark.parametrize("name", sorted(EXTRA))

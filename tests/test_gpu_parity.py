@@ -33,28 +33,28 @@ def _check(case, split_tokens=0, what=""):
 
 # ------------------------------------------------------------ the workloads
 
-def test_config1_tiny_f32():
-    _check(synth.config(1), what="tiny f32 B1 H4/2 D64 L256")
+def test_tiny_f32():
+    _check(synth.workload(1), what="tiny f32 B1 H4/2 D64 L256")
 
 
-def test_paged_f16_like_config2_small():
+def test_paged_f16_small():
     c = synth.paged_case(102, 4, 32, 8, 128, 16, len_range=(512, 1200), kv_dtype=synth.F16,
                          scale=float(np.float32(1 / math.sqrt(128))))
     _check(c, what="paged f16 B4 L512-1200")
 
 
 @pytest.mark.parametrize("window", [0, 300])
-def test_tiered_like_config3_small(window):
+def test_tiered_int8_small(window):
     c = synth.tiered_case(103, 2, 32, 8, 128, 16, [700, 613], [450, 420], 256, softcap=50.0, window=window)
     _check(c, what=f"tiered int8 B2 L700 W{window} cap50 ring-wrap")
 
 
-def test_long_paged_like_config4_small():
+def test_long_paged_small():
     c = synth.paged_case(104, 1, 64, 8, 128, 64, lens=[5000], kv_dtype=synth.F16)
     _check(c, what="paged f16 G8 L5000 bs64")
 
 
-def test_sparse_like_config5_small():
+def test_sparse_small():
     c = synth.sparse_case(105, 2, 32, 8, 128, 64, 64, 4, [2048, 1999])
     _check(c, what="sparse local+strided L2048 SB64")
 
