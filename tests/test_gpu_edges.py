@@ -150,3 +150,28 @@ def test_extreme_int8_scales():
     log(f"  max abs {err:.3e}, max |ref| {np.max(np.abs(ro)):.3e}, lse {np.max(np.abs(lg - rl)):.3e}")
     assert err <= 1e-3 * np.max(np.abs(ro))
     assert np.max(np.abs(lg - rl)) <= 1e-3
+
+
+def test_workspace_reused_across_calls_of_other_shapes():
+    # One workspace, first filled with 0xFF bytes, serves calls on other caches and
+    # shapes in turn (balanced schedule and static splits).  Each result must equal,
+    # bit for bit, the same call with a fresh workspace of its own: no call may read
+    # from the workspace anything that it did not write itself.
+    import torch
+    cases = [
+        synth.paged_case(102, 4, 32, 8, 128, 16, len_range=(512, 1200), kv_dtype=synth.F16),
+        synth.tiered_case(103, 2, 32, 8, 128, 16, [700, 613], [450, 420], 256, softcap=50.0),
+        synth.sparse_case(105, 2, 32, 8, 128, 64, 64, 4, [2048, 1999]),
+        synth.ring_case(401, 3, 32, 8, 128, 256, [1000, 100, 257], softcap=30.0),
+        synth.paged_case(106, 3, 32, 8, 128, 16, len_range=(100, 900), kv_dtype=synth.F16, query_len=4),
+        synth.paged_case(107, 5, 16, 2, 64, 16, len_range=(1, 300), kv_dtype=synth.F16),
+        synth.paged_case(102, 4, 32, 8, 128, 16, len_range=(512, 1200), kv_dtype=synth.F16),
+    ]
+    ws = torch.full((64 << 20,), 255, dtype=torch.uint8, device="cuda:0")
+    for i, c in enumerate(cases):
+        dc = DeviceCase(c)
+        for st in (0, 256):
+            log(f"workspace reuse: call {i} ({c.kind}, B={c.params['num_seqs']}) split_tokens={st}")
+            o0, l0 = dc.run_np(st)
+            o1, l1 = dc.run_np(st, workspace=ws)
+            assert np.array_equal(o0, o1) and np.array_equal(l0, l1), (i, c.kind, st)
