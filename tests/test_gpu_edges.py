@@ -175,3 +175,27 @@ def test_workspace_reused_across_calls_of_other_shapes():
             o0, l0 = dc.run_np(st)
             o1, l1 = dc.run_np(st, workspace=ws)
             assert np.array_equal(o0, o1) and np.array_equal(l0, l1), (i, c.kind, st)
+
+
+def test_call_is_ordered_on_the_callers_stream():
+    # On a side stream: q zeroed, a backlog of copies, q restored, then the call.  The
+    # call sees the restored q only if it runs on that stream, after the restore;
+    # launched on any other stream it would run during the backlog and read zeros.
+    import torch
+    c = synth.paged_case(108, 4, 32, 8, 128, 16, len_range=(300, 2000), kv_dtype=synth.F16)
+    dc = DeviceCase(c)
+    want_o, want_l = dc.run_np()
+    side = torch.cuda.Stream()
+    src = torch.empty(128 << 20, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    keep = dc.q.clone()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(side):
+        dc.q.zero_()
+        for _ in range(16):
+            dst.copy_(src)
+        dc.q.copy_(keep)
+        out, lse = dc.run()
+    side.synchronize()
+    log("side-stream call done")
+    assert np.array_equal(out.cpu().numpy(), want_o) and np.array_equal(lse.cpu().numpy(), want_l)
