@@ -1,25 +1,31 @@
 """Decode-attention benchmark on one MI355X.
 
 One step = one complete decode call (split kernel + combine kernel) over one
-batch of the paged-f16 workload: 32 sequences, 32 query / 8 kv heads,
-head_dim 128, block size 16, per-sequence context uniform in [512, 4096],
-block table a random permutation of a shared pool, f16 K/V ~ N(0,1), f32 Q,
-scale 1/sqrt(128), causal.  Inputs are seeded and synthetic and are resident
-in HBM before timing starts; the caches are rotated over enough copies (>= 1
-GB) that consecutive steps cannot hit the 256 MB Infinity Cache.
+batch of the headline workload, the largest configuration that fits one GPU:
+long-context paged f16 decode, 4 sequences of 131072 tokens, 64 query / 8 kv
+heads, head_dim 128, block size 64, block table a random permutation of a
+shared pool, f16 K/V ~ N(0,1), f32 Q, scale 1/sqrt(128), causal (2.15 GB of KV
+per call).  Inputs are seeded and synthetic and are resident in HBM before
+timing starts; caches smaller than 1 GB are rotated over enough copies that
+consecutive steps cannot hit the 256 MB Infinity Cache.
 
 Prints one JSON line.  `value` is KV-read GB/s: algorithmic K+V bytes of the
 visible (token, kv_head) rows, each read once per (sequence, kv head), divided
-by the wall time per step.  `roofline` prices the dominant (split) kernel
-against MI355X HBM peak with its event-timed duration; `cpu_baseline` times the
-fp64 oracle on this host's cores over the same workload.  With --all the other
-workloads (tiny, tiered int8 W=0/4096, long-context, block-sparse) are
-measured the same way and reported under "workloads".
+by the wall time per step over the K timed steps.  `roofline` prices the
+dominant (split) kernel against MI355X HBM peak with its event-timed duration;
+`cpu_baseline` times the fp64 oracle on this host's cores over the same
+workload.  `workloads` holds one line per configuration (tiny, paged f16,
+tiered int8 at windows 0 and 4096, block-sparse; with --all also the other
+caches): step time as median and p10/p90 over >= 50 timed calls, the split
+kernel's rate and roofline fraction, the whole output compared with the oracle
+element by element, and the oracle's own time on this host.
 """
 from __future__ import annotations
 
 import argparse
 import ctypes
+import dataclasses
+import glob
 import json
 import math
 import os
@@ -34,7 +40,15 @@ import numpy as np  # noqa: E402
 HBM_PEAK_GBS = 8000.0
 MALL_BYTES = 1.0e9     # rotate cache copies until each step touches new memory
 KERNEL_SOURCES = [os.path.join(ROOT, "int8_quantized_kv_amd", "csrc", f) for f in ("decode_kernels.h", "dattn.hip")]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_balanced_paged_f16_B32_H32x8_D128.txt")
+TRAFFIC_GLOB = os.path.join(ROOT, "profiles", "traffic_*.txt")
+SAMPLES = 50           # timed calls (batches of back-to-back calls) for the step-time distribution
+SAMPLE_US = 500.0      # target GPU time of one sample's batch
+# the configurations, as (label, workload index, window)
+CONFIGS = [("tiny", 1, 0), ("paged_f16", 2, 0), ("tiered_int8_w0", 3, 0), ("tiered_int8_w4096", 3, 4096),
+           ("long_paged_f16", 4, 0), ("block_sparse", 5, 0)]
+HEADLINE = 4
+# the oracle on one thread, on a bounded sample of sequences (all heads of each)
+ONE_THREAD_SEQS = {1: 1, 2: 4, 5: 8}
 
 
 def log(msg):
@@ -56,16 +70,17 @@ def visible_range(case, b):
     return lo, hi, q
 
 
-def kv_bytes(case) -> int:
+def kv_bytes(case, seqs=None) -> int:
     """Algorithmic KV bytes of one decode call: K + V (+ int8 scales) of each visible
     (token, kv head) row once per (sequence, kv head) -- with several queries per
     sequence, a row visible to any of them; for the block-sparse cache a row counts
-    once for the union of the blocks its GQA group selects."""
+    once for the union of the blocks its GQA group selects.  `seqs` restricts the
+    count to some sequences."""
     p = case.params
     B, H, Hkv, D = p["num_seqs"], p["num_heads"], p["num_kv_heads"], p["head_dim"]
     G = H // Hkv
     total = 0
-    for b in range(B):
+    for b in (range(B) if seqs is None else seqs):
         lo, hi, q = visible_range(case, b)
         if hi < lo:
             continue
@@ -224,9 +239,31 @@ def cache_bytes(case):
     return sum(a.nbytes for a in arrs)
 
 
+def sample_times(r, est_us, n=SAMPLES):
+    """Step-time distribution: n samples, each a batch of back-to-back full calls
+    between two HIP events on the launch stream (consecutive samples share an
+    event), sized to about SAMPLE_US of GPU time so that the event's own cost is
+    spread over the batch.  Returns per-call microseconds (median, p10, p90)."""
+    import torch
+    per = max(1, min(64, int(math.ceil(SAMPLE_US / max(est_us, 1.0)))))
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    i = 0
+    ev[0].record()
+    for s in range(n):
+        for _ in range(per):
+            r.call(i, "all")
+            i += 1
+        ev[s + 1].record()
+    torch.cuda.synchronize()
+    us = np.array([ev[s].elapsed_time(ev[s + 1]) * 1e3 / per for s in range(n)])
+    return dict(samples=n, calls_per_sample=per, timed_calls=n * per, median_us=round(float(np.median(us)), 3),
+                p10_us=round(float(np.percentile(us, 10)), 3), p90_us=round(float(np.percentile(us, 90)), 3))
+
+
 def measure(case, steps, warmup, copies=None):
-    """Time `steps` full calls (wall clock, inputs resident) and, separately, event-timed
-    split-only and combine-only calls on the same stream."""
+    """Time `steps` full calls (wall clock, inputs resident), then the step-time
+    distribution over >= SAMPLES timed calls, then event-timed split-only and
+    combine-only calls on the same stream, then graph replay."""
     import torch
     if copies is None:
         copies = max(1, int(math.ceil(MALL_BYTES / max(cache_bytes(case), 1))))
@@ -239,22 +276,28 @@ def measure(case, steps, warmup, copies=None):
         r.call(i, "all")
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / steps
-    # Per-kernel durations: `steps` back-to-back launches of one phase between two
-    # events recorded on the launch stream (events around a single launch would add
-    # the dispatch overhead of that launch to every sample).
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    dist = sample_times(r, wall * 1e6)
+    # Per-kernel durations: back-to-back launches of one phase between two events
+    # recorded on the launch stream (events around a single launch would add the
+    # dispatch overhead of that launch to every sample).
+    nk = max(steps, SAMPLES)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
     ev[0].record()
-    for i in range(steps):
+    for i in range(nk):
         r.call(i, "split")
     ev[1].record()
-    for i in range(steps):
+    for i in range(nk):
         r.call(i, "combine")
     ev[2].record()
     torch.cuda.synchronize()
-    split_ms = ev[0].elapsed_time(ev[1]) / steps
-    comb_ms = ev[1].elapsed_time(ev[2]) / steps
+    split_ms = ev[0].elapsed_time(ev[1]) / nk
+    comb_ms = ev[1].elapsed_time(ev[2]) / nk
+    # the timed region's result (the last full call wrote out / lse; split- and
+    # combine-only calls of identical parameters leave the same values)
+    out, lse = r.result()
     graph_ms = graph_call_ms(r)
-    return r, dict(wall_s=wall, split_ms=split_ms, combine_ms=comb_ms, copies=copies, graph_ms=graph_ms)
+    return dict(wall_s=wall, split_ms=split_ms, combine_ms=comb_ms, copies=copies, graph_ms=graph_ms, dist=dist,
+                kernel_launches=nk, out=out, lse=lse)
 
 
 def measure_append(B=16, Hkv=8, D=128, hot_window=512, bs=16, calls=200, warmup=20):
@@ -323,17 +366,19 @@ def kernel_source_sha():
     return h.hexdigest()
 
 
-def measured_traffic(workload=None):
-    """HBM bytes per launch of the split kernel from the committed counter summary
-    (FETCH_SIZE + WRITE_SIZE, scaled by a copy kernel of known size), or None when
-    the summary is missing or was taken on a different kernel source."""
-    try:
-        t = json.load(open(TRAFFIC_FILE))
-    except (OSError, ValueError):
-        return None
-    if t.get("kernel_source_sha256") != kernel_source_sha() or (workload and t.get("workload") != workload):
-        return None
-    return t.get("hbm_bytes_per_launch")
+def measured_traffic(workload):
+    """HBM bytes per launch of the workload's split kernel from its committed
+    counter summary (FETCH_SIZE + WRITE_SIZE, scaled by a copy kernel of known
+    size), or None when there is none or it was taken on another kernel source."""
+    sha = kernel_source_sha()
+    for path in sorted(glob.glob(TRAFFIC_GLOB)):
+        try:
+            t = json.load(open(path))
+        except (OSError, ValueError):
+            continue
+        if t.get("workload") == workload and t.get("kernel_source_sha256") == sha:
+            return t.get("hbm_bytes_per_launch")
+    return None
 
 
 def copy_calibration(mib):
@@ -419,49 +464,88 @@ def copy_reference(nbytes=300 << 20, copies=4, reps=20):
     return round(2 * nbytes * reps / (e0.elapsed_time(e1) / 1e3) / 1e9, 1)
 
 
-def cpu_baseline(case, kvb, min_seconds=10.0):
-    """The fp64 oracle (as it stands) over the whole workload, repeated until at least
-    min_seconds have passed; returns KV GB/s in the same unit as the GPU line."""
+def with_window(case, window):
+    """The same cache and queries with another sliding window (the tiered
+    configuration runs at two windows over identical data)."""
+    p = dict(case.params, sliding_window=int(window))
+    name = case.name.replace("_W0_", f"_W{window}_") if "_W0_" in case.name else f"{case.name}_W{window}"
+    return dataclasses.replace(case, params=p, name=name)
+
+
+def seq_pairs(case, seqs):
+    """Flat (sequence, query, head) row indices of every row of the given sequences."""
+    p = case.params
+    rows = max(1, p.get("query_len", 1)) * p["num_heads"]
+    return np.concatenate([np.arange(b * rows, (b + 1) * rows) for b in seqs]).astype(np.int32)
+
+
+def oracle_leg(case, min_seconds=0.0, nthreads=0, seqs=None):
+    """The fp64 oracle (as it stands) over all rows of the given sequences (all of
+    them by default), repeated until at least min_seconds have passed (once at
+    least).  Returns (out, lse) of the first run and the timing in the GPU line's
+    units: algorithmic KV GB/s of those sequences and sequences (query tokens) per
+    second."""
     import oracle
-    reps, t0 = 0, time.perf_counter()
+    pairs = None if seqs is None else seq_pairs(case, seqs)
+    nseq = case.params["num_seqs"] if seqs is None else len(seqs)
+    reps, t0, res = 0, time.perf_counter(), None
     while True:
-        oracle.run(case)
+        r = oracle.run(case, pairs=pairs, nthreads=nthreads)
+        res = res or r
         reps += 1
         el = time.perf_counter() - t0
         if el >= min_seconds:
             break
-    return dict(value=round(kvb * reps / el / 1e9, 4), unit="GB/s", cores=int(oracle.max_threads()), kind="oracle",
-                cpu_model=cpu_model(),
-                sample=f"whole workload ({case.name}), {reps} run(s) in {el:.1f} s, fp64, OpenMP over (seq, head)",
-                seconds_per_call=round(el / reps, 4))
+    kvb = kv_bytes(case, seqs)
+    threads = nthreads if nthreads > 0 else int(oracle.max_threads())
+    what = "whole workload" if seqs is None else f"all rows of {nseq} of {case.params['num_seqs']} sequences"
+    qn = max(1, case.params.get("query_len", 1))
+    timing = dict(value=round(kvb * reps / el / 1e9, 4), unit="GB/s", cores=threads, kind="oracle",
+                  queries_per_s=round(nseq * qn * reps / el, 2), seconds_per_run=round(el / reps, 4),
+                  sample=f"{what} ({case.name}), {reps} run(s) in {el:.1f} s, fp64, "
+                         f"OpenMP over (sequence, head) rows on {threads} thread(s)")
+    return res, timing
 
 
-def line_for(case, steps, warmup, check=True):
-    import synth  # noqa: F401
+def parity(out, lse, ref_o, ref_l):
+    """Every output element and every lse against the oracle, at the tolerance the
+    tests use: max abs error <= 1e-3 and <= 1e-3 of max |reference| (normwise),
+    lse within 1e-3; rows with no visible key must be exactly (0, -inf)."""
+    out = np.asarray(out, np.float64).reshape(ref_o.shape)
+    lse = np.asarray(lse, np.float64).reshape(ref_l.shape)
+    empty = ~np.isfinite(ref_l)
+    ok = bool(np.all(lse[empty] == -np.inf) and np.all(out[empty] == 0.0))
+    full = ~empty
+    err = float(np.max(np.abs(out[full] - ref_o[full]))) if full.any() else 0.0
+    ref = float(np.max(np.abs(ref_o[full]))) if full.any() else 1.0
+    lerr = float(np.max(np.abs(lse[full] - ref_l[full]))) if full.any() else 0.0
+    ok = ok and bool(np.all(np.isfinite(out[full]))) and err <= 1e-3 and err <= 1e-3 * ref and lerr <= 1e-3
+    return dict(rows=int(ref_l.size), max_abs_err=err, normwise_rel_err=err / max(ref, 1e-30), lse_err=lerr, ok=ok)
+
+
+def line_for(case, steps, warmup, label=None, oracle_seconds=0.0, one_thread_seqs=None, check=True):
+    """One configuration: timing, split-kernel roofline, whole-output parity and
+    the oracle's own time on this host (check=False: timing only)."""
     kvb = kv_bytes(case)
-    r, m = measure(case, steps, warmup)
-    B = case.params["num_seqs"] * max(1, case.params.get("query_len", 1))   # query tokens per call
-    res = dict(workload=case.name, kv_bytes=kvb, ms_per_call=round(m["wall_s"] * 1e3, 5),
+    m = measure(case, steps, warmup)
+    nq = case.params["num_seqs"] * max(1, case.params.get("query_len", 1))   # query tokens per call
+    split_gbs = kvb / (m["split_ms"] / 1e3) / 1e9
+    res = dict(config=label, workload=case.name, kv_bytes=kvb, ms_per_call=round(m["wall_s"] * 1e3, 5),
                kv_gbs=round(kvb / m["wall_s"] / 1e9, 2), pct_peak=round(100 * kvb / m["wall_s"] / 1e9 / HBM_PEAK_GBS, 2),
-               queries_per_s=round(B / m["wall_s"], 1), split_ms=round(m["split_ms"], 5),
-               combine_ms=round(m["combine_ms"], 5), split_gbs=round(kvb / (m["split_ms"] / 1e3) / 1e9, 2),
-               graph_ms_per_call=round(m["graph_ms"], 5),
-               cache_copies=m["copies"])
-    if check:
-        # sampled parity of the timed launch configuration against the oracle
-        import oracle
-        out, lse = r.result()
-        p = case.params
-        rng = np.random.default_rng(0)
-        nb = p["num_seqs"] * max(1, p.get("query_len", 1)) * p["num_heads"]
-        pairs = np.unique(np.concatenate([[0, nb - 1], rng.integers(0, nb, 14)])).astype(np.int32)
-        ro, rl = oracle.run(case, pairs=pairs)
-        go = out.reshape(nb, -1)[pairs]
-        gl = lse.reshape(nb)[pairs]
-        err = float(np.max(np.abs(go - ro)))
-        res["sample_max_abs_err"] = err
-        res["sample_rel_err"] = err / float(np.max(np.abs(ro)))
-        res["sample_lse_err"] = float(np.max(np.abs(gl - rl)))
+               queries_per_s=round(nq / m["wall_s"], 1), step_us=m["dist"],
+               step_median_gbs=round(kvb / (m["dist"]["median_us"] / 1e6) / 1e9, 2),
+               split_ms=round(m["split_ms"], 5), combine_ms=round(m["combine_ms"], 5),
+               split_gbs=round(split_gbs, 2), split_roofline_frac=round(split_gbs / HBM_PEAK_GBS, 4),
+               split_traffic=measured_traffic(case.name), kernel_launches=m["kernel_launches"],
+               graph_ms_per_call=round(m["graph_ms"], 5), cache_copies=m["copies"])
+    if not check:
+        return res, m
+    (ro, rl), timing = oracle_leg(case, oracle_seconds)
+    res["parity"] = parity(m["out"], m["lse"], ro, rl)
+    res["oracle"] = timing
+    if one_thread_seqs:
+        _, t1 = oracle_leg(case, 0.0, nthreads=1, seqs=list(range(one_thread_seqs)))
+        res["oracle_1thread"] = t1
     return res, m
 
 
@@ -484,17 +568,30 @@ def workload(idx, window=0):
     return synth.workload(idx, window=window)
 
 
+def config_case(idx, window, cache):
+    """The configuration's case; the tiered data is generated once for both windows."""
+    if idx == 3:
+        if "tiered" not in cache:
+            cache["tiered"] = workload(3)
+        return with_window(cache["tiered"], window)
+    return workload(idx, window=window)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--all", action="store_true", help="also measure the other workloads")
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--all", action="store_true", help="also measure the other caches' workloads (6-10)")
+    ap.add_argument("--only", action="store_true",
+                    help="measure the headline workload alone (no other lines, write path or CPU baseline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", type=int, default=2,
-                    help="headline workload index (default 2; 6 = the tiered workload with an f16 cold tier, "
-                         "7 = a sliding-window ring f16 cache, 8 = four queries per sequence, 9 = sixteen, "
-                         "10 = four over the block-sparse cache)")
+    ap.add_argument("--workload", type=int, default=HEADLINE,
+                    help="headline workload index (default 4, the long-context paged f16 configuration; 1 tiny, "
+                         "2 paged f16, 3 tiered int8, 5 block-sparse, 6 the tiered workload with an f16 cold tier, "
+                         "7 a sliding-window ring f16 cache, 8 four queries per sequence, 9 sixteen, 10 four over "
+                         "the block-sparse cache)")
+    ap.add_argument("--window", type=int, default=0, help="sliding window of the headline workload")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run 5 device copies of MIB MiB (for scaling memory counters)")
     args = ap.parse_args()
@@ -504,7 +601,6 @@ def main():
         sys.exit(2)
 
     import torch
-    import synth
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
@@ -513,14 +609,16 @@ def main():
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
 
+    cache = {}
     log("generating headline workload ...")
-    case = workload(args.workload)
+    case = config_case(args.workload, args.window, cache)
     log(f"workload {case.name}: KV bytes {kv_bytes(case)}")
-    head, m = line_for(case, args.steps, args.warmup)
+    base_s = 0.0 if (args.no_cpu_baseline or args.only) else 10.0
+    head, m = line_for(case, args.steps, args.warmup, label="headline", oracle_seconds=base_s,
+                       one_thread_seqs=ONE_THREAD_SEQS.get(args.workload), check=not args.only)
     log(json.dumps(head))
     kvb = head["kv_bytes"]
-    split_s = m["split_ms"] / 1e3
-    achieved = kvb / split_s / 1e9
+    achieved = kvb / (m["split_ms"] / 1e3) / 1e9
     B, H, D = case.q.shape[0], case.q.shape[-2], case.q.shape[-1]
     G = H // case.params["num_kv_heads"]
     kind = {"paged": "paged f16" if case.k_cache is not None and case.k_cache.dtype == np.float16 else "paged f32",
@@ -539,42 +637,48 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f16",
-        "data": "synthetic (seeded numpy N(0,1) Q/K/V, uniform lengths, permuted block pool)",
+        "data": "synthetic (seeded numpy N(0,1) Q/K/V, permuted block pool)",
         "config": {"workload": case.name, "global_batch": int(B), "num_heads": int(H),
                    "num_kv_heads": int(case.params["num_kv_heads"]), "head_dim": int(D),
-                   "block_size": int(case.params["block_size"]),
+                   "block_size": int(case.params["block_size"]), "sliding_window": int(case.params["sliding_window"]),
                    "seq_len_range": [int(lens.min()), int(lens.max())],
                    "total_tokens": int(lens.sum()), "parallelism": "single GPU"},
         "pct_of_hbm_peak": head["pct_peak"],
         "queries_per_s": head["queries_per_s"],
+        "step_us": head["step_us"],
         "kernels": {"split_ms": head["split_ms"], "combine_ms": head["combine_ms"],
-                    "graph_ms_per_call": head["graph_ms_per_call"]},
+                    "graph_ms_per_call": head["graph_ms_per_call"], "launches_timed": head["kernel_launches"]},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(case.name),
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": head["split_traffic"],
                      "kernel": f"split kernel <D={D}, G={G}, {kind}>",
                      "bytes_per_launch": kvb},
-        "parity_sample": {k: head[k] for k in ("sample_max_abs_err", "sample_rel_err", "sample_lse_err")},
-        "copy_reference_gbs": copy_reference(),
     }
-    ceiling = read_reference()
-    out["roofline"]["measured_read_ceiling_gbs"] = ceiling
-    out["roofline"]["frac_of_measured_ceiling"] = round(achieved / ceiling, 4)
-    log("timing the tiered write path ...")
-    out["write_path"] = measure_append()
-    if not args.no_cpu_baseline:
-        log("timing the oracle on the host ...")
-        out["cpu_baseline"] = cpu_baseline(case, kvb)
-    if args.all:
-        extra = []
-        for idx, kw in ((1, {}), (3, dict(window=0)), (3, dict(window=4096)), (4, {}), (5, {}),
-                        (6, dict(window=0)), (6, dict(window=4096)), (7, {}), (8, {}), (9, {}), (10, {})):
-            log(f"generating workload {idx} {kw} ...")
-            c = workload(idx, **kw)
-            res, _ = line_for(c, max(20, args.steps // 4), max(5, args.warmup // 4))
+    if "parity" in head:
+        out["parity"] = head["parity"]
+    if not args.only:
+        out["copy_reference_gbs"] = copy_reference()
+        ceiling = read_reference()
+        out["roofline"]["measured_read_ceiling_gbs"] = ceiling
+        out["roofline"]["frac_of_measured_ceiling"] = round(achieved / ceiling, 4)
+        log("timing the tiered write path ...")
+        out["write_path"] = measure_append()
+        if not args.no_cpu_baseline:
+            out["cpu_baseline"] = head["oracle"]
+            out["cpu_baseline"]["cpu_model"] = cpu_model()
+        lines = []
+        todo = [(label, idx, w) for label, idx, w in CONFIGS if (idx, w) != (args.workload, args.window)]
+        if args.all:
+            todo += [("tiered_f16_w0", 6, 0), ("tiered_f16_w4096", 6, 4096), ("ring_f16", 7, 0),
+                     ("multi_query_4", 8, 0), ("multi_query_16", 9, 0), ("block_sparse_multi_query_4", 10, 0)]
+        for label, idx, w in todo:
+            log(f"generating workload {idx} window {w} ...")
+            c = config_case(idx, w, cache)
+            res, _ = line_for(c, args.steps, args.warmup, label=label, one_thread_seqs=ONE_THREAD_SEQS.get(idx))
             log(json.dumps(res))
-            extra.append(res)
+            lines.append(res)
             del c
-        out["workloads"] = extra
+        out["workloads"] = lines
+        out["parity_all_ok"] = bool(head["parity"]["ok"] and all(x["parity"]["ok"] for x in lines))
     print(json.dumps(out), flush=True)
 
 

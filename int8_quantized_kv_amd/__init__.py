@@ -22,11 +22,16 @@ Cache layouts (C-contiguous):
 q may also be float16 (converted exactly).
 Outputs: out [B, H, D] float32 or float16 (out_dtype), lse [B, H] float32;
 want_out=False writes lse only.
+
+Every decode function needs max_seq_len, a host-side upper bound of seq_lens
+that sizes the grid: the binding never reads device memory, so a call
+enqueues work without synchronising the stream and can be captured in a graph.
+Shapes are checked before anything is enqueued: every per-sequence array
+(seq_lens, cold_lens, q_pos, block tables) must have one row per sequence.
 """
 from __future__ import annotations
 
 import ctypes
-import math
 import os
 from typing import Optional
 
@@ -146,9 +151,21 @@ def _need(t, name, dtypes, ndim, device):
         raise ValueError(f"{name} must be contiguous")
     if t.device != device:
         raise ValueError(f"{name} is on {t.device}, expected {device}")
+    return t
+
+
+def _rows(B, **tensors):
+    """Every per-sequence array has one row per sequence: the kernels index
+    row b of each for every b < B, so a short array would be read past its end."""
+    for name, t in tensors.items():
+        if t is not None and t.shape[0] != B:
+            raise ValueError(f"{name} has {t.shape[0]} rows, expected one per sequence ({B})")
+
+
+def _on_gpu(t, name):
+    """Checked after the shapes: every other array was required to be on t's device."""
     if t.device.type != "cuda":
         raise ValueError(f"{name} must be a GPU tensor (got {t.device}); the library reads device memory only")
-    return t
 
 
 def _ptr(t):
@@ -207,10 +224,15 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def _max_len(seq_lens, max_seq_len):
+def _max_len(max_seq_len):
+    """max_seq_len sizes the grid on the host; it is a required argument because
+    reading it from the device array seq_lens would synchronise the stream (and
+    break graph capture)."""
     if max_seq_len is None:
-        max_seq_len = int(seq_lens.max().item()) if seq_lens.numel() else 0  # synchronises
-    return max_seq_len
+        raise ValueError("max_seq_len is required (an upper bound of seq_lens known on the host)")
+    if int(max_seq_len) < 0:
+        raise ValueError(f"max_seq_len must be >= 0 (got {max_seq_len})")
+    return int(max_seq_len)
 
 
 def dattn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, *, q_pos=None, scale: float = 0.0,
@@ -233,9 +255,10 @@ def dattn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, *, q_pos=None
     NB, bs, Hkv, D = k_cache.shape
     if tuple(v_cache.shape) != tuple(k_cache.shape) or q.shape[-1] != D:
         raise ValueError("k_cache, v_cache and q disagree on shape")
-    if block_table.shape[0] != q.shape[0] or seq_lens.shape[0] != q.shape[0]:
-        raise ValueError("block_table / seq_lens must have one row per sequence")
-    p = _params(q, Hkv, D, bs, block_table.shape[1], NB, _max_len(seq_lens, max_seq_len), scale, causal,
+    _rows(q.shape[0], block_table=block_table, seq_lens=seq_lens, q_pos=q_pos)
+    max_seq_len = _max_len(max_seq_len)
+    _on_gpu(q, "q")
+    p = _params(q, Hkv, D, bs, block_table.shape[1], NB, max_seq_len, scale, causal,
                 sliding_window, softcap, split_tokens, phases, out_dtype)
     ws = dattn_workspace_size(p, KIND_PAGED)
     out, lse, workspace = _outputs(q, out, lse, want_lse, workspace, ws, out_dtype, want_out)
@@ -274,7 +297,10 @@ def dattn_decode_tiered_int8(q, k_hot, v_hot, k_cold, v_cold, k_scale, v_scale, 
             or tuple(v_cold.shape) != tuple(k_cold.shape) or tuple(k_scale.shape) != (NB, bs, Hkv) \
             or tuple(v_scale.shape) != (NB, bs, Hkv) or k_hot.shape[0] != B:
         raise ValueError("tiered cache tensors disagree on shape")
-    p = _params(q, Hkv, D, bs, cold_block_table.shape[1], NB, _max_len(seq_lens, max_seq_len), scale, causal,
+    _rows(B, cold_block_table=cold_block_table, seq_lens=seq_lens, cold_lens=cold_lens, q_pos=q_pos)
+    max_seq_len = _max_len(max_seq_len)
+    _on_gpu(q, "q")
+    p = _params(q, Hkv, D, bs, cold_block_table.shape[1], NB, max_seq_len, scale, causal,
                 sliding_window, softcap, split_tokens, phases, out_dtype)
     ws = dattn_workspace_size(p, KIND_TIERED_INT8)
     out, lse, workspace = _outputs(q, out, lse, want_lse, workspace, ws, out_dtype, want_out)
@@ -311,7 +337,10 @@ def dattn_decode_tiered_f16(q, k_hot, v_hot, k_cold, v_cold, cold_block_table, s
     if Dh != D or Dc != D or Hkv2 != Hkv or tuple(v_hot.shape) != tuple(k_hot.shape) \
             or tuple(v_cold.shape) != tuple(k_cold.shape) or k_hot.shape[0] != B:
         raise ValueError("tiered cache tensors disagree on shape")
-    p = _params(q, Hkv, D, bs, cold_block_table.shape[1], NB, _max_len(seq_lens, max_seq_len), scale, causal,
+    _rows(B, cold_block_table=cold_block_table, seq_lens=seq_lens, cold_lens=cold_lens, q_pos=q_pos)
+    max_seq_len = _max_len(max_seq_len)
+    _on_gpu(q, "q")
+    p = _params(q, Hkv, D, bs, cold_block_table.shape[1], NB, max_seq_len, scale, causal,
                 sliding_window, softcap, split_tokens, phases, out_dtype)
     ws = dattn_workspace_size(p, KIND_TIERED_F16)
     out, lse, workspace = _outputs(q, out, lse, want_lse, workspace, ws, out_dtype, want_out)
@@ -339,9 +368,12 @@ def dattn_decode_ring_f16(q, k_ring, v_ring, seq_lens, *, q_pos=None, scale: flo
         _need(q_pos, "q_pos", (torch.int32,), 1, dev)
     B, D = q.shape[0], q.shape[-1]
     Bk, W, Hkv, Dk = k_ring.shape
-    if Bk != B or Dk != D or tuple(v_ring.shape) != tuple(k_ring.shape) or seq_lens.shape[0] != B:
+    if Bk != B or Dk != D or tuple(v_ring.shape) != tuple(k_ring.shape):
         raise ValueError("ring tensors disagree on shape")
-    p = _params(q, Hkv, D, 1, 1, 1, _max_len(seq_lens, max_seq_len), scale, causal, W, softcap, split_tokens,
+    _rows(B, seq_lens=seq_lens, q_pos=q_pos)
+    max_seq_len = _max_len(max_seq_len)
+    _on_gpu(q, "q")
+    p = _params(q, Hkv, D, 1, 1, 1, max_seq_len, scale, causal, W, softcap, split_tokens,
                 phases, out_dtype)
     ws = dattn_workspace_size(p, KIND_RING_F16)
     out, lse, workspace = _outputs(q, out, lse, want_lse, workspace, ws, out_dtype, want_out)
@@ -377,6 +409,7 @@ def dattn_append_tiered_int8(k_new, v_new, k_hot, v_hot, k_cold, v_cold, k_scale
             or tuple(k_scale.shape) != (NB, bs, Hkv) or tuple(v_scale.shape) != (NB, bs, Hkv) \
             or cold_block_table.shape[0] != B or seq_lens.shape[0] != B or cold_lens.shape[0] != B:
         raise ValueError("tiered cache tensors disagree on shape")
+    _on_gpu(k_new, "k_new")
     p = DattnParams(B, Hkv, Hkv, D, 0.0, 0, 0, 0.0, bs, cold_block_table.shape[1], NB, 0, 0, 0)
     _check(lib().dattn_append_tiered_int8(ctypes.byref(p), _ptr(k_new), _ptr(v_new), _ptr(k_hot), _ptr(v_hot),
                                           hot_window, _ptr(k_cold), _ptr(v_cold), _ptr(k_scale), _ptr(v_scale),
@@ -403,9 +436,14 @@ def dattn_decode_block_sparse(q, k_cache, v_cache, block_table, seq_lens, sparse
     if q_pos is not None:
         _need(q_pos, "q_pos", (torch.int32,), 1, dev)
     NB, bs, Hkv, D = k_cache.shape
+    if tuple(v_cache.shape) != tuple(k_cache.shape) or q.shape[-1] != D:
+        raise ValueError("k_cache, v_cache and q disagree on shape")
     if row_ptr.shape[0] != col_idx.shape[0]:
         raise ValueError("row_ptr and col_idx must have one row per layout")
-    p = _params(q, Hkv, D, bs, block_table.shape[1], NB, _max_len(seq_lens, max_seq_len), scale, causal,
+    _rows(q.shape[0], block_table=block_table, seq_lens=seq_lens, q_pos=q_pos)
+    max_seq_len = _max_len(max_seq_len)
+    _on_gpu(q, "q")
+    p = _params(q, Hkv, D, bs, block_table.shape[1], NB, max_seq_len, scale, causal,
                 sliding_window, softcap, split_tokens, phases, out_dtype)
     ws = dattn_workspace_size(p, KIND_BLOCK_SPARSE, sparse_block)
     out, lse, workspace = _outputs(q, out, lse, want_lse, workspace, ws, out_dtype, want_out)
@@ -415,12 +453,6 @@ def dattn_decode_block_sparse(q, k_cache, v_cache, block_table, seq_lens, sparse
                                            col_idx.shape[1], _ptr(out), _ptr(lse), _ptr(workspace),
                                            workspace.numel(), _stream(stream)))
     return out, lse
-
-
-def default_scale(head_dim: int) -> float:
-    """1/sqrt(head_dim) rounded to f32, the value scale=0 selects."""
-    import struct
-    return struct.unpack("f", struct.pack("f", 1.0 / math.sqrt(head_dim)))[0]
 
 
 def dattn_append_ring_f16(k_new, v_new, k_ring, v_ring, seq_lens, *, stream=None):
@@ -437,6 +469,7 @@ def dattn_append_ring_f16(k_new, v_new, k_ring, v_ring, seq_lens, *, stream=None
     if tuple(v_new.shape) != (B, Hkv, D) or tuple(v_ring.shape) != tuple(k_ring.shape) or k_ring.shape[0] != B \
             or k_ring.shape[2] != Hkv or k_ring.shape[3] != D or seq_lens.shape[0] != B:
         raise ValueError("ring tensors disagree on shape")
+    _on_gpu(k_new, "k_new")
     p = DattnParams(B, Hkv, Hkv, D, 0.0, 0, int(k_ring.shape[1]), 0.0, 1, 1, 1, 0, 0, 0)
     _check(lib().dattn_append_ring_f16(ctypes.byref(p), _ptr(k_new), _ptr(v_new), _ptr(k_ring), _ptr(v_ring),
                                        _ptr(seq_lens), _stream(stream)))
@@ -447,6 +480,7 @@ def dattn_stream_read(src, sink, *, stream=None):
     (sink: a 1-element int32 GPU tensor) -- the measured read ceiling."""
     torch = _torch()
     _need(sink, "sink", (torch.int32,), 1, src.device)
+    _on_gpu(src, "src")
     if not src.is_contiguous() or src.device.type != "cuda":
         raise ValueError("src must be a contiguous GPU tensor")
     _check(lib().dattn_stream_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink), _stream(stream)))

@@ -1683,9 +1683,12 @@ __global__ DATTN_BOUNDS(MQ) __attribute__((amdgpu_waves_per_eu(2))) void sparse_
 //
 // Merge the partials of one (sequence, head): M = max m_s,
 // l = sum l_s 2^{m_s - M}, out = sum acc_s 2^{m_s - M} / l, lse = (M + log2 l) ln 2.
-// One workgroup per (sequence, head).  Partials with l = 0 (no visible key)
-// are skipped.  out is f32, or f16 rounded to nearest even from the f32
-// result; with out == nullptr only lse is written (acc is then not read).
+// One workgroup per (sequence, head).  Partials with l = 0 exactly (no
+// visible key) are skipped; any other l, NaN included, is merged, so a NaN
+// that reached a partial from a visible K, V or Q value reaches out and lse as
+// it does in the plain definition.  out is f32, or f16 rounded to nearest even
+// from the f32 result; with out == nullptr only lse is written (acc is then
+// not read).
 
 struct OutRow {
   void* p;     // first element of the (sequence, head) row, or nullptr
@@ -1735,7 +1738,7 @@ __device__ __forceinline__ void merge_partials(const Loc& loc, int n, const OutR
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      if (v[u].y > 0.f) {   // skipped: empty pieces (their acc is never read into the sum)
+      if (v[u].y != 0.f) {   // skipped: empty pieces (their acc is never read into the sum)
         const float m_new = fmaxf(m, v[u].x);
         const float ca = fast_exp2(m - m_new), cb = fast_exp2(v[u].x - m_new);
         L = L * ca + v[u].y * cb;
@@ -1758,11 +1761,11 @@ __device__ __forceinline__ void merge_partials(const Loc& loc, int n, const OutR
   __syncthreads();
   float M = -__builtin_inff();
 #pragma unroll
-  for (int g = 0; g < 8; ++g) M = redl[g] > 0.f ? fmaxf(M, redm[g]) : M;
+  for (int g = 0; g < 8; ++g) M = redl[g] != 0.f ? fmaxf(M, redm[g]) : M;
   float wg[8], Lt = 0.f;
 #pragma unroll
   for (int g = 0; g < 8; ++g) {
-    wg[g] = redl[g] > 0.f ? fast_exp2(redm[g] - M) : 0.f;
+    wg[g] = redl[g] != 0.f ? fast_exp2(redm[g] - M) : 0.f;
     Lt += redl[g] * wg[g];
   }
   if (out.p) {
@@ -1770,10 +1773,10 @@ __device__ __forceinline__ void merge_partials(const Loc& loc, int n, const OutR
       float ot = 0.f;
 #pragma unroll
       for (int g = 0; g < 8; ++g) ot += red[g][d] * wg[g];
-      out.store(d, Lt > 0.f ? ot / Lt : 0.f);
+      out.store(d, Lt != 0.f ? ot / Lt : 0.f);
     }
   }
-  if (tid == 0 && lse_out) *lse_out = Lt > 0.f ? (M + __builtin_log2f(Lt)) * kLn2 : -__builtin_inff();
+  if (tid == 0 && lse_out) *lse_out = Lt != 0.f ? (M + __builtin_log2f(Lt)) * kLn2 : -__builtin_inff();
 }
 
 // The same merge by 32 threads for one row with few partials: the partials
@@ -1804,7 +1807,7 @@ __device__ __forceinline__ void merge_row(const Loc& loc, int n, const OutRow ou
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      if (v[u].y > 0.f) {
+      if (v[u].y != 0.f) {
         const float m_new = fmaxf(m, v[u].x);
         const float ca = fast_exp2(m - m_new), cb = fast_exp2(v[u].x - m_new);
         L = L * ca + v[u].y * cb;
@@ -1820,9 +1823,9 @@ __device__ __forceinline__ void merge_row(const Loc& loc, int n, const OutRow ou
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) out.store(128 * j + 4 * c + e, L > 0.f ? o[j][e] / L : 0.f);
+      for (int e = 0; e < 4; ++e) out.store(128 * j + 4 * c + e, L != 0.f ? o[j][e] / L : 0.f);
   }
-  if (c == 0 && lse_out) *lse_out = L > 0.f ? (m + __builtin_log2f(L)) * kLn2 : -__builtin_inff();
+  if (c == 0 && lse_out) *lse_out = L != 0.f ? (m + __builtin_log2f(L)) * kLn2 : -__builtin_inff();
 }
 
 // Eight rows per workgroup: a row with at most kShortRow partials is merged

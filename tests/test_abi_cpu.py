@@ -250,6 +250,77 @@ def test_binding_refuses_host_tensors(lib):
         dk.dattn_decode_paged(q.double(), k, k, bt, sl, max_seq_len=1)
 
 
+def _host_decode_args(B=2, H=4, Hkv=2, D=64, bs=16, nb=4, mb=2, hw=16):
+    """Host tensors of consistent shapes for every decode wrapper (never launched:
+    the wrappers check shapes before they look at the device)."""
+    torch = pytest.importorskip("torch")
+    i32 = lambda *s: torch.zeros(s, dtype=torch.int32)  # noqa: E731
+    f16 = lambda *s: torch.zeros(s, dtype=torch.float16)  # noqa: E731
+    return dict(q=torch.zeros((B, H, D), dtype=torch.float32), k_cache=f16(nb, bs, Hkv, D), block_table=i32(B, mb),
+                seq_lens=i32(B), cold_lens=i32(B), q_pos=i32(B), k_hot=f16(B, hw, Hkv, D),
+                k_cold=i32(nb, bs, Hkv, D // 4), k_scale=f16(nb, bs, Hkv), k_cold16=f16(nb, bs, Hkv, D),
+                k_ring=f16(B, hw, Hkv, D), row_ptr=i32(4, 3), col_idx=i32(4, 8))
+
+
+def _decode_calls(a):
+    """name -> (callable taking the per-sequence arrays as keywords)."""
+    def paged(block_table, seq_lens, q_pos, **_):
+        return dk.dattn_decode_paged(a["q"], a["k_cache"], a["k_cache"], block_table, seq_lens, q_pos=q_pos,
+                                     max_seq_len=16)
+
+    def tiered(block_table, seq_lens, q_pos, cold_lens, **_):
+        return dk.dattn_decode_tiered_int8(a["q"], a["k_hot"], a["k_hot"], a["k_cold"], a["k_cold"], a["k_scale"],
+                                           a["k_scale"], block_table, seq_lens, cold_lens, q_pos=q_pos,
+                                           max_seq_len=16)
+
+    def tiered_f16(block_table, seq_lens, q_pos, cold_lens, **_):
+        return dk.dattn_decode_tiered_f16(a["q"], a["k_hot"], a["k_hot"], a["k_cold16"], a["k_cold16"], block_table,
+                                          seq_lens, cold_lens, q_pos=q_pos, max_seq_len=16)
+
+    def ring(seq_lens, q_pos, **_):
+        return dk.dattn_decode_ring_f16(a["q"], a["k_ring"], a["k_ring"], seq_lens, q_pos=q_pos, max_seq_len=16)
+
+    def sparse(block_table, seq_lens, q_pos, **_):
+        return dk.dattn_decode_block_sparse(a["q"], a["k_cache"], a["k_cache"], block_table, seq_lens, 16,
+                                            a["row_ptr"], a["col_idx"], q_pos=q_pos, max_seq_len=16)
+
+    return dict(paged=(paged, ("block_table", "seq_lens", "q_pos")),
+                tiered=(tiered, ("block_table", "seq_lens", "q_pos", "cold_lens")),
+                tiered_f16=(tiered_f16, ("block_table", "seq_lens", "q_pos", "cold_lens")),
+                ring=(ring, ("seq_lens", "q_pos")),
+                sparse=(sparse, ("block_table", "seq_lens", "q_pos")))
+
+
+def test_binding_checks_rows_per_sequence(lib):
+    """A per-sequence array with fewer (or more) rows than q has sequences is
+    refused before anything is enqueued; the kernels would read row b of it for
+    every b < B.  With every shape right the call fails only on the device check
+    (host tensors), so the row checks come first."""
+    a = _host_decode_args()
+    for name, (fn, arrays) in _decode_calls(a).items():
+        good = {k: a[k] for k in ("block_table", "seq_lens", "q_pos", "cold_lens")}
+        with pytest.raises(ValueError, match="GPU"):
+            fn(**good)
+        for arr in arrays:
+            for rows in (1, 3):
+                bad = dict(good)
+                t = good[arr]
+                bad[arr] = t.new_zeros((rows,) + tuple(t.shape[1:]))
+                with pytest.raises(ValueError, match="rows"):
+                    fn(**bad)
+
+
+def test_binding_needs_max_seq_len(lib):
+    """max_seq_len sizes the grid on the host; the binding never reads it from
+    the device array (that would synchronise), so leaving it out is an error."""
+    a = _host_decode_args()
+    with pytest.raises(ValueError, match="max_seq_len"):
+        dk.dattn_decode_paged(a["q"], a["k_cache"], a["k_cache"], a["block_table"], a["seq_lens"])
+    with pytest.raises(ValueError, match="max_seq_len"):
+        dk.dattn_decode_ring_f16(a["q"], a["k_ring"], a["k_ring"], a["seq_lens"])
+    assert not hasattr(dk, "default_scale")
+
+
 def test_append_validates_before_any_hip_call(lib):
     P = ctypes.c_void_p
     fake = P(0x1000)   # never dereferenced: every call below fails validation or is empty

@@ -111,7 +111,7 @@ def test_append_then_decode_matches_oracle():
         assert np.array_equal(_host(g, w).view(np.uint8), w.view(np.uint8)), name
     q = rng.standard_normal((B, H, D)).astype(np.float32)
     out, lse = dk.dattn_decode_tiered_int8(torch.from_numpy(q).cuda(), *dstate[:6], dtable, dstate[6], dstate[7],
-                                           softcap=30.0, sliding_window=100)
+                                           softcap=30.0, sliding_window=100, max_seq_len=int(want[6].max()))
     p = oracle.Params(B, H, Hkv, D, sliding_window=100, softcap=30.0, block_size=bs, max_blocks_per_seq=max_blocks,
                       num_blocks=num_blocks)
     ro, rl = oracle.decode_tiered_int8(p, q, want[0], want[1], hw, want[2], want[3], want[4], want[5], table,

@@ -1,8 +1,13 @@
 """Full-size workloads on the GPU, in the launch configuration the benchmark
-times (library-chosen split size), checked against the oracle on sampled
-(sequence, head) pairs that the oracle computes one by one, plus properties
-that hold at any size (finite outputs, lse not below the log of the largest
-single weight, which the oracle pins per sample)."""
+times (library-chosen schedule), compared with the fp64 oracle on EVERY
+output element and every lse: all (sequence, query, head) rows of the five
+configurations (the tiered one at both windows) and of the other caches'
+full-size workloads.  At these sizes the balanced schedule runs hundreds of
+workers per kv-head group whose ranges cross sequence boundaries, so a slot or
+offset mistake confined to a few sequences shows here even when the small
+cases pass.  The oracle runs on all host cores (seconds per workload)."""
+import time
+
 import numpy as np
 import pytest
 
@@ -11,10 +16,12 @@ from gpu_util import DeviceCase, compare, log, oracle_run
 
 pytestmark = pytest.mark.gpu
 
-WORKLOADS = [(2, {}), (3, {"window": 0}), (3, {"window": 4096}), (4, {}), (5, {})]
-# the tiered workload's shape with an f16 cold tier, the window ring, four and sixteen queries per sequence,
-# four queries over the block-sparse cache
-EXTRA = {"tiered_f16": lambda: synth.tiered_f16_workload(0), "ring": synth.ring_workload,
+WORKLOADS = [(1, {}), (2, {}), (3, {"window": 0}), (3, {"window": 4096}), (4, {}), (5, {})]
+# the tiered workload's shape with an f16 cold tier (both windows), the window ring, four and sixteen queries
+# per sequence, four queries over the block-sparse cache
+EXTRA = {"tiered_f16_w0": lambda: synth.tiered_f16_workload(0),
+         "tiered_f16_w4096": lambda: synth.tiered_f16_workload(4096),
+         "ring": synth.ring_workload,
          "multi_query": lambda: synth.multi_query_workload(4),
          "multi_query_16": lambda: synth.multi_query_workload(16),
          "sparse_multi_query": lambda: synth.sparse_multi_query_workload(4)}
@@ -30,27 +37,27 @@ def _gpu():
     yield
 
 
-def _sampled(case, seed):
+def _whole(case):
     import torch
     log(f"full-size {case.name}")
     dc = DeviceCase(case)
     out, lse = dc.run_np()
     del dc
     torch.cuda.empty_cache()
-    p = case.params
-    nbh = p["num_seqs"] * max(1, p.get("query_len", 1)) * p["num_heads"]
-    assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
-    rng = np.random.default_rng(seed)
-    pairs = np.unique(np.concatenate([[0, nbh - 1, p["num_heads"] - 1], rng.integers(0, nbh, 21)])).astype(np.int32)
-    ref_o, ref_l = oracle_run(case, pairs=pairs)
-    compare(out.reshape(nbh, -1)[pairs], lse.reshape(nbh)[pairs], ref_o, ref_l, what=f"{case.name} sampled")
+    t0 = time.perf_counter()
+    ref_o, ref_l = oracle_run(case)
+    log(f"  oracle over the whole workload: {time.perf_counter() - t0:.1f} s")
+    assert out.shape == ref_o.shape and lse.shape == ref_l.shape
+    # no configuration has an empty visible set: every row is finite and compared
+    assert np.all(np.isfinite(ref_l)), f"{case.name}: the oracle has an empty row"
+    compare(out, lse, ref_o, ref_l, what=f"{case.name} every row")
 
 
-@pytest.mark.parametrize("idx,kw", WORKLOADS, ids=["paged", "tiered_w0", "tiered_w4096", "long", "sparse"])
-def test_full_size_sampled(idx, kw):
-    _sampled(synth.workload(idx, **kw), idx)
+@pytest.mark.parametrize("idx,kw", WORKLOADS, ids=["tiny", "paged", "tiered_w0", "tiered_w4096", "long", "sparse"])
+def test_full_size_every_row(idx, kw):
+    _whole(synth.workload(idx, **kw))
 
 
 @pytest.mark.parametrize("name", sorted(EXTRA))
-def test_full_size_sampled_other_caches(name):
-    _sampled(EXTRA[name](), 11)
+def test_full_size_every_row_other_caches(name):
+    _whole(EXTRA[name]())

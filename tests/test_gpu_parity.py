@@ -307,3 +307,39 @@ def test_multi_query_nonlive_rows_hold_nan(qn):
     t.k_hot[~ring_live] = np.float16(np.nan)
     t.v_hot[~ring_live] = np.float16(np.inf)
     _check(t, what=f"tiered Qn{qn} NaN/Inf outside the live rows and ring slots")
+
+
+# ------------------------------------------------- NaN in a row a query uses
+
+def _check_nan(case, split_tokens, what):
+    """NaN in visible rows: the GPU gives NaN exactly where the fp64 oracle does
+    (a NaN key poisons every head of its group, a NaN value element one output
+    dim, a NaN int8 value scale the whole row of values); the rest matches."""
+    log(f"case {case.kind} {what} split_tokens={split_tokens}")
+    og, lg = DeviceCase(case).run_np(split_tokens)
+    orf, lrf = oracle_run(case)
+    assert np.isnan(orf).any(), f"{what}: the planted NaN reaches no oracle output"
+    assert np.array_equal(np.isnan(og), np.isnan(orf)), f"{what}: NaN pattern of out differs from the oracle"
+    assert np.array_equal(np.isnan(lg), np.isnan(lrf)), f"{what}: NaN pattern of lse differs from the oracle"
+    ok = ~np.isnan(orf)
+    err = float(np.max(np.abs(og[ok] - orf[ok])))
+    assert err <= 1e-3 and err <= 1e-3 * float(np.max(np.abs(orf[ok]))), f"{what}: max abs error {err}"
+    okl = ~np.isnan(lrf)
+    assert float(np.max(np.abs(lg[okl] - lrf[okl]))) <= 1e-3, f"{what}: lse error"
+
+
+@pytest.mark.parametrize("split_tokens", [0, 64])
+def test_nan_in_live_rows_reaches_the_output(split_tokens):
+    """Merging splits must not drop a piece whose running sum is NaN: only a
+    piece with no visible key (l = 0 exactly) is skipped."""
+    c = synth.paged_case(130, 3, 16, 4, 128, 16, lens=[300, 700, 50], kv_dtype=synth.F16)
+    tb = c.block_table
+    c.k_cache[tb[1, 123 // 16], 123 % 16, 2, 7] = np.float16(np.nan)    # key of seq 1, kv head 2
+    c.v_cache[tb[0, 5 // 16], 5 % 16, 1, 17] = np.float16(np.nan)      # one value dim of seq 0, kv head 1
+    _check_nan(c, split_tokens, "paged f16 NaN key and NaN value element")
+    t = synth.tiered_case(131, 3, 16, 4, 128, 16, [700, 300, 40], [450, 260, 0], 256, softcap=30.0)
+    ctb = t.cold_block_table
+    t.k_scale[ctb[0, 200 // 16], 200 % 16, 3] = np.float16(np.nan)      # cold key scale, seq 0, kv head 3
+    t.v_scale[ctb[1, 17 // 16], 17 % 16, 0] = np.float16(np.nan)        # cold value scale, seq 1, kv head 0
+    t.k_hot[2, 33 % t.hot_window, 1, 64] = np.float16(np.nan)           # hot key, seq 2, kv head 1
+    _check_nan(t, split_tokens, "tiered int8 NaN scales and NaN hot key")
