@@ -187,6 +187,29 @@ int dattn_decode_tiered_int8(const dattn_params* p, const void* q, const uint16_
                              size_t workspace_bytes, void* stream);
 
 /*
+ * dattn_decode_tiered_int8 for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments without the workspace.  The split partials go
+ * to a static scratch array inside the library, 32 MiB on each device (held
+ * from the first call on that device until the process ends).  A call whose
+ * partials need more (dattn_workspace_size with DATTN_KIND_TIERED_INT8 above
+ * 32 MiB) returns DATTN_ERR_UNSUPPORTED before anything is enqueued.  The call
+ * allocates nothing; the caller still provides q, the cache arrays, out and
+ * lse.  Every call on a device uses that device's one scratch array: calls
+ * that overlap on one device (other streams, other host threads) race and
+ * give wrong results; calls ordered on one stream are safe.  Nothing in the
+ * scratch needs clearing between calls (each call writes every partial it
+ * reads).  The first call on a device looks up the scratch's device address
+ * (hipGetSymbolAddress) with that device current.
+ */
+int dattn_decode_tiered_int8_static(const dattn_params* p, const void* q, const uint16_t* k_hot,
+                                    const uint16_t* v_hot, int32_t hot_window, const uint32_t* k_cold,
+                                    const uint32_t* v_cold, const uint16_t* k_scale, const uint16_t* v_scale,
+                                    const int32_t* cold_block_table, const int32_t* seq_lens,
+                                    const int32_t* cold_lens, const int32_t* q_pos, void* out, float* lse,
+                                    void* stream);
+
+/*
  * Tiered cache with an f16 cold tier (attention.js executeAttentionTiered:
  * f16 hot and cold buffers, the cold tier paged through a page table by
  * default, the hot tier a ring): tokens t < cold_lens[b] are f16 rows of a

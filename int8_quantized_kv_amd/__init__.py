@@ -37,7 +37,7 @@ from typing import Optional
 
 __all__ = [
     "DattnError", "DattnParams", "lib", "library_path", "dattn_workspace_size",
-    "dattn_decode_paged", "dattn_decode_tiered_int8", "dattn_decode_tiered_f16", "dattn_decode_ring_f16",
+    "dattn_decode_paged", "dattn_decode_tiered_int8", "dattn_decode_tiered_int8_static", "dattn_decode_tiered_f16", "dattn_decode_ring_f16",
     "dattn_decode_block_sparse", "dattn_append_tiered_int8", "dattn_append_ring_f16",
     "dattn_stream_read", "dattn_last_error", "dattn_version",
     "KIND_PAGED", "KIND_TIERED_INT8", "KIND_BLOCK_SPARSE", "KIND_TIERED_F16", "KIND_RING_F16",
@@ -99,6 +99,7 @@ def lib():
         L.dattn_workspace_size.argtypes = [PP, i32, i32, ctypes.POINTER(sz)]
         L.dattn_decode_paged.argtypes = [PP, P, P, P, i32, P, P, P, P, P, P, sz, P]
         L.dattn_decode_tiered_int8.argtypes = [PP, P, P, P, i32, P, P, P, P, P, P, P, P, P, P, P, sz, P]
+        L.dattn_decode_tiered_int8_static.argtypes = [PP, P, P, P, i32, P, P, P, P, P, P, P, P, P, P, P]
         L.dattn_decode_tiered_f16.argtypes = [PP, P, P, P, i32, P, P, P, P, P, P, P, P, P, sz, P]
         L.dattn_decode_ring_f16.argtypes = [PP, P, P, P, P, P, P, P, P, sz, P]
         L.dattn_decode_block_sparse.argtypes = [PP, P, P, P, P, P, P, i32, i32, P, i32, P, i32, P, P, P, sz, P]
@@ -106,6 +107,7 @@ def lib():
         L.dattn_append_ring_f16.argtypes = [PP, P, P, P, P, P, P]
         L.dattn_stream_read.argtypes = [P, sz, P, P]
         for f in (L.dattn_workspace_size, L.dattn_decode_paged, L.dattn_decode_tiered_int8,
+                  L.dattn_decode_tiered_int8_static,
                   L.dattn_decode_tiered_f16, L.dattn_decode_ring_f16, L.dattn_decode_block_sparse,
                   L.dattn_append_tiered_int8, L.dattn_append_ring_f16, L.dattn_stream_read):
             f.restype = ctypes.c_int
@@ -212,7 +214,7 @@ def _outputs(q, out, lse, want_lse, workspace, ws_bytes, out_dtype=None, want_ou
         _need(lse, "lse", (torch.float32,), len(lshape), q.device)
         if tuple(lse.shape) != lshape:
             raise ValueError(f"lse must have shape {lshape}")
-    if workspace is None:
+    if workspace is None and ws_bytes is not None:   # ws_bytes None: the call takes no workspace
         workspace = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device=q.device)
     return out, lse, workspace
 
@@ -309,6 +311,50 @@ def dattn_decode_tiered_int8(q, k_hot, v_hot, k_cold, v_cold, k_scale, v_scale, 
                                           _ptr(cold_block_table), _ptr(seq_lens), _ptr(cold_lens), _ptr(q_pos),
                                           _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
                                           _stream(stream)))
+    return out, lse
+
+
+def dattn_decode_tiered_int8_static(q, k_hot, v_hot, k_cold, v_cold, k_scale, v_scale, cold_block_table, seq_lens,
+                                    cold_lens, *, q_pos=None, scale: float = 0.0, causal: bool = True,
+                                    sliding_window: int = 0, softcap: float = 0.0,
+                                    max_seq_len: Optional[int] = None, split_tokens: int = 0, out=None, lse=None,
+                                    want_lse: bool = True, stream=None, phases: int = PHASE_ALL, out_dtype=None,
+                                    want_out: bool = True):
+    """dattn_decode_tiered_int8 with the split partials in the library's static
+    device scratch (32 MiB per device) instead of a workspace: for callers that
+    cannot allocate device memory.  Calls that overlap on one device race; out
+    and lse are allocated here only when the caller does not pass them."""
+    torch = _torch()
+    dev = q.device
+    _need(q, "q", (torch.float32, torch.float16), q.dim() if q.dim() in (3, 4) else 3, dev)
+    _need(k_hot, "k_hot", (torch.float16,), 4, dev)
+    _need(v_hot, "v_hot", (torch.float16,), 4, dev)
+    _need(k_cold, "k_cold", (torch.int32, torch.uint32), 4, dev)
+    _need(v_cold, "v_cold", (k_cold.dtype,), 4, dev)
+    _need(k_scale, "k_scale", (torch.float16,), 3, dev)
+    _need(v_scale, "v_scale", (torch.float16,), 3, dev)
+    _need(cold_block_table, "cold_block_table", (torch.int32,), 2, dev)
+    _need(seq_lens, "seq_lens", (torch.int32,), 1, dev)
+    _need(cold_lens, "cold_lens", (torch.int32,), 1, dev)
+    if q_pos is not None:
+        _need(q_pos, "q_pos", (torch.int32,), 1, dev)
+    B, D = q.shape[0], q.shape[-1]
+    _, hot_window, Hkv, Dh = k_hot.shape
+    NB, bs, Hkv2, W4 = k_cold.shape
+    if Dh != D or Hkv2 != Hkv or W4 * 4 != D or tuple(v_hot.shape) != tuple(k_hot.shape) \
+            or tuple(v_cold.shape) != tuple(k_cold.shape) or tuple(k_scale.shape) != (NB, bs, Hkv) \
+            or tuple(v_scale.shape) != (NB, bs, Hkv) or k_hot.shape[0] != B:
+        raise ValueError("tiered cache tensors disagree on shape")
+    _rows(B, cold_block_table=cold_block_table, seq_lens=seq_lens, cold_lens=cold_lens, q_pos=q_pos)
+    max_seq_len = _max_len(max_seq_len)
+    _on_gpu(q, "q")
+    p = _params(q, Hkv, D, bs, cold_block_table.shape[1], NB, max_seq_len, scale, causal, sliding_window, softcap,
+                split_tokens, phases, out_dtype)
+    out, lse, _ = _outputs(q, out, lse, want_lse, None, None, out_dtype, want_out)
+    _check(lib().dattn_decode_tiered_int8_static(ctypes.byref(p), _ptr(q), _ptr(k_hot), _ptr(v_hot), hot_window,
+                                                 _ptr(k_cold), _ptr(v_cold), _ptr(k_scale), _ptr(v_scale),
+                                                 _ptr(cold_block_table), _ptr(seq_lens), _ptr(cold_lens),
+                                                 _ptr(q_pos), _ptr(out), _ptr(lse), _stream(stream)))
     return out, lse
 
 

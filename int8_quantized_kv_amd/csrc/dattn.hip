@@ -475,6 +475,38 @@ __global__ __launch_bounds__(1024) void stream_read_kernel(const dattn::u4* __re
   if (x == 0x9E3779B9u) sink[0] = x;
 }
 
+// Scratch of the no-allocation entry point (dattn_decode_tiered_int8_static):
+// the split partials of a call live here instead of in a caller-provided
+// workspace.  Each device holds its own copy from the first use of the
+// library's code object on it until the process ends.  In host code the name
+// below only stands in for the device array: its device address comes from
+// hipGetSymbolAddress, once per device, and that address is what the kernels
+// are given.
+constexpr size_t kStaticScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+std::map<int, void*> g_scratch;   // device -> address of its scratch (under g_mu)
+
+// Device address of the current device's scratch, looked up on the first call
+// on that device with the device current.
+int static_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(DATTN_ERR_LAUNCH, "hipGetDevice failed: %s", hipGetErrorString(e));
+  std::lock_guard<std::mutex> lk(g_mu);
+  auto it = g_scratch.find(dev);
+  if (it == g_scratch.end()) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(DATTN_ERR_LAUNCH, "hipGetSymbolAddress of the static scratch failed on device %d: %s", dev,
+                  hipGetErrorString(e));
+    it = g_scratch.emplace(dev, p).first;
+  }
+  *ptr = it->second;
+  return DATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -589,6 +621,31 @@ int dattn_decode_tiered_int8(const dattn_params* p, const void* q, const uint16_
   return launch(dattn::split_kernel(dattn::kTiered, p->head_dim, cap, pl.G, contig),
                 dattn::split_kernel(dattn::kBalTiered, p->head_dim, cap, pl.G, contig), p, pl, a, out, lse,
                 (hipStream_t)stream);
+}
+
+int dattn_decode_tiered_int8_static(const dattn_params* p, const void* q, const uint16_t* k_hot,
+                                    const uint16_t* v_hot, int32_t hot_window, const uint32_t* k_cold,
+                                    const uint32_t* v_cold, const uint16_t* k_scale, const uint16_t* v_scale,
+                                    const int32_t* cold_block_table, const int32_t* seq_lens,
+                                    const int32_t* cold_lens, const int32_t* q_pos, void* out, float* lse,
+                                    void* stream) {
+  g_err.clear();
+  // the sizes are checked on the host before the scratch is looked up
+  Plan pl;
+  int rc = make_plan(p, DATTN_KIND_TIERED_INT8, 0, pl);
+  if (rc) return rc;
+  if (pl.workspace > kStaticScratchBytes)
+    return fail(DATTN_ERR_UNSUPPORTED,
+                "this call needs %zu bytes of scratch; the static scratch of dattn_decode_tiered_int8_static holds "
+                "%zu (use dattn_decode_tiered_int8 with a workspace)",
+                pl.workspace, kStaticScratchBytes);
+  if (hot_window < 1) return fail(DATTN_ERR_INVALID, "hot_window must be >= 1 (got %d)", hot_window);
+  if (p->num_seqs == 0) return DATTN_OK;
+  void* ws = nullptr;
+  if ((rc = static_scratch(&ws))) return rc;
+  return dattn_decode_tiered_int8(p, q, k_hot, v_hot, hot_window, k_cold, v_cold, k_scale, v_scale,
+                                  cold_block_table, seq_lens, cold_lens, q_pos, out, lse, ws, kStaticScratchBytes,
+                                  stream);
 }
 
 int dattn_decode_tiered_f16(const dattn_params* p, const void* q, const uint16_t* k_hot, const uint16_t* v_hot,
