@@ -459,6 +459,7 @@ struct StoreF16 {
   static constexpr int RE = D;  // elements per kv-head row
   static constexpr int NT = Lay<D>::NT;
   static constexpr bool kScaled = false;
+  static constexpr bool kPairScales = false;
   using VW = typename WordVec<D / 32>::T;   // D/16 halves of one V row
   struct KFrag {
     u4 r[D / 32];
@@ -492,6 +493,7 @@ struct StoreF16 {
 #pragma unroll
     for (int e = 0; e < 4; ++e) v.r[e] = load_at<VW>(sbase(vt + e * rs), vo);
   }
+  template <int P = 0>
   __device__ __forceinline__ f4 scores(const KFrag& k, const QF16<D>& q) const {
     f4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -508,7 +510,7 @@ struct StoreF16 {
   // With SAN the rows of keys outside the key range (kvalid false: p = 0,
   // contents unknown) are zeroed first, so that no Inf or NaN they may hold
   // reaches the sum.
-  template <bool SAN>
+  template <bool SAN, int P = 0>
   __device__ __forceinline__ void pv(const KFrag&, const VFrag& v_in, const float (&p)[4], const bool (&valid)[4],
                                      f4 (&o)[NT]) const {
     VFrag v = v_in;
@@ -536,6 +538,7 @@ struct StoreF32 {
   static constexpr int RE = D;
   static constexpr int NT = Lay<D>::NT;
   static constexpr bool kScaled = false;
+  static constexpr bool kPairScales = false;
   struct KFrag {
     f4 r[D / 16];
   };
@@ -573,6 +576,7 @@ struct StoreF32 {
 #pragma unroll
       for (int h = 0; h < D / 64; ++h) v.r[e][h] = load_at<f4>(sbase(vt + e * rs), vo, 16 * h);
   }
+  template <int P = 0>
   __device__ __forceinline__ f4 scores(const KFrag& k, const QF32<D>& q) const {
     f4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -586,7 +590,7 @@ struct StoreF32 {
   }
   // One 16x16x4 product per (key e, n-tile t): A = p of key 4*(l/16)+e for
   // head l%16 (k = l/16), B = that key's dim (D/16)*(l%16) + t.
-  template <bool SAN>
+  template <bool SAN, int P = 0>
   __device__ __forceinline__ void pv(const KFrag&, const VFrag& v_in, const float (&p)[4], const bool (&valid)[4],
                                      f4 (&o)[NT]) const {
     VFrag v = v_in;
@@ -605,15 +609,25 @@ struct StoreF32 {
 };
 
 // ---- int8 rows of D/4 words + one f16 scale per (row, kv head)
+//
+// Scales travel in groups: lane r of 16-lane row g holds, for r in [0, 4), the
+// K scale of key 4g + r of a tile A; [4, 8) the V scale of that key; [8, 12)
+// and [12, 16) the same for a tile B.  scores<P> and pv<SAN, P> take tile P's
+// (0: A, 1: B) from lanes 8P + e and 8P + 4 + e of the row with a DPP row
+// broadcast.  Contiguous tiles load the scales of two consecutive tiles with
+// one 2-byte gather (measured: the two gathers per tile the scales used to
+// cost were ~4% of the tiered kernel's time); the gather path loads tile A's
+// K and V scales with one.
 template <int D>
 struct StoreI8 {
   static constexpr int RE = D / 4;
   static constexpr int NT = Lay<D>::NT;
   static constexpr bool kScaled = true;
+  static constexpr bool kPairScales = true;
   using VW = typename WordVec<D / 64>::T;   // D/16 codes of one V row
   struct KFrag {
     u4 r[D / 64];
-    uint16_t ks, vs;   // scales of key 4g + kkey%4 (row-broadcast to the score layout)
+    uint16_t sc;   // this lane's entry of a scale group (above)
   };
   struct VFrag {
     VW r[4];
@@ -629,28 +643,30 @@ struct StoreI8 {
     const uint32_t* kr = kbase + (size_t)rk(tr.krow) * RE;
 #pragma unroll
     for (int c2 = 0; c2 < D / 64; ++c2) k.r[c2] = ntload<u4>(kr + 16 * c2 + 4 * lg.g);
-    k.ks = ntload<uint16_t>(ksc + rk(tr.xrow));
-    k.vs = ntload<uint16_t>(vsc + rk(tr.xrow));
+    k.sc = ntload<uint16_t>(((lg.kkey & 4) ? vsc : ksc) + rk(tr.xrow));   // tile A of a group
 #pragma unroll
     for (int e = 0; e < 4; ++e) v.r[e] = ntload<VW>(vbase + (size_t)rk(tr.srow[e]) * RE + (NT / 4) * lg.kkey);
   }
+  // K and V codes of rows row0 .. row0+15 (the scales come from load_scales)
   __device__ __forceinline__ void load_tile(uint32_t row0, const LaneGeo& lg, KFrag& k, VFrag& v) const {
     const size_t r0 = (size_t)row0 * (uint32_t)Hkv;
     const size_t rs = (size_t)(uint32_t)Hkv * (RE * 4);   // bytes per row of the pool
     const char* kt = (const char*)(kbase + r0 * RE);
     const char* vt = (const char*)(vbase + r0 * RE);
-    const char* kst = (const char*)(ksc + r0);
-    const char* vst = (const char*)(vsc + r0);
     const uint32_t ko = tie(((uint32_t)(lg.kkey * Hkv + kvh) * RE + 4 * lg.g) * 4, kt);
     const uint32_t vo = tie(((uint32_t)(4 * lg.g * Hkv + kvh) * RE + (NT / 4) * lg.kkey) * 4, vt);
-    const uint32_t so = tie((uint32_t)((4 * lg.g + (lg.kkey & 3)) * Hkv + kvh) * 2, kst);
 #pragma unroll
     for (int c2 = 0; c2 < D / 64; ++c2) k.r[c2] = load_at<u4>(kt, ko, 64 * c2);
-    k.ks = load_at<uint16_t>(kst, so);
-    k.vs = load_at<uint16_t>(vst, so);
 #pragma unroll
     for (int e = 0; e < 4; ++e) v.r[e] = load_at<VW>(sbase(vt + e * rs), vo);
   }
+  // The scale group of the 16-row tiles starting at rows rowA and rowB.
+  __device__ __forceinline__ void load_scales(uint32_t rowA, uint32_t rowB, const LaneGeo& lg, KFrag& k) const {
+    const int r = lg.kkey;
+    const size_t row = (size_t)((r & 8) ? rowB : rowA) + 4 * lg.g + (r & 3);
+    k.sc = ntload<uint16_t>(((r & 4) ? vsc : ksc) + row * (uint32_t)Hkv + kvh);
+  }
+  template <int P = 0>
   __device__ __forceinline__ f4 scores(const KFrag& k, const QF16<D>& q) const {
     f4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -662,23 +678,24 @@ struct StoreI8 {
       acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, q.hi[2 * c2 + 1], acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, q.lo[2 * c2 + 1], acc, 0, 0, 0);
     }
-    // key scale of key 4g + e sits in lane e of the row
-    const float s = h2f(k.ks);
-    acc[0] *= row_bcast<0>(s);
-    acc[1] *= row_bcast<1>(s);
-    acc[2] *= row_bcast<2>(s);
-    acc[3] *= row_bcast<3>(s);
+    // key scale of key 4g + e of tile P sits in lane 8P + e of the row
+    const float s = h2f(k.sc);
+    acc[0] *= row_bcast<8 * P + 0>(s);
+    acc[1] *= row_bcast<8 * P + 1>(s);
+    acc[2] *= row_bcast<8 * P + 2>(s);
+    acc[3] *= row_bcast<8 * P + 3>(s);
     return acc;
   }
   // The value scale of each key goes with p (A = p * scale as a bf16 hi/lo
   // pair); B = the lane's four codes of dim (D/16)*(l%16) + t, exact in bf16.
   // With SAN, q of keys outside the key range is set to 0 (their scale may be
   // anything); codes are finite whatever the bytes.
-  template <bool SAN>
+  template <bool SAN, int P = 0>
   __device__ __forceinline__ void pv(const KFrag& k, const VFrag& v, const float (&p)[4], const bool (&valid)[4],
                                      f4 (&o)[NT]) const {
-    const float s = h2f(k.vs);
-    float q[4] = {p[0] * row_bcast<0>(s), p[1] * row_bcast<1>(s), p[2] * row_bcast<2>(s), p[3] * row_bcast<3>(s)};
+    const float s = h2f(k.sc);   // value scale of key 4g + e of tile P: lane 8P + 4 + e of the row
+    float q[4] = {p[0] * row_bcast<8 * P + 4>(s), p[1] * row_bcast<8 * P + 5>(s), p[2] * row_bcast<8 * P + 6>(s),
+                  p[3] * row_bcast<8 * P + 7>(s)};
     if constexpr (SAN) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) q[e] = valid[e] ? q[e] : 0.0f;
@@ -1016,10 +1033,20 @@ __device__ __forceinline__ void run_tiles(const DecodeArgs& a, const Store& st, 
   using VFrag = typename Store::VFrag;
   KFrag kb[NBUF];
   VFrag vb[NBUF];
+  // Scaled rows with two buffers: slot 0 loads the scale group of its tile and
+  // the next one (slot 1's); slot 1 gets a copy when slot 0 is consumed, before
+  // slot 0 is refilled.
+  constexpr bool PAIR = FAST && Store::kPairScales && NBUF == 2;
   auto issue = [&](int t0, auto slotc) {
     constexpr int slot = decltype(slotc)::value;
     if constexpr (FAST) {
-      st.load_tile(map.tile_row0(t0), lg, kb[slot], vb[slot]);
+      const uint32_t row0 = map.tile_row0(t0);
+      st.load_tile(row0, lg, kb[slot], vb[slot]);
+      if constexpr (PAIR) {
+        if constexpr (slot == 0) st.load_scales(row0, map.tile_row0(t0 + kTile), lg, kb[0]);
+      } else if constexpr (Store::kPairScales) {
+        st.load_scales(row0, row0, lg, kb[slot]);
+      }
     } else {
       TileRows tr;
       tr.krow = map.row(t0 + lg.kkey);
@@ -1034,7 +1061,11 @@ __device__ __forceinline__ void run_tiles(const DecodeArgs& a, const Store& st, 
   };
   auto consume = [&](int t0, auto slotc) {
     constexpr int slot = decltype(slotc)::value;
-    const f4 raw = st.scores(kb[slot], qf);
+    constexpr int PS = PAIR ? slot : 0;   // which tile of the scale group
+    const f4 raw = st.template scores<PS>(kb[slot], qf);
+    if constexpr (PAIR) {
+      if constexpr (slot == 0) kb[1].sc = kb[0].sc;
+    }
     bool valid[4], kvalid[4];
     map.tile_valid(t0, lg, valid, kvalid);
     if constexpr (MQ) {
@@ -1046,7 +1077,7 @@ __device__ __forceinline__ void run_tiles(const DecodeArgs& a, const Store& st, 
     }
     float p[4];
     if (on.softmax_tile(a.capl2, raw, valid, p)) on.rescale(lane);
-    st.template pv<FAST>(kb[slot], vb[slot], p, kvalid, on.o);
+    st.template pv<FAST, PS>(kb[slot], vb[slot], p, kvalid, on.o);
   };
 
   if (tfirst >= tend) {
@@ -1157,10 +1188,9 @@ struct Share {
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       v.r[e] = *(const VW*)(buf + 16 * (KCH + pos(4 * lg.g + e, vbyte / 16)) + (vbyte & 15));
-    if constexpr (kScaled) {
+    if constexpr (kScaled) {   // tile A of a scale group: K scales, then V scales at +32 bytes
       const int key = 4 * lg.g + (lg.kkey & 3);
-      k.ks = *(const uint16_t*)(buf + kScaleOff + 2 * key);
-      k.vs = *(const uint16_t*)(buf + kScaleOff + 32 + 2 * key);
+      k.sc = *(const uint16_t*)(buf + kScaleOff + ((lg.kkey & 4) ? 32 : 0) + 2 * key);
     }
   }
 };
