@@ -312,9 +312,9 @@ Balanced plan_balanced(const dattn_params* p, const Plan& pl, const void* fn, si
   if (bl.workers > max_workers_per_group(pl.vheads)) bl.workers = max_workers_per_group(pl.vheads);
   // A worker's piece of one sequence has at most C tiles (every tile costs at
   // least one unit); C <= ceil(N / workers) with N bounded by two units per
-  // tile plus the start-up units of every sequence.
+  // tile plus the start-up and cold-to-hot units of every sequence.
   const int64_t tmax = ((int64_t)p->max_seq_len + 15) / 16 + 1;
-  const int64_t nmax = (int64_t)p->num_seqs * (2 * tmax + dattn::kSeqUnits);
+  const int64_t nmax = (int64_t)p->num_seqs * (2 * tmax + dattn::kSeqUnits + dattn::kTransUnits);
   // A small call gets no more workers than it can feed with kMinWorkerUnits
   // units each (by the bound nmax): a resident round of mostly idle workers
   // costs more than the work itself.

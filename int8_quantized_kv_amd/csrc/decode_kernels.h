@@ -325,6 +325,40 @@ __device__ __forceinline__ void convert_q(const DecodeArgs& a, int lane, const Q
   }
 }
 
+// Q fragments built in the int8 order, moved into the f16 order in registers
+// (the tiered sweep's change from cold to hot keys).  Number the 8-dim pieces
+// p = dim / 8: the int8 order puts p = 8(c/2) + 2g + c%2 in slab c of lane row
+// g, the f16 order p = 4c + g.  Writing g = 2a + b and c = 2x + y, the f16
+// order's (a, b, x, y) holds the int8 order's piece at row 2y + a, slab
+// 2x + b: exchanging the row's low bit with the slab's low bit
+// (v_permlane16_swap between slabs 2x and 2x+1), then the row's high bit with
+// the slab's low bit (v_permlane32_swap) gives it.
+template <int D>
+__device__ __forceinline__ void q_i8_to_f16_order(QF16<D>& qf) {
+  auto swaps = [](h8& lo_slab, h8& hi_slab) {
+    u4 A = __builtin_bit_cast(u4, lo_slab), B = __builtin_bit_cast(u4, hi_slab);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const auto r = __builtin_amdgcn_permlane16_swap(A[k], B[k], false, false);
+      A[k] = r[0];
+      B[k] = r[1];
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const auto r = __builtin_amdgcn_permlane32_swap(A[k], B[k], false, false);
+      A[k] = r[0];
+      B[k] = r[1];
+    }
+    lo_slab = __builtin_bit_cast(h8, A);
+    hi_slab = __builtin_bit_cast(h8, B);
+  };
+#pragma unroll
+  for (int x = 0; x < D / 64; ++x) {
+    swaps(qf.hi[2 * x], qf.hi[2 * x + 1]);
+    swaps(qf.lo[2 * x], qf.lo[2 * x + 1]);
+  }
+}
+
 // f32 MFMA path (16x16x4): slab c of lane l is dim 16*(c/4) + 4*(l/16) + c%4.
 template <int D>
 struct QRaw32 {
@@ -1405,11 +1439,13 @@ __device__ __forceinline__ void tiered_segment(const DecodeArgs& a, int b, int k
   if (hb < te) {
     RingMap map{b, hb, te - 1, a.hw, FM};
     StoreF16<D> st{(const _Float16*)a.k_hot, (const _Float16*)a.v_hot, a.num_kv_heads, kvh};
-    const bool had_cold = !CF16 && tb < ce;   // Q was laid out for int8 keys
+    const bool had_cold = !CF16 && tb < ce;   // Q was converted in the int8 order
     sweep<D, G, CAP, FM, MQ, RBK>(a, st, map, qf,
                              [&](QF16<D>& q) {
-                               if (had_cold) load_q_raw16<D, G, false, MQ>(a, b, kvh, lane, qraw, col0);
-                               convert_q<D, G, MQ>(a, lane, qraw, q, col0);
+                               if (had_cold)
+                                 q_i8_to_f16_order<D>(q);
+                               else
+                                 convert_q<D, G, MQ>(a, lane, qraw, q, col0);
                              },
                              lg, on, hb & ~(kTile - 1), te, lane, qlo, qhi, col0, ring);
   }
@@ -1501,12 +1537,21 @@ __global__ DATTN_BOUNDS(MQ) __attribute__((amdgpu_waves_per_eu(2))) void tiered_
 #define DATTN_SEQ_UNITS 4
 #endif
 constexpr int kSeqUnits = DATTN_SEQ_UNITS;
+// A sequence of the int8 tiered cache whose visible keys reach both tiers
+// also costs kTransUnits between its last cold tile and its first hot tile:
+// the worker that crosses the boundary drains its load pipeline, reloads Q
+// in the f16 dims order and refills the pipeline from the ring.
+#ifndef DATTN_TRANS_UNITS
+#define DATTN_TRANS_UNITS 2
+#endif
+constexpr int kTransUnits = DATTN_TRANS_UNITS;
 
 template <int KIND>
 struct SeqCost {
   int lo, hi, base;   // visible keys [lo, hi]; tile i starts at key base + 16i
   int ntiles, ncold;  // tiles < ncold cost 1 unit, the others 2 (int8 tiered only)
   int head;           // start-up units (0 for a sequence with no visible key)
+  int trans;          // units between the cold and the hot tiles (int8 tiered only)
   __device__ __forceinline__ void init(const DecodeArgs& a, int b) {
     int q;
     visible_range(a, b, lo, hi, q);
@@ -1515,12 +1560,13 @@ struct SeqCost {
     ncold = ntiles;
     if constexpr (KIND == 2 || KIND == 6) ncold = min(ntiles, max(0, (a.cold_lens[b] - base + kTile - 1) / kTile));
     head = ntiles > 0 ? kSeqUnits : 0;
+    trans = (KIND == 2 || KIND == 6) && ncold > 0 && ntiles > ncold ? kTransUnits : 0;
   }
-  __device__ __forceinline__ int units() const { return head + ncold + 2 * (ntiles - ncold); }
+  __device__ __forceinline__ int units() const { return head + ncold + trans + 2 * (ntiles - ncold); }
   // first tile whose first unit is >= u (0 <= u <= units())
   __device__ __forceinline__ int tile_at(int u) const {
     u = max(u - head, 0);
-    return u <= ncold ? u : ncold + (u - ncold + 1) / 2;
+    return u <= ncold ? u : ncold + max(0, u - ncold - trans + 1) / 2;
   }
 };
 
