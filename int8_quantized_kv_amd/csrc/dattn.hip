@@ -322,7 +322,9 @@ Balanced plan_balanced(const dattn_params* p, const Plan& pl, const void* fn, si
   if (feed < bl.workers) bl.workers = (int)(feed > 0 ? feed : 1);
   const int64_t cmax = (nmax + bl.workers - 1) / bl.workers;
   const int64_t entries = pl.no_table ? 0 : cmax * 16 / p->block_size + 2;
-  bl.lds = (size_t)(((p->num_seqs + 4) & ~3) + entries) * sizeof(int32_t);
+  // LDS: the unit prefix P, the per-sequence stash (small batches), the table entries
+  bl.lds = (size_t)(dattn::prefix_stride(p->num_seqs) + 3 * dattn::stash_stride(p->num_seqs) + entries) *
+           sizeof(int32_t);
   bl.on = bl.lds <= kMaxBalancedLds;
   return bl;
 }

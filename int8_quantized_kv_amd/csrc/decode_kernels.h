@@ -1395,11 +1395,11 @@ __device__ __forceinline__ void paged_segment(const DecodeArgs& a, int b, int kv
 // The same for the tiered cache: keys below cold_lens[b] from the paged cold
 // pool (int8 words with f16 scales, or f16 rows when CF16), the rest from the
 // f16 ring.
+// C: cold_lens[b] (0 for the window ring, which has no cold tier).
 template <int D, int G, bool CAP, bool FM, bool CF16, bool MQ = false, int RBK = 1>
-__device__ __forceinline__ void tiered_segment(const DecodeArgs& a, int b, int kvh, int lane, int tb, int te,
+__device__ __forceinline__ void tiered_segment(const DecodeArgs& a, int b, int kvh, int lane, int tb, int te, int C,
                                                int32_t* lds_tbl, const PartialDst& dst, int col0 = 0,
                                                char* ring = nullptr) {
-  const int C = a.cold_lens ? a.cold_lens[b] : 0;   // no cold tier: a window ring
   const int ce = min(te, C);   // cold part [tb, ce)
   const int hb = max(tb, C);   // hot part  [hb, te)
   QRaw16<D> qraw;              // int8 cold keys use the int8 dim map, f16 keys the f16 one
@@ -1435,6 +1435,9 @@ __device__ __forceinline__ void tiered_segment(const DecodeArgs& a, int b, int k
       sweep<D, G, CAP, FM, MQ, RBK>(a, st, map, qf, [&](QF16<D>& q) { convert_q<D, G, MQ>(a, lane, qraw, q, col0); },
                                lg, on, tb & ~(kTile - 1), ce, lane, qlo, qhi, col0, ring);
     }
+  } else {
+    // no cold keys: Q in the f16 order now, so that the raw Q is dead in both sweeps
+    convert_q<D, G, MQ>(a, lane, qraw, qf, col0);
   }
   if (hb < te) {
     RingMap map{b, hb, te - 1, a.hw, FM};
@@ -1442,10 +1445,7 @@ __device__ __forceinline__ void tiered_segment(const DecodeArgs& a, int b, int k
     const bool had_cold = !CF16 && tb < ce;   // Q was converted in the int8 order
     sweep<D, G, CAP, FM, MQ, RBK>(a, st, map, qf,
                              [&](QF16<D>& q) {
-                               if (had_cold)
-                                 q_i8_to_f16_order<D>(q);
-                               else
-                                 convert_q<D, G, MQ>(a, lane, qraw, q, col0);
+                               if (had_cold) q_i8_to_f16_order<D>(q);
                              },
                              lg, on, hb & ~(kTile - 1), te, lane, qlo, qhi, col0, ring);
   }
@@ -1505,7 +1505,7 @@ __global__ DATTN_BOUNDS(MQ) __attribute__((amdgpu_waves_per_eu(2))) void tiered_
   visible_range(a, b, lo, hi, qp);
   const int tb = max(split * a.split_tokens, lo);
   const int te = min((split + 1) * a.split_tokens, hi + 1);
-  tiered_segment<D, G, CAP, FM, CF16, MQ, RBK>(a, b, kvh, lane, tb, te, lds_tbl,
+  tiered_segment<D, G, CAP, FM, CF16, MQ, RBK>(a, b, kvh, lane, tb, te, a.cold_lens ? a.cold_lens[b] : 0, lds_tbl,
                                           split_dst(a, b, kvh, MQ ? a.grp : G, split, D), col0, (char*)lds_all);
 }
 
@@ -1552,13 +1552,21 @@ struct SeqCost {
   int ntiles, ncold;  // tiles < ncold cost 1 unit, the others 2 (int8 tiered only)
   int head;           // start-up units (0 for a sequence with no visible key)
   int trans;          // units between the cold and the hot tiles (int8 tiered only)
+  int cold;           // cold_lens[b] for the tiered kinds (0 without a cold tier), else 0
+  static constexpr bool kTiered = KIND == 2 || KIND == 3 || KIND == 6 || KIND == 7;
   __device__ __forceinline__ void init(const DecodeArgs& a, int b) {
-    int q;
-    visible_range(a, b, lo, hi, q);
+    int q, l, h;
+    visible_range(a, b, l, h, q);
+    init_vals(l, h, kTiered && a.cold_lens ? a.cold_lens[b] : 0);
+  }
+  __device__ __forceinline__ void init_vals(int l, int h, int c) {
+    lo = l;
+    hi = h;
+    cold = c;
     base = lo & ~(kTile - 1);
     ntiles = hi < lo ? 0 : (hi >> 4) - (lo >> 4) + 1;
     ncold = ntiles;
-    if constexpr (KIND == 2 || KIND == 6) ncold = min(ntiles, max(0, (a.cold_lens[b] - base + kTile - 1) / kTile));
+    if constexpr (KIND == 2 || KIND == 6) ncold = min(ntiles, max(0, (cold - base + kTile - 1) / kTile));
     head = ntiles > 0 ? kSeqUnits : 0;
     trans = (KIND == 2 || KIND == 6) && ncold > 0 && ntiles > ncold ? kTransUnits : 0;
   }
@@ -1570,10 +1578,21 @@ struct SeqCost {
   }
 };
 
-// P[0..B] (exclusive prefix of unit counts) into LDS; returns N = P[B].
+// Batches of at most kStashSeqs sequences keep each sequence's visible range
+// and cold length in LDS (three arrays of stash_stride(B) entries after P), so
+// that a worker starting a sequence does not read them from memory again: one
+// dependent round trip less before its first tiles.
+constexpr int kStashSeqs = 256;
+__host__ __device__ constexpr int stash_stride(int B) { return B <= kStashSeqs ? (B + 3) & ~3 : 0; }
+__host__ __device__ constexpr int prefix_stride(int B) { return (B + 4) & ~3; }
+
+// P[0..B] (exclusive prefix of unit counts) into LDS, and the stash when B is
+// small enough; returns N = P[B].
 template <int KIND>
 __device__ __forceinline__ int unit_prefix(const DecodeArgs& a, int32_t* P) {
   const int B = a.num_seqs;
+  const int ss = stash_stride(B);
+  int32_t* stash = P + prefix_stride(B);
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
     int run = 0;
@@ -1584,6 +1603,11 @@ __device__ __forceinline__ int unit_prefix(const DecodeArgs& a, int32_t* P) {
         SeqCost<KIND> sc;
         sc.init(a, b);
         c = sc.units();
+        if (ss) {
+          stash[b] = sc.lo;
+          stash[ss + b] = sc.hi;
+          stash[2 * ss + b] = sc.cold;
+        }
       }
       int x = c;
 #pragma unroll
@@ -1615,7 +1639,9 @@ void balanced_kernel(DecodeArgs a) {
   char* ring = (char*)lds_all;
   const int B = a.num_seqs;
   int32_t* P = lds;
-  int32_t* tbl = lds + ((B + 4) & ~3);
+  const int ss = stash_stride(B);
+  const int32_t* stash = lds + prefix_stride(B);
+  int32_t* tbl = lds + prefix_stride(B) + 3 * ss;
   const int w = blockIdx.x, nw = gridDim.x;
   const int lane = threadIdx.x & 63;
   int kvh, col0;
@@ -1644,14 +1670,17 @@ void balanced_kernel(DecodeArgs a) {
     while (P[b + 1] <= x0) ++b;
     const int seg_end = min(x1, P[b + 1]);
     SeqCost<KIND> sc;
-    sc.init(a, b);
+    if (ss)
+      sc.init_vals(stash[b], stash[ss + b], stash[2 * ss + b]);
+    else
+      sc.init(a, b);
     const int tb = max(sc.lo, sc.base + kTile * sc.tile_at(x0 - P[b]));
     const int te = min(sc.hi + 1, sc.base + kTile * sc.tile_at(seg_end - P[b]));
     const PartialDst dst = slot_dst(a, w + b, kvh, KIND >= 4 ? a.grp : G, D);
     if constexpr (KIND == 2)
-      tiered_segment<D, G, CAP, FM, false>(a, b, kvh, lane, tb, te, tbl, dst);
+      tiered_segment<D, G, CAP, FM, false>(a, b, kvh, lane, tb, te, sc.cold, tbl, dst);
     else if constexpr (KIND == 3)
-      tiered_segment<D, G, CAP, FM, true>(a, b, kvh, lane, tb, te, tbl, dst);
+      tiered_segment<D, G, CAP, FM, true>(a, b, kvh, lane, tb, te, sc.cold, tbl, dst);
     else if constexpr (KIND == 1)
       paged_segment<D, G, CAP, float, FM>(a, b, kvh, lane, tb, te, tbl, dst);
     else if constexpr (KIND == 4)
@@ -1659,9 +1688,9 @@ void balanced_kernel(DecodeArgs a) {
     else if constexpr (KIND == 5)
       paged_segment<D, G, CAP, float, FM, true>(a, b, kvh, lane, tb, te, tbl, dst, col0, ring);
     else if constexpr (KIND == 6)
-      tiered_segment<D, G, CAP, FM, false, true, RBK>(a, b, kvh, lane, tb, te, tbl, dst, col0, ring);
+      tiered_segment<D, G, CAP, FM, false, true, RBK>(a, b, kvh, lane, tb, te, sc.cold, tbl, dst, col0, ring);
     else if constexpr (KIND == 7)
-      tiered_segment<D, G, CAP, FM, true, true, RBK>(a, b, kvh, lane, tb, te, tbl, dst, col0, ring);
+      tiered_segment<D, G, CAP, FM, true, true, RBK>(a, b, kvh, lane, tb, te, sc.cold, tbl, dst, col0, ring);
     else
       paged_segment<D, G, CAP, _Float16, FM>(a, b, kvh, lane, tb, te, tbl, dst);
     x0 = seg_end;
