@@ -343,3 +343,26 @@ def test_nan_in_live_rows_reaches_the_output(split_tokens):
     t.v_scale[ctb[1, 17 // 16], 17 % 16, 0] = np.float16(np.nan)        # cold value scale, seq 1, kv head 0
     t.k_hot[2, 33 % t.hot_window, 1, 64] = np.float16(np.nan)           # hot key, seq 2, kv head 1
     _check_nan(t, split_tokens, "tiered int8 NaN scales and NaN hot key")
+
+
+@pytest.mark.parametrize("Hkv,offset", [(8, 0), (8, 1), (3, 0), (2, 1), (1, 0)])
+def test_int8_scale_gathers(Hkv, offset):
+    """Scale gathers of contiguous int8 tiles with odd and even kv-head counts,
+    and scale arrays that start on or 2 bytes past a 4-byte boundary (offset 1),
+    against the oracle."""
+    import torch
+    c = synth.tiered_case(150 + 2 * Hkv + offset, 3, 4 * Hkv, Hkv, 128, 16, [900, 700, 250], [700, 600, 0], 256,
+                          softcap=30.0)
+    dc = DeviceCase(c)
+    if offset:
+        for name in ("k_scale", "v_scale"):
+            t = getattr(dc, name)
+            buf = torch.empty(t.numel() + 1, dtype=t.dtype, device=t.device)
+            v = buf[1:].view(t.shape)
+            v.copy_(t)
+            assert v.data_ptr() % 4 == 2
+            setattr(dc, name, v)
+    log(f"int8 scale gathers Hkv={Hkv} offset={offset}")
+    og, lg = dc.run_np()
+    ro, rl = oracle_run(c)
+    compare(og, lg, ro, rl, what=f"int8 scale gathers Hkv{Hkv} offset{offset}")
