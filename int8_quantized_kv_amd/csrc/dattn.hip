@@ -620,9 +620,11 @@ int dattn_decode_tiered_int8(const dattn_params* p, const void* q, const uint16_
     return launch(dattn::split_kernel(dattn::kTieredMQ, p->head_dim, cap, 16, contig),
                   dattn::split_kernel(dattn::kBalTieredMQ, p->head_dim, cap, 16, contig), p, pl, a, out, lse,
                   (hipStream_t)stream);
-  return launch(dattn::split_kernel(dattn::kTiered, p->head_dim, cap, pl.G, contig),
-                dattn::split_kernel(dattn::kBalTiered, p->head_dim, cap, pl.G, contig), p, pl, a, out, lse,
-                (hipStream_t)stream);
+  // scales gathered as 4-byte words when every word holding one of them is aligned
+  const bool scw = p->num_kv_heads % 2 == 0 && (uintptr_t)k_scale % 4 == 0 && (uintptr_t)v_scale % 4 == 0;
+  return launch(dattn::split_kernel(scw ? dattn::kTieredW : dattn::kTiered, p->head_dim, cap, pl.G, contig),
+                dattn::split_kernel(scw ? dattn::kBalTieredW : dattn::kBalTiered, p->head_dim, cap, pl.G, contig), p, pl,
+                a, out, lse, (hipStream_t)stream);
 }
 
 int dattn_decode_tiered_int8_static(const dattn_params* p, const void* q, const uint16_t* k_hot,

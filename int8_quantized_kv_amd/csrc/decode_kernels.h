@@ -651,8 +651,12 @@ struct StoreF32 {
 // broadcast.  Contiguous tiles load the scales of two consecutive tiles with
 // one 2-byte gather (measured: the two gathers per tile the scales used to
 // cost were ~4% of the tiered kernel's time); the gather path loads tile A's
-// K and V scales with one.
-template <int D>
+// K and V scales with one.  SCW (the host checks that the kv-head count is
+// even and both scale arrays are 4-byte aligned): each lane gathers the 4-byte
+// word holding its kv head's scale and its neighbour's, and keeps its half by
+// the kv head's parity; measured, 2-byte gathers cost more (tiered split
+// kernel 52.7 against 51.9 us).
+template <int D, bool SCW = false>
 struct StoreI8 {
   static constexpr int RE = D / 4;
   static constexpr int NT = Lay<D>::NT;
@@ -698,7 +702,13 @@ struct StoreI8 {
   __device__ __forceinline__ void load_scales(uint32_t rowA, uint32_t rowB, const LaneGeo& lg, KFrag& k) const {
     const int r = lg.kkey;
     const size_t row = (size_t)((r & 8) ? rowB : rowA) + 4 * lg.g + (r & 3);
-    k.sc = ntload<uint16_t>(((r & 4) ? vsc : ksc) + row * (uint32_t)Hkv + kvh);
+    const uint16_t* rs = ((r & 4) ? vsc : ksc) + row * (uint32_t)Hkv;   // the row's scales
+    if constexpr (SCW) {
+      const uint32_t w = ntload<uint32_t>(rs + (kvh & ~1));
+      k.sc = (uint16_t)(w >> (16 * (kvh & 1)));
+    } else {
+      k.sc = ntload<uint16_t>(rs + kvh);
+    }
   }
   template <int P = 0>
   __device__ __forceinline__ f4 scores(const KFrag& k, const QF16<D>& q) const {
@@ -1159,8 +1169,8 @@ struct ShareGeo<StoreF16<D>> {
   static constexpr int RB = 2 * D;   // bytes per row
   static constexpr bool kScaled = false;
 };
-template <int D>
-struct ShareGeo<StoreI8<D>> {
+template <int D, bool SCW>
+struct ShareGeo<StoreI8<D, SCW>> {
   static constexpr int RB = D;
   static constexpr bool kScaled = true;
 };
@@ -1395,8 +1405,9 @@ __device__ __forceinline__ void paged_segment(const DecodeArgs& a, int b, int kv
 // The same for the tiered cache: keys below cold_lens[b] from the paged cold
 // pool (int8 words with f16 scales, or f16 rows when CF16), the rest from the
 // f16 ring.
-// C: cold_lens[b] (0 for the window ring, which has no cold tier).
-template <int D, int G, bool CAP, bool FM, bool CF16, bool MQ = false, int RBK = 1>
+// C: cold_lens[b] (0 for the window ring, which has no cold tier).  SCW: the
+// int8 scales are gathered as 4-byte words (StoreI8).
+template <int D, int G, bool CAP, bool FM, bool CF16, bool MQ = false, int RBK = 1, bool SCW = false>
 __device__ __forceinline__ void tiered_segment(const DecodeArgs& a, int b, int kvh, int lane, int tb, int te, int C,
                                                int32_t* lds_tbl, const PartialDst& dst, int col0 = 0,
                                                char* ring = nullptr) {
@@ -1431,7 +1442,7 @@ __device__ __forceinline__ void tiered_segment(const DecodeArgs& a, int b, int k
       sweep<D, G, CAP, FM, MQ, RBK>(a, st, map, qf, [&](QF16<D>& q) { convert_q<D, G, MQ>(a, lane, qraw, q, col0); },
                                lg, on, tb & ~(kTile - 1), ce, lane, qlo, qhi, col0, ring);
     } else {
-      StoreI8<D> st{(const uint32_t*)a.k, (const uint32_t*)a.v, a.k_scale, a.v_scale, a.num_kv_heads, kvh};
+      StoreI8<D, SCW> st{(const uint32_t*)a.k, (const uint32_t*)a.v, a.k_scale, a.v_scale, a.num_kv_heads, kvh};
       sweep<D, G, CAP, FM, MQ, RBK>(a, st, map, qf, [&](QF16<D>& q) { convert_q<D, G, MQ>(a, lane, qraw, q, col0); },
                                lg, on, tb & ~(kTile - 1), ce, lane, qlo, qhi, col0, ring);
     }
@@ -1493,7 +1504,7 @@ __global__ DATTN_BOUNDS(MQ) __attribute__((amdgpu_waves_per_eu(2))) void paged_s
                                       split_dst(a, b, kvh, MQ ? a.grp : G, split, D), col0, (char*)lds_all);
 }
 
-template <int D, int G, bool CAP, bool FM, bool CF16, bool MQ = false, int RBK = 1>
+template <int D, int G, bool CAP, bool FM, bool CF16, bool MQ = false, int RBK = 1, bool SCW = false>
 __global__ DATTN_BOUNDS(MQ) __attribute__((amdgpu_waves_per_eu(2))) void tiered_split_kernel(DecodeArgs a) {
   extern __shared__ int32_t lds_all[];
   int32_t* lds_tbl = MQ ? lds_all + a.tile_lds / 4 : lds_all;
@@ -1505,7 +1516,7 @@ __global__ DATTN_BOUNDS(MQ) __attribute__((amdgpu_waves_per_eu(2))) void tiered_
   visible_range(a, b, lo, hi, qp);
   const int tb = max(split * a.split_tokens, lo);
   const int te = min((split + 1) * a.split_tokens, hi + 1);
-  tiered_segment<D, G, CAP, FM, CF16, MQ, RBK>(a, b, kvh, lane, tb, te, a.cold_lens ? a.cold_lens[b] : 0, lds_tbl,
+  tiered_segment<D, G, CAP, FM, CF16, MQ, RBK, SCW>(a, b, kvh, lane, tb, te, a.cold_lens ? a.cold_lens[b] : 0, lds_tbl,
                                           split_dst(a, b, kvh, MQ ? a.grp : G, split, D), col0, (char*)lds_all);
 }
 
@@ -1546,6 +1557,11 @@ constexpr int kSeqUnits = DATTN_SEQ_UNITS;
 #endif
 constexpr int kTransUnits = DATTN_TRANS_UNITS;
 
+// KIND 2 and 8: tiered int8 (8 gathers the scales as words); 6: the same with
+// several queries per sequence.
+constexpr bool kind_i8(int K) { return K == 2 || K == 6 || K == 8; }
+constexpr bool kind_mq(int K) { return K >= 4 && K <= 7; }
+
 template <int KIND>
 struct SeqCost {
   int lo, hi, base;   // visible keys [lo, hi]; tile i starts at key base + 16i
@@ -1553,7 +1569,7 @@ struct SeqCost {
   int head;           // start-up units (0 for a sequence with no visible key)
   int trans;          // units between the cold and the hot tiles (int8 tiered only)
   int cold;           // cold_lens[b] for the tiered kinds (0 without a cold tier), else 0
-  static constexpr bool kTiered = KIND == 2 || KIND == 3 || KIND == 6 || KIND == 7;
+  static constexpr bool kTiered = kind_i8(KIND) || KIND == 3 || KIND == 7;
   __device__ __forceinline__ void init(const DecodeArgs& a, int b) {
     int q, l, h;
     visible_range(a, b, l, h, q);
@@ -1566,9 +1582,9 @@ struct SeqCost {
     base = lo & ~(kTile - 1);
     ntiles = hi < lo ? 0 : (hi >> 4) - (lo >> 4) + 1;
     ncold = ntiles;
-    if constexpr (KIND == 2 || KIND == 6) ncold = min(ntiles, max(0, (cold - base + kTile - 1) / kTile));
+    if constexpr (kind_i8(KIND)) ncold = min(ntiles, max(0, (cold - base + kTile - 1) / kTile));
     head = ntiles > 0 ? kSeqUnits : 0;
-    trans = (KIND == 2 || KIND == 6) && ncold > 0 && ntiles > ncold ? kTransUnits : 0;
+    trans = kind_i8(KIND) && ncold > 0 && ntiles > ncold ? kTransUnits : 0;
   }
   __device__ __forceinline__ int units() const { return head + ncold + trans + 2 * (ntiles - ncold); }
   // first tile whose first unit is >= u (0 <= u <= units())
@@ -1632,10 +1648,10 @@ __device__ __forceinline__ int unit_prefix(const DecodeArgs& a, int32_t* P) {
 // and a third tile of loads in flight per wave are both slower -- about
 // 32 KiB of loads in flight per SIMD is what HBM rewards here.
 template <int D, int G, bool CAP, int KIND, bool FM, int RBK = 1>
-__global__ DATTN_BOUNDS(KIND >= 4) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ DATTN_BOUNDS(kind_mq(KIND)) __attribute__((amdgpu_waves_per_eu(2)))
 void balanced_kernel(DecodeArgs a) {
   extern __shared__ int32_t lds_all[];
-  int32_t* lds = KIND >= 4 ? lds_all + a.tile_lds / 4 : lds_all;
+  int32_t* lds = kind_mq(KIND) ? lds_all + a.tile_lds / 4 : lds_all;
   char* ring = (char*)lds_all;
   const int B = a.num_seqs;
   int32_t* P = lds;
@@ -1645,7 +1661,7 @@ void balanced_kernel(DecodeArgs a) {
   const int w = blockIdx.x, nw = gridDim.x;
   const int lane = threadIdx.x & 63;
   int kvh, col0;
-  wave_head<(KIND >= 4)>(a, kvh, col0);
+  wave_head<kind_mq(KIND)>(a, kvh, col0);
   const int N = unit_prefix<KIND>(a, P);
   const int C = (N + nw - 1) / nw;
   if (w == 0 && blockIdx.z == 0) {
@@ -1676,9 +1692,11 @@ void balanced_kernel(DecodeArgs a) {
       sc.init(a, b);
     const int tb = max(sc.lo, sc.base + kTile * sc.tile_at(x0 - P[b]));
     const int te = min(sc.hi + 1, sc.base + kTile * sc.tile_at(seg_end - P[b]));
-    const PartialDst dst = slot_dst(a, w + b, kvh, KIND >= 4 ? a.grp : G, D);
+    const PartialDst dst = slot_dst(a, w + b, kvh, kind_mq(KIND) ? a.grp : G, D);
     if constexpr (KIND == 2)
       tiered_segment<D, G, CAP, FM, false>(a, b, kvh, lane, tb, te, sc.cold, tbl, dst);
+    else if constexpr (KIND == 8)
+      tiered_segment<D, G, CAP, FM, false, false, 1, true>(a, b, kvh, lane, tb, te, sc.cold, tbl, dst);
     else if constexpr (KIND == 3)
       tiered_segment<D, G, CAP, FM, true>(a, b, kvh, lane, tb, te, sc.cold, tbl, dst);
     else if constexpr (KIND == 1)

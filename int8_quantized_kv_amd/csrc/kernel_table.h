@@ -25,6 +25,8 @@ enum SplitKind : int {
   kBalTieredMQ,    // balanced schedule, the same
   kBalTieredF16MQ,
   kSparseMQ,       // static splits over the CSR union, several queries per sequence
+  kTieredW,        // static splits, tiered int8, scales gathered as 4-byte words (even Hkv, aligned scales)
+  kBalTieredW,     // balanced schedule, the same
 };
 
 // Split kernel for (kind, GQA group G in {1, 2, 4, 8}, contiguous 16-row

@@ -40,6 +40,8 @@ void* instance(int kind) {
       case kBalF32: return (void*)&balanced_kernel<D, G, CAP, 1, FM>;
       case kBalTiered: return (void*)&balanced_kernel<D, G, CAP, 2, FM>;
       case kBalTieredF16: return (void*)&balanced_kernel<D, G, CAP, 3, FM>;
+      case kTieredW: return (void*)&tiered_split_kernel<D, G, CAP, FM, false, false, 1, true>;
+      case kBalTieredW: return (void*)&balanced_kernel<D, G, CAP, 8, FM>;
       default: return nullptr;
     }
   }
