@@ -1,7 +1,8 @@
 """GPU parity at the edges of the plans: batches larger than the balanced
 schedule takes (static splits), the largest GQA group and head counts, one
-kv head, head_dim 64 on every cache, and sequences of one key -- checked
-against the oracle on sampled (sequence, head) pairs."""
+kv head, head_dim 64 on every cache, sequences of one key, and more tiered
+sequences than the balanced kernel keeps in LDS -- checked against the oracle
+on sampled (sequence, head) pairs, or on every row where that is cheap."""
 import numpy as np
 import pytest
 
@@ -92,6 +93,23 @@ def test_head_dim_64(kind):
     else:
         c = synth.sparse_case(717, 2, 32, 8, 64, 64, 64, 4, [2048, 700])
     _sampled(c, f"{kind} D64")
+
+
+@pytest.mark.parametrize("window", [0, 200])
+def test_tiered_int8_beyond_the_per_sequence_stash(window):
+    # more sequences than the balanced kernel keeps in LDS (256), so each
+    # worker reads a sequence's range and cold length from memory when it
+    # starts it; lengths up to 700 with a 128-token ring make most sweeps cross
+    # from the int8 tier into the ring (the transition units of the schedule)
+    rng = np.random.default_rng(730 + window)
+    B = 300
+    lens = rng.integers(1, 701, size=B)
+    cold = np.maximum(0, lens - rng.integers(0, 129, size=B))
+    c = synth.tiered_case(730 + window, B, 32, 8, 128, 16, lens, cold, 128, softcap=30.0, window=window)
+    log(f"edge tiered int8 B{B} beyond the stash, window {window}")
+    og, lg = DeviceCase(c).run_np()
+    ro, rl = oracle_run(c)
+    compare(og, lg, ro, rl, what=f"tiered int8 B{B} window {window}, every row")
 
 
 def test_single_key_sequences_everywhere():
