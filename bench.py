@@ -673,8 +673,9 @@ def main():
         out["parity"] = head["parity"]
     if not args.only:
         out["copy_reference_gbs"] = copy_reference()
-        # the streaming ceiling at the headline's bytes per launch, and at 300 MB (the other lines' size)
-        ceiling = read_reference(nbytes=kvb // 16 * 16, copies=max(2, int(math.ceil(MALL_BYTES / kvb))))
+        # the streaming ceiling at the headline's bytes per launch (at least 300 MB), and at 300 MB
+        nb = max(kvb, 300 << 20) // 16 * 16
+        ceiling = read_reference(nbytes=nb, copies=max(2, int(math.ceil(MALL_BYTES / nb))))
         out["roofline"]["measured_read_ceiling_gbs"] = ceiling
         out["roofline"]["frac_of_measured_ceiling"] = round(achieved / ceiling, 4)
         out["roofline"]["measured_read_ceiling_300mb_gbs"] = read_reference()
