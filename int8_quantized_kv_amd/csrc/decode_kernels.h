@@ -494,6 +494,7 @@ struct StoreF16 {
   static constexpr int NT = Lay<D>::NT;
   static constexpr bool kScaled = false;
   static constexpr bool kPairScales = false;
+  static constexpr bool kSanRows = true;   // sanitize() zeroes V rows (pv<SAN> would on every tile)
   using VW = typename WordVec<D / 32>::T;   // D/16 halves of one V row
   struct KFrag {
     u4 r[D / 32];
@@ -544,14 +545,16 @@ struct StoreF16 {
   // With SAN the rows of keys outside the key range (kvalid false: p = 0,
   // contents unknown) are zeroed first, so that no Inf or NaN they may hold
   // reaches the sum.
+  // V rows of keys outside the key range (kvalid false) zeroed.
+  __device__ __forceinline__ void sanitize(VFrag& v, const bool (&kvalid)[4]) const {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v.r[e] = kvalid[e] ? v.r[e] : VW{};
+  }
   template <bool SAN, int P = 0>
   __device__ __forceinline__ void pv(const KFrag&, const VFrag& v_in, const float (&p)[4], const bool (&valid)[4],
                                      f4 (&o)[NT]) const {
     VFrag v = v_in;
-    if constexpr (SAN) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v.r[e] = valid[e] ? v.r[e] : VW{};
-    }
+    if constexpr (SAN) sanitize(v, valid);
     h4 hi, lo;
     split_f16(p, hi, lo);
 #pragma unroll
@@ -573,6 +576,7 @@ struct StoreF32 {
   static constexpr int NT = Lay<D>::NT;
   static constexpr bool kScaled = false;
   static constexpr bool kPairScales = false;
+  static constexpr bool kSanRows = true;
   struct KFrag {
     f4 r[D / 16];
   };
@@ -624,16 +628,17 @@ struct StoreF32 {
   }
   // One 16x16x4 product per (key e, n-tile t): A = p of key 4*(l/16)+e for
   // head l%16 (k = l/16), B = that key's dim (D/16)*(l%16) + t.
+  __device__ __forceinline__ void sanitize(VFrag& v, const bool (&kvalid)[4]) const {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+      for (int h = 0; h < D / 64; ++h) v.r[e][h] = kvalid[e] ? v.r[e][h] : f4{0.f, 0.f, 0.f, 0.f};
+  }
   template <bool SAN, int P = 0>
   __device__ __forceinline__ void pv(const KFrag&, const VFrag& v_in, const float (&p)[4], const bool (&valid)[4],
                                      f4 (&o)[NT]) const {
     VFrag v = v_in;
-    if constexpr (SAN) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-#pragma unroll
-        for (int h = 0; h < D / 64; ++h) v.r[e][h] = valid[e] ? v.r[e][h] : f4{0.f, 0.f, 0.f, 0.f};
-    }
+    if constexpr (SAN) sanitize(v, valid);
 #pragma unroll
     for (int e = 0; e < 4; ++e)
 #pragma unroll
@@ -662,6 +667,7 @@ struct StoreI8 {
   static constexpr int NT = Lay<D>::NT;
   static constexpr bool kScaled = true;
   static constexpr bool kPairScales = true;
+  static constexpr bool kSanRows = false;   // codes are finite; pv<SAN> zeroes the scaled p instead
   using VW = typename WordVec<D / 64>::T;   // D/16 codes of one V row
   struct KFrag {
     u4 r[D / 64];
@@ -786,6 +792,8 @@ struct PagedMap {
     return phys * bs.d + ((uint32_t)t0 - blk * bs.d);
   }
   __device__ __forceinline__ bool visible(int t, int) const { return t >= lo && t <= hi; }
+  // the tile of keys [t0, t0 + 16) holds keys outside [lo, hi] (wave-uniform)
+  __device__ __forceinline__ bool tile_edge(int t0) const { return t0 < lo || t0 + (kTile - 1) > hi; }
   // valid: (key t0 + 4g + e, head lane%16) takes part; kvalid: that key is
   // inside [lo, hi], so its row holds cache data (one unsigned compare each)
   __device__ __forceinline__ void tile_valid(int t0, const LaneGeo& lg, bool (&valid)[4], bool (&kvalid)[4]) const {
@@ -809,6 +817,7 @@ struct RingMap {
     return (uint32_t)b * hw.d + fmod_((uint32_t)t0, hw);
   }
   __device__ __forceinline__ bool visible(int t, int) const { return t >= lo && t <= hi; }
+  __device__ __forceinline__ bool tile_edge(int t0) const { return t0 < lo || t0 + (kTile - 1) > hi; }
   __device__ __forceinline__ void tile_valid(int t0, const LaneGeo& lg, bool (&valid)[4], bool (&kvalid)[4]) const {
     const uint32_t rel = (uint32_t)(t0 + 4 * lg.g - lo), span = (uint32_t)(hi - lo);
 #pragma unroll
@@ -861,6 +870,7 @@ struct SparseMap {
     resolve(slot, t, mk);
     return ((mk >> head) & 1u) && t >= lo && t <= hi;
   }
+  __device__ __forceinline__ bool tile_edge(int) const { return true; }   // every tile is sanitized
   // A contiguous tile lies in one union entry: resolve it once.  valid adds
   // the head mask (lane%16 is the head in the score layout); kvalid is the
   // key range alone (slots past the end have no key: never valid).
@@ -1052,6 +1062,28 @@ __device__ __forceinline__ void write_empty_mq(const PartialDst& dst, int lane, 
   }
 }
 
+// Several queries per sequence over a paged or ring map: the keys a lane's
+// score column sees in a sweep over [lo, hi] are [max(lo, qlo), min(hi, qhi)],
+// so key t0 + 4g + e takes part iff (unsigned)(t0 + off + e) <= span, one
+// compare per key (off = 4g - the range's first key; an empty range never
+// matches, as t0 + 2^30 + e stays far from 0).
+template <class M>
+constexpr bool kRangeMap = std::is_same_v<M, PagedMap> || std::is_same_v<M, RingMap>;
+struct ColRange {
+  int off;
+  uint32_t span;
+  __device__ __forceinline__ void init(int lo, int hi, int qlo, int qhi, int g) {
+    const int vlo = max(lo, qlo), vhi = min(hi, qhi);
+    off = vhi >= vlo ? 4 * g - vlo : (1 << 30);
+    span = vhi >= vlo ? (uint32_t)(vhi - vlo) : 0u;
+  }
+  __device__ __forceinline__ void valid(int t0, bool (&v)[4]) const {
+    const uint32_t x = (uint32_t)(t0 + off);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = x + (uint32_t)e <= span;
+  }
+};
+
 // ------------------------------------------------------------ tile engine
 //
 // Sweep positions [tfirst, tend) in tiles of 16 keeping NBUF-1 tiles of loads
@@ -1081,6 +1113,8 @@ __device__ __forceinline__ void run_tiles(const DecodeArgs& a, const Store& st, 
   // the next one (slot 1's); slot 1 gets a copy when slot 0 is consumed, before
   // slot 0 is refilled.
   constexpr bool PAIR = FAST && Store::kPairScales && NBUF == 2;
+  ColRange cr;
+  if constexpr (MQ && kRangeMap<Map>) cr.init(map.lo, map.hi, qlo, qhi, lg.g);
   auto issue = [&](int t0, auto slotc) {
     constexpr int slot = decltype(slotc)::value;
     if constexpr (FAST) {
@@ -1112,7 +1146,9 @@ __device__ __forceinline__ void run_tiles(const DecodeArgs& a, const Store& st, 
     }
     bool valid[4], kvalid[4];
     map.tile_valid(t0, lg, valid, kvalid);
-    if constexpr (MQ) {
+    if constexpr (MQ && kRangeMap<Map>) {
+      cr.valid(t0, valid);
+    } else if constexpr (MQ) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int t = t0 + 4 * lg.g + e;
@@ -1121,7 +1157,13 @@ __device__ __forceinline__ void run_tiles(const DecodeArgs& a, const Store& st, 
     }
     float p[4];
     if (on.softmax_tile(a.capl2, raw, valid, p)) on.rescale(lane);
-    st.template pv<FAST, PS>(kb[slot], vb[slot], p, kvalid, on.o);
+    if constexpr (FAST && Store::kSanRows) {
+      // only a tile at the sweep's edge reads rows outside the key range
+      if (map.tile_edge(t0)) st.sanitize(vb[slot], kvalid);
+      st.template pv<false, PS>(kb[slot], vb[slot], p, kvalid, on.o);
+    } else {
+      st.template pv<FAST, PS>(kb[slot], vb[slot], p, kvalid, on.o);
+    }
   };
 
   if (tfirst >= tend) {
@@ -1250,6 +1292,8 @@ __device__ __forceinline__ void run_tiles_shared(const DecodeArgs& a, const Stor
   using SH = Share<Store, RBK>;
   constexpr int NS = SH::NS;
   typename SH::Regs sh[NS];
+  ColRange cr;
+  if constexpr (kRangeMap<Map>) cr.init(map.lo, map.hi, qlo, qhi, lg.g);
   auto issue = [&](int t0, auto slotc) { SH::load(st, map.tile_row0(t0), wv, lane, sh[decltype(slotc)::value]); };
   auto consume = [&](int t0, int i, auto slotc) {
     constexpr int slot = decltype(slotc)::value;
@@ -1263,14 +1307,23 @@ __device__ __forceinline__ void run_tiles_shared(const DecodeArgs& a, const Stor
     const f4 raw = st.scores(kf, qf);
     bool valid[4], kvalid[4];
     map.tile_valid(t0, lg, valid, kvalid);
+    if constexpr (kRangeMap<Map>) {
+      cr.valid(t0, valid);
+    } else {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int t = t0 + 4 * lg.g + e;
-      valid[e] = valid[e] && t >= qlo && t <= qhi;
+      for (int e = 0; e < 4; ++e) {
+        const int t = t0 + 4 * lg.g + e;
+        valid[e] = valid[e] && t >= qlo && t <= qhi;
+      }
     }
     float p[4];
     if (on.softmax_tile(a.capl2, raw, valid, p)) on.rescale(lane);
-    st.template pv<true>(kf, vf, p, kvalid, on.o);
+    if constexpr (Store::kSanRows) {
+      if (map.tile_edge(t0)) st.sanitize(vf, kvalid);
+      st.template pv<false>(kf, vf, p, kvalid, on.o);
+    } else {
+      st.template pv<true>(kf, vf, p, kvalid, on.o);
+    }
   };
 
   if (tfirst >= tend) {
