@@ -3,6 +3,8 @@ what the reading and the mathematics fix, independently of the oracle's code:
 numpy's own f32 -> f16 rounding, a vectorised numpy restatement of the
 quantiser, its error bound, and the cache that a history of appends must leave
 (built directly from the token history)."""
+import os
+
 import numpy as np
 import pytest
 
@@ -54,6 +56,33 @@ def test_quantize_row_matches_the_reading(D):
         words, s = oracle.quantize_row(x[r].view(np.uint16))
         assert s == int(scales[r].view(np.uint16)), r
         assert np.array_equal(words, pack_bytes(codes[r])), r
+
+
+def _golden_rows():
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "quantizer_rows.txt")
+    rows = []
+    for line in open(path):
+        if line.startswith("#") or not line.strip():
+            continue
+        name, sbits, xs, cs = (f.strip() for f in line.split("|"))
+        rows.append((name, int(sbits, 16), [float(v) for v in xs.split()], [int(v) for v in cs.split()]))
+    return rows
+
+
+@pytest.mark.parametrize("row", _golden_rows(), ids=lambda r: r[0])
+def test_quantize_row_hand_worked_ties_and_clip(row):
+    """Rows worked by hand (tests/golden/quantizer_rows.txt): ties to even at
+    two scales, a subnormal f16 scale whose codes clip at 127, a zero row."""
+    name, sbits, xs, codes = row
+    x = np.zeros(64, np.float16)
+    x[:len(xs)] = np.array(xs, np.float32).astype(np.float16)
+    assert np.array_equal(x[:len(xs)].astype(np.float64), np.array(xs)), "inputs must be exact f16 values"
+    words, s = oracle.quantize_row(x.view(np.uint16))
+    assert s == sbits, (name, hex(s))
+    want = np.zeros(64, np.int64)
+    want[:len(codes)] = codes
+    got = [oracle.int8_lane(int(words[d // 4]), d % 4) for d in range(64)]
+    assert got == want.tolist(), name
 
 
 def test_quantize_row_error_bound_and_full_range():
