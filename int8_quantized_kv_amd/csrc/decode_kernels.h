@@ -550,21 +550,33 @@ struct StoreF16 {
 #pragma unroll
     for (int e = 0; e < 4; ++e) v.r[e] = kvalid[e] ? v.r[e] : VW{};
   }
-  template <bool SAN, int P = 0>
+  // W32 (multi-query sweeps, where the matrix cores are busy): one 16x16x32
+  // product per n-tile instead of two 16x16x16 ones -- k slots 8g + [0, 4)
+  // carry p_hi and 8g + [4, 8) p_lo, each against the same four V values, and
+  // on gfx950 the K = 32 product takes the cycles of a K = 16 one.  Measured:
+  // sixteen queries per sequence 79.6 -> 77.5 us; the one-query sweeps, which
+  // wait on memory, gain nothing (and the tiered cache lost 2% at W = 4096).
+  template <bool SAN, int P = 0, bool W32 = false>
   __device__ __forceinline__ void pv(const KFrag&, const VFrag& v_in, const float (&p)[4], const bool (&valid)[4],
                                      f4 (&o)[NT]) const {
     VFrag v = v_in;
     if constexpr (SAN) sanitize(v, valid);
     h4 hi, lo;
     split_f16(p, hi, lo);
+    const h8 a = __builtin_shufflevector(hi, lo, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;
       const uint32_t b01 = __builtin_amdgcn_perm(word_at(v.r[1], t >> 1), word_at(v.r[0], t >> 1), sel);
       const uint32_t b23 = __builtin_amdgcn_perm(word_at(v.r[3], t >> 1), word_at(v.r[2], t >> 1), sel);
       const h4 b = __builtin_bit_cast(h4, u2v{b01, b23});
-      o[t] = __builtin_amdgcn_mfma_f32_16x16x16f16(hi, b, o[t], 0, 0, 0);
-      o[t] = __builtin_amdgcn_mfma_f32_16x16x16f16(lo, b, o[t], 0, 0, 0);
+      if constexpr (W32) {
+        o[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, __builtin_shufflevector(b, b, 0, 1, 2, 3, 0, 1, 2, 3), o[t],
+                                                      0, 0, 0);
+      } else {
+        o[t] = __builtin_amdgcn_mfma_f32_16x16x16f16(hi, b, o[t], 0, 0, 0);
+        o[t] = __builtin_amdgcn_mfma_f32_16x16x16f16(lo, b, o[t], 0, 0, 0);
+      }
     }
   }
 };
@@ -634,7 +646,7 @@ struct StoreF32 {
 #pragma unroll
       for (int h = 0; h < D / 64; ++h) v.r[e][h] = kvalid[e] ? v.r[e][h] : f4{0.f, 0.f, 0.f, 0.f};
   }
-  template <bool SAN, int P = 0>
+  template <bool SAN, int P = 0, bool W32 = false>
   __device__ __forceinline__ void pv(const KFrag&, const VFrag& v_in, const float (&p)[4], const bool (&valid)[4],
                                      f4 (&o)[NT]) const {
     VFrag v = v_in;
@@ -740,7 +752,7 @@ struct StoreI8 {
   // pair); B = the lane's four codes of dim (D/16)*(l%16) + t, exact in bf16.
   // With SAN, q of keys outside the key range is set to 0 (their scale may be
   // anything); codes are finite whatever the bytes.
-  template <bool SAN, int P = 0>
+  template <bool SAN, int P = 0, bool W32 = false>
   __device__ __forceinline__ void pv(const KFrag& k, const VFrag& v, const float (&p)[4], const bool (&valid)[4],
                                      f4 (&o)[NT]) const {
     const float s = h2f(k.sc);   // value scale of key 4g + e of tile P: lane 8P + 4 + e of the row
@@ -1160,9 +1172,9 @@ __device__ __forceinline__ void run_tiles(const DecodeArgs& a, const Store& st, 
     if constexpr (FAST && Store::kSanRows) {
       // only a tile at the sweep's edge reads rows outside the key range
       if (map.tile_edge(t0)) st.sanitize(vb[slot], kvalid);
-      st.template pv<false, PS>(kb[slot], vb[slot], p, kvalid, on.o);
+      st.template pv<false, PS, MQ>(kb[slot], vb[slot], p, kvalid, on.o);
     } else {
-      st.template pv<FAST, PS>(kb[slot], vb[slot], p, kvalid, on.o);
+      st.template pv<FAST, PS, MQ>(kb[slot], vb[slot], p, kvalid, on.o);
     }
   };
 
@@ -1320,9 +1332,9 @@ __device__ __forceinline__ void run_tiles_shared(const DecodeArgs& a, const Stor
     if (on.softmax_tile(a.capl2, raw, valid, p)) on.rescale(lane);
     if constexpr (Store::kSanRows) {
       if (map.tile_edge(t0)) st.sanitize(vf, kvalid);
-      st.template pv<false>(kf, vf, p, kvalid, on.o);
+      st.template pv<false, 0, true>(kf, vf, p, kvalid, on.o);
     } else {
-      st.template pv<true>(kf, vf, p, kvalid, on.o);
+      st.template pv<true, 0, true>(kf, vf, p, kvalid, on.o);
     }
   };
 
