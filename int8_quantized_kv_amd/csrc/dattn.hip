@@ -69,6 +69,11 @@ constexpr size_t kMaxBalancedLds = 16384;
 // 1024 rows of about 10 partials the one-row-per-workgroup merge is faster.
 constexpr int64_t kRowsMinRows = 2048;
 constexpr int64_t kRowsWorkersPerSeq = 8;
+// Fewer rows whose partials are few (at most kWaveWorkersPerSeq balanced
+// workers per sequence and kv-head group): one wave per row.  Measured on the
+// combine alone: paged f16 B = 32 (about 6 partials per row) 3.79 -> 3.22 us,
+// window ring 3.84 -> 3.13 us, tiny 2.73 -> 2.51 us.
+constexpr int64_t kWaveWorkersPerSeq = 6;
 #ifndef DATTN_F16_WAVES_PER_CU
 #define DATTN_F16_WAVES_PER_CU 4
 #endif
@@ -441,6 +446,18 @@ int launch(void* split_fn, void* bal_fn, const dattn_params* p, const Plan& pl, 
         hipLaunchKernelGGL(dattn::combine_rows_kernel<128>, rgrid, dim3(256), 0, st, a.part_acc, a.part_ml, out,
                            f16, lse, pl.num_splits, nbh);
     }
+    return check_launch("combine kernel");
+  }
+  // Rows with few partials (about workers / B + 2 per row): one wave per row.
+  const bool wave = bl.on && (int64_t)bl.workers <= kWaveWorkersPerSeq * (int64_t)p->num_seqs;
+  if (wave) {
+    const dim3 wgrid((nbh + 3) / 4);
+    if (p->head_dim == 64)
+      hipLaunchKernelGGL(dattn::combine_balanced_wave_kernel<64>, wgrid, dim3(256), 0, st, a.part_acc, a.part_ml,
+                         a.sched, out, f16, lse, a.heads_out, nbh);
+    else
+      hipLaunchKernelGGL(dattn::combine_balanced_wave_kernel<128>, wgrid, dim3(256), 0, st, a.part_acc,
+                         a.part_ml, a.sched, out, f16, lse, a.heads_out, nbh);
     return check_launch("combine kernel");
   }
   if (bl.on) {

@@ -2124,6 +2124,90 @@ __global__ __launch_bounds__(256) void combine_balanced_rows_kernel(const float*
   merge_rows<D>(loc_of, n_of, out, out_f16 != 0, lse, nbh);
 }
 
+// One wave per row, for rows with few partials: the wave's 64 / (D/4) lane
+// groups (D/4 lanes of four dims each) fold the partials h, h + groups, ...
+// with a running max, four loads in flight, then the groups are merged with
+// row swaps (permlane32, and permlane16 for D = 64).  The merge of two states
+// is symmetric, so both partners end with the same bits.  No LDS, no barrier.
+template <int D, class Loc>
+__device__ __forceinline__ void merge_row_wave(const Loc& loc, int n, const OutRow out, float* __restrict__ lse_out,
+                                               int lane) {
+  static_assert(D == 64 || D == 128, "one wave per row covers D = 64 or 128");
+  constexpr int DL = D / 4;        // lanes per group
+  constexpr int NG = 64 / DL;      // groups per wave
+  constexpr int U = 4;
+  const int h = lane / DL, c = lane % DL;
+  float m = -__builtin_inff(), L = 0.f;
+  f4 o = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = h; s0 < n; s0 += NG * U) {
+    float2 v[U];
+    f4 x[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int s = s0 + NG * u;
+      v[u] = s < n ? loc.ml(s) : make_float2(-__builtin_inff(), 0.f);
+      if (s < n && out.p) x[u] = *(const f4*)(loc.acc(s) + 4 * c);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (v[u].y != 0.f) {   // skipped: empty pieces
+        const float m_new = fmaxf(m, v[u].x);
+        const float ca = fast_exp2(m - m_new), cb = fast_exp2(v[u].x - m_new);
+        L = L * ca + v[u].y * cb;
+        if (out.p) o = o * ca + x[u] * cb;
+        m = m_new;
+      }
+    }
+  }
+  auto merge = [&](auto swap) {
+    float m1, m2, l1, l2;
+    swap(m, m1, m2);
+    swap(L, l1, l2);
+    float a[4], b[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) swap(o[e], a[e], b[e]);
+    const float M = fmaxf(m1, m2);
+    const float Mu = M == -__builtin_inff() ? 0.0f : M;
+    const float ca = fast_exp2(m1 - Mu), cb = fast_exp2(m2 - Mu);
+    L = l1 * ca + l2 * cb;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = a[e] * ca + b[e] * cb;
+    m = M;
+  };
+  merge([](float x, float& a, float& b) { swap32(x, a, b); });
+  if constexpr (NG == 4) merge([](float x, float& a, float& b) { swap16(x, a, b); });
+  if (h == 0 && out.p) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) out.store(4 * c + e, L != 0.f ? o[e] / L : 0.f);
+  }
+  if (lane == 0 && lse_out) *lse_out = L != 0.f ? (m + __builtin_log2f(L)) * kLn2 : -__builtin_inff();
+}
+
+// Balanced schedule, one wave per (sequence, head) row, four rows per
+// workgroup (the partials of (b, h) found as in combine_balanced_kernel); for
+// calls whose rows have few partials.
+template <int D>
+__global__ __launch_bounds__(256) void combine_balanced_wave_kernel(const float* __restrict__ part_acc,
+                                                                    const float2* __restrict__ part_ml,
+                                                                    const int32_t* __restrict__ sched,
+                                                                    void* __restrict__ out, int out_f16,
+                                                                    float* __restrict__ lse, int H, int nbh) {
+  const int bh = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (bh >= nbh) return;
+  const int b = bh / H, h = bh - b * H;
+  const int C = sched[1];
+  const int p0 = sched[2 + b], p1 = sched[3 + b];
+  int n = 0;
+  size_t slot0 = 0;
+  if (p1 > p0 && C > 0) {
+    const int w0 = p0 / C, w1 = (p1 - 1) / C;
+    n = w1 - w0 + 1;
+    slot0 = (size_t)(w0 + b);
+  }
+  const SlotLoc loc{part_acc + (slot0 * H + h) * D, part_ml + slot0 * H + h, H, D};
+  merge_row_wave<D>(loc, n, out_row(out, out_f16 != 0, bh, D), lse ? lse + bh : nullptr, threadIdx.x & 63);
+}
+
 // Static splits with at most kShortRow splits, eight rows per workgroup.
 template <int D>
 __global__ __launch_bounds__(256) void combine_rows_kernel(const float* __restrict__ part_acc,
