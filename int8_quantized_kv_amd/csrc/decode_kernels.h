@@ -1805,24 +1805,40 @@ __global__ DATTN_BOUNDS(MQ) __attribute__((amdgpu_waves_per_eu(2))) void sparse_
   // head c % grp) pair of column c = col0 + j) selects the blocks of the CSR
   // row of its query's position in its head's layout; a query before
   // position 0 selects none.
+  // Two dependent round trips for all columns at once: lane j < ncols reads
+  // its row's bounds, then every lane reads one column index of every row per
+  // pass (rows longer than 64 entries take more passes).
   const int ncols = MQ ? min(16, a.grp * a.qn - col0) : G;
-  if (lo <= hi) {
-    for (int j = 0; j < ncols; ++j) {
-      const int c = col0 + j;
-      const int qj = MQ ? qp + c / a.grp : max(qp, 0);
-      if (qj < 0) continue;
-      const uint32_t r = fdiv((uint32_t)qj, a.sb);
-      if ((int)r + 1 >= a.row_stride) continue;
-      const int head = MQ ? kvh * a.grp + c % a.grp : kvh * G + j;
-      const int layout = head % a.num_layouts;
-      const int32_t* rp = a.row_ptr + (size_t)layout * a.row_stride;
-      const int start = max(rp[r], 0);
-      const int end = min(rp[r + 1], a.col_stride);
-      const int32_t* cols = a.col_idx + (size_t)layout * a.col_stride;
-      for (int e = start + lane; e < end; e += 64) {
-        const int c = cols[e];
-        if (c >= 0 && c <= (int)r && c < nb) atomicOr(&mask[c], 1u << j);
-      }
+  int rstart = 0, rlen = 0, rrow = 0, rlay = 0;   // lane j: column j's CSR row
+  if (lo <= hi && lane < ncols) {
+    const int c = col0 + lane;
+    const int qj = MQ ? qp + c / a.grp : max(qp, 0);
+    const uint32_t r = qj >= 0 ? fdiv((uint32_t)qj, a.sb) : 0u;
+    if (qj >= 0 && (int)r + 1 < a.row_stride) {
+      const int head = MQ ? kvh * a.grp + c % a.grp : kvh * G + lane;
+      rlay = head % a.num_layouts;
+      const int32_t* rp = a.row_ptr + (size_t)rlay * a.row_stride;
+      rstart = max(rp[r], 0);
+      rlen = max(min(rp[r + 1], a.col_stride) - rstart, 0);
+      rrow = (int)r;
+    }
+  }
+  int maxlen = rlen;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) maxlen = max(maxlen, __shfl_xor(maxlen, o, 64));
+  constexpr int kCols = MQ ? 16 : G;
+  for (int off = 0; off < maxlen; off += 64) {
+    int cj[kCols];
+#pragma unroll
+    for (int j = 0; j < kCols; ++j) {
+      const int st = __shfl(rstart, j, 64), ln = __shfl(rlen, j, 64), ly = __shfl(rlay, j, 64);
+      const int e = off + lane;
+      cj[j] = (j < ncols && e < ln) ? a.col_idx[(size_t)ly * a.col_stride + st + e] : -1;
+    }
+#pragma unroll
+    for (int j = 0; j < kCols; ++j) {
+      const int r = __shfl(rrow, j, 64);
+      if (cj[j] >= 0 && cj[j] <= r && cj[j] < nb) atomicOr(&mask[cj[j]], 1u << j);
     }
   }
   __syncthreads();
