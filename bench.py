@@ -263,16 +263,41 @@ def sample_times(r, est_us, n=SAMPLES):
 WARM_MS = 30.0   # the device's clock needs about this much busy time to settle
 
 
-def measure(case, steps, warmup, copies=None, warm_ms=0.0):
+def preheat(r, ms):
+    """About `ms` of the library's streaming-read kernel over the runner's first
+    cache tensor (the bytes the calls read, uploaded just before): the device's
+    clock settles during it, after the idle spell of the upload."""
+    import torch
+    import int8_quantized_kv_amd as dk
+    def tensors(x):
+        if isinstance(x, (list, tuple)):
+            for y in x:
+                yield from tensors(y)
+        elif isinstance(x, torch.Tensor):
+            yield x
+    src = max(tensors(r.keep), key=lambda t: t.numel() * t.element_size())
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(4):
+            dk.dattn_stream_read(src, sink)
+        torch.cuda.synchronize()
+
+
+def measure(case, steps, warmup, copies=None, warm_ms=0.0, preheat_ms=0.0):
     """Time `steps` full calls (wall clock, inputs resident), then event-timed
     split-only and combine-only calls on the same stream right after them, then
     the step-time distribution over >= SAMPLES timed calls, then graph replay.
     The `warmup` untimed calls come first; with warm_ms > 0 more untimed calls
-    follow them until about warm_ms of wall time has passed."""
+    follow them until about warm_ms of wall time has passed.  preheat_ms > 0:
+    that much of the streaming-read kernel over the uploaded cache runs before
+    the warm-up calls."""
     import torch
     if copies is None:
         copies = max(1, int(math.ceil(MALL_BYTES / max(cache_bytes(case), 1))))
     r = Runner(case, copies)
+    if preheat_ms > 0:
+        preheat(r, preheat_ms)
     for i in range(warmup):
         r.call(i, "all")
     torch.cuda.synchronize()
@@ -537,11 +562,12 @@ def parity(out, lse, ref_o, ref_l):
     return dict(rows=int(ref_l.size), max_abs_err=err, normwise_rel_err=err / max(ref, 1e-30), lse_err=lerr, ok=ok)
 
 
-def line_for(case, steps, warmup, label=None, oracle_seconds=0.0, one_thread_seqs=None, check=True, warm_ms=0.0):
+def line_for(case, steps, warmup, label=None, oracle_seconds=0.0, one_thread_seqs=None, check=True, warm_ms=0.0,
+             preheat_ms=0.0):
     """One configuration: timing, split-kernel roofline, whole-output parity and
     the oracle's own time on this host (check=False: timing only)."""
     kvb = kv_bytes(case)
-    m = measure(case, steps, warmup, warm_ms=warm_ms)
+    m = measure(case, steps, warmup, warm_ms=warm_ms, preheat_ms=preheat_ms)
     nq = case.params["num_seqs"] * max(1, case.params.get("query_len", 1))   # query tokens per call
     split_gbs = kvb / (m["split_ms"] / 1e3) / 1e9
     res = dict(config=label, workload=case.name, kv_bytes=kvb, ms_per_call=round(m["wall_s"] * 1e3, 5),
@@ -630,8 +656,11 @@ def main():
     case = config_case(args.workload, args.window, cache)
     log(f"workload {case.name}: KV bytes {kv_bytes(case)}")
     base_s = 0.0 if (args.no_cpu_baseline or args.only) else 10.0
+    # The headline's `warmup` calls follow about WARM_MS of the streaming-read kernel over the cache
+    # just uploaded: the upload leaves the device idle, and a few warm-up calls alone time the timed
+    # steps on a clock that is still ramping (2-4% slower).
     head, m = line_for(case, args.steps, args.warmup, label="headline", oracle_seconds=base_s,
-                       one_thread_seqs=ONE_THREAD_SEQS.get(args.workload), check=not args.only)
+                       one_thread_seqs=ONE_THREAD_SEQS.get(args.workload), check=not args.only, preheat_ms=WARM_MS)
     log(json.dumps(head))
     kvb = head["kv_bytes"]
     achieved = kvb / (m["split_ms"] / 1e3) / 1e9

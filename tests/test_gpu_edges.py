@@ -59,6 +59,21 @@ def test_combine_rows_with_one_long_sequence():
     compare(og.reshape(300 * H, -1)[pairs], lg.reshape(300 * H)[pairs], ro, rl, what="combine rows, long row")
 
 
+@pytest.mark.parametrize("D,B", [(128, 32), (64, 40)])
+def test_combine_wave_with_one_long_sequence(D, B):
+    # fewer than 2048 rows whose sequences meet few workers each: the combine
+    # takes one wave per row; the one long sequence's rows have far more
+    # partials than a wave folds in one round (D = 64: four lane groups)
+    rng = np.random.default_rng(715 + D)
+    lens = rng.integers(1, 65, size=B)
+    lens[B // 3] = 60000
+    c = synth.paged_case(715 + D, B, 32, 8, D, 16, lens=lens, kv_dtype=synth.F16, softcap=30.0)
+    log(f"edge combine wave, one long sequence, D={D} B={B}")
+    og, lg = DeviceCase(c).run_np()
+    ro, rl = oracle_run(c)
+    compare(og, lg, ro, rl, what=f"combine wave, long row, D={D}")
+
+
 @pytest.mark.parametrize("longest,split_tokens", [(1024, 64), (1100, 64), (1100, 128)])
 def test_combine_rows_static_splits(longest, split_tokens):
     # 72 x 32 rows: with at most 16 splits per row the static path's combine takes
