@@ -554,7 +554,7 @@ struct StoreF16 {
   // product per n-tile instead of two 16x16x16 ones -- k slots 8g + [0, 4)
   // carry p_hi and 8g + [4, 8) p_lo, each against the same four V values, and
   // on gfx950 the K = 32 product takes the cycles of a K = 16 one.  Measured:
-  // sixteen queries per sequence 79.6 -> 77.5 us; the one-query sweeps, which
+  // sixteen queries per sequence 78.3 -> 75.2 us; the one-query sweeps, which
   // wait on memory, gain nothing (and the tiered cache lost 2% at W = 4096).
   template <bool SAN, int P = 0, bool W32 = false>
   __device__ __forceinline__ void pv(const KFrag&, const VFrag& v_in, const float (&p)[4], const bool (&valid)[4],
@@ -1090,7 +1090,7 @@ struct ColRange {
     span = vhi >= vlo ? (uint32_t)(vhi - vlo) : 0u;
   }
   __device__ __forceinline__ void valid(int t0, bool (&v)[4]) const {
-    const uint32_t x = (uint32_t)(t0 + off);
+    const uint32_t x = (uint32_t)t0 + (uint32_t)off;   // modulo 2^32, as the compares expect
 #pragma unroll
     for (int e = 0; e < 4; ++e) v[e] = x + (uint32_t)e <= span;
   }
