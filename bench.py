@@ -724,6 +724,11 @@ def main():
             # a small configuration's warm-up calls alone do not settle the clock
             res, _ = line_for(c, args.steps, args.warmup, label=label, one_thread_seqs=ONE_THREAD_SEQS.get(idx),
                               warm_ms=WARM_MS)
+            # the plain streaming read at this line's KV bytes per launch: what a launch of that size reaches
+            nbl = max(res["kv_bytes"], 1 << 20) // 16 * 16
+            res["read_ceiling_gbs"] = read_reference(nbytes=nbl, copies=max(2, int(math.ceil(MALL_BYTES / nbl))),
+                                                     reps=min(2000, max(20, int(math.ceil(0.005 * 7e12 / nbl)))))
+            res["split_frac_of_read_ceiling"] = round(res["split_gbs"] / res["read_ceiling_gbs"], 4)
             log(json.dumps(res))
             lines.append(res)
             del c
