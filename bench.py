@@ -593,7 +593,8 @@ def workload(idx, window=0):
     """Workloads 1-5 of the input generators, 6: the tiered workload's shape
     with an f16 cold tier, 7: a sliding-window ring f16 cache, 8 and 9: four
     and sixteen queries per sequence over a paged f16 cache of workload 2's
-    shape, 10: four queries per sequence over the block-sparse workload."""
+    shape, 10: four queries per sequence over the block-sparse workload, 11: four
+    over the tiered int8 workload."""
     import synth
     if idx == 6:
         return synth.tiered_f16_workload(window)
@@ -605,6 +606,8 @@ def workload(idx, window=0):
         return synth.multi_query_workload(16)
     if idx == 10:
         return synth.sparse_multi_query_workload(4)
+    if idx == 11:
+        return synth.tiered_multi_query_workload(4)
     return synth.workload(idx, window=window)
 
 
@@ -632,7 +635,7 @@ def main():
                     help="headline workload index (default 4, the long-context paged f16 configuration; 1 tiny, "
                          "2 paged f16, 3 tiered int8, 5 block-sparse, 6 the tiered workload with an f16 cold tier, "
                          "7 a sliding-window ring f16 cache, 8 four queries per sequence, 9 sixteen, 10 four over "
-                         "the block-sparse cache)")
+                         "the block-sparse cache, 11 four over the tiered int8 cache)")
     ap.add_argument("--window", type=int, default=0, help="sliding window of the headline workload")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run 5 device copies of MIB MiB (for scaling memory counters)")
@@ -717,7 +720,8 @@ def main():
         todo = [(label, idx, w) for label, idx, w in CONFIGS if (idx, w) != (args.workload, args.window)]
         if args.all:
             todo += [("tiered_f16_w0", 6, 0), ("tiered_f16_w4096", 6, 4096), ("ring_f16", 7, 0),
-                     ("multi_query_4", 8, 0), ("multi_query_16", 9, 0), ("block_sparse_multi_query_4", 10, 0)]
+                     ("multi_query_4", 8, 0), ("multi_query_16", 9, 0), ("block_sparse_multi_query_4", 10, 0),
+                     ("tiered_int8_multi_query_4", 11, 0)]
         for label, idx, w in todo:
             log(f"generating workload {idx} window {w} ...")
             c = config_case(idx, w, cache)

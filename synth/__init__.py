@@ -442,6 +442,16 @@ def sparse_multi_query_workload(query_len: int = 4) -> Case:
                        name=f"sparse_f16_mq{query_len}_B8_H32x8_D128_L16384")
 
 
+def tiered_multi_query_workload(query_len: int = 4) -> Case:
+    """Multi-query decode over the tiered int8 workload's shape: B=16, 32/8 heads,
+    D=128, L=8192 = 7680 int8 cold + 512 f16 hot (ring of 512), softcap 50; the
+    last query_len tokens of each sequence are the queries."""
+    B = 16
+    return tiered_case(11, B, 32, 8, 128, 16, lens=[8192] * B, cold_lens=[7680] * B, hot_window=512,
+                       softcap=50.0, scale=float(np.float32(1.0 / math.sqrt(128))), query_len=query_len,
+                       name=f"tiered_int8_mq{query_len}_B16_H32x8_D128_L8192_cap50")
+
+
 def tiered_f16_workload(window: int = 0) -> Case:
     """The tiered workload's shape with an f16 cold tier: B=16, 32/8 heads, D=128,
     L=8192 = 7680 f16 cold (bs=16, permuted pool) + 512 f16 hot (ring of 512), softcap 50."""
