@@ -60,6 +60,8 @@ typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef short s4 __attribute__((ext_vector_type(4)));
 typedef float f2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
+typedef short s8v __attribute__((ext_vector_type(8)));
 
 constexpr int kTile = 16;          // keys per tile
 #ifndef DATTN_MAX_THREADS
@@ -764,13 +766,19 @@ struct StoreI8 {
     }
     s4 hi, lo;
     split_bf16(q, hi, lo);
+    const bf8 a = __builtin_bit_cast(bf8, __builtin_shufflevector(hi, lo, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const int w = t >> 2, byte = t & 3;
       const s4 b = pack_bf16(i8_at(word_at(v.r[0], w), byte), i8_at(word_at(v.r[1], w), byte),
                              i8_at(word_at(v.r[2], w), byte), i8_at(word_at(v.r[3], w), byte));
-      o[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(hi, b, o[t], 0, 0, 0);
-      o[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(lo, b, o[t], 0, 0, 0);
+      if constexpr (W32) {   // as StoreF16::pv: p_hi and p_lo in the two k halves of one K = 32 product
+        const s8v bb = __builtin_shufflevector(b, b, 0, 1, 2, 3, 0, 1, 2, 3);
+        o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf8, bb), o[t], 0, 0, 0);
+      } else {
+        o[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(hi, b, o[t], 0, 0, 0);
+        o[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(lo, b, o[t], 0, 0, 0);
+      }
     }
   }
 };
