@@ -61,19 +61,30 @@ constexpr int kMaxWaves = 4096;
 constexpr int kMaxQueryRows = 128;
 constexpr int kMaxBalancedSeqs = 4096;
 constexpr size_t kMaxBalancedLds = 16384;
-// The row-group combine (eight rows per workgroup) is used for calls with at
-// least kRowsMinRows output rows whose rows have few partials: at most
-// kRowsWorkersPerSeq workers per sequence and kv-head group under the
-// balanced schedule, at most 16 static splits.  Measured on multi-query
-// decode (4096 and 16384 rows): combine 11.2 -> 8.6 us and 29 -> 17 us; with
-// 1024 rows of about 10 partials the one-row-per-workgroup merge is faster.
-constexpr int64_t kRowsMinRows = 2048;
-constexpr int64_t kRowsWorkersPerSeq = 8;
-// Fewer rows whose partials are few (at most kWaveWorkersPerSeq balanced
-// workers per sequence and kv-head group): one wave per row.  Measured on the
-// combine alone: paged f16 B = 32 (about 6 partials per row) 3.79 -> 3.22 us,
-// window ring 3.84 -> 3.13 us, tiny 2.73 -> 2.51 us.
-constexpr int64_t kWaveWorkersPerSeq = 6;
+// The row-group combine (eight rows per workgroup) serves static splits: calls
+// with at least kRowsMinRows output rows and at most 16 splits per row.
+// Measured on multi-query decode (4096 and 16384 rows): combine 11.2 -> 8.6 us
+// and 29 -> 17 us against one workgroup per row.
+#ifndef DATTN_ROWS_MIN_ROWS
+#define DATTN_ROWS_MIN_ROWS 2048
+#endif
+constexpr int64_t kRowsMinRows = DATTN_ROWS_MIN_ROWS;
+// Balanced calls use one wave per row when their rows have few partials (at
+// most kWaveWorkersPerSeq workers per sequence and kv-head group), or when
+// there are at least kRowsMinRows rows with at most kWaveManyRowsWorkersPerSeq
+// workers per sequence; one workgroup per row otherwise.  Measured on the
+// combine alone: paged f16 B = 32 (about 6 partials per row) 3.79 -> 3.22 us
+// and window ring 3.84 -> 3.13 us against one workgroup per row; four queries
+// per sequence (4096 rows) 5.8 -> 4.0 us, sixteen (16384 rows) 14.0 -> 9.7 us
+// and four over the tiered int8 cache (2048 rows, about 18 partials each)
+// 5.8 -> 4.4 us against the row-group kernel.  With 512 rows of about 18
+// partials (tiered int8, one query) one workgroup per row stays faster (3.3
+// against 3.8 us): a quarter of the workgroups leaves most CUs idle.
+#ifndef DATTN_WAVE_WORKERS_PER_SEQ
+#define DATTN_WAVE_WORKERS_PER_SEQ 6
+#endif
+constexpr int64_t kWaveWorkersPerSeq = DATTN_WAVE_WORKERS_PER_SEQ;
+constexpr int64_t kWaveManyRowsWorkersPerSeq = 16;
 #ifndef DATTN_F16_WAVES_PER_CU
 #define DATTN_F16_WAVES_PER_CU 4
 #endif
@@ -423,33 +434,11 @@ int launch(void* split_fn, void* bal_fn, const dattn_params* p, const Plan& pl, 
   const int nbh = p->num_seqs * a.heads_out;
   const dim3 cgrid(nbh);   // one workgroup per (sequence, query, head)
   const int f16 = p->out_dtype == DATTN_F16;
-  // Many rows with few partials: eight rows per workgroup, 32 threads each.
-  // A sequence meets about workers / B + 2 workers of its group under the
-  // balanced schedule (more for a long sequence among short ones, which the
-  // kernel then merges with the whole workgroup).
-  const bool rows = nbh >= kRowsMinRows && (bl.on ? (int64_t)bl.workers <= kRowsWorkersPerSeq * (int64_t)p->num_seqs
-                                                  : pl.num_splits <= dattn::kShortRow);
-  if (rows) {
-    const dim3 rgrid((nbh + 7) / 8);
-    if (bl.on) {
-      if (p->head_dim == 64)
-        hipLaunchKernelGGL(dattn::combine_balanced_rows_kernel<64>, rgrid, dim3(256), 0, st, a.part_acc, a.part_ml,
-                           a.sched, out, f16, lse, a.heads_out, nbh);
-      else
-        hipLaunchKernelGGL(dattn::combine_balanced_rows_kernel<128>, rgrid, dim3(256), 0, st, a.part_acc,
-                           a.part_ml, a.sched, out, f16, lse, a.heads_out, nbh);
-    } else {
-      if (p->head_dim == 64)
-        hipLaunchKernelGGL(dattn::combine_rows_kernel<64>, rgrid, dim3(256), 0, st, a.part_acc, a.part_ml, out, f16,
-                           lse, pl.num_splits, nbh);
-      else
-        hipLaunchKernelGGL(dattn::combine_rows_kernel<128>, rgrid, dim3(256), 0, st, a.part_acc, a.part_ml, out,
-                           f16, lse, pl.num_splits, nbh);
-    }
-    return check_launch("combine kernel");
-  }
-  // Rows with few partials (about workers / B + 2 per row): one wave per row.
-  const bool wave = bl.on && (int64_t)bl.workers <= kWaveWorkersPerSeq * (int64_t)p->num_seqs;
+  // Balanced schedule: a sequence meets about workers / B + 2 workers of its
+  // group (more for a long sequence among short ones).
+  const int64_t per_seq = bl.on ? ((int64_t)bl.workers + p->num_seqs - 1) / p->num_seqs : 0;
+  const bool wave = bl.on && (per_seq <= kWaveWorkersPerSeq ||
+                              (nbh >= kRowsMinRows && per_seq <= kWaveManyRowsWorkersPerSeq));
   if (wave) {
     const dim3 wgrid((nbh + 3) / 4);
     if (p->head_dim == 64)
@@ -458,6 +447,18 @@ int launch(void* split_fn, void* bal_fn, const dattn_params* p, const Plan& pl, 
     else
       hipLaunchKernelGGL(dattn::combine_balanced_wave_kernel<128>, wgrid, dim3(256), 0, st, a.part_acc,
                          a.part_ml, a.sched, out, f16, lse, a.heads_out, nbh);
+    return check_launch("combine kernel");
+  }
+  // Static splits, many rows with few partials: eight rows per workgroup, 32
+  // threads each.
+  if (!bl.on && nbh >= kRowsMinRows && pl.num_splits <= dattn::kShortRow) {
+    const dim3 rgrid((nbh + 7) / 8);
+    if (p->head_dim == 64)
+      hipLaunchKernelGGL(dattn::combine_rows_kernel<64>, rgrid, dim3(256), 0, st, a.part_acc, a.part_ml, out, f16,
+                         lse, pl.num_splits, nbh);
+    else
+      hipLaunchKernelGGL(dattn::combine_rows_kernel<128>, rgrid, dim3(256), 0, st, a.part_acc, a.part_ml, out,
+                         f16, lse, pl.num_splits, nbh);
     return check_launch("combine kernel");
   }
   if (bl.on) {

@@ -1911,6 +1911,26 @@ struct OutRow {
     else
       ((float*)p)[d] = x;
   }
+  // Elements d .. d + 3 (d a multiple of 4): one 8- or 16-byte store when the
+  // row is aligned to it (the output's base address decides it for every row).
+  __device__ __forceinline__ void store4(int d, f4 x) const {
+    if (f16) {
+      const h4 y = {(_Float16)x[0], (_Float16)x[1], (_Float16)x[2], (_Float16)x[3]};
+      if (((uintptr_t)p & 7) == 0) {
+        *(h4*)((_Float16*)p + d) = y;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ((_Float16*)p)[d + e] = y[e];
+      }
+    } else {
+      if (((uintptr_t)p & 15) == 0) {
+        *(f4*)((float*)p + d) = x;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ((float*)p)[d + e] = x[e];
+      }
+    }
+  }
 };
 
 __device__ __forceinline__ OutRow out_row(void* out, bool f16, int bh, int D) {
@@ -2004,64 +2024,48 @@ __device__ __forceinline__ void merge_row(const Loc& loc, int n, const OutRow ou
   f4 o[NJ];
 #pragma unroll
   for (int j = 0; j < NJ; ++j) o[j] = f4{0.f, 0.f, 0.f, 0.f};
+  // Loads without branches: past the last partial a lane reloads it (weighted
+  // out below), and lanes beyond the row's dims (D = 64) reload dims 0..3.
+  const int cl = c < DC ? c : 0;
   for (int s0 = 0; s0 < n; s0 += U) {
     float2 v[U];
     f4 x[U][NJ];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int s = s0 + u;
-      v[u] = s < n ? loc.ml(s) : make_float2(-__builtin_inff(), 0.f);
-      if (s < n && c < DC && out.p) {
+      const int s = min(s0 + u, n - 1);
+      v[u] = loc.ml(s);
+      if (out.p) {
         const float* row = loc.acc(s);
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) x[u][j] = *(const f4*)(row + 128 * j + 4 * c);
+        for (int j = 0; j < NJ; ++j) x[u][j] = *(const f4*)(row + 128 * j + 4 * cl);
       }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      if (v[u].y != 0.f) {
+      if (s0 + u < n && v[u].y != 0.f) {
         const float m_new = fmaxf(m, v[u].x);
         const float ca = fast_exp2(m - m_new), cb = fast_exp2(v[u].x - m_new);
         L = L * ca + v[u].y * cb;
-        if (c < DC) {
 #pragma unroll
-          for (int j = 0; j < NJ; ++j) o[j] = o[j] * ca + x[u][j] * cb;
-        }
+        for (int j = 0; j < NJ; ++j) o[j] = o[j] * ca + x[u][j] * cb;
         m = m_new;
       }
     }
   }
   if (out.p && c < DC) {
 #pragma unroll
-    for (int j = 0; j < NJ; ++j)
+    for (int j = 0; j < NJ; ++j) {
+      f4 y;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) out.store(128 * j + 4 * c + e, L != 0.f ? o[j][e] / L : 0.f);
+      for (int e = 0; e < 4; ++e) y[e] = L != 0.f ? o[j][e] / L : 0.f;
+      out.store4(128 * j + 4 * c, y);
+    }
   }
   if (c == 0 && lse_out) *lse_out = L != 0.f ? (m + __builtin_log2f(L)) * kLn2 : -__builtin_inff();
 }
 
-// Eight rows per workgroup: a row with at most kShortRow partials is merged
-// by its own 32 threads; a longer one (a long sequence in a batch of short
-// ones) by all 256 threads afterwards, one row at a time.  n_of(row) must give
-// every thread the same count.
+// Static splits of at most kShortRow pieces per row take the row-group combine.
 constexpr int kShortRow = 16;
-template <int D, class LocOf, class NOf>
-__device__ __forceinline__ void merge_rows(const LocOf& loc_of, const NOf& n_of, void* out, bool out_f16,
-                                           float* lse, int nbh) {
-  const int tid = threadIdx.x, row0 = blockIdx.x * 8;
-  const int row = row0 + (tid >> 5);
-  if (row < nbh) {
-    const int n = n_of(row);
-    if (n <= kShortRow) merge_row<D>(loc_of(row), n, out_row(out, out_f16, row, D), lse ? lse + row : nullptr, tid & 31);
-  }
-  for (int r = row0; r < min(row0 + 8, nbh); ++r) {
-    const int n = n_of(r);
-    if (n > kShortRow) {
-      merge_partials<D>(loc_of(r), n, out_row(out, out_f16, r, D), lse ? lse + r : nullptr);
-      __syncthreads();   // the LDS of the merge is reused by the next long row
-    }
-  }
-}
 
 // Static splits: partials of (b, h) at [bh, s] for s < S.
 struct SplitLoc {
@@ -2112,42 +2116,6 @@ __global__ __launch_bounds__(256) void combine_balanced_kernel(const float* __re
   merge_partials<D>(loc, n, out_row(out, out_f16 != 0, bh, D), lse ? lse + bh : nullptr);
 }
 
-// Balanced schedule, eight rows per workgroup (the partials of (b, h) found
-// as in combine_balanced_kernel); for calls whose rows have few partials.
-template <int D>
-__global__ __launch_bounds__(256) void combine_balanced_rows_kernel(const float* __restrict__ part_acc,
-                                                                    const float2* __restrict__ part_ml,
-                                                                    const int32_t* __restrict__ sched,
-                                                                    void* __restrict__ out, int out_f16,
-                                                                    float* __restrict__ lse, int H, int nbh) {
-  const int C = sched[1];
-  auto span = [&](int bh, int& n, size_t& slot0) {
-    const int b = bh / H;
-    const int p0 = sched[2 + b], p1 = sched[3 + b];
-    n = 0;
-    slot0 = 0;
-    if (p1 > p0 && C > 0) {
-      const int w0 = p0 / C, w1 = (p1 - 1) / C;
-      n = w1 - w0 + 1;
-      slot0 = (size_t)(w0 + b);
-    }
-  };
-  auto n_of = [&](int bh) {
-    int n;
-    size_t slot0;
-    span(bh, n, slot0);
-    return n;
-  };
-  auto loc_of = [&](int bh) {
-    int n;
-    size_t slot0;
-    span(bh, n, slot0);
-    const int h = bh - (bh / H) * H;
-    return SlotLoc{part_acc + (slot0 * H + h) * D, part_ml + slot0 * H + h, H, D};
-  };
-  merge_rows<D>(loc_of, n_of, out, out_f16 != 0, lse, nbh);
-}
-
 // One wave per row, for rows with few partials: the wave's 64 / (D/4) lane
 // groups (D/4 lanes of four dims each) fold the partials h, h + groups, ...
 // with a running max, four loads in flight, then the groups are merged with
@@ -2167,14 +2135,14 @@ __device__ __forceinline__ void merge_row_wave(const Loc& loc, int n, const OutR
     float2 v[U];
     f4 x[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int s = s0 + NG * u;
-      v[u] = s < n ? loc.ml(s) : make_float2(-__builtin_inff(), 0.f);
-      if (s < n && out.p) x[u] = *(const f4*)(loc.acc(s) + 4 * c);
+    for (int u = 0; u < U; ++u) {   // past the last partial a lane reloads it, weighted out below
+      const int s = min(s0 + NG * u, n - 1);
+      v[u] = loc.ml(s);
+      if (out.p) x[u] = *(const f4*)(loc.acc(s) + 4 * c);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      if (v[u].y != 0.f) {   // skipped: empty pieces
+      if (s0 + NG * u < n && v[u].y != 0.f) {   // skipped: empty pieces
         const float m_new = fmaxf(m, v[u].x);
         const float ca = fast_exp2(m - m_new), cb = fast_exp2(v[u].x - m_new);
         L = L * ca + v[u].y * cb;
@@ -2201,8 +2169,10 @@ __device__ __forceinline__ void merge_row_wave(const Loc& loc, int n, const OutR
   merge([](float x, float& a, float& b) { swap32(x, a, b); });
   if constexpr (NG == 4) merge([](float x, float& a, float& b) { swap16(x, a, b); });
   if (h == 0 && out.p) {
+    f4 y;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) out.store(4 * c + e, L != 0.f ? o[e] / L : 0.f);
+    for (int e = 0; e < 4; ++e) y[e] = L != 0.f ? o[e] / L : 0.f;
+    out.store4(4 * c, y);
   }
   if (lane == 0 && lse_out) *lse_out = L != 0.f ? (m + __builtin_log2f(L)) * kLn2 : -__builtin_inff();
 }
@@ -2232,14 +2202,16 @@ __global__ __launch_bounds__(256) void combine_balanced_wave_kernel(const float*
   merge_row_wave<D>(loc, n, out_row(out, out_f16 != 0, bh, D), lse ? lse + bh : nullptr, threadIdx.x & 63);
 }
 
-// Static splits with at most kShortRow splits, eight rows per workgroup.
+// Static splits with at most kShortRow splits: eight rows per workgroup, each
+// merged by its own 32 threads.
 template <int D>
 __global__ __launch_bounds__(256) void combine_rows_kernel(const float* __restrict__ part_acc,
                                                            const float2* __restrict__ part_ml, void* __restrict__ out,
                                                            int out_f16, float* __restrict__ lse, int S, int nbh) {
-  auto n_of = [&](int) { return S; };
-  auto loc_of = [&](int bh) { return SplitLoc{part_acc + (size_t)bh * S * D, part_ml + (size_t)bh * S, D}; };
-  merge_rows<D>(loc_of, n_of, out, out_f16 != 0, lse, nbh);
+  const int row = blockIdx.x * 8 + (threadIdx.x >> 5);
+  if (row >= nbh) return;
+  const SplitLoc loc{part_acc + (size_t)row * S * D, part_ml + (size_t)row * S, D};
+  merge_row<D>(loc, S, out_row(out, out_f16 != 0, row, D), lse ? lse + row : nullptr, threadIdx.x & 31);
 }
 
 }  // namespace dattn

@@ -42,10 +42,10 @@ def test_many_short_sequences(B):
     _sampled(c, f"paged f16 B{B} L 1-64")
 
 
-def test_combine_rows_with_one_long_sequence():
-    # 300 sequences share the workers, so the combine takes eight rows per
-    # workgroup; the one long sequence has far more partials than a row group
-    # merges alone and is merged by the whole workgroup
+def test_combine_many_rows_with_one_long_sequence():
+    # 300 sequences share the workers, so the combine takes one wave per row;
+    # the one long sequence's rows have far more partials than a wave folds in
+    # one round
     rng = np.random.default_rng(714)
     lens = rng.integers(1, 65, size=300)
     lens[137] = 40000
@@ -72,6 +72,48 @@ def test_combine_wave_with_one_long_sequence(D, B):
     og, lg = DeviceCase(c).run_np()
     ro, rl = oracle_run(c)
     compare(og, lg, ro, rl, what=f"combine wave, long row, D={D}")
+
+
+def _combine_path_case(path):
+    """A call whose combine takes the named kernel: one wave per row (few
+    partials per row), one workgroup per row (two long sequences), the row-group
+    kernel of static splits (2304 rows, at most 8 splits each), or one workgroup
+    per row of static splits (few rows)."""
+    rng = np.random.default_rng(716)
+    if path == "wave":
+        return synth.paged_case(716, 32, 32, 8, 128, 16, lens=rng.integers(1, 600, size=32), kv_dtype=synth.F16), 0
+    if path == "workgroup":
+        return synth.paged_case(717, 2, 32, 8, 128, 16, lens=[20000, 13001], kv_dtype=synth.F16), 0
+    if path == "rows":
+        return synth.paged_case(718, 72, 32, 8, 128, 16, lens=rng.integers(0, 513, size=72), kv_dtype=synth.F16), 64
+    return synth.paged_case(719, 3, 32, 8, 64, 16, lens=[700, 1, 333], kv_dtype=synth.F16), 64
+
+
+@pytest.mark.parametrize("path", ["wave", "workgroup", "rows", "static"])
+def test_combine_outputs_off_vector_alignment(path):
+    """The combine kernels store four output elements at once only where the
+    output starts on an 8-byte (f16) or 16-byte (f32) boundary: an output one
+    element past it must hold the same bits as an aligned one, and the f16
+    output the f32 result rounded to f16."""
+    import torch
+    c, split_tokens = _combine_path_case(path)
+    dc = DeviceCase(c)
+    log(f"edge combine {path}: outputs one element off alignment")
+    o32, l32 = dc.run(split_tokens)
+    o16, _ = dc.run(split_tokens, out_dtype=torch.float16)
+    shifted = {}
+    for dt in (torch.float32, torch.float16):
+        buf = torch.full((o32.numel() + 1,), float("nan"), dtype=dt, device=o32.device)
+        view = buf[1:].view(o32.shape)
+        assert view.data_ptr() % 8 != 0
+        o, _ = dc.run(split_tokens, out=view, out_dtype=dt)
+        shifted[dt] = o
+    torch.cuda.synchronize()
+    assert torch.equal(shifted[torch.float32], o32)
+    assert torch.equal(shifted[torch.float16], o16)
+    assert torch.equal(o16, o32.to(torch.float16))
+    ro, rl = oracle_run(c)
+    compare(o32.cpu().numpy(), l32.cpu().numpy(), ro, rl, what=f"combine {path}")
 
 
 @pytest.mark.parametrize("longest,split_tokens", [(1024, 64), (1100, 64), (1100, 128)])
