@@ -85,6 +85,13 @@ constexpr int64_t kRowsMinRows = DATTN_ROWS_MIN_ROWS;
 #endif
 constexpr int64_t kWaveWorkersPerSeq = DATTN_WAVE_WORKERS_PER_SEQ;
 constexpr int64_t kWaveManyRowsWorkersPerSeq = 16;
+// At least kRowsMinRows rows and at most kHalfWorkersPerSeq workers per
+// sequence (rows of about four partials, one round of a half wave's loads):
+// 32 lanes per row, two rows per wave.  Sixteen queries per sequence (16384
+// rows, two workers per sequence) 9.7 -> 6.8 us, and 10.4 -> 9.2 us with one
+// 60000-token sequence among them; with four workers per sequence one wave per
+// row stays ahead where a long sequence makes long rows (6.2 against 9.0 us).
+constexpr int64_t kHalfWorkersPerSeq = 2;
 #ifndef DATTN_F16_WAVES_PER_CU
 #define DATTN_F16_WAVES_PER_CU 4
 #endif
@@ -439,6 +446,16 @@ int launch(void* split_fn, void* bal_fn, const dattn_params* p, const Plan& pl, 
   const int64_t per_seq = bl.on ? ((int64_t)bl.workers + p->num_seqs - 1) / p->num_seqs : 0;
   const bool wave = bl.on && (per_seq <= kWaveWorkersPerSeq ||
                               (nbh >= kRowsMinRows && per_seq <= kWaveManyRowsWorkersPerSeq));
+  if (wave && nbh >= kRowsMinRows && per_seq <= kHalfWorkersPerSeq) {
+    const dim3 hgrid((nbh + 7) / 8);
+    if (p->head_dim == 64)
+      hipLaunchKernelGGL(dattn::combine_balanced_half_kernel<64>, hgrid, dim3(256), 0, st, a.part_acc, a.part_ml,
+                         a.sched, out, f16, lse, a.heads_out, nbh);
+    else
+      hipLaunchKernelGGL(dattn::combine_balanced_half_kernel<128>, hgrid, dim3(256), 0, st, a.part_acc,
+                         a.part_ml, a.sched, out, f16, lse, a.heads_out, nbh);
+    return check_launch("combine kernel");
+  }
   if (wave) {
     const dim3 wgrid((nbh + 3) / 4);
     if (p->head_dim == 64)

@@ -2202,6 +2202,32 @@ __global__ __launch_bounds__(256) void combine_balanced_wave_kernel(const float*
   merge_row_wave<D>(loc, n, out_row(out, out_f16 != 0, bh, D), lse ? lse + bh : nullptr, threadIdx.x & 63);
 }
 
+// Balanced schedule, two rows per wave (eight per workgroup), each merged by
+// its own 32 lanes (the partials of (b, h) found as in combine_balanced_kernel);
+// for many rows of about four partials or fewer, which one round of loads
+// covers.
+template <int D>
+__global__ __launch_bounds__(256) void combine_balanced_half_kernel(const float* __restrict__ part_acc,
+                                                                    const float2* __restrict__ part_ml,
+                                                                    const int32_t* __restrict__ sched,
+                                                                    void* __restrict__ out, int out_f16,
+                                                                    float* __restrict__ lse, int H, int nbh) {
+  const int bh = blockIdx.x * 8 + (threadIdx.x >> 5);
+  if (bh >= nbh) return;
+  const int b = bh / H, h = bh - b * H;
+  const int C = sched[1];
+  const int p0 = sched[2 + b], p1 = sched[3 + b];
+  int n = 0;
+  size_t slot0 = 0;
+  if (p1 > p0 && C > 0) {
+    const int w0 = p0 / C, w1 = (p1 - 1) / C;
+    n = w1 - w0 + 1;
+    slot0 = (size_t)(w0 + b);
+  }
+  const SlotLoc loc{part_acc + (slot0 * H + h) * D, part_ml + slot0 * H + h, H, D};
+  merge_row<D>(loc, n, out_row(out, out_f16 != 0, bh, D), lse ? lse + bh : nullptr, threadIdx.x & 31);
+}
+
 // Static splits with at most kShortRow splits: eight rows per workgroup, each
 // merged by its own 32 threads.
 template <int D>

@@ -43,9 +43,9 @@ def test_many_short_sequences(B):
 
 
 def test_combine_many_rows_with_one_long_sequence():
-    # 300 sequences share the workers, so the combine takes one wave per row;
-    # the one long sequence's rows have far more partials than a wave folds in
-    # one round
+    # 300 sequences share the workers, so the combine takes half a wave per
+    # row; the one long sequence's rows have far more partials than 32 lanes
+    # fold in one round
     rng = np.random.default_rng(714)
     lens = rng.integers(1, 65, size=300)
     lens[137] = 40000
@@ -76,10 +76,14 @@ def test_combine_wave_with_one_long_sequence(D, B):
 
 def _combine_path_case(path):
     """A call whose combine takes the named kernel: one wave per row (few
-    partials per row), one workgroup per row (two long sequences), the row-group
-    kernel of static splits (2304 rows, at most 8 splits each), or one workgroup
-    per row of static splits (few rows)."""
+    partials per row), half a wave per row (16384 rows of sixteen queries, about
+    two workers per sequence, D = 64), one workgroup per row (two long
+    sequences), the row-group kernel of static splits (2304 rows, at most 8
+    splits each), or one workgroup per row of static splits (few rows)."""
     rng = np.random.default_rng(716)
+    if path == "half":
+        return synth.paged_case(720, 32, 32, 8, 64, 16, lens=rng.integers(16, 301, size=32), kv_dtype=synth.F16,
+                                query_len=16), 0
     if path == "wave":
         return synth.paged_case(716, 32, 32, 8, 128, 16, lens=rng.integers(1, 600, size=32), kv_dtype=synth.F16), 0
     if path == "workgroup":
@@ -89,7 +93,7 @@ def _combine_path_case(path):
     return synth.paged_case(719, 3, 32, 8, 64, 16, lens=[700, 1, 333], kv_dtype=synth.F16), 64
 
 
-@pytest.mark.parametrize("path", ["wave", "workgroup", "rows", "static"])
+@pytest.mark.parametrize("path", ["wave", "half", "workgroup", "rows", "static"])
 def test_combine_outputs_off_vector_alignment(path):
     """The combine kernels store four output elements at once only where the
     output starts on an 8-byte (f16) or 16-byte (f32) boundary: an output one
