@@ -205,12 +205,13 @@ __device__ __forceinline__ float h2f(uint16_t bits) { return (float)__builtin_bi
 // p = hi + lo with hi, lo in f16 (about 22 significant bits while p stays in
 // f16 range; p <= 2^8 here).
 __device__ __forceinline__ void split_f16(const float (&p)[4], h4& hi, h4& lo) {
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const _Float16 h = (_Float16)p[e];
-    hi[e] = h;
-    lo[e] = (_Float16)(p[e] - (float)h);
-  }
+  // pairs converted at once (round to nearest even, as one at a time)
+  const h2 h01 = __builtin_convertvector(f2{p[0], p[1]}, h2);
+  const h2 h23 = __builtin_convertvector(f2{p[2], p[3]}, h2);
+  const h2 l01 = __builtin_convertvector(f2{p[0] - (float)h01[0], p[1] - (float)h01[1]}, h2);
+  const h2 l23 = __builtin_convertvector(f2{p[2] - (float)h23[0], p[3] - (float)h23[1]}, h2);
+  hi = __builtin_shufflevector(h01, h23, 0, 1, 2, 3);
+  lo = __builtin_shufflevector(l01, l23, 0, 1, 2, 3);
 }
 
 // Four floats rounded to bf16 (round to nearest even), as an MFMA operand.
