@@ -59,7 +59,7 @@ class Step:
         p = synth.paged_case(602, 4, 32, 8, 128, 16, lens=[700, 90, 1500, 3], query_len=2)
         self.p = {k: _dev(getattr(p, k)) for k in ("q", "k_cache", "v_cache", "block_table", "seq_lens")}
         # sixteen queries per sequence: row-block waves sharing tiles through LDS, and the
-        # eight-rows-per-workgroup combine (8 x 16 x 32 rows)
+        # one-wave-per-row combine (8 x 16 x 32 rows, eight workers per sequence)
         w = synth.paged_case(603, 8, 32, 8, 128, 16, lens=[900, 40, 1300, 17, 600, 2000, 256, 5], query_len=16)
         self.w = {k: _dev(getattr(w, k)) for k in ("q", "k_cache", "v_cache", "block_table", "seq_lens")}
         self.out_w = torch.empty((8, 16, 32, 128), dtype=torch.float32, device="cuda")
