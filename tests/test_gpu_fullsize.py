@@ -18,13 +18,14 @@ pytestmark = pytest.mark.gpu
 
 WORKLOADS = [(1, {}), (2, {}), (3, {"window": 0}), (3, {"window": 4096}), (4, {}), (5, {})]
 # the tiered workload's shape with an f16 cold tier (both windows), the window ring, four and sixteen queries
-# per sequence, four queries over the block-sparse cache
+# per sequence, four queries over the block-sparse cache and over the tiered int8 cache
 EXTRA = {"tiered_f16_w0": lambda: synth.tiered_f16_workload(0),
          "tiered_f16_w4096": lambda: synth.tiered_f16_workload(4096),
          "ring": synth.ring_workload,
          "multi_query": lambda: synth.multi_query_workload(4),
          "multi_query_16": lambda: synth.multi_query_workload(16),
-         "sparse_multi_query": lambda: synth.sparse_multi_query_workload(4)}
+         "sparse_multi_query": lambda: synth.sparse_multi_query_workload(4),
+         "tiered_int8_multi_query": lambda: synth.tiered_multi_query_workload(4)}
 
 
 @pytest.fixture(scope="module", autouse=True)
