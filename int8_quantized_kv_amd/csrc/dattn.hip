@@ -77,7 +77,9 @@ constexpr int64_t kRowsMinRows = DATTN_ROWS_MIN_ROWS;
 // and window ring 3.84 -> 3.13 us against one workgroup per row; four queries
 // per sequence (4096 rows) 5.8 -> 4.0 us, sixteen (16384 rows) 14.0 -> 9.7 us
 // and four over the tiered int8 cache (2048 rows, about 18 partials each)
-// 5.8 -> 4.4 us against the row-group kernel.  With 512 rows of about 18
+// 5.8 -> 4.4 us against eight rows per workgroup with the long rows merged
+// afterwards by the whole workgroup (slower even with no long row, and 17 us
+// with long ones, merged one row at a time).  With 512 rows of about 18
 // partials (tiered int8, one query) one workgroup per row stays faster (3.3
 // against 3.8 us): a quarter of the workgroups leaves most CUs idle.
 #ifndef DATTN_WAVE_WORKERS_PER_SEQ

@@ -2096,6 +2096,24 @@ struct SlotLoc {
   __device__ __forceinline__ const float* acc(int s) const { return acc0 + (size_t)s * H * D; }
 };
 
+// Row bh = (b, h): its n partials from the schedule (C units per worker, the
+// unit prefix P at sched[2 ..]): workers w0 .. w1 meet sequence b, and their
+// pieces of it sit in slots w0 + b .. w1 + b.
+__device__ __forceinline__ SlotLoc balanced_row(const float* part_acc, const float2* part_ml,
+                                                const int32_t* __restrict__ sched, int H, int D, int bh, int& n) {
+  const int b = bh / H, h = bh - b * H;
+  const int C = sched[1];
+  const int p0 = sched[2 + b], p1 = sched[3 + b];
+  n = 0;
+  size_t slot0 = 0;
+  if (p1 > p0 && C > 0) {
+    const int w0 = p0 / C, w1 = (p1 - 1) / C;
+    n = w1 - w0 + 1;
+    slot0 = (size_t)(w0 + b);
+  }
+  return SlotLoc{part_acc + (slot0 * H + h) * D, part_ml + slot0 * H + h, H, D};
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void combine_balanced_kernel(const float* __restrict__ part_acc,
                                                                const float2* __restrict__ part_ml,
@@ -2103,17 +2121,8 @@ __global__ __launch_bounds__(256) void combine_balanced_kernel(const float* __re
                                                                void* __restrict__ out, int out_f16,
                                                                float* __restrict__ lse, int H, int nbh) {
   const int bh = blockIdx.x;
-  const int b = bh / H, h = bh - b * H;
-  const int C = sched[1];
-  const int p0 = sched[2 + b], p1 = sched[3 + b];
-  int n = 0;
-  size_t slot0 = 0;
-  if (p1 > p0 && C > 0) {
-    const int w0 = p0 / C, w1 = (p1 - 1) / C;
-    n = w1 - w0 + 1;
-    slot0 = (size_t)(w0 + b);
-  }
-  const SlotLoc loc{part_acc + (slot0 * H + h) * D, part_ml + slot0 * H + h, H, D};
+  int n;
+  const SlotLoc loc = balanced_row(part_acc, part_ml, sched, H, D, bh, n);
   merge_partials<D>(loc, n, out_row(out, out_f16 != 0, bh, D), lse ? lse + bh : nullptr);
 }
 
@@ -2179,8 +2188,7 @@ __device__ __forceinline__ void merge_row_wave(const Loc& loc, int n, const OutR
 }
 
 // Balanced schedule, one wave per (sequence, head) row, four rows per
-// workgroup (the partials of (b, h) found as in combine_balanced_kernel); for
-// calls whose rows have few partials.
+// workgroup; for calls whose rows have few partials.
 template <int D>
 __global__ __launch_bounds__(256) void combine_balanced_wave_kernel(const float* __restrict__ part_acc,
                                                                     const float2* __restrict__ part_ml,
@@ -2189,24 +2197,14 @@ __global__ __launch_bounds__(256) void combine_balanced_wave_kernel(const float*
                                                                     float* __restrict__ lse, int H, int nbh) {
   const int bh = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (bh >= nbh) return;
-  const int b = bh / H, h = bh - b * H;
-  const int C = sched[1];
-  const int p0 = sched[2 + b], p1 = sched[3 + b];
-  int n = 0;
-  size_t slot0 = 0;
-  if (p1 > p0 && C > 0) {
-    const int w0 = p0 / C, w1 = (p1 - 1) / C;
-    n = w1 - w0 + 1;
-    slot0 = (size_t)(w0 + b);
-  }
-  const SlotLoc loc{part_acc + (slot0 * H + h) * D, part_ml + slot0 * H + h, H, D};
+  int n;
+  const SlotLoc loc = balanced_row(part_acc, part_ml, sched, H, D, bh, n);
   merge_row_wave<D>(loc, n, out_row(out, out_f16 != 0, bh, D), lse ? lse + bh : nullptr, threadIdx.x & 63);
 }
 
 // Balanced schedule, two rows per wave (eight per workgroup), each merged by
-// its own 32 lanes (the partials of (b, h) found as in combine_balanced_kernel);
-// for many rows of about four partials or fewer, which one round of loads
-// covers.
+// its own 32 lanes; for many rows of about four partials or fewer, which one
+// round of loads covers.
 template <int D>
 __global__ __launch_bounds__(256) void combine_balanced_half_kernel(const float* __restrict__ part_acc,
                                                                     const float2* __restrict__ part_ml,
@@ -2215,17 +2213,8 @@ __global__ __launch_bounds__(256) void combine_balanced_half_kernel(const float*
                                                                     float* __restrict__ lse, int H, int nbh) {
   const int bh = blockIdx.x * 8 + (threadIdx.x >> 5);
   if (bh >= nbh) return;
-  const int b = bh / H, h = bh - b * H;
-  const int C = sched[1];
-  const int p0 = sched[2 + b], p1 = sched[3 + b];
-  int n = 0;
-  size_t slot0 = 0;
-  if (p1 > p0 && C > 0) {
-    const int w0 = p0 / C, w1 = (p1 - 1) / C;
-    n = w1 - w0 + 1;
-    slot0 = (size_t)(w0 + b);
-  }
-  const SlotLoc loc{part_acc + (slot0 * H + h) * D, part_ml + slot0 * H + h, H, D};
+  int n;
+  const SlotLoc loc = balanced_row(part_acc, part_ml, sched, H, D, bh, n);
   merge_row<D>(loc, n, out_row(out, out_f16 != 0, bh, D), lse ? lse + bh : nullptr, threadIdx.x & 31);
 }
 
