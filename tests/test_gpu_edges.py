@@ -98,13 +98,16 @@ def test_combine_outputs_off_vector_alignment(path):
     """The combine kernels store four output elements at once only where the
     output starts on an 8-byte (f16) or 16-byte (f32) boundary: an output one
     element past it must hold the same bits as an aligned one, and the f16
-    output the f32 result rounded to f16."""
+    output the f32 result rounded to f16.  Without an output (lse only) the
+    lse is the same."""
     import torch
     c, split_tokens = _combine_path_case(path)
     dc = DeviceCase(c)
-    log(f"edge combine {path}: outputs one element off alignment")
+    log(f"edge combine {path}: outputs one element off alignment, and lse only")
     o32, l32 = dc.run(split_tokens)
     o16, _ = dc.run(split_tokens, out_dtype=torch.float16)
+    o_none, l_only = dc.run(split_tokens, want_out=False)
+    assert o_none is None
     shifted = {}
     for dt in (torch.float32, torch.float16):
         buf = torch.full((o32.numel() + 1,), float("nan"), dtype=dt, device=o32.device)
@@ -116,6 +119,7 @@ def test_combine_outputs_off_vector_alignment(path):
     assert torch.equal(shifted[torch.float32], o32)
     assert torch.equal(shifted[torch.float16], o16)
     assert torch.equal(o16, o32.to(torch.float16))
+    assert torch.equal(l_only, l32)
     ro, rl = oracle_run(c)
     compare(o32.cpu().numpy(), l32.cpu().numpy(), ro, rl, what=f"combine {path}")
 
